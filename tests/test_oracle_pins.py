@@ -1,0 +1,505 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something it does not compute itself:
+values printed on the pages (tests/golden), closed forms, brute force on
+tiny inputs, hand-worked examples, invariants the method guarantees, and
+special cases that reduce to a plain library routine.
+
+Citations:
+  [AH17]  "Sparse Communication for Distributed Gradient Descent" (Aji & Heafield)
+  [AHB19] "Combining Global Sparse Gradients with Local Gradients in Distributed
+          Neural Network Training" (Aji, Heafield & Bogoychev)
+  [SBC]   "Sparse Binary Compression: Towards Distributed Deep Learning with
+          minimal Communication" (Sattler et al.)
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = float(v)
+    return vals
+
+
+# ---------------------------------------------------------------- keep count
+def test_keep_count_flat_1m_workload(orc):
+    # The flat 2^20-element workload is specified at drop ratio 99% with k = 10486.
+    assert orc.keep_count(1 << 20, 10000) == 10486
+
+
+@pytest.mark.parametrize("n", [1, 7, 10, 64, 100, 999, 1000, 1001, 4096, 2359296, (1 << 31) - 1])
+@pytest.mark.parametrize("ppm", [0, 1, 1000, 10000, 250000, 999999, 1000000])
+def test_keep_count_is_smallest_k_reaching_fraction(orc, n, ppm):
+    # [AH17] Abstract / [SBC] Sparse Binarization: keep (at least) the fraction p.
+    # k is the least integer with k/n >= ppm/1e6, never more than n.
+    k = orc.keep_count(n, ppm)
+    assert 0 <= k <= n
+    assert Fraction(k, n) >= Fraction(ppm, 10**6)
+    if k > 0:
+        assert Fraction(k - 1, n) < Fraction(ppm, 10**6)
+
+
+def test_keep_count_small_tensors_keep_one(orc):
+    # A 64-element BN vector at top-0.1% still sends its largest entry.
+    assert orc.keep_count(64, 1000) == 1
+    # 1 - 0.99 is not exactly 0.01 in binary floating point; integers avoid k = 2 at n = 100.
+    assert orc.keep_count(100, 10000) == 1
+
+
+# ------------------------------------------------------------- Rice lengths
+def test_rice_mean_bits_matches_page(orc):
+    # [SBC] §II Optimal Position Encoding prints 8.38 bits and x1.9 vs 16 bits at p = 0.01.
+    gold = read_golden("rice_bits_p001.txt")
+    e7 = orc.rice_expected_bits(7, gold["p"])
+    assert round(e7, 2) == gold["mean_bits"]
+    assert round(16.0 / e7, 1) == gold["ratio_vs_16bit"]
+
+
+@pytest.mark.parametrize("b,p", [(0, 0.5), (3, 0.1), (6, 0.01), (7, 0.01), (9, 0.001), (2, 0.9)])
+def test_rice_expected_bits_equals_series(orc, b, p):
+    # Direct sum over the geometric gap law P(z) = (1-p)^z p of the code length b + 1 + floor(z/2^b).
+    total, z, mass = 0.0, 0, 0.0
+    while mass < 1 - 1e-15 and z < 10_000_000:
+        pz = (1 - p) ** z * p
+        total += pz * (b + 1 + (z >> b))
+        mass += pz
+        z += 1
+    assert orc.rice_expected_bits(b, p) == pytest.approx(total, rel=1e-9)
+
+
+def test_rice_param_argmin(orc):
+    assert orc.rice_param(0.01) == 6
+    assert orc.rice_param(0.001) == 9
+    # [SBC] §I: dense updates need no position bits; with every element present all gaps are 0.
+    assert orc.rice_param(1.0) == 0
+    assert orc.rice_expected_bits(0, 1.0) == 1.0
+
+
+def test_rice_measured_bits_page_value(orc):
+    # Encode Bernoulli(0.01) positions with b = 7 and compare the mean code length with the page's 8.38.
+    rng = np.random.default_rng(7)
+    n = 4_000_000
+    pos = np.flatnonzero(rng.random(n) < 0.01).astype(np.int32)
+    counts = np.array([pos.size, pos.size], np.int64)
+    enc = orc.encode(pos, counts, [0, n], orc.GLOBAL, 7)
+    mean_bits = int(enc.nbits[0]) / pos.size
+    # std of one code length ~ sqrt(q)/(1-q) (geometric unary part); 4 sigma band
+    q = (1 - 0.01) ** 128
+    sigma = math.sqrt(q) / (1 - q) / math.sqrt(pos.size)
+    assert abs(mean_bits - 8.38) < 4 * sigma + 0.005
+
+
+# ------------------------------------------------------- exact selection
+vec = st.lists(st.sampled_from([0.0, -0.0, 0.5, -0.5, 0.25, -0.25, 1.0, -1.0, 3.0, -2.0, 1e-40, -1e-40]),
+               min_size=0, max_size=14)
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(g=vec, rv=vec, ppm=st.sampled_from([0, 1, 100000, 250000, 500000, 999999, 1000000]),
+       cuts=st.lists(st.integers(0, 14), max_size=3), scope=st.sampled_from([0, 1]))
+def test_exact_select_matches_rank_count(orc, g, rv, ppm, cuts, scope):
+    n = min(len(g), len(rv))
+    g = np.array(g[:n], np.float32)
+    r = np.array(rv[:n], np.float32)
+    bounds = sorted({0, n} | {c for c in cuts if c <= n})
+    seg_off = np.array(bounds if len(bounds) > 1 else [0, n], np.int64)
+    acc = (r + g).astype(np.float32)          # numpy fp32 add is IEEE round-to-nearest-even
+    groups = [(0, n)] if scope == 0 else [(int(seg_off[t]), int(seg_off[t + 1])) for t in range(len(seg_off) - 1)]
+    want = []
+    for lo, hi in groups:
+        k = bf.ceil_frac((hi - lo) * ppm, 10**6)
+        want += bf.kept_by_rank(acc, lo, hi, k)
+    want = sorted(want)
+    r2 = r.copy()
+    sp = orc.compress_exact(g, r2, seg_off, scope, ppm)
+    assert sp.idx.tolist() == want
+    assert sp.val.view(np.uint32).tolist() == acc[want].view(np.uint32).tolist()
+    expect_r = acc.copy()
+    expect_r[want] = 0.0
+    assert r2.view(np.uint32).tolist() == expect_r.view(np.uint32).tolist()
+    for t in range(len(seg_off) - 1):
+        assert sp.counts[t] == sum(1 for i in want if seg_off[t] <= i < seg_off[t + 1])
+    assert sp.counts[-1] == len(want)
+
+
+def test_worked_example_topk(orc):
+    # acc = [0.5, -0.5, 0.25, -1.0, 0.5, 0.0], k = 3: -1.0 first, then the 0.5-magnitude tie
+    # is won by indices 0 and 1 over 4 (lower index wins).
+    acc = np.array([0.5, -0.5, 0.25, -1.0, 0.5, 0.0], np.float32)
+    r = np.zeros(6, np.float32)
+    sp = orc.compress_exact(acc, r, [0, 6], orc.GLOBAL, 500000)   # 50% of 6 = 3
+    assert sp.idx.tolist() == [0, 1, 3]
+    assert sp.val.tolist() == [0.5, -0.5, -1.0]
+    assert r.tolist() == [0.0, 0.0, 0.25, 0.0, 0.5, 0.0]
+
+
+def test_exact_invariants_flat_1m(orc):
+    import workloads as W
+    w = W.FLAT_1M
+    r = np.zeros(w.numel, np.float32)
+    k = orc.keep_count(w.numel, w.keep_ppm)
+    for step in range(w.steps):
+        g = W.gradient(w, 0, step).numpy()
+        acc = (r + g).astype(np.float32)
+        sp = orc.compress_exact(g, r, w.seg_off, w.scope, w.keep_ppm)
+        assert sp.idx.size == k == sp.counts[-1]
+        assert np.all(np.diff(sp.idx) > 0)
+        kept = np.zeros(w.numel, bool)
+        kept[sp.idx] = True
+        mk = np.abs(acc[kept]).min()
+        md = np.abs(acc[~kept]).max()
+        assert mk >= md
+        if mk == md:   # ties at the threshold go to the lower indices
+            assert np.flatnonzero(kept & (np.abs(acc) == mk)).max() < np.flatnonzero(~kept & (np.abs(acc) == md)).min()
+        # residual + sent == acc, bitwise
+        rebuilt = r.copy()
+        rebuilt[sp.idx] = rebuilt[sp.idx] + sp.val
+        assert np.array_equal(rebuilt.view(np.uint32), acc.view(np.uint32))
+        assert np.all(r[sp.idx].view(np.uint32) == 0)
+
+
+def test_resume_equals_straight_run(orc, tmp_path):
+    # The only state carried between steps is the residual: save/restore it mid-run.
+    import workloads as W
+    w = W.FLAT_1M
+    gs = [W.gradient(w, 0, s, numel=65536).numpy() for s in range(3)]
+    r1 = np.zeros(65536, np.float32)
+    outs1 = [orc.compress_exact(g, r1, [0, 65536], 0, 10000) for g in gs]
+    r2 = np.zeros(65536, np.float32)
+    outs2 = [orc.compress_exact(g, r2, [0, 65536], 0, 10000) for g in gs[:2]]
+    np.save(tmp_path / "res.npy", r2)
+    r3 = np.load(tmp_path / "res.npy")
+    outs2.append(orc.compress_exact(gs[2], r3, [0, 65536], 0, 10000))
+    assert np.array_equal(r1.view(np.uint32), r3.view(np.uint32))
+    for a, b in zip(outs1, outs2):
+        assert np.array_equal(a.idx, b.idx) and np.array_equal(a.val.view(np.uint32), b.val.view(np.uint32))
+
+
+def test_delay_one_is_plain_step_and_delay_two_sums(orc):
+    # [SBC] §II Communication Delay: n = 1 is regular DSGD; with n = 2 the first draw is
+    # only accumulated, so the exchange sees fp32(g1 + g2).
+    rng = np.random.default_rng(3)
+    g1 = rng.laplace(0, 1e-3, 5000).astype(np.float32)
+    g2 = rng.laplace(0, 1e-3, 5000).astype(np.float32)
+    r = np.zeros(5000, np.float32)
+    orc.accumulate(g1, r)
+    assert np.array_equal(r, g1)
+    sp = orc.compress_exact(g2, r, [0, 5000], 0, 10000)
+    r_ref = np.zeros(5000, np.float32)
+    sp_ref = orc.compress_exact((g1 + g2).astype(np.float32), r_ref, [0, 5000], 0, 10000)
+    assert np.array_equal(sp.idx, sp_ref.idx) and np.array_equal(sp.val, sp_ref.val)
+    assert np.array_equal(r, r_ref)
+
+
+# ------------------------------------------------------------ sampled mode
+def test_sampled_full_sample_is_superlevel_set(orc):
+    rng = np.random.default_rng(11)
+    n = 20000
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    g[100:140] = 0.003          # ties, some of which straddle the threshold
+    r0 = np.zeros(n, np.float32)
+    k = orc.keep_count(n, 10000)
+    # sample_min >= n -> every element is sampled: T is the k-th largest |acc|
+    r = r0.copy()
+    sp = orc.compress_sampled(g, r, [0, n], 0, 10000, cap=n, sample_div=1, sample_min=n)
+    T = np.sort(np.abs(g))[::-1][k - 1]
+    assert sp.idx.tolist() == np.flatnonzero(np.abs(g) >= T).tolist()
+    re = r0.copy()
+    ex = orc.compress_exact(g, re, [0, n], 0, 10000)
+    assert set(ex.idx.tolist()) <= set(sp.idx.tolist())
+
+
+def test_sampled_count_within_binomial_band(orc):
+    rng = np.random.default_rng(5)
+    n = 1 << 21
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    r = np.zeros(n, np.float32)
+    sp = orc.compress_sampled(g, r, [0, n], 0, 10000, cap=n)
+    kept = np.zeros(n, bool)
+    kept[sp.idx] = True
+    assert np.abs(g[kept]).min() > np.abs(g[~kept]).max()    # superlevel set
+    s = orc.sample_count(n)
+    p = 0.01
+    rel_sigma = math.sqrt((1 - p) / (s * p))
+    assert abs(sp.idx.size / (n * p) - 1) < 5 * rel_sigma + 2.0 / (s * p)
+
+
+def test_sampled_truncation_keeps_residual(orc):
+    rng = np.random.default_rng(9)
+    n = 10000
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    r = np.zeros(n, np.float32)
+    full = orc.compress_sampled(g, r.copy(), [0, n], 0, 100000, cap=n, sample_min=n)
+    cap = full.idx.size // 2
+    r2 = np.zeros(n, np.float32)
+    sp = orc.compress_sampled(g, r2, [0, n], 0, 100000, cap=cap, sample_min=n)
+    assert sp.status & orc.STATUS_TRUNCATED
+    assert sp.idx.tolist() == full.idx[:cap].tolist()
+    rest = full.idx[cap:]
+    assert np.array_equal(r2[rest], g[rest])
+    assert np.all(r2[sp.idx] == 0)
+
+
+# -------------------------------------------------------------- binarize
+def _w1_sparse(orc):
+    acc = np.array([0.5, -0.5, 0.25, -1.0, 0.5, 0.0], np.float32)
+    r = np.zeros(6, np.float32)
+    sp = orc.compress_exact(acc, r, [0, 6], orc.GLOBAL, 500000)
+    return sp, r
+
+
+def test_worked_example_sbc(orc):
+    # Kept values 0.5 | -0.5, -1.0: mean+ = 0.5, mean- = 0.75 -> the negative side is sent
+    # as one mean -0.75 ([SBC] §II Sparse Binarization), the rest returns to the residual.
+    sp, r = _w1_sparse(orc)
+    out = orc.binarize(sp, 1, orc.BIN_SBC, r)
+    assert out.idx.tolist() == [1, 3]
+    assert out.means.tolist() == [-0.75]
+    assert out.counts.tolist() == [2, 2]
+    assert r.tolist() == [0.5, 0.25, 0.25, -0.25, 0.5, 0.0]
+
+
+def test_worked_example_2bit(orc):
+    sp, r = _w1_sparse(orc)
+    out = orc.binarize(sp, 1, orc.BIN_2BIT, r)
+    codes = [(int(out.codes[0]) >> (2 * j)) & 3 for j in range(3)]
+    assert codes == [1, 2, 2]
+    assert out.means.tolist() == [0.5, -0.75]
+    assert r.tolist() == [0.0, 0.25, 0.25, -0.25, 0.5, 0.0]
+
+
+@settings(max_examples=150, deadline=None)
+@given(vals=st.lists(st.floats(-4, 4, allow_nan=False, width=32), min_size=1, max_size=40),
+       cut=st.integers(0, 40))
+def test_sbc_means_are_exact_projections(orc, vals, cut):
+    # The sent mean is the least-squares single value of its side ([SBC] appendix C projection):
+    # compare with the exact rational mean rounded to fp32; the chosen side has the larger |mean|.
+    v = np.array(vals, np.float32)
+    n = v.size
+    cut = min(cut, n)
+    seg_off = np.array([0, cut, n], np.int64)
+    sp = type("S", (), {})()
+    sp.idx = np.arange(n, dtype=np.int32)
+    sp.val = v
+    sp.counts = np.array([cut, n - cut, n], np.int64)
+    r = np.zeros(n, np.float32)
+    out = orc.binarize(sp, 2, orc.BIN_SBC, r)
+    e0 = 0
+    for t in range(2):
+        seg = v[seg_off[t]:seg_off[t + 1]]
+        pos, neg = seg[seg > 0], seg[seg < 0]
+        mp = float(np.float32(float(bf.exact_mean(pos)))) if pos.size else 0.0
+        mn = float(np.float32(float(bf.exact_mean(-neg)))) if neg.size else 0.0
+        sent = out.idx[e0:e0 + out.counts[t]]
+        e0 += out.counts[t]
+        if pos.size == 0 and neg.size == 0:
+            assert sent.size == 0 and out.means[t] == 0
+            continue
+        m = float(out.means[t])
+        side_pos = m > 0 or (m == 0 and pos.size > 0)
+        exp = mp if side_pos else mn
+        assert abs(abs(m) - exp) <= bf.ulp32(exp)
+        other = mn if side_pos else mp
+        assert abs(m) >= other - 2 * bf.ulp32(max(other, 1e-30))
+        want_idx = seg_off[t] + np.flatnonzero(seg > 0 if side_pos else seg < 0)
+        assert sent.tolist() == want_idx.tolist()
+        # residuals: sent entries keep v - mean, the others get v back
+        for i in range(seg_off[t], seg_off[t + 1]):
+            want = np.float32(v[i] - np.float32(m)) if i in set(want_idx.tolist()) else v[i]
+            assert r[i].view(np.uint32) == np.float32(want).view(np.uint32)
+        # projection: the residual of the sent side sums to ~0
+        if want_idx.size:
+            res = sum(Fraction(float(v[i])) for i in want_idx) - want_idx.size * Fraction(m)
+            assert abs(float(res)) <= want_idx.size * bf.ulp32(abs(m)) + 1e-30
+
+
+# ------------------------------------------------------------------- Rice
+def test_worked_example_rice_b2(orc):
+    # positions [0, 5, 6, 20] -> gaps [0, 4, 0, 13]; b = 2 codes 000|1000|000|111010
+    enc = orc.encode(np.array([0, 5, 6, 20], np.int32), np.array([4, 4], np.int64), [0, 32], orc.GLOBAL, 2)
+    assert int(enc.nbits[0]) == 16
+    assert enc.words.tolist() == [0x00005C08]
+    assert enc.chunk_off.tolist() == [0]
+
+
+def test_worked_example_rice_b3(orc):
+    # positions [3, 40] -> gaps [3, 36]; b = 3 codes 0110|11110001
+    enc = orc.encode(np.array([3, 40], np.int32), np.array([2, 2], np.int64), [0, 64], orc.GLOBAL, 3)
+    assert int(enc.nbits[0]) == 12
+    assert enc.words.tolist() == [0x000008F6]
+
+
+@settings(max_examples=200, deadline=None)
+@given(data=st.data(), b=st.integers(0, 9), nseg=st.integers(1, 4), scope=st.sampled_from([0, 1]))
+def test_rice_matches_bit_strings(orc, data, b, nseg, scope):
+    sizes = [data.draw(st.integers(0, 700)) for _ in range(nseg)]
+    seg_off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(seg_off[-1])
+    sel = sorted(data.draw(st.sets(st.integers(0, max(n - 1, 0)), max_size=min(n, 300)))) if n else []
+    idx = np.array(sel, np.int32)
+    counts = np.array([sum(1 for i in sel if seg_off[t] <= i < seg_off[t + 1]) for t in range(nseg)] + [len(sel)],
+                      np.int64)
+    enc = orc.encode(idx, counts, seg_off, scope, b)
+    streams = [(0, n, sel)] if scope == 0 else \
+        [(int(seg_off[t]), int(seg_off[t + 1]), [i for i in sel if seg_off[t] <= i < seg_off[t + 1]])
+         for t in range(nseg)]
+    words = []
+    chunks = []
+    for s, (lo, hi, items) in enumerate(streams):
+        local = [i - lo for i in items]
+        bits = bf.rice_bits_string(local, b)
+        assert int(enc.nbits[s]) == len(bits)
+        assert int(enc.word_off[s]) == len(words)
+        words += bf.pack_bits(bits)
+        # chunk table: bit offset of codes 0, 256, 512, ...
+        for c in range(0, len(local), orc.CHUNK_CODES):
+            chunks.append(len(bf.rice_bits_string(local[:c], b)))
+        back, used = bf.parse_rice(bits, len(local), b)
+        assert back == local and used == len(bits)
+        # oracle decoder agrees
+        w0, w1 = int(enc.word_off[s]), int(enc.word_off[s + 1])
+        pos, stt = orc.decode_stream(enc.words[w0:w1], int(enc.nbits[s]), len(local), b, hi - lo)
+        assert stt == 0 and pos.tolist() == local
+    assert enc.words.tolist() == words
+    assert enc.chunk_off.tolist() == chunks
+
+
+def test_rice_size_bound(orc):
+    # bits <= k (b+1) + floor((n-k)/2^b): the sum of floor(z/2^b) is at most floor(sum z / 2^b).
+    rng = np.random.default_rng(1)
+    for b in (0, 3, 6, 9):
+        n = 50000
+        pos = np.flatnonzero(rng.random(n) < 0.02).astype(np.int32)
+        enc = orc.encode(pos, np.array([pos.size, pos.size], np.int64), [0, n], 0, b)
+        assert int(enc.nbits[0]) <= pos.size * (b + 1) + ((n - pos.size) >> b)
+
+
+def test_decode_detects_corruption(orc):
+    pos = np.array([2, 9, 40, 41, 300], np.int32)
+    enc = orc.encode(pos, np.array([5, 5], np.int64), [0, 512], 0, 3)
+    nb = int(enc.nbits[0])
+    _, st = orc.decode_stream(enc.words, nb, 5, 3, 512)
+    assert st == 0
+    _, st = orc.decode_stream(enc.words, nb - 2, 5, 3, 512)        # truncated stream
+    assert st & orc.STATUS_CORRUPT
+    _, st = orc.decode_stream(enc.words, nb, 5, 3, 200)             # position beyond the shape
+    assert st & orc.STATUS_CORRUPT
+    _, st = orc.decode_stream(enc.words, nb, 4, 3, 512)             # bits left over
+    assert st & orc.STATUS_CORRUPT
+    _, st = orc.decode_stream(enc.words, nb, 5, 3, 512, chunk_off=np.array([1], np.uint64))
+    assert st & orc.STATUS_CORRUPT
+
+
+# ------------------------------------------------------ decode + accumulate
+def _random_message(orc, rng, n, seg_off, ppm, g_scale=1e-3):
+    g = rng.laplace(0, g_scale, n).astype(np.float32)
+    r = np.zeros(n, np.float32)
+    return orc.compress_exact(g, r, seg_off, 0, ppm), g
+
+
+def test_single_raw_message_densifies(orc):
+    rng = np.random.default_rng(2)
+    n = 3000
+    sp, _ = _random_message(orc, rng, n, [0, n], 50000)
+    out = np.zeros(n, np.float32)
+    st = orc.decode_accumulate([orc.Message(sp.counts, idx=sp.idx, val=sp.val)], [0, n], out)
+    want = np.zeros(n, np.float32)
+    want[sp.idx] = sp.val
+    assert st == 0 and np.array_equal(out.view(np.uint32), want.view(np.uint32))
+
+
+def test_ordered_sum_equals_dense_numpy(orc):
+    # [SBC] §I (server / all-reduce sum) with [AHB19] Abstract (local dense gradient as base):
+    # out = base + densify(m0) + ... added in worker order, present entries only.
+    rng = np.random.default_rng(4)
+    seg = [0, 700, 701, 4000]
+    n = seg[-1]
+    base = rng.normal(0, 1e-3, n).astype(np.float32)
+    base[::97] = -0.0
+    msgs, dense = [], []
+    for w in range(5):
+        sp, _ = _random_message(orc, rng, n, seg, 30000)
+        if w % 2:
+            enc = orc.encode(sp.idx, sp.counts, seg, 1, 4)
+            msgs.append(orc.Message(sp.counts, golomb=True, scope=1, b=4, val=sp.val, enc=enc))
+        else:
+            msgs.append(orc.Message(sp.counts, idx=sp.idx, val=sp.val))
+        dense.append(sp)
+    out = base.copy()
+    st = orc.decode_accumulate(msgs, seg, out)
+    want = base.copy()
+    for sp in dense:
+        m = np.zeros(n, bool)
+        m[sp.idx] = True
+        d = np.zeros(n, np.float32)
+        d[sp.idx] = sp.val
+        want[m] = want[m] + d[m]
+    assert st == 0 and np.array_equal(out.view(np.uint32), want.view(np.uint32))
+    # absent entries keep the base bits (including -0.0)
+    untouched = np.ones(n, bool)
+    for sp in dense:
+        untouched[sp.idx] = False
+    assert np.array_equal(out[untouched].view(np.uint32), base[untouched].view(np.uint32))
+
+
+def test_sbc_and_2bit_messages_round_trip(orc):
+    rng = np.random.default_rng(8)
+    seg = np.array([0, 1000, 1064, 5000], np.int64)
+    n = int(seg[-1])
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    r = np.zeros(n, np.float32)
+    sp = orc.compress_exact(g, r, seg, 1, 20000)
+    r_sbc = r.copy()
+    sbc = orc.binarize(sp, 3, orc.BIN_SBC, r_sbc)
+    enc = orc.encode(sbc.idx, sbc.counts, seg, 1, 5)
+    out = np.zeros(n, np.float32)
+    st = orc.decode_accumulate([orc.Message(sbc.counts, vkind=orc.VAL_SBC, golomb=True, scope=1, b=5,
+                                            means=sbc.means, enc=enc)], seg, out)
+    assert st == 0
+    e0 = 0
+    for t in range(3):
+        ids = sbc.idx[e0:e0 + sbc.counts[t]]
+        e0 += sbc.counts[t]
+        assert np.all(out[ids] == sbc.means[t])
+    assert np.count_nonzero(out) == sbc.idx.size
+    # sent + residual == acc within one rounding per entry
+    acc = g
+    rec = (r_sbc + out).astype(np.float32)
+    assert np.all(np.abs(rec - acc) <= np.spacing(np.abs(acc)) + 1e-45)
+    # 2-bit
+    r2 = r.copy()
+    q = orc.binarize(sp, 3, orc.BIN_2BIT, r2)
+    out2 = np.zeros(n, np.float32)
+    st = orc.decode_accumulate([orc.Message(q.counts, vkind=orc.VAL_2BIT, idx=q.idx, codes=q.codes,
+                                            means=q.means)], seg, out2)
+    assert st == 0
+    assert set(np.unique(out2[sp.idx]).tolist()) <= set(q.means.tolist())
+    assert np.all(np.sign(out2[sp.idx]) == np.sign(sp.val))
+
+
+def test_sbc_equal_means_send_positive_side(orc):
+    # Reading of [SBC] §II Sparse Binarization when both means are equal: the positive side is sent.
+    sp = type("S", (), {})()
+    sp.idx = np.array([0, 1, 2, 3], np.int32)
+    sp.val = np.array([0.5, -0.25, -0.75, 0.5], np.float32)
+    sp.counts = np.array([4, 4], np.int64)
+    r = np.zeros(4, np.float32)
+    out = orc.binarize(sp, 1, orc.BIN_SBC, r)
+    assert out.means.tolist() == [0.5] and out.idx.tolist() == [0, 3]
+    assert r.tolist() == [0.0, -0.25, -0.75, 0.0]
