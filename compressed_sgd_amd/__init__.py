@@ -1,0 +1,243 @@
+"""compressed_sgd_amd -- Python binding of libsgc (MI355X / gfx950).
+
+Thin ctypes marshalling over the C ABI declared in include/sgc.h: every step
+of the path runs in the library's HIP kernels; this module only allocates
+device tensors (torch), passes their pointers and the current stream, and
+turns return codes into exceptions.  There is no CPU fallback: if libsgc.so
+is missing or no GPU is present, the calls raise.
+
+The entry points keep the C names without the ``sgc_`` prefix:
+``compress``, ``binarize``, ``encode``, ``decode_accumulate``, plus the
+``Layout`` of segment sizes shared by both ends of the exchange.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch  # loads the HIP runtime first; libsgc binds to that same runtime
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsgc.so")
+
+OK, EINVAL, ENOSPC, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4
+STATUS_TRUNCATED, STATUS_CORRUPT, STATUS_DENSE_PATH, STATUS_BAD_INPUT = 1, 2, 4, 8
+EXACT, SAMPLED, ACCUMULATE_ONLY = 0, 1, 2
+GLOBAL, PER_SEGMENT = 0, 1
+BIN_SBC, BIN_2BIT = 0, 1
+MSG_RAW_F32, MSG_RAW_2BIT, MSG_GOLOMB_F32, MSG_GOLOMB_SBC, MSG_GOLOMB_2BIT = 0, 1, 2, 3, 4
+INIT_ZERO, INIT_BASE, INIT_INPLACE = 0, 1, 2
+CHUNK_CODES = 256
+
+EXPORTED = (
+    "sgc_layout_create", "sgc_layout_destroy", "sgc_layout_numel", "sgc_layout_nseg",
+    "sgc_keep_count", "sgc_rice_param", "sgc_strerror", "sgc_abi_version",
+    "sgc_compress_workspace", "sgc_compress",
+    "sgc_binarize_workspace", "sgc_binarize",
+    "sgc_encode_word_bound", "sgc_encode_chunk_bound", "sgc_encode_workspace", "sgc_encode",
+    "sgc_decode_accumulate_workspace", "sgc_decode_accumulate",
+)
+
+
+class SGCError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {lib().sgc_strerror(code).decode()} ({code})")
+
+
+class CompressOpts(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("scope", C.c_int32), ("keep_ppm", C.c_uint32),
+                ("sample_div", C.c_uint32), ("sample_min", C.c_uint32)]
+
+
+class MessageDesc(C.Structure):
+    _fields_ = [("format", C.c_int32), ("scope", C.c_int32), ("rice_b", C.c_int32), ("reserved", C.c_int32),
+                ("cap", C.c_int64), ("counts", C.c_void_p), ("idx", C.c_void_p), ("val", C.c_void_p),
+                ("codes", C.c_void_p), ("means", C.c_void_p), ("words", C.c_void_p), ("word_off", C.c_void_p),
+                ("nbits", C.c_void_p), ("chunk_off", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libsgc (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64, u32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32, C.c_size_t
+        L.sgc_layout_create.argtypes = [P, i32, C.POINTER(P)]
+        L.sgc_layout_create.restype = C.c_int
+        L.sgc_layout_destroy.argtypes = [P]
+        L.sgc_layout_destroy.restype = None
+        L.sgc_layout_numel.argtypes = [P]
+        L.sgc_layout_numel.restype = i64
+        L.sgc_layout_nseg.argtypes = [P]
+        L.sgc_layout_nseg.restype = i32
+        L.sgc_keep_count.argtypes = [i64, u32]
+        L.sgc_keep_count.restype = i64
+        L.sgc_rice_param.argtypes = [C.c_double]
+        L.sgc_rice_param.restype = i32
+        L.sgc_strerror.argtypes = [C.c_int]
+        L.sgc_strerror.restype = C.c_char_p
+        L.sgc_abi_version.argtypes = []
+        L.sgc_abi_version.restype = i32
+        L.sgc_compress_workspace.argtypes = [P, P, i64]
+        L.sgc_compress_workspace.restype = sz
+        L.sgc_compress.argtypes = [P, P, P, P, P, P, i64, P, P, P, sz, P]
+        L.sgc_compress.restype = C.c_int
+        L.sgc_binarize_workspace.argtypes = [P, i64]
+        L.sgc_binarize_workspace.restype = sz
+        L.sgc_binarize.argtypes = [P, i32, P, P, P, i64, P, P, P, P, P, P, sz, P]
+        L.sgc_binarize.restype = C.c_int
+        L.sgc_encode_word_bound.argtypes = [P, i32, i32, i64]
+        L.sgc_encode_word_bound.restype = i64
+        L.sgc_encode_chunk_bound.argtypes = [P, i32, i64]
+        L.sgc_encode_chunk_bound.restype = i64
+        L.sgc_encode_workspace.argtypes = [P, i32, i64]
+        L.sgc_encode_workspace.restype = sz
+        L.sgc_encode.argtypes = [P, i32, i32, P, P, i64, P, i64, P, P, P, i64, P, P, sz, P]
+        L.sgc_encode.restype = C.c_int
+        L.sgc_decode_accumulate_workspace.argtypes = [P, P, i32]
+        L.sgc_decode_accumulate_workspace.restype = sz
+        L.sgc_decode_accumulate.argtypes = [P, P, i32, i32, P, P, P, P, sz, P]
+        L.sgc_decode_accumulate.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != OK:
+        raise SGCError(rc, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return C.c_void_p(s.cuda_stream)
+
+
+def _require_gpu(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ helpers
+def keep_count(n: int, keep_ppm: int) -> int:
+    return int(lib().sgc_keep_count(n, keep_ppm))
+
+
+def rice_param(p: float) -> int:
+    return int(lib().sgc_rice_param(p))
+
+
+def abi_version() -> int:
+    return int(lib().sgc_abi_version())
+
+
+class Layout:
+    """Segment sizes of the flat parameter vector (one per tensor, in order)."""
+
+    def __init__(self, seg_numel: Sequence[int]):
+        self.seg_numel = [int(x) for x in seg_numel]
+        arr = (C.c_int64 * max(len(self.seg_numel), 1))(*self.seg_numel)
+        h = C.c_void_p()
+        _check(lib().sgc_layout_create(arr, len(self.seg_numel), C.byref(h)), "sgc_layout_create")
+        self._h = h
+        self.n = sum(self.seg_numel)
+        self.nseg = len(self.seg_numel)
+        off = [0]
+        for m in self.seg_numel:
+            off.append(off[-1] + m)
+        self.seg_off = off
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.sgc_layout_destroy(h)
+            self._h = None
+
+    def group_sizes(self, scope: int) -> List[int]:
+        return [self.n] if scope == GLOBAL else list(self.seg_numel)
+
+    def keep_total(self, scope: int, keep_ppm: int) -> int:
+        return sum(keep_count(m, keep_ppm) for m in self.group_sizes(scope))
+
+
+_ws_cache: Dict[Tuple[int, str], torch.Tensor] = {}
+
+
+def workspace(nbytes: int, device: torch.device, slot: str = "default") -> torch.Tensor:
+    """A cached uint8 device buffer of at least nbytes (one per device and slot).
+
+    Calls that share a slot must not overlap in time (same stream is fine).
+    """
+    key = (device.index if device.index is not None else torch.cuda.current_device(), slot)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+# ----------------------------------------------------------------- compress
+@dataclass
+class Compressed:
+    idx: torch.Tensor      # int32 [cap], first counts[-1] valid
+    val: torch.Tensor      # float32 [cap]
+    counts: torch.Tensor   # int64 [nseg+1]
+    status: torch.Tensor   # uint32 [1] (stored as int32)
+    cap: int
+
+    def total(self) -> int:
+        return int(self.counts[-1].item())
+
+
+def compress(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode: int = EXACT,
+             scope: int = GLOBAL, keep_ppm: int = 10000, sample_div: int = 1000, sample_min: int = 65536,
+             cap: Optional[int] = None, out: Optional[Compressed] = None, ws: Optional[torch.Tensor] = None,
+             stream=None) -> Optional[Compressed]:
+    """One step: residual += grad, select, emit, zero the residual at kept entries.
+
+    mode ACCUMULATE_ONLY only adds (communication delay) and returns None.
+    """
+    for t, name in ((grad, "grad"), (residual, "residual")):
+        _require_gpu(t, name)
+        if t.dtype != torch.float32 or t.numel() != layout.n:
+            raise ValueError(f"{name} must be float32 with {layout.n} elements")
+    dev = grad.device
+    opts = CompressOpts(mode, scope, keep_ppm, sample_div, sample_min)
+    st = _stream(dev, stream)
+    if mode == ACCUMULATE_ONLY:
+        _check(lib().sgc_compress(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), None, None, 0, None,
+                                  None, None, 0, st), "sgc_compress")
+        return None
+    if cap is None:
+        k = layout.keep_total(scope, keep_ppm)
+        cap = k if mode == EXACT else min(layout.n, 2 * k + 4096)
+    if out is None:
+        out = Compressed(torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+                         torch.empty(max(cap, 1), dtype=torch.float32, device=dev),
+                         torch.empty(layout.nseg + 1, dtype=torch.int64, device=dev),
+                         torch.zeros(1, dtype=torch.int32, device=dev), cap)
+    nbytes = lib().sgc_compress_workspace(layout.handle, C.byref(opts), cap)
+    if ws is None:
+        ws = workspace(nbytes, dev, "compress")
+    _check(lib().sgc_compress(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), _ptr(out.idx),
+                              _ptr(out.val), cap, _ptr(out.counts), _ptr(out.status), _ptr(ws), ws.numel(), st),
+           "sgc_compress")
+    return out

@@ -1,0 +1,198 @@
+// sgc_common.h -- internals shared by the HIP sources of libsgc (gfx950).
+//
+// Citations (page title, then section):
+//   [AH17]  "Sparse Communication for Distributed Gradient Descent" (Aji & Heafield)
+//   [AHB19] "Combining Global Sparse Gradients with Local Gradients in Distributed
+//           Neural Network Training" (Aji, Heafield & Bogoychev)
+//   [SBC]   "Sparse Binary Compression: Towards Distributed Deep Learning with
+//           minimal Communication" (Sattler et al.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "../../include/sgc.h"
+
+namespace sgc {
+
+// ---------------------------------------------------------------- geometry
+// Pass-1 tile: 256 threads x 8 float4 slots.  Tiles never straddle a
+// selection group; inside a group they sit on a 4-element-aligned grid so
+// that every full slot is one aligned 16-byte access.
+constexpr int kBlock = 256;
+constexpr int kSlots = 8;
+constexpr int64_t kTile = (int64_t)kBlock * 4 * kSlots;  // 8192 elements
+// Candidate slots per tile region; a tile with more candidates is redone
+// from the residual (which holds acc after pass 1).
+constexpr int kTileCap = 512;
+// Chunk of the selection / compaction kernels: 256 threads x 16 contiguous.
+constexpr int kPer = 16;
+constexpr int64_t kChunk = (int64_t)kBlock * kPer;  // 4096 entries
+// Radix digits of the 31-bit magnitude key: bits 30..20, 19..10, 9..0.
+constexpr int kBins = 2048;
+// Rice encoder block: codes per encode block, and look-ahead codes.
+constexpr int64_t kEncCodes = 2048;
+constexpr int kEncAhead = 32;
+// Dense output tile of decode-accumulate.
+constexpr int64_t kOutTile = 4096;
+
+constexpr uint32_t kNoKey = 0x80000000u;  // above every 31-bit magnitude key
+
+// ------------------------------------------------------- shared arithmetic
+// Magnitude key: for finite floats the order of |x| is the order of the
+// unsigned integer formed by the low 31 bits (+0 and -0 share key 0).
+__host__ __device__ inline uint32_t mag_key(float x)
+{
+    union { float f; uint32_t u; } c;
+    c.f = x;
+    return c.u & 0x7fffffffu;
+}
+
+// k = ceil(m * ppm / 1e6), at most m ([AH17] Abstract; [SBC] §II Sparse
+// Binarization).  m < 2^31 and ppm <= 1e6 keep the product below 2^51.
+__host__ __device__ inline int64_t keep_count(int64_t m, uint32_t ppm)
+{
+    if (m <= 0) return 0;
+    int64_t k = (m * (int64_t)ppm + 999999) / 1000000;
+    return k < m ? k : m;
+}
+
+// Sample size of the sampled-threshold mode.
+__host__ __device__ inline int64_t sampled_count(int64_t m, uint32_t div, uint32_t smin)
+{
+    if (m <= 0) return 0;
+    int64_t s = (m + (int64_t)div - 1) / (int64_t)div;
+    if (s < (int64_t)smin) s = smin;
+    return s < m ? s : m;
+}
+
+// Sample size used by the exact mode only to place a safe lower bound for
+// its candidate set (the result does not depend on it).
+__host__ __device__ inline int64_t probe_count(int64_t m)
+{
+    if (m <= 0) return 0;
+    int64_t s = m / 256;
+    if (s < 4096) s = 4096;
+    if (s > 65536) s = 65536;
+    return s < m ? s : m;
+}
+
+// Pass-1 tiles of a group [lo, hi): aligned grid starting at lo & ~3.
+__host__ __device__ inline int64_t group_tiles(int64_t lo, int64_t hi)
+{
+    if (hi <= lo) return 0;
+    int64_t a = lo & ~(int64_t)3;
+    return (hi - a + kTile - 1) / kTile;
+}
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest i in [0, len) with a[i] <= x, for ascending a with a[0] <= x.
+template <typename T>
+__device__ inline int64_t find_bucket(const T* a, int64_t len, T x)
+{
+    int64_t lo = 0, hi = len - 1;
+    while (lo < hi) {
+        int64_t mid = (lo + hi + 1) >> 1;
+        if (a[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// --------------------------------------------------------- block helpers
+// Exclusive scan of one value per thread over a 256-thread block.  `tmp`
+// is shared scratch of kBlock/64 + 1 entries.  Returns the exclusive prefix
+// and writes the block total to *total.  Every thread must call it.
+template <typename T>
+__device__ inline T block_exclusive_scan(T v, T* tmp, T* total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    T x = v;
+    // inclusive scan inside the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        T y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        T run = 0;
+        for (int w = 0; w < kBlock / 64; ++w) { T t = tmp[w]; tmp[w] = run; run += t; }
+        tmp[kBlock / 64] = run;
+    }
+    __syncthreads();
+    T res = tmp[wave] + x - v;
+    *total = tmp[kBlock / 64];
+    __syncthreads();
+    return res;
+}
+
+// ------------------------------------------------------------- layout
+struct DevTables {
+    int64_t* seg_off = nullptr;   // [nseg+1]
+    int64_t* seg_tile = nullptr;  // [nseg+1] pass-1 tile prefix per segment
+    int64_t* glob_off = nullptr;  // [2] = {0, n}
+    int64_t* glob_tile = nullptr; // [2] = {0, tiles of [0, n)}
+    void* block = nullptr;
+};
+
+}  // namespace sgc
+
+struct sgc_layout {
+    int32_t nseg = 0;
+    int64_t n = 0;
+    std::vector<int64_t> seg_off;   // [nseg+1]
+    std::vector<int64_t> seg_tile;  // [nseg+1]
+    std::mutex mu;
+    std::map<int, sgc::DevTables> dev;
+};
+
+namespace sgc {
+
+// Selection groups of a scope: GLOBAL -> {[0, n)}, PER_SEGMENT -> segments.
+struct Groups {
+    int32_t G;
+    const int64_t* off;   // device [G+1]
+    const int64_t* tile;  // device [G+1]
+    int64_t ntiles;       // host
+};
+
+int device_tables(sgc_layout* L, DevTables** out);
+Groups groups_of(sgc_layout* L, const DevTables* d, int32_t scope);
+std::vector<int64_t> host_group_off(const sgc_layout* L, int32_t scope);
+
+// Workspace carving: the same sequence of take() calls sizes the workspace
+// (base == nullptr) and assigns the pointers.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base((char*)b) {}
+    template <typename T>
+    T* take(int64_t count)
+    {
+        off = (off + 255) & ~(size_t)255;
+        T* p = base ? (T*)(base + off) : nullptr;
+        off += (size_t)(count > 0 ? count : 1) * sizeof(T);
+        return p;
+    }
+};
+
+inline int hip_ok(hipError_t e) { return e == hipSuccess ? SGC_OK : SGC_EHIP; }
+#define SGC_LAUNCH_CHECK()                                   \
+    do {                                                     \
+        if (hipGetLastError() != hipSuccess) return SGC_EHIP; \
+    } while (0)
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Zero `count` 32-bit words with a kernel (no memset nodes in a stream that
+// may be captured into a graph).
+int fill_u32(void* p, int64_t count, uint32_t value, hipStream_t s);
+
+}  // namespace sgc

@@ -1,0 +1,178 @@
+"""GPU parity of sgc_compress against the CPU oracle (bit-exact).
+
+Indices, kept values, residuals and per-segment counts must match the
+oracle bit for bit, for exact and sampled selection, global and per-segment
+scope, across ragged segment tables, ties, zeros, clustered inputs that
+overflow the per-tile candidate regions, and inputs that defeat the probe
+sample (the full-pass path).
+"""
+import numpy as np
+import pytest
+import torch
+
+import compressed_sgd_amd as sgc
+import workloads as W
+from gpu_util import announce, assert_bitwise, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def check_step(orc, layout, g, r, *, mode, scope, ppm, cap=None, sample_div=1000, sample_min=65536, what=""):
+    """Run one compress step on both sides; r (host) is advanced like the GPU residual."""
+    announce(f"compress {what} n={layout.n} nseg={layout.nseg} mode={mode} scope={scope} ppm={ppm}")
+    gd, rd = dev(g), dev(r)
+    out = sgc.compress(layout, gd, rd, mode=mode, scope=scope, keep_ppm=ppm, cap=cap,
+                       sample_div=sample_div, sample_min=sample_min)
+    torch.cuda.synchronize()
+    seg_off = np.array(layout.seg_off, np.int64)
+    if mode == sgc.EXACT:
+        ref = orc.compress_exact(g, r, seg_off, scope, ppm, cap=out.cap)
+    else:
+        ref = orc.compress_sampled(g, r, seg_off, scope, ppm, out.cap, sample_div, sample_min)
+    counts = host(out.counts)
+    total = int(counts[-1])
+    assert_bitwise(counts, ref.counts, f"{what} counts")
+    assert_bitwise(host(out.idx)[:total], ref.idx, f"{what} idx")
+    assert_bitwise(host(out.val)[:total], ref.val, f"{what} val")
+    assert_bitwise(host(rd), r, f"{what} residual")
+    st = int(host(out.status)[0])
+    if mode == sgc.SAMPLED:
+        assert (st & sgc.STATUS_TRUNCATED) == (ref.status & 1), f"{what} truncation flag"
+    return out, st
+
+
+@pytest.mark.parametrize("steps", [3])
+def test_flat_1m_exact_three_steps(orc, steps):
+    w = W.FLAT_1M
+    layout = sgc.Layout(w.seg_numel)
+    r = np.zeros(w.numel, np.float32)
+    for s in range(steps):
+        g = W.gradient(w, 0, s).numpy()
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=w.scope, ppm=w.keep_ppm, what=f"flat-1M step {s}")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("scope", [0, 1])
+@pytest.mark.parametrize("ppm", [0, 1000, 10000, 250000, 1000000])
+def test_ragged_segments(orc, seed, scope, ppm):
+    rng = np.random.default_rng(100 + seed)
+    sizes = [0, 1, 3, 5, 10, 17, 4095, 4097, 8191, 8193, 12345, 0, 64, 70001]
+    rng.shuffle(sizes)
+    layout = sgc.Layout(sizes)
+    n = layout.n
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    r = np.zeros(n, np.float32)
+    for s in range(2):
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=ppm, what=f"ragged seed{seed} s{s}")
+        g = rng.laplace(0, 1e-3, n).astype(np.float32)
+
+
+@pytest.mark.parametrize("scope", [0, 1])
+def test_ties_and_zeros(orc, scope):
+    rng = np.random.default_rng(7)
+    layout = sgc.Layout([30000, 50000, 7, 20000])
+    n = layout.n
+    # coarse quantized values: massive ties at every magnitude, signed zeros
+    g = (rng.integers(-6, 7, n) * 0.125).astype(np.float32)
+    g[rng.random(n) < 0.3] = -0.0
+    r = np.zeros(n, np.float32)
+    check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=10000, what="quantized ties")
+    # all zeros: the threshold is 0 and the lowest indices win
+    z = np.zeros(n, np.float32)
+    z[::3] = -0.0
+    r2 = np.zeros(n, np.float32)
+    check_step(orc, layout, z, r2, mode=sgc.EXACT, scope=scope, ppm=10000, what="all zeros")
+
+
+def test_probe_defeated_takes_full_pass_path(orc):
+    # Large values sit exactly where the probe samples (every 256th element from 128 at
+    # n = 2^20), so the sample overestimates the threshold and too few candidates pass.
+    n = 1 << 20
+    g = np.random.default_rng(1).normal(0, 1e-4, n).astype(np.float32)
+    g[128::256] = 1.0 + np.arange(n // 256, dtype=np.float32) * 1e-3
+    layout = sgc.Layout([n])
+    r = np.zeros(n, np.float32)
+    out, st = check_step(orc, layout, g, r, mode=sgc.EXACT, scope=0, ppm=10000, what="probe defeated")
+    assert st & sgc.STATUS_DENSE_PATH
+
+
+def test_clustered_overflowing_tiles(orc):
+    # All large values in a few contiguous runs: some tiles hold far more candidates than
+    # their region, and those tiles are redone from the residual.
+    n = 1 << 21
+    rng = np.random.default_rng(5)
+    g = rng.normal(0, 1e-5, n).astype(np.float32)
+    for start in (5000, 300000, 1500007):
+        g[start:start + 9000] = rng.laplace(0, 1.0, 9000).astype(np.float32)
+    layout = sgc.Layout([n // 2, n // 2])
+    for scope in (0, 1):
+        r = np.zeros(n, np.float32)
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=10000, what=f"clustered scope{scope}")
+        r = np.zeros(n, np.float32)
+        check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=scope, ppm=10000, cap=n, what=f"clustered sampled{scope}")
+
+
+@pytest.mark.parametrize("scope", [0, 1])
+@pytest.mark.parametrize("ppm", [1000, 10000])
+def test_sampled_matches_oracle(orc, scope, ppm):
+    rng = np.random.default_rng(11)
+    layout = sgc.Layout([1 << 20, 300000, 4096, 1, 99999])
+    n = layout.n
+    r = np.zeros(n, np.float32)
+    for s in range(2):
+        g = rng.laplace(0, 1e-3, n).astype(np.float32)
+        check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=scope, ppm=ppm, what=f"sampled s{s}")
+
+
+def test_sampled_truncation(orc):
+    rng = np.random.default_rng(12)
+    n = 500000
+    layout = sgc.Layout([n])
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    r = np.zeros(n, np.float32)
+    out, st = check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=0, ppm=10000, cap=3000, what="truncated")
+    assert st & sgc.STATUS_TRUNCATED
+
+
+def test_accumulate_only(orc):
+    rng = np.random.default_rng(13)
+    for n in (1, 3, 4, 1023, 1 << 20, (1 << 20) + 7):
+        layout = sgc.Layout([n])
+        g = rng.laplace(0, 1e-3, n).astype(np.float32)
+        r = rng.laplace(0, 1e-3, n).astype(np.float32)
+        rd = dev(r)
+        sgc.compress(layout, dev(g), rd, mode=sgc.ACCUMULATE_ONLY)
+        orc.accumulate(g, r)
+        assert_bitwise(host(rd), r, f"accumulate n={n}")
+
+
+def test_mlp_mnist_global_two_steps(orc):
+    w = W.MLP_MNIST
+    layout = sgc.Layout(w.seg_numel)
+    r = np.zeros(w.numel, np.float32)
+    for s in range(2):
+        g = W.gradient(w, 0, s).numpy()
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=w.scope, ppm=w.keep_ppm, what=f"mlp step {s}")
+
+
+def test_resnet50_delay_per_tensor(orc):
+    w = W.RESNET50
+    layout = sgc.Layout(w.seg_numel)
+    r = np.zeros(w.numel, np.float32)
+    rd = dev(r)
+    for s in range(w.delay - 1):
+        g = W.gradient(w, 0, s).numpy()
+        sgc.compress(layout, dev(g), rd, mode=sgc.ACCUMULATE_ONLY)
+        orc.accumulate(g, r)
+    assert_bitwise(host(rd), r, "resnet delay accumulate")
+    g = W.gradient(w, 0, w.delay - 1).numpy()
+    check_step(orc, layout, g, r, mode=sgc.EXACT, scope=w.scope, ppm=w.keep_ppm, what="resnet exchange")
+
+
+def test_empty_layout(orc):
+    layout = sgc.Layout([0, 0])
+    g = torch.zeros(0, dtype=torch.float32, device="cuda")
+    r = torch.zeros(0, dtype=torch.float32, device="cuda")
+    out = sgc.compress(layout, g, r, keep_ppm=10000)
+    torch.cuda.synchronize()
+    assert host(out.counts).tolist() == [0, 0, 0]
