@@ -241,3 +241,143 @@ def compress(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode
                               _ptr(out.val), cap, _ptr(out.counts), _ptr(out.status), _ptr(ws), ws.numel(), st),
            "sgc_compress")
     return out
+
+
+# ----------------------------------------------------------------- binarize
+@dataclass
+class Binarized:
+    idx: Optional[torch.Tensor]    # SBC: sent indices (int32 [cap]); 2-bit: copy of the input indices
+    counts: torch.Tensor           # int64 [nseg+1]
+    means: torch.Tensor            # SBC: [nseg] signed means; 2-bit: [2*nseg] (+mean_pos, -mean_neg)
+    codes: Optional[torch.Tensor]  # 2-bit: int32 view of uint32 words [ceil(cap/16)]
+    mode: int
+    cap: int
+
+
+def binarize(layout: Layout, comp: Compressed, residual: torch.Tensor, mode: int = BIN_SBC, *,
+             ws: Optional[torch.Tensor] = None, stream=None) -> Binarized:
+    """Sparse binarization (SBC) or 2-bit quantization of a compress result."""
+    _require_gpu(residual, "residual")
+    dev = residual.device
+    cap = comp.cap
+    out = Binarized(torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+                    torch.empty(layout.nseg + 1, dtype=torch.int64, device=dev),
+                    torch.empty(layout.nseg if mode == BIN_SBC else 2 * layout.nseg, dtype=torch.float32,
+                                device=dev),
+                    torch.zeros(max((cap + 15) // 16, 1), dtype=torch.int32, device=dev) if mode == BIN_2BIT
+                    else None, mode, cap)
+    nbytes = lib().sgc_binarize_workspace(layout.handle, cap)
+    if ws is None:
+        ws = workspace(nbytes, dev, "binarize")
+    _check(lib().sgc_binarize(layout.handle, mode, _ptr(comp.idx), _ptr(comp.val), _ptr(comp.counts), cap,
+                              _ptr(residual), _ptr(out.idx), _ptr(out.counts), _ptr(out.means), _ptr(out.codes),
+                              _ptr(ws), ws.numel(), _stream(dev, stream)), "sgc_binarize")
+    return out
+
+
+# ------------------------------------------------------------------- encode
+@dataclass
+class Encoded:
+    words: torch.Tensor      # int32 view of the uint32 stream words
+    word_off: torch.Tensor   # int64 view of uint64 [nstreams+1]
+    nbits: torch.Tensor      # int64 view of uint64 [nstreams]
+    chunk_off: torch.Tensor  # int64 view of uint64 chunk table
+    status: torch.Tensor
+    scope: int
+    b: int
+    cap: int
+
+
+def encode(layout: Layout, idx: torch.Tensor, counts: torch.Tensor, cap: int, *, scope: int = GLOBAL,
+           b: Optional[int] = None, keep_ppm: Optional[int] = None, out: Optional[Encoded] = None,
+           ws: Optional[torch.Tensor] = None, stream=None) -> Encoded:
+    """Rice-code the index gaps of a sparse message.
+
+    b defaults to the parameter that minimises the mean code length at the
+    nominal density keep_ppm / 1e6.
+    """
+    _require_gpu(idx, "idx")
+    dev = idx.device
+    if b is None:
+        if keep_ppm is None:
+            raise ValueError("give b or keep_ppm")
+        b = rice_param(keep_ppm / 1e6)
+    nstreams = 1 if scope == GLOBAL else layout.nseg
+    wcap = int(lib().sgc_encode_word_bound(layout.handle, scope, b, cap))
+    ccap = int(lib().sgc_encode_chunk_bound(layout.handle, scope, cap))
+    if wcap < 0 or ccap < 0:
+        raise ValueError("bad encode arguments")
+    if out is None or out.words.numel() < wcap or out.chunk_off.numel() < ccap:
+        out = Encoded(torch.empty(max(wcap, 1), dtype=torch.int32, device=dev),
+                      torch.empty(nstreams + 1, dtype=torch.int64, device=dev),
+                      torch.empty(nstreams, dtype=torch.int64, device=dev),
+                      torch.empty(max(ccap, 1), dtype=torch.int64, device=dev),
+                      torch.zeros(1, dtype=torch.int32, device=dev), scope, b, cap)
+    out.scope, out.b, out.cap = scope, b, cap
+    nbytes = lib().sgc_encode_workspace(layout.handle, scope, cap)
+    if ws is None:
+        ws = workspace(nbytes, dev, "encode")
+    _check(lib().sgc_encode(layout.handle, scope, b, _ptr(idx), _ptr(counts), cap, _ptr(out.words),
+                            out.words.numel(), _ptr(out.word_off), _ptr(out.nbits), _ptr(out.chunk_off),
+                            out.chunk_off.numel(), _ptr(out.status), _ptr(ws), ws.numel(), _stream(dev, stream)),
+           "sgc_encode")
+    return out
+
+
+# -------------------------------------------------------- decode + accumulate
+@dataclass
+class Message:
+    """One received message: device tensors + format (see sgc_message)."""
+    format: int
+    counts: torch.Tensor
+    cap: int
+    scope: int = GLOBAL
+    b: int = 0
+    idx: Optional[torch.Tensor] = None
+    val: Optional[torch.Tensor] = None
+    codes: Optional[torch.Tensor] = None
+    means: Optional[torch.Tensor] = None
+    enc: Optional[Encoded] = None
+
+    def desc(self) -> MessageDesc:
+        e = self.enc
+        return MessageDesc(self.format, self.scope, self.b, 0, self.cap, _ptr(self.counts), _ptr(self.idx),
+                           _ptr(self.val), _ptr(self.codes), _ptr(self.means),
+                           None if e is None else _ptr(e.words), None if e is None else _ptr(e.word_off),
+                           None if e is None else _ptr(e.nbits), None if e is None else _ptr(e.chunk_off))
+
+
+def raw_message(comp: Compressed) -> Message:
+    return Message(MSG_RAW_F32, comp.counts, comp.cap, idx=comp.idx, val=comp.val)
+
+
+def golomb_message(comp_or_bin, enc: Encoded) -> Message:
+    """A Rice-coded message from an encode result and the values it carries."""
+    if isinstance(comp_or_bin, Compressed):
+        return Message(MSG_GOLOMB_F32, comp_or_bin.counts, enc.cap, scope=enc.scope, b=enc.b,
+                       val=comp_or_bin.val, enc=enc)
+    bn = comp_or_bin
+    if bn.mode == BIN_SBC:
+        return Message(MSG_GOLOMB_SBC, bn.counts, enc.cap, scope=enc.scope, b=enc.b, means=bn.means, enc=enc)
+    return Message(MSG_GOLOMB_2BIT, bn.counts, enc.cap, scope=enc.scope, b=enc.b, codes=bn.codes,
+                   means=bn.means, enc=enc)
+
+
+def decode_accumulate(layout: Layout, msgs: Sequence[Message], out: torch.Tensor, *, init: int = INIT_ZERO,
+                      base: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out = init; then add every message in order (present entries only)."""
+    _require_gpu(out, "out")
+    dev = out.device
+    W = len(msgs)
+    arr = (MessageDesc * max(W, 1))(*[m.desc() for m in msgs])
+    nbytes = lib().sgc_decode_accumulate_workspace(layout.handle, arr, W)
+    if W > 0 and nbytes == 0:
+        raise SGCError(EINVAL, "sgc_decode_accumulate_workspace")
+    if ws is None:
+        ws = workspace(nbytes, dev, "decode")
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(lib().sgc_decode_accumulate(layout.handle, arr, W, init, _ptr(base), _ptr(out), _ptr(status), _ptr(ws),
+                                       ws.numel(), _stream(dev, stream)), "sgc_decode_accumulate")
+    return status

@@ -1,0 +1,339 @@
+// binarize.hip -- sparse binarization / 2-bit quantization of kept values.
+//
+// [SBC] §II Sparse Binarization: after top-p selection by magnitude the
+// positive and negative kept values of a tensor are each summarised by
+// their mean; only the side whose mean is larger in absolute value stays
+// nonzero and is sent as that single mean.  [SBC] appendix C: the mean is
+// the unique least-squares single value of the side.  [SBC] §II Residual
+// Accumulation: whatever is not sent stays in the residual.  [AH17]
+// Abstract: dropping can be combined with quantization (2-bit ternary here).
+//
+// GPU design: per-chunk partial sums (count and double sum per sign, fixed
+// in-block tree order), one block per segment reduces its chunks in a fixed
+// order, one block decides sides / means and scans the chunk output offsets,
+// then an apply kernel writes the message and the residual.
+#include "sgc_common.h"
+
+namespace sgc {
+
+struct BinWs {
+    int64_t* estart;   // [nseg+1] entry prefix per segment
+    int64_t* cpre;     // [nseg+1] chunk prefix per segment
+    uint32_t* ccp;     // [nch] positive count per chunk
+    uint32_t* ccn;     // [nch] negative count per chunk
+    double* csp;       // [nch] positive sum per chunk
+    double* csn;       // [nch] |negative| sum per chunk
+    int64_t* cout;     // [nch+1] output offset per chunk (SBC)
+    float* mpos;       // [nseg]
+    float* mneg;       // [nseg]
+    int32_t* side;     // [nseg] +1, -1, 0
+    int64_t* segcp;    // [nseg]
+    int64_t* segcn;    // [nseg]
+    double* segsp;     // [nseg]
+    double* segsn;     // [nseg]
+};
+
+static int64_t bin_nch_max(const sgc_layout* L, int64_t cap) { return cdiv(cap, kChunk) + L->nseg + 1; }
+
+static void carve_bin(Carver& c, const sgc_layout* L, int64_t cap, BinWs* w)
+{
+    const int64_t ns = L->nseg, nch = bin_nch_max(L, cap);
+    w->estart = c.take<int64_t>(ns + 1);
+    w->cpre = c.take<int64_t>(ns + 1);
+    w->ccp = c.take<uint32_t>(nch);
+    w->ccn = c.take<uint32_t>(nch);
+    w->csp = c.take<double>(nch);
+    w->csn = c.take<double>(nch);
+    w->cout = c.take<int64_t>(nch + 1);
+    w->mpos = c.take<float>(ns);
+    w->mneg = c.take<float>(ns);
+    w->side = c.take<int32_t>(ns);
+    w->segcp = c.take<int64_t>(ns);
+    w->segcn = c.take<int64_t>(ns);
+    w->segsp = c.take<double>(ns);
+    w->segsn = c.take<double>(ns);
+}
+
+// Entry and chunk prefixes.  Counts are clamped into [0, cap] so that a
+// malformed count table can never move a read outside the inputs.
+__global__ void k_bin_setup(const int64_t* __restrict__ counts, int32_t nseg, int64_t cap, BinWs w)
+{
+    if (threadIdx.x || blockIdx.x) return;
+    int64_t e = 0, c = 0;
+    for (int32_t t = 0; t < nseg; ++t) {
+        w.estart[t] = e;
+        w.cpre[t] = c;
+        int64_t m = counts[t];
+        m = m < 0 ? 0 : (m > cap - e ? cap - e : m);
+        e += m;
+        c += cdiv(m, kChunk);
+    }
+    w.estart[nseg] = e;
+    w.cpre[nseg] = c;
+}
+
+// Deterministic block sum (fixed shuffle tree, then waves in order).
+template <typename T>
+__device__ inline T block_sum(T v, T* tmp)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_down(v, d, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) tmp[wave] = v;
+    __syncthreads();
+    T s = 0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += tmp[i];
+    __syncthreads();
+    return s;  // valid in thread 0
+}
+
+__global__ __launch_bounds__(kBlock) void k_bin_sums(const float* __restrict__ val, int32_t nseg, BinWs w)
+{
+    __shared__ double dt[kBlock / 64];
+    __shared__ uint32_t ut[kBlock / 64];
+    const int64_t nch = w.cpre[nseg];
+    for (int64_t c = blockIdx.x; c < nch; c += gridDim.x) {
+        const int64_t t = find_bucket(w.cpre, (int64_t)nseg + 1, c);
+        const int64_t base = w.estart[t] + (c - w.cpre[t]) * kChunk;
+        const int64_t end = min(base + kChunk, w.estart[t + 1]);
+        uint32_t cp = 0, cn = 0;
+        double sp = 0.0, sn = 0.0;
+        const int64_t b = base + (int64_t)threadIdx.x * kPer;
+        for (int j = 0; j < kPer; ++j) {
+            const int64_t i = b + j;
+            if (i < end) {
+                const float v = val[i];
+                if (v > 0.0f) { ++cp; sp += (double)v; }
+                else if (v < 0.0f) { ++cn; sn += -(double)v; }
+            }
+        }
+        cp = block_sum<uint32_t>(cp, ut);
+        cn = block_sum<uint32_t>(cn, ut);
+        sp = block_sum<double>(sp, dt);
+        sn = block_sum<double>(sn, dt);
+        if (threadIdx.x == 0) {
+            w.ccp[c] = cp;
+            w.ccn[c] = cn;
+            w.csp[c] = sp;
+            w.csn[c] = sn;
+        }
+    }
+}
+
+// One block per segment: reduce its chunk partials in a fixed order.
+__global__ __launch_bounds__(kBlock) void k_bin_segsum(int32_t nseg, BinWs w)
+{
+    __shared__ double dt[kBlock / 64];
+    __shared__ int64_t it[kBlock / 64];
+    for (int64_t t = blockIdx.x; t < nseg; t += gridDim.x) {
+        int64_t cp = 0, cn = 0;
+        double sp = 0.0, sn = 0.0;
+        for (int64_t c = w.cpre[t] + threadIdx.x; c < w.cpre[t + 1]; c += kBlock) {
+            cp += w.ccp[c];
+            cn += w.ccn[c];
+            sp += w.csp[c];
+            sn += w.csn[c];
+        }
+        cp = block_sum<int64_t>(cp, it);
+        cn = block_sum<int64_t>(cn, it);
+        sp = block_sum<double>(sp, dt);
+        sn = block_sum<double>(sn, dt);
+        if (threadIdx.x == 0) {
+            w.segcp[t] = cp;
+            w.segcn[t] = cn;
+            w.segsp[t] = sp;
+            w.segsn[t] = sn;
+        }
+    }
+}
+
+// Means, side choice (fp32 comparison, positive wins a tie), outputs and
+// the SBC chunk output offsets.
+__global__ __launch_bounds__(1024) void k_bin_resolve(int32_t nseg, int32_t mode, BinWs w,
+                                                     int64_t* __restrict__ out_counts, float* __restrict__ out_means)
+{
+    for (int64_t t = threadIdx.x; t < nseg; t += blockDim.x) {
+        const int64_t cp = w.segcp[t], cn = w.segcn[t];
+        const float mp = cp ? (float)(w.segsp[t] / (double)cp) : 0.0f;
+        const float mn = cn ? (float)(w.segsn[t] / (double)cn) : 0.0f;
+        w.mpos[t] = mp;
+        w.mneg[t] = mn;
+        int32_t side = 0;
+        if (cp + cn > 0) side = (mp >= mn) ? 1 : -1;
+        w.side[t] = side;
+        if (mode == SGC_BIN_SBC) {
+            out_means[t] = side > 0 ? mp : side < 0 ? -mn : 0.0f;
+            out_counts[t] = side > 0 ? cp : side < 0 ? cn : 0;
+        } else {
+            out_means[2 * t] = mp;
+            out_means[2 * t + 1] = -mn;
+            out_counts[t] = w.estart[t + 1] - w.estart[t];
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int64_t run = 0;
+        if (mode == SGC_BIN_SBC) {
+            for (int32_t t = 0; t < nseg; ++t) run += out_counts[t];
+        } else {
+            run = w.estart[nseg];
+        }
+        out_counts[nseg] = run;
+    }
+    if (mode != SGC_BIN_SBC) return;
+    // chunk output offsets: flat exclusive scan of the chosen count per chunk
+    __shared__ int64_t tmp[1024 / 64 + 1];
+    const int64_t nch = w.cpre[nseg];
+    const int64_t per = cdiv(nch, (int64_t)blockDim.x);
+    const int64_t b = threadIdx.x * per, e = min(b + per, nch);
+    int64_t local = 0;
+    for (int64_t c = b; c < e; ++c) {
+        const int64_t t = find_bucket(w.cpre, (int64_t)nseg + 1, c);
+        local += w.side[t] > 0 ? w.ccp[c] : w.side[t] < 0 ? w.ccn[c] : 0;
+    }
+    // block exclusive scan (1024 threads)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t x = local;
+    for (int d = 1; d < 64; d <<= 1) {
+        int64_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int64_t run = 0;
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) { int64_t q = tmp[i]; tmp[i] = run; run += q; }
+    }
+    __syncthreads();
+    int64_t run = tmp[wave] + x - local;
+    for (int64_t c = b; c < e; ++c) {
+        w.cout[c] = run;
+        const int64_t t = find_bucket(w.cpre, (int64_t)nseg + 1, c);
+        run += w.side[t] > 0 ? w.ccp[c] : w.side[t] < 0 ? w.ccn[c] : 0;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_bin_apply_sbc(const int32_t* __restrict__ idx, const float* __restrict__ val,
+                                                         int32_t nseg, BinWs w, float* __restrict__ res,
+                                                         int64_t n, int32_t* __restrict__ out_idx, int64_t cap)
+{
+    __shared__ uint32_t tmp[kBlock / 64 + 1];
+    const int64_t nch = w.cpre[nseg];
+    for (int64_t c = blockIdx.x; c < nch; c += gridDim.x) {
+        const int64_t t = find_bucket(w.cpre, (int64_t)nseg + 1, c);
+        const int32_t side = w.side[t];
+        const float mean = side > 0 ? w.mpos[t] : side < 0 ? -w.mneg[t] : 0.0f;
+        const int64_t base = w.estart[t] + (c - w.cpre[t]) * kChunk;
+        const int64_t end = min(base + kChunk, w.estart[t + 1]);
+        const int64_t b = base + (int64_t)threadIdx.x * kPer;
+        uint32_t sel = 0, cnt = 0;
+        for (int j = 0; j < kPer; ++j) {
+            const int64_t i = b + j;
+            if (i < end) {
+                const float v = val[i];
+                const bool s = (side > 0 && v > 0.0f) || (side < 0 && v < 0.0f);
+                sel |= (uint32_t)s << j;
+                cnt += s;
+            }
+        }
+        uint32_t tot;
+        int64_t pos = w.cout[c] + block_exclusive_scan<uint32_t>(cnt, tmp, &tot);
+        for (int j = 0; j < kPer; ++j) {
+            const int64_t i = b + j;
+            if (i < end) {
+                const float v = val[i];
+                const int32_t id = idx[i];
+                if ((uint32_t)id >= (uint32_t)n) continue;
+                if (sel & (1u << j)) {
+                    if (pos < cap) out_idx[pos] = id;
+                    ++pos;
+                    res[id] = v - mean;
+                } else {
+                    res[id] = v;
+                }
+            }
+        }
+    }
+}
+
+// One thread per output word of 16 two-bit codes.
+__global__ __launch_bounds__(kBlock) void k_bin_apply_2bit(const int32_t* __restrict__ idx, const float* __restrict__ val,
+                                                          int32_t nseg, BinWs w, float* __restrict__ res, int64_t n,
+                                                          int32_t* __restrict__ out_idx, uint32_t* __restrict__ codes)
+{
+    const int64_t total = w.estart[nseg];
+    const int64_t nwords = cdiv(total, 16);
+    for (int64_t wd = (int64_t)blockIdx.x * kBlock + threadIdx.x; wd < nwords; wd += (int64_t)gridDim.x * kBlock) {
+        const int64_t j0 = wd * 16;
+        int64_t t = find_bucket(w.estart, (int64_t)nseg + 1, j0);
+        uint32_t word = 0;
+        for (int q = 0; q < 16; ++q) {
+            const int64_t j = j0 + q;
+            if (j >= total) break;
+            while (j >= w.estart[t + 1]) ++t;
+            const float v = val[j];
+            const uint32_t code = v > 0.0f ? 1u : v < 0.0f ? 2u : 0u;
+            const float qv = code == 1u ? w.mpos[t] : code == 2u ? -w.mneg[t] : 0.0f;
+            const int32_t id = idx[j];
+            if ((uint32_t)id < (uint32_t)n) res[id] = v - qv;
+            if (out_idx) out_idx[j] = id;
+            word |= code << (2 * q);
+        }
+        codes[wd] = word;
+    }
+}
+
+}  // namespace sgc
+
+using namespace sgc;
+
+extern "C" size_t sgc_binarize_workspace(const sgc_layout* L, int64_t cap)
+{
+    if (!L || cap < 0) return 0;
+    Carver c(nullptr);
+    BinWs w;
+    carve_bin(c, L, cap, &w);
+    return c.off;
+}
+
+extern "C" int sgc_binarize(const sgc_layout* Lc, int32_t mode, const int32_t* idx, const float* val,
+                            const int64_t* counts, int64_t cap, float* residual, int32_t* out_idx,
+                            int64_t* out_counts, float* out_means, uint32_t* out_codes, void* ws, size_t ws_bytes,
+                            sgc_stream_t stream)
+{
+    sgc_layout* L = const_cast<sgc_layout*>(Lc);
+    if (!L || (mode != SGC_BIN_SBC && mode != SGC_BIN_2BIT)) return SGC_EINVAL;
+    if (cap < 0 || cap >= ((int64_t)1 << 31)) return SGC_EINVAL;
+    if (!counts || !out_counts || !out_means || (L->n > 0 && !residual)) return SGC_EINVAL;
+    if (cap > 0 && (!idx || !val)) return SGC_EINVAL;
+    if (mode == SGC_BIN_SBC && cap > 0 && !out_idx) return SGC_EINVAL;
+    if (mode == SGC_BIN_2BIT && cap > 0 && !out_codes) return SGC_EINVAL;
+    Carver c0(nullptr);
+    BinWs w0;
+    carve_bin(c0, L, cap, &w0);
+    if (!ws || ws_bytes < c0.off) return SGC_ENOSPC;
+    Carver c(ws);
+    BinWs w;
+    carve_bin(c, L, cap, &w);
+    hipStream_t s = (hipStream_t)stream;
+    const int32_t nseg = L->nseg;
+    const int64_t nch_max = bin_nch_max(L, cap);
+    const unsigned cb = (unsigned)std::min<int64_t>(nch_max, 2048);
+    k_bin_setup<<<1, 64, 0, s>>>(counts, nseg, cap, w);
+    SGC_LAUNCH_CHECK();
+    k_bin_sums<<<cb, kBlock, 0, s>>>(val, nseg, w);
+    SGC_LAUNCH_CHECK();
+    k_bin_segsum<<<(unsigned)std::min<int64_t>(nseg, 1024), kBlock, 0, s>>>(nseg, w);
+    SGC_LAUNCH_CHECK();
+    k_bin_resolve<<<1, 1024, 0, s>>>(nseg, mode, w, out_counts, out_means);
+    SGC_LAUNCH_CHECK();
+    if (mode == SGC_BIN_SBC) {
+        k_bin_apply_sbc<<<cb, kBlock, 0, s>>>(idx, val, nseg, w, residual, L->n, out_idx, cap);
+    } else {
+        const unsigned wb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(cdiv(cap, 16), kBlock), 4096));
+        k_bin_apply_2bit<<<wb, kBlock, 0, s>>>(idx, val, nseg, w, residual, L->n, out_idx, out_codes);
+    }
+    SGC_LAUNCH_CHECK();
+    return SGC_OK;
+}

@@ -1,0 +1,328 @@
+// rice.hip -- Rice (power-of-two Golomb) coding of index gaps (sgc_encode).
+//
+// [SBC] §II Optimal Position Encoding: the distances between nonzero
+// elements are Golomb coded instead of their positions.  [SBC] appendix A:
+// both ends know the tensor shapes, so a stream carries no shape data.
+//
+// Code of a gap z (zeros skipped before the next entry) with parameter b:
+// floor(z / 2^b) one-bits, a zero-bit, then the b low bits of z LSB-first.
+// Stream bit i is bit (i mod 32) of the stream's word i / 32.
+//
+// GPU design: encode blocks of 2048 codes that never straddle a stream.
+//  1. lengths: per block the sum of code lengths;
+//  2. scan:    block bit offsets (flat scan), stream bit counts and word
+//              offsets (streams start on word boundaries);
+//  3. pack:    per block, code offsets in LDS, then every output word whose
+//              first bit lies in the block is assembled by one thread from
+//              the codes that overlap it (binary search in LDS, plus up to
+//              32 look-ahead codes of the next block): plain stores, no
+//              atomics, no pre-zeroing; the chunk table (bit offset of every
+//              256th code) is written on the way.
+#include "sgc_common.h"
+
+namespace sgc {
+
+struct EncWs {
+    int64_t* cnt;    // [S] codes per stream
+    int64_t* ent;    // [S+1] first entry of each stream
+    int64_t* base;   // [S] position of the stream's element 0
+    int64_t* size;   // [S] elements covered by the stream
+    int64_t* ebpre;  // [S+1] encode-block prefix
+    int64_t* chpre;  // [S+1] chunk-table prefix
+    uint64_t* ebits; // [neb] bits per encode block
+    uint64_t* eboff; // [neb+1] flat exclusive prefix of ebits
+    uint64_t* sbit0; // [S] flat bit offset of each stream's first block
+    uint32_t* bad;   // [1] malformed-input flags
+    uint32_t* st;    // [1] status target when the caller passes none
+};
+
+static int32_t enc_streams(const sgc_layout* L, int32_t scope) { return scope == SGC_GLOBAL ? 1 : L->nseg; }
+static int64_t enc_neb_max(const sgc_layout* L, int32_t scope, int64_t cap)
+{
+    return cdiv(cap, kEncCodes) + enc_streams(L, scope) + 1;
+}
+
+static void carve_enc(Carver& c, const sgc_layout* L, int32_t scope, int64_t cap, EncWs* w)
+{
+    const int64_t S = enc_streams(L, scope), neb = enc_neb_max(L, scope, cap);
+    w->cnt = c.take<int64_t>(S);
+    w->ent = c.take<int64_t>(S + 1);
+    w->base = c.take<int64_t>(S);
+    w->size = c.take<int64_t>(S);
+    w->ebpre = c.take<int64_t>(S + 1);
+    w->chpre = c.take<int64_t>(S + 1);
+    w->ebits = c.take<uint64_t>(neb);
+    w->eboff = c.take<uint64_t>(neb + 1);
+    w->sbit0 = c.take<uint64_t>(S);
+    w->bad = c.take<uint32_t>(1);
+    w->st = c.take<uint32_t>(1);
+}
+
+__global__ void k_enc_setup(const int64_t* __restrict__ counts, const int64_t* __restrict__ seg_off, int32_t nseg,
+                            int32_t scope, int64_t cap, EncWs w)
+{
+    if (threadIdx.x || blockIdx.x) return;
+    const int32_t S = scope == SGC_GLOBAL ? 1 : nseg;
+    int64_t e = 0, eb = 0, ch = 0;
+    w.bad[0] = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        int64_t m = scope == SGC_GLOBAL ? counts[nseg] : counts[s];
+        if (m < 0 || m > cap - e) {  // malformed counts: never read past cap entries
+            w.bad[0] = 1;
+            m = m < 0 ? 0 : cap - e;
+        }
+        w.cnt[s] = m;
+        w.ent[s] = e;
+        w.base[s] = scope == SGC_GLOBAL ? 0 : seg_off[s];
+        w.size[s] = scope == SGC_GLOBAL ? seg_off[nseg] : seg_off[s + 1] - seg_off[s];
+        w.ebpre[s] = eb;
+        w.chpre[s] = ch;
+        e += m;
+        eb += cdiv(m, kEncCodes);
+        ch += cdiv(m, (int64_t)SGC_CHUNK_CODES);
+    }
+    w.ent[S] = e;
+    w.ebpre[S] = eb;
+    w.chpre[S] = ch;
+}
+
+struct EncBlock {
+    int64_t s, e0, e1, ahead;
+};
+
+__device__ inline EncBlock enc_block(const EncWs& w, int32_t S, int64_t b)
+{
+    EncBlock k;
+    k.s = find_bucket(w.ebpre, (int64_t)S + 1, b);
+    k.e0 = w.ent[k.s] + (b - w.ebpre[k.s]) * kEncCodes;
+    k.e1 = min(k.e0 + kEncCodes, w.ent[k.s + 1]);
+    k.ahead = min((int64_t)kEncAhead, w.ent[k.s + 1] - k.e1);
+    return k;
+}
+
+// Gap before entry j of stream s; flags malformed input (not strictly
+// ascending, or outside the stream) and codes it as a zero gap.
+__device__ inline uint32_t enc_gap(const int32_t* __restrict__ idx, const EncWs& w, int64_t s, int64_t j, bool* bad)
+{
+    const int64_t pos = (int64_t)idx[j] - w.base[s];
+    const int64_t prev = j == w.ent[s] ? -1 : (int64_t)idx[j - 1] - w.base[s];
+    const int64_t z = pos - prev - 1;
+    if (z < 0 || pos >= w.size[s]) {
+        *bad = true;
+        return 0;
+    }
+    return (uint32_t)z;
+}
+
+__global__ __launch_bounds__(kBlock) void k_enc_len(const int32_t* __restrict__ idx, int32_t S, int32_t b, EncWs w)
+{
+    __shared__ uint64_t tmp[kBlock / 64 + 1];
+    const int64_t neb = w.ebpre[S];
+    for (int64_t blk = blockIdx.x; blk < neb; blk += gridDim.x) {
+        const EncBlock k = enc_block(w, S, blk);
+        uint64_t bits = 0;
+        bool bad = false;
+        for (int64_t j = k.e0 + threadIdx.x; j < k.e1; j += kBlock) {
+            const uint32_t z = enc_gap(idx, w, k.s, j, &bad);
+            bits += (uint64_t)(z >> b) + 1 + (uint64_t)b;
+        }
+        if (bad) atomicOr(w.bad, 1u);
+        uint64_t tot;
+        block_exclusive_scan<uint64_t>(bits, tmp, &tot);
+        if (threadIdx.x == 0) w.ebits[blk] = tot;
+    }
+}
+
+__global__ __launch_bounds__(1024) void k_enc_scan(int32_t S, int64_t word_cap, EncWs w,
+                                                  uint64_t* __restrict__ word_off, uint64_t* __restrict__ nbits,
+                                                  uint32_t* status)
+{
+    __shared__ uint64_t tmp[1024 / 64 + 1];
+    const int64_t neb = w.ebpre[S];
+    const int64_t per = cdiv(neb, (int64_t)blockDim.x);
+    const int64_t b = threadIdx.x * per, e = min(b + per, neb);
+    uint64_t local = 0;
+    for (int64_t i = b; i < e; ++i) local += w.ebits[i];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t x = local;
+    for (int d = 1; d < 64; d <<= 1) {
+        uint64_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t run = 0;
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) { uint64_t q = tmp[i]; tmp[i] = run; run += q; }
+        tmp[blockDim.x >> 6] = run;
+    }
+    __syncthreads();
+    uint64_t run = tmp[wave] + x - local;
+    for (int64_t i = b; i < e; ++i) {
+        w.eboff[i] = run;
+        run += w.ebits[i];
+    }
+    if (threadIdx.x == 0) w.eboff[neb] = tmp[blockDim.x >> 6];
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    uint64_t words = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        const uint64_t b0 = w.eboff[w.ebpre[s]];
+        const uint64_t nb = w.eboff[w.ebpre[s + 1]] - b0;
+        w.sbit0[s] = b0;
+        word_off[s] = words;
+        nbits[s] = nb;
+        words += (nb + 31) / 32;
+    }
+    word_off[S] = words;
+    if (words > (uint64_t)word_cap) w.bad[0] |= 2u;  // only reachable with malformed input
+    if (w.bad[0]) *status |= SGC_STATUS_BAD_INPUT;
+}
+
+constexpr int kEncLds = (int)kEncCodes + kEncAhead;
+constexpr int kEncPer = (kEncLds + kBlock - 1) / kBlock;  // entries per thread in the LDS prefix
+
+__global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__ idx, int32_t S, int32_t b, EncWs w,
+                                                    uint32_t* __restrict__ words, const uint64_t* __restrict__ word_off,
+                                                    uint64_t* __restrict__ chunk_off)
+{
+    __shared__ uint32_t zs[kEncLds];
+    __shared__ uint32_t off[kEncLds + 1];
+    __shared__ uint32_t tmp[kBlock / 64 + 1];
+    if (w.bad[0] & 2u) return;
+    const int64_t neb = w.ebpre[S];
+    for (int64_t blk = blockIdx.x; blk < neb; blk += gridDim.x) {
+        const EncBlock k = enc_block(w, S, blk);
+        const int nown = (int)(k.e1 - k.e0), ntot = nown + (int)k.ahead;
+        // gaps and code lengths, thread-contiguous so the prefix is one block scan
+        uint32_t len[kEncPer];
+        uint32_t local = 0;
+        bool bad = false;
+#pragma unroll
+        for (int q = 0; q < kEncPer; ++q) {
+            const int i = threadIdx.x * kEncPer + q;
+            len[q] = 0;
+            if (i < ntot) {
+                const uint32_t z = enc_gap(idx, w, k.s, k.e0 + i, &bad);
+                zs[i] = z;
+                len[q] = (z >> b) + 1 + (uint32_t)b;
+                local += len[q];
+            }
+        }
+        uint32_t tot;
+        uint32_t run = block_exclusive_scan<uint32_t>(local, tmp, &tot);
+#pragma unroll
+        for (int q = 0; q < kEncPer; ++q) {
+            const int i = threadIdx.x * kEncPer + q;
+            if (i < ntot) {
+                off[i] = run;
+                run += len[q];
+            }
+        }
+        if (threadIdx.x == kBlock - 1) off[ntot] = tot;  // ntot <= kEncLds
+        __syncthreads();
+        const uint64_t B0 = w.eboff[blk] - w.sbit0[k.s];  // stream-relative first bit of the block
+        const uint64_t B1 = B0 + off[nown];
+        const int64_t q0 = k.e0 - w.ent[k.s];            // stream-relative index of the first code
+        uint32_t* sw = words + word_off[k.s];
+        // chunk table: bit offset of every SGC_CHUNK_CODES-th code
+        for (int i = threadIdx.x * SGC_CHUNK_CODES; i < nown; i += kBlock * SGC_CHUNK_CODES)
+            chunk_off[w.chpre[k.s] + (q0 + i) / SGC_CHUNK_CODES] = B0 + off[i];
+        const uint64_t wfirst = (B0 + 31) / 32, wend = (B1 + 31) / 32;
+        for (uint64_t wd = wfirst + threadIdx.x; wd < wend; wd += kBlock) {
+            const uint64_t W0 = wd * 32;
+            // first code whose end lies past W0 (its start is <= W0 or it is code 0)
+            int lo = 0, hi = ntot - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (B0 + off[mid + 1] <= W0) lo = mid + 1; else hi = mid;
+            }
+            uint32_t v = 0;
+            for (int i = lo; i < ntot; ++i) {
+                const uint64_t o = B0 + off[i];
+                if (o >= W0 + 32) break;
+                const uint32_t z = zs[i];
+                const uint64_t q = z >> b;
+                // unary one-bits [o, o+q)
+                const uint64_t a0 = o > W0 ? o : W0;
+                const uint64_t a1 = (o + q) < (W0 + 32) ? (o + q) : (W0 + 32);
+                if (a0 < a1) {
+                    const uint32_t nbit = (uint32_t)(a1 - a0);
+                    const uint32_t m = nbit >= 32 ? 0xffffffffu : ((1u << nbit) - 1u);
+                    v |= m << (uint32_t)(a0 - W0);
+                }
+                // remainder bits start after the terminating zero
+                if (b > 0) {
+                    const int64_t sh = (int64_t)(o + q + 1) - (int64_t)W0;
+                    const uint64_t rem = (uint64_t)(z & ((1u << b) - 1u));
+                    if (sh >= 0 && sh < 32) v |= (uint32_t)(rem << sh);
+                    else if (sh < 0 && -sh < b) v |= (uint32_t)(rem >> (-sh));
+                }
+            }
+            sw[wd] = v;
+        }
+        __syncthreads();  // LDS reuse by the next block of this workgroup
+    }
+}
+
+}  // namespace sgc
+
+using namespace sgc;
+
+extern "C" int64_t sgc_encode_word_bound(const sgc_layout* L, int32_t scope, int32_t b, int64_t cap)
+{
+    if (!L || (scope != SGC_GLOBAL && scope != SGC_PER_SEGMENT) || b < 0 || b > 30 || cap < 0) return -1;
+    const int64_t bits = cap * (int64_t)(b + 1) + (L->n >> b);
+    return cdiv(bits, 32) + enc_streams(L, scope);
+}
+
+extern "C" int64_t sgc_encode_chunk_bound(const sgc_layout* L, int32_t scope, int64_t cap)
+{
+    if (!L || (scope != SGC_GLOBAL && scope != SGC_PER_SEGMENT) || cap < 0) return -1;
+    return cdiv(cap, (int64_t)SGC_CHUNK_CODES) + enc_streams(L, scope);
+}
+
+extern "C" size_t sgc_encode_workspace(const sgc_layout* L, int32_t scope, int64_t cap)
+{
+    if (!L || (scope != SGC_GLOBAL && scope != SGC_PER_SEGMENT) || cap < 0) return 0;
+    Carver c(nullptr);
+    EncWs w;
+    carve_enc(c, L, scope, cap, &w);
+    return c.off;
+}
+
+extern "C" int sgc_encode(const sgc_layout* Lc, int32_t scope, int32_t b, const int32_t* idx, const int64_t* counts,
+                          int64_t cap, uint32_t* out_words, int64_t word_cap, uint64_t* out_word_off,
+                          uint64_t* out_nbits, uint64_t* out_chunk_off, int64_t chunk_cap, uint32_t* dstatus,
+                          void* ws, size_t ws_bytes, sgc_stream_t stream)
+{
+    sgc_layout* L = const_cast<sgc_layout*>(Lc);
+    if (!L || (scope != SGC_GLOBAL && scope != SGC_PER_SEGMENT) || b < 0 || b > 30) return SGC_EINVAL;
+    if (cap < 0 || cap >= ((int64_t)1 << 31) || !counts || !out_word_off || !out_nbits) return SGC_EINVAL;
+    if (cap > 0 && (!idx || !out_words || !out_chunk_off)) return SGC_EINVAL;
+    if (word_cap < sgc_encode_word_bound(L, scope, b, cap)) return SGC_ENOSPC;
+    if (chunk_cap < sgc_encode_chunk_bound(L, scope, cap)) return SGC_ENOSPC;
+    Carver c0(nullptr);
+    EncWs w0;
+    carve_enc(c0, L, scope, cap, &w0);
+    if (!ws || ws_bytes < c0.off) return SGC_ENOSPC;
+    Carver c(ws);
+    EncWs w;
+    carve_enc(c, L, scope, cap, &w);
+    DevTables* dt = nullptr;
+    int rc = device_tables(L, &dt);
+    if (rc) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const int32_t S = enc_streams(L, scope);
+    uint32_t* status = dstatus ? dstatus : w.st;
+    k_enc_setup<<<1, 64, 0, s>>>(counts, dt->seg_off, L->nseg, scope, cap, w);
+    SGC_LAUNCH_CHECK();
+    const unsigned gb = (unsigned)std::min<int64_t>(enc_neb_max(L, scope, cap), 4096);
+    k_enc_len<<<gb, kBlock, 0, s>>>(idx, S, b, w);
+    SGC_LAUNCH_CHECK();
+    k_enc_scan<<<1, 1024, 0, s>>>(S, word_cap, w, out_word_off, out_nbits, status);
+    SGC_LAUNCH_CHECK();
+    k_enc_pack<<<gb, kBlock, 0, s>>>(idx, S, b, w, out_words, out_word_off, out_chunk_off);
+    SGC_LAUNCH_CHECK();
+    return SGC_OK;
+}
