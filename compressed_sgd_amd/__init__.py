@@ -37,7 +37,7 @@ EXPORTED = (
     "sgc_compress_workspace", "sgc_compress",
     "sgc_binarize_workspace", "sgc_binarize",
     "sgc_encode_word_bound", "sgc_encode_chunk_bound", "sgc_encode_workspace", "sgc_encode",
-    "sgc_decode_accumulate_workspace", "sgc_decode_accumulate",
+    "sgc_decode_accumulate_workspace", "sgc_decode_accumulate", "sgc_set_pass_events",
 )
 
 
@@ -107,6 +107,8 @@ def lib():
         L.sgc_decode_accumulate_workspace.restype = sz
         L.sgc_decode_accumulate.argtypes = [P, P, i32, i32, P, P, P, P, sz, P]
         L.sgc_decode_accumulate.restype = C.c_int
+        L.sgc_set_pass_events.argtypes = [P, P]
+        L.sgc_set_pass_events.restype = C.c_int
         _lib = L
     return _lib
 
@@ -381,3 +383,12 @@ def decode_accumulate(layout: Layout, msgs: Sequence[Message], out: torch.Tensor
     _check(lib().sgc_decode_accumulate(layout.handle, arr, W, init, _ptr(base), _ptr(out), _ptr(status), _ptr(ws),
                                        ws.numel(), _stream(dev, stream)), "sgc_decode_accumulate")
     return status
+
+
+def set_pass_events(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]) -> None:
+    """Time the fused pass of later compress calls with these (already recorded once) events."""
+    if start is None:
+        _check(lib().sgc_set_pass_events(None, None), "sgc_set_pass_events")
+    else:
+        _check(lib().sgc_set_pass_events(C.c_void_p(start.cuda_event), C.c_void_p(stop.cuda_event)),
+               "sgc_set_pass_events")

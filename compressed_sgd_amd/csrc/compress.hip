@@ -7,26 +7,34 @@
 // only residual += grad is done (SGC_ACCUMULATE_ONLY).
 //
 // GPU design (one HBM pass over the gradient in the common case):
-//  1. probe   -- gather a small systematic sample of acc per group and
-//                select from it a lower bound key_lo for the magnitude key
-//                (exact mode: a margin below the estimated k-th largest;
-//                sampled mode: the method's threshold itself).
-//  2. pass 1  -- stream g and r once: acc = r + g, store acc to r, and emit
-//                every element with key >= key_lo into a per-tile region
-//                (wave ballots + LDS offsets, index order kept).
-//  3. gather  -- scan the tile counts and copy the regions into one ordered
-//                candidate array (a tile whose region overflowed is redone
-//                from r, which now holds acc).  Sampled mode: this IS the
-//                output.
-//  4. select  -- exact k-th largest key per group over the candidates by a
-//                3-digit radix select (11+10+10 bits, LDS histograms).  If
-//                a group has fewer than k candidates (the sample misled) or
-//                the candidate array is full, the group is selected and
-//                compacted straight from r instead (same result, more
-//                passes; reported as SGC_STATUS_DENSE_PATH).
-//  5. compact -- keep key > T, plus the first `quota` entries with key == T
+//  1. probe   -- read a small sample of acc per group (runs of 16 elements)
+//                and radix-select two bounds from it: key_lo, a margin below
+//                the estimated k-th largest magnitude key (the candidate
+//                bound), and key_z, a margin above it (elements at or above
+//                it are almost surely kept).  Sampled mode instead takes
+//                the method's own systematic sample and threshold T, with
+//                key_lo = key_z = T.
+//  2. pass 1  -- stream g and r once: acc = r + g; every element with
+//                key >= key_lo goes into its tile's candidate region (wave
+//                ballots + LDS offsets, index order kept); r is stored as
+//                acc, or as +0 for key >= key_z, so that most kept entries
+//                leave the residual without a second, scattered write.  A
+//                tile whose region overflows stores plain acc everywhere.
+//  3. scan    -- tile counts -> offsets (per 4096-tile super block, then
+//                one small scan); per group: candidate count, and whether
+//                the group is selected from its candidates or, if the probe
+//                misled (fewer than k candidates) or the candidate array is
+//                full, straight from the residual.
+//  4. gather  -- one workgroup per 16 tiles copies their regions into one
+//                ordered candidate array (sampled mode: into the output);
+//                an overflowed tile is redone from r (= acc there).
+//  5. select  -- exact k-th largest key per group over its candidates by a
+//                3-digit radix select (11+10+10 bits, LDS histograms).
+//  6. compact -- keep key > T, plus the first `quota` entries with key == T
 //                in index order (lower index wins the tie); write idx/val
-//                ascending and zero the residual at the kept positions.
+//                ascending; zero the residual only where pass 1 did not,
+//                and give back acc to any entry pass 1 zeroed but the exact
+//                selection did not keep.
 #include "sgc_common.h"
 
 namespace sgc {
@@ -34,26 +42,31 @@ namespace sgc {
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSrcSamples = 0, kSrcCand = 1, kSrcDense = 2;
+constexpr int kSuper = 4096;                     // tiles per scan super block
+constexpr int kGatherTiles = 16;                 // tiles per gather workgroup
+constexpr uint32_t kAccFlag = 0x80000000u;       // candidate index flag: r still holds acc there
 
 struct CompressWs {
     int64_t* k;        // [G] keep count
     int64_t* s;        // [G] probe / sample size
     int64_t* spre;     // [G+1] sample prefix
     int64_t* kpre;     // [G+1] keep-count prefix (exact output offsets)
-    uint32_t* key_lo;  // [G] pass-1 candidate bound
-    int32_t* src_kind; // [G] selection source
-    int64_t* src_base; // [G]
-    int64_t* src_len;  // [G]
-    int64_t* rank;     // [G] wanted rank (1-based); 0 = select nothing
-    int64_t* cpre;     // [G+1] chunk prefix over the selection source
-    uint32_t* prefix;  // [G] radix-select prefix -> T
-    int64_t* mrem;     // [G] remaining rank -> quota of ties at T
-    int64_t* cnt_gt;   // [G] elements with key > T
-    uint32_t* hist;    // [G * kBins]
+    uint32_t* key_lo;  // [G] candidate bound
+    uint32_t* key_z;   // [G] pass-1 zeroing bound
+    // radix-select state, 2G virtual groups (probe: lower and upper bound)
+    int32_t* src_kind; // [2G]
+    int64_t* src_base; // [2G]
+    int64_t* src_len;  // [2G]
+    int64_t* rank;     // [2G] wanted rank (1-based); 0 = select nothing
+    int64_t* cpre;     // [2G+1] chunk prefix over the selection source
+    uint32_t* prefix;  // [2G] radix-select prefix -> T
+    int64_t* mrem;     // [2G] remaining rank -> quota of ties at T
+    uint32_t* hist;    // [2G * kBins]
     int64_t* cstart;   // [G] candidate array start per group
     float* samples;    // [S]
     uint32_t* tile_cnt;// [NT]
-    int64_t* tile_pre; // [NT+1]
+    int64_t* tile_loc; // [NT] exclusive prefix inside the super block
+    int64_t* sup_pre;  // [NS+1] super block prefix
     int32_t* reg_idx;  // [NT * kTileCap]
     float* reg_val;    // [NT * kTileCap]
     int32_t* cand_idx; // [capc]
@@ -62,21 +75,22 @@ struct CompressWs {
     uint32_t* ch_eq;   // [nch_max]
     int64_t* ch_gt_pre;// [nch_max+1]
     int64_t* ch_eq_pre;// [nch_max+1]
-    int64_t* scal;     // [8]: 0 output total
+    int64_t* scal;     // [8]: 0 output total, 1 candidate total
     uint32_t* status;  // [1] used when the caller passes no dstatus
 };
 
 struct CompressSizes {
     int32_t G;
-    int64_t NT, S, capc, nch_max;
+    int64_t NT, NS, S, capc, nch_max;
 };
 
-static CompressSizes compress_sizes(const sgc_layout* L, const sgc_compress_opts* o, int64_t /*cap*/)
+static CompressSizes compress_sizes(const sgc_layout* L, const sgc_compress_opts* o)
 {
     CompressSizes z;
     std::vector<int64_t> off = host_group_off(L, o->scope);
     z.G = (int32_t)off.size() - 1;
     z.NT = (o->scope == SGC_GLOBAL) ? group_tiles(0, L->n) : L->seg_tile[L->nseg];
+    z.NS = cdiv(z.NT, kSuper);
     z.S = 0;
     int64_t K = 0;
     for (int32_t g = 0; g < z.G; ++g) {
@@ -85,31 +99,32 @@ static CompressSizes compress_sizes(const sgc_layout* L, const sgc_compress_opts
         K += keep_count(m, o->keep_ppm);
     }
     z.capc = (o->mode == SGC_EXACT) ? std::min<int64_t>(L->n, 4 * K + 262144) : 0;
-    z.nch_max = cdiv(L->n + z.capc + z.S, kChunk) + 2 * (int64_t)z.G + 2;
+    z.nch_max = cdiv(L->n + z.capc + 2 * z.S, kChunk) + 4 * (int64_t)z.G + 2;
     return z;
 }
 
 static void carve_compress(Carver& c, const CompressSizes& z, int mode, CompressWs* w)
 {
-    const int64_t G = z.G;
+    const int64_t G = z.G, V = 2 * (int64_t)z.G;
     w->k = c.take<int64_t>(G);
     w->s = c.take<int64_t>(G);
     w->spre = c.take<int64_t>(G + 1);
     w->kpre = c.take<int64_t>(G + 1);
     w->key_lo = c.take<uint32_t>(G);
-    w->src_kind = c.take<int32_t>(G);
-    w->src_base = c.take<int64_t>(G);
-    w->src_len = c.take<int64_t>(G);
-    w->rank = c.take<int64_t>(G);
-    w->cpre = c.take<int64_t>(G + 1);
-    w->prefix = c.take<uint32_t>(G);
-    w->mrem = c.take<int64_t>(G);
-    w->cnt_gt = c.take<int64_t>(G);
-    w->hist = c.take<uint32_t>(G * kBins);
+    w->key_z = c.take<uint32_t>(G);
+    w->src_kind = c.take<int32_t>(V);
+    w->src_base = c.take<int64_t>(V);
+    w->src_len = c.take<int64_t>(V);
+    w->rank = c.take<int64_t>(V);
+    w->cpre = c.take<int64_t>(V + 1);
+    w->prefix = c.take<uint32_t>(V);
+    w->mrem = c.take<int64_t>(V);
+    w->hist = c.take<uint32_t>(V * kBins);
     w->cstart = c.take<int64_t>(G);
     w->samples = c.take<float>(z.S);
     w->tile_cnt = c.take<uint32_t>(z.NT);
-    w->tile_pre = c.take<int64_t>(z.NT + 1);
+    w->tile_loc = c.take<int64_t>(z.NT);
+    w->sup_pre = c.take<int64_t>(z.NS + 1);
     w->reg_idx = c.take<int32_t>(z.NT * kTileCap);
     w->reg_val = c.take<float>(z.NT * kTileCap);
     if (mode == SGC_EXACT) {
@@ -129,26 +144,33 @@ static void carve_compress(Carver& c, const CompressSizes& z, int mode, Compress
     w->status = c.take<uint32_t>(1);
 }
 
+// Global exclusive prefix of tile t (t == NT gives the total).
+__device__ inline int64_t tile_prefix(const CompressWs& w, int64_t NT, int64_t t)
+{
+    return t >= NT ? w.sup_pre[cdiv(NT, kSuper)] : w.sup_pre[t / kSuper] + w.tile_loc[t];
+}
+
 // ------------------------------------------------------------ accumulate
 __global__ __launch_bounds__(kBlock) void k_accumulate(const float* __restrict__ g, float* __restrict__ r, int64_t n)
 {
     const int64_t n4 = n >> 2;
     const f4* g4 = (const f4*)g;
     f4* r4 = (f4*)r;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kBlock) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < n4) {
         f4 a = __builtin_nontemporal_load(r4 + i);
         f4 b = __builtin_nontemporal_load(g4 + i);
         __builtin_nontemporal_store(a + b, r4 + i);
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
-        int64_t i = (n4 << 2) + threadIdx.x;
-        r[i] = r[i] + g[i];
+        const int64_t j = (n4 << 2) + threadIdx.x;
+        r[j] = r[j] + g[j];
     }
 }
 
 // ----------------------------------------------------------------- setup
-// One thread walks the groups: keep counts, sample sizes, prefixes, and
-// the rank each group's probe selection needs.
+// One thread walks the groups: keep counts, probe sizes, prefixes, and the
+// two ranks (lower / upper bound) each group's probe selection needs.
 __global__ void k_setup(const int64_t* __restrict__ goff, int32_t G, int32_t mode, uint32_t ppm, uint32_t div,
                         uint32_t smin, CompressWs w)
 {
@@ -158,72 +180,95 @@ __global__ void k_setup(const int64_t* __restrict__ goff, int32_t G, int32_t mod
         const int64_t m = goff[g + 1] - goff[g];
         const int64_t k = keep_count(m, ppm);
         const int64_t s = (mode == SGC_EXACT) ? probe_count(m) : sampled_count(m, div, smin);
-        int64_t rank = 0;
-        uint32_t klo = kNoKey;
+        int64_t rlo = 0, rhi = 0;
+        uint32_t klo = kNoKey, kz = kNoKey;
         if (mode == SGC_EXACT) {
             if (k > 0) {
                 if (s == m) {
-                    rank = k;  // the probe saw every element: its k-th key is the exact threshold
+                    rlo = rhi = k;  // the probe read every element: its k-th key is the threshold
                 } else {
-                    // expected sampled keys above the true threshold, plus a 6-sigma margin
-                    double e = (double)s * (double)k / (double)m;
-                    int64_t mm = (int64_t)(e + 6.0 * sqrt(e) + 8.0) + 1;
-                    if (mm >= s) klo = 0;  // the bound would be the sample minimum: take every element
-                    else rank = mm;
+                    // expected sampled keys above the true threshold, 6-sigma margins either side
+                    const double e = (double)s * (double)k / (double)m;
+                    const double d = 6.0 * sqrt(e) + 8.0;
+                    const int64_t lo = (int64_t)(e + d) + 1;
+                    const int64_t hi = (int64_t)(e - d);
+                    if (lo >= s) klo = 0;  // the bound would be the sample minimum: take every element
+                    else rlo = lo;
+                    if (hi >= 1) rhi = hi;
                 }
             }
         } else {
-            rank = keep_count(s, ppm);
+            rlo = keep_count(s, ppm);  // the method's threshold; zeroing uses the same key
         }
         w.k[g] = k;
         w.s[g] = s;
         w.spre[g] = sp;
         w.kpre[g] = kp;
         w.key_lo[g] = klo;
-        w.rank[g] = rank;
-        w.src_kind[g] = kSrcSamples;
-        w.src_base[g] = sp;
-        w.src_len[g] = rank > 0 ? s : 0;
-        w.cpre[g] = cp;
-        w.prefix[g] = 0;
-        w.mrem[g] = rank;
-        w.cnt_gt[g] = 0;
+        w.key_z[g] = kz;
+        for (int v = 0; v < 2; ++v) {
+            const int64_t vg = 2 * (int64_t)g + v;
+            const int64_t r = v == 0 ? rlo : rhi;
+            w.rank[vg] = r;
+            w.src_kind[vg] = kSrcSamples;
+            w.src_base[vg] = sp;
+            w.src_len[vg] = r > 0 ? s : 0;
+            w.cpre[vg] = cp;
+            w.prefix[vg] = 0;
+            w.mrem[vg] = r;
+            cp += cdiv(w.src_len[vg], kChunk);
+        }
         sp += s;
         kp += k;
-        cp += cdiv(w.src_len[g], kChunk);
     }
     w.spre[G] = sp;
     w.kpre[G] = kp;
-    w.cpre[G] = cp;
+    w.cpre[2 * G] = cp;
 }
 
-// Systematic sample of acc = r + g at floor((2j+1) m / (2s)) within each group.
+// Probe: acc = r + g at the sample positions.  Exact mode: runs of kRun
+// contiguous elements at systematic unit positions (the whole group if it
+// is small).  Sampled mode: the method's systematic single-element sample
+// floor((2j+1) m / (2s)).
 __global__ __launch_bounds__(kBlock) void k_probe(const float* __restrict__ grad, const float* __restrict__ res,
-                                                 const int64_t* __restrict__ goff, int32_t G, CompressWs w, int64_t S)
+                                                 const int64_t* __restrict__ goff, int32_t G, int32_t mode,
+                                                 CompressWs w, int64_t S)
 {
     for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < S; j += (int64_t)gridDim.x * kBlock) {
         const int64_t g = find_bucket(w.spre, (int64_t)G + 1, j);
         const int64_t m = goff[g + 1] - goff[g];
         const int64_t s = w.s[g];
         const uint64_t jj = (uint64_t)(j - w.spre[g]);
-        const int64_t pos = goff[g] + (int64_t)(((2 * jj + 1) * (uint64_t)m) / (2 * (uint64_t)s));
+        int64_t pos;
+        if (mode == SGC_EXACT) {
+            const int64_t P = probe_points(m);
+            if (P == 0) {
+                pos = goff[g] + (int64_t)jj;
+            } else {
+                const uint64_t pt = jj / kRun, units = (uint64_t)(m / kRun);
+                const uint64_t unit = ((2 * pt + 1) * units) / (2 * (uint64_t)P);
+                pos = goff[g] + (int64_t)(unit * kRun + jj % kRun);
+            }
+        } else {
+            pos = goff[g] + (int64_t)(((2 * jj + 1) * (uint64_t)m) / (2 * (uint64_t)s));
+        }
         w.samples[j] = res[pos] + grad[pos];
     }
 }
 
 // ----------------------------------------------------------- radix select
-// Histogram of one digit over every selection source chunk whose group is
-// still open and whose key matches the digits chosen so far.
+// Histogram of one digit over every selection source chunk whose (virtual)
+// group is still open and whose key matches the digits chosen so far.
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ res, int32_t G, CompressWs w)
+__global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ res, int32_t V, CompressWs w)
 {
     constexpr int shift = D == 0 ? 20 : D == 1 ? 10 : 0;
     constexpr uint32_t mask = D == 0 ? 0x7ffu : 0x3ffu;
     constexpr int nb = D == 0 ? 2048 : 1024;
     __shared__ uint32_t h[nb];
-    const int64_t nch = w.cpre[G];
+    const int64_t nch = w.cpre[V];
     for (int64_t c = blockIdx.x; c < nch; c += gridDim.x) {
-        const int64_t g = find_bucket(w.cpre, (int64_t)G + 1, c);
+        const int64_t g = find_bucket(w.cpre, (int64_t)V + 1, c);
         if (w.mrem[g] == 0) continue;
         for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
         __syncthreads();
@@ -237,7 +282,7 @@ __global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ r
             if (D == 0 || (key >> (shift + 10)) == pre) atomicAdd(&h[(key >> shift) & mask], 1u);
         }
         __syncthreads();
-        uint32_t* gh = w.hist + (int64_t)g * kBins;
+        uint32_t* gh = w.hist + g * kBins;
         for (int b = threadIdx.x; b < nb; b += kBlock)
             if (h[b]) atomicAdd(&gh[b], h[b]);
         __syncthreads();
@@ -246,7 +291,7 @@ __global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ r
 
 // Pick the digit holding the wanted rank (counted from the largest key).
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_srs_resolve(int32_t G, CompressWs w)
+__global__ __launch_bounds__(kBlock) void k_srs_resolve(CompressWs w)
 {
     constexpr int nb = D == 0 ? 2048 : 1024;
     constexpr int bits = D == 0 ? 11 : 10;
@@ -270,7 +315,6 @@ __global__ __launch_bounds__(kBlock) void k_srs_resolve(int32_t G, CompressWs w)
             const int64_t c = gh[bin];
             if (run + c >= target) {
                 w.prefix[g] = (w.prefix[g] << bits) | (uint32_t)bin;
-                w.cnt_gt[g] += run;
                 w.mrem[g] = target - run;
                 break;
             }
@@ -281,37 +325,48 @@ __global__ __launch_bounds__(kBlock) void k_srs_resolve(int32_t G, CompressWs w)
     for (int i = 1; i <= per; ++i) gh[top - i] = 0;
 }
 
-// After the probe selection: pass-1 bound of every group that selected.
-__global__ void k_probe_done(int32_t G, CompressWs w)
+// After the probe selection: the candidate and zeroing bounds of each group.
+__global__ void k_probe_done(int32_t G, int32_t mode, CompressWs w)
 {
-    for (int32_t g = blockIdx.x * kBlock + threadIdx.x; g < G; g += gridDim.x * kBlock)
-        if (w.rank[g] > 0) w.key_lo[g] = w.prefix[g];
+    for (int32_t g = blockIdx.x * kBlock + threadIdx.x; g < G; g += gridDim.x * kBlock) {
+        if (w.rank[2 * g] > 0) w.key_lo[g] = w.prefix[2 * g];
+        if (mode == SGC_EXACT) {
+            if (w.rank[2 * g + 1] > 0) w.key_z[g] = w.prefix[2 * g + 1];
+        } else {
+            w.key_z[g] = w.key_lo[g];
+        }
+    }
 }
 
 // ---------------------------------------------------------------- pass 1
-// Writes the candidates of one tile in index order through `sink(pos, i, v)`.
-// ADD: acc = r + g is formed and stored to r (pass 1); otherwise r already
-// holds acc (redo of an overflowed tile).  Returns the tile's candidate count
-// to every thread.
+// Candidates of one tile in index order through `sink(pos, i, v)`.  ADD:
+// acc = r + g is formed and r is stored (acc, or +0 for key >= kz when the
+// region does not overflow); otherwise r already holds acc (redo of an
+// overflowed tile).  Returns the tile's candidate count to every thread.
+// Indices are 32-bit (n < 2^31); the tile base is uniform, so each access
+// is a scalar base plus one 32-bit lane offset.  A tile that lies entirely
+// inside its group skips every per-element range check.
 template <bool ADD, typename Sink>
-__device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float* __restrict__ res, int64_t lo,
-                                           int64_t hi, int64_t A, uint32_t klo, Sink sink)
+__device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float* __restrict__ res, int32_t lo,
+                                           int32_t hi, int32_t A, uint32_t klo, uint32_t kz, Sink sink)
 {
     __shared__ uint32_t wtot[kSlots][kBlock / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool full = A >= lo && A + (int32_t)kTile <= hi;  // uniform
+    const f4* rb = (const f4*)(res + A);
+    const f4* gb = (const f4*)(grad + A);
     f4 acc[kSlots];
+    if (full) {
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
-        const int64_t e = A + 4 * ((int64_t)u * kBlock + tid);
-        if (e >= lo && e + 4 <= hi) {
-            if (ADD) {
-                f4 rv = __builtin_nontemporal_load((const f4*)(res + e));
-                f4 gv = __builtin_nontemporal_load((const f4*)(grad + e));
-                acc[u] = rv + gv;
-            } else {
-                acc[u] = *(const f4*)(res + e);
-            }
-        } else {
+        for (int u = 0; u < kSlots; ++u) {
+            const int o = u * kBlock + tid;
+            if (ADD) acc[u] = __builtin_nontemporal_load(rb + o) + __builtin_nontemporal_load(gb + o);
+            else acc[u] = rb[o];
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kSlots; ++u) {
+            const int32_t e = A + 4 * (u * kBlock + tid);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float a = 0.0f;
@@ -320,28 +375,16 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
             }
         }
     }
-    if (ADD) {
-#pragma unroll
-        for (int u = 0; u < kSlots; ++u) {
-            const int64_t e = A + 4 * ((int64_t)u * kBlock + tid);
-            if (e >= lo && e + 4 <= hi) {
-                __builtin_nontemporal_store(acc[u], (f4*)(res + e));
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (e + j >= lo && e + j < hi) res[e + j] = acc[u][j];
-            }
-        }
-    }
-    uint32_t flags[kSlots], pre[kSlots];
+    uint32_t flags = 0;  // 4 bits per slot
+    uint32_t pre[kSlots];
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
-        const int64_t e = A + 4 * ((int64_t)u * kBlock + tid);
+        const int32_t e = A + 4 * (u * kBlock + tid);
         uint32_t f = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (e + j >= lo && e + j < hi && mag_key(acc[u][j]) >= klo) f |= 1u << j;
-        flags[u] = f;
+            if ((full || (e + j >= lo && e + j < hi)) && mag_key(acc[u][j]) >= klo) f |= 1u << j;
+        flags |= f << (4 * u);
         const uint32_t cnt = __popc(f);
         const uint64_t b0 = __ballot(cnt & 1u), b1 = __ballot(cnt & 2u), b2 = __ballot(cnt & 4u);
         const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -349,23 +392,54 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
         if (lane == 0) wtot[u][wave] = __popcll(b0) + 2u * __popcll(b1) + 4u * __popcll(b2);
     }
     __syncthreads();
-    uint32_t run = 0, base[kSlots];
+    // offset of this lane's first candidate in slot u: every candidate of the
+    // earlier slots, then of the earlier waves in slot u, then the wave prefix
+    uint32_t run = 0;
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
+        const uint32_t slot_base = run;
+        uint32_t before = 0;
         for (int v = 0; v < kBlock / 64; ++v) {
-            if (v == wave) base[u] = run;
-            run += wtot[u][v];
+            const uint32_t c = wtot[u][v];
+            before += v < wave ? c : 0u;
+            run += c;
         }
+        pre[u] += slot_base + before;
     }
     __syncthreads();  // wtot is reused by the next call in this block
+    if (ADD) {
+        const uint32_t z = run <= (uint32_t)kTileCap ? kz : kNoKey;  // overflow: keep acc everywhere
+        f4* rw = (f4*)(res + A);
+        if (full) {
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
-        if (!flags[u]) continue;
-        const int64_t e = A + 4 * ((int64_t)u * kBlock + tid);
-        uint32_t pos = base[u] + pre[u];
+            for (int u = 0; u < kSlots; ++u) {
+                f4 st = acc[u];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (flags[u] & (1u << j)) sink(pos++, e + j, acc[u][j]);
+                for (int j = 0; j < 4; ++j)
+                    if (mag_key(st[j]) >= z) st[j] = 0.0f;
+                __builtin_nontemporal_store(st, rw + u * kBlock + tid);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kSlots; ++u) {
+                const int32_t e = A + 4 * (u * kBlock + tid);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (e + j >= lo && e + j < hi) res[e + j] = mag_key(acc[u][j]) >= z ? 0.0f : acc[u][j];
+            }
+        }
+    }
+    if (flags) {
+#pragma unroll
+        for (int u = 0; u < kSlots; ++u) {
+            const uint32_t f = (flags >> (4 * u)) & 15u;
+            if (!f) continue;
+            const int32_t e = A + 4 * (u * kBlock + tid);
+            uint32_t pos = pre[u];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (f & (1u << j)) sink(pos++, e + j, acc[u][j]);
+        }
     }
     return run;
 }
@@ -381,21 +455,21 @@ __global__ __launch_bounds__(kBlock) void k_pass1(const float* __restrict__ grad
 {
     const int64_t t = blockIdx.x;
     const int64_t g = tile_group(gtile, G, t);
-    const int64_t lo = goff[g], hi = goff[g + 1];
-    const int64_t A = (lo & ~(int64_t)3) + (t - gtile[g]) * kTile;
+    const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
+    const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
     int32_t* ridx = w.reg_idx + t * kTileCap;
     float* rval = w.reg_val + t * kTileCap;
-    const uint32_t cnt = tile_candidates<true>(grad, res, lo, hi, A, w.key_lo[g],
-                                               [&](uint32_t pos, int64_t i, float v) {
+    const uint32_t cnt = tile_candidates<true>(grad, res, lo, hi, A, w.key_lo[g], w.key_z[g],
+                                               [&](uint32_t pos, int32_t i, float v) {
                                                    if (pos < (uint32_t)kTileCap) {
-                                                       ridx[pos] = (int32_t)i;
+                                                       ridx[pos] = i;
                                                        rval[pos] = v;
                                                    }
                                                });
     if (threadIdx.x == 0) w.tile_cnt[t] = cnt;
 }
 
-// --------------------------------------------------------- scans (1 block)
+// ----------------------------------------------------------------- scans
 constexpr int kScanThreads = 1024;
 
 template <typename T>
@@ -459,17 +533,55 @@ __device__ inline void scan_u32_to_i64(const uint32_t* in, int64_t* out, int64_t
     __syncthreads();
 }
 
-// Tile-count prefix, then per group: candidate count, source of the main
-// selection (candidates, or the dense residual), and chunk prefix.
-__global__ __launch_bounds__(kScanThreads) void k_tile_scan(const int64_t* __restrict__ goff,
-                                                           const int64_t* __restrict__ gtile, int32_t G, int64_t NT,
-                                                           int32_t mode, int64_t capc, int64_t cap, CompressWs w,
-                                                           uint32_t* status)
+// Tile prefix inside each super block of kSuper tiles (16 per thread).
+__global__ __launch_bounds__(kBlock) void k_tile_scan1(int64_t NT, CompressWs w)
 {
-    scan_u32_to_i64(w.tile_cnt, w.tile_pre, NT);
+    __shared__ int64_t tmp[kBlock / 64 + 1];
+    constexpr int per = kSuper / kBlock;
+    const int64_t t0 = (int64_t)blockIdx.x * kSuper + threadIdx.x * per;
+    uint32_t c[per];
+    int64_t local = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        c[q] = t0 + q < NT ? w.tile_cnt[t0 + q] : 0u;
+        local += c[q];
+    }
+    int64_t total;
+    int64_t run = block_exclusive_scan<int64_t>(local, tmp, &total);
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        if (t0 + q < NT) w.tile_loc[t0 + q] = run;
+        run += c[q];
+    }
+    if (threadIdx.x == 0) w.sup_pre[blockIdx.x] = total;  // block sum; k_tile_scan2 makes it a prefix
+}
+
+// Super block prefix, then per group: candidate count, source of the main
+// selection (candidates, or the dense residual), and chunk prefix.
+__global__ __launch_bounds__(kScanThreads) void k_tile_scan2(const int64_t* __restrict__ goff,
+                                                            const int64_t* __restrict__ gtile, int32_t G, int64_t NT,
+                                                            int32_t mode, int64_t capc, int64_t cap, CompressWs w,
+                                                            uint32_t* status)
+{
+    __shared__ int64_t tmp[kScanThreads / 64 + 1];
+    const int64_t NS = cdiv(NT, kSuper);
+    // exclusive scan of the NS block sums in place (NS is at most a few hundred)
+    const int64_t per = cdiv(NS, kScanThreads);
+    const int64_t b = threadIdx.x * per, e = min(b + per, NS);
+    int64_t local = 0;
+    for (int64_t i = b; i < e; ++i) local += w.sup_pre[i];
+    int64_t total;
+    int64_t run = block1024_exclusive_scan<int64_t>(local, tmp, &total);
+    for (int64_t i = b; i < e; ++i) {
+        const int64_t v = w.sup_pre[i];
+        w.sup_pre[i] = run;
+        run += v;
+    }
+    __syncthreads();
     if (threadIdx.x != 0) return;
+    w.sup_pre[NS] = total;
+    w.scal[1] = total;
     if (mode == SGC_SAMPLED) {
-        const int64_t total = w.tile_pre[NT];
         w.scal[0] = total < cap ? total : cap;
         if (total > cap) *status |= SGC_STATUS_TRUNCATED;
         return;
@@ -477,7 +589,7 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_scan(const int64_t* __res
     int64_t used = 0, cp = 0;
     bool dense = false;
     for (int32_t g = 0; g < G; ++g) {
-        const int64_t cg = w.tile_pre[gtile[g + 1]] - w.tile_pre[gtile[g]];
+        const int64_t cg = tile_prefix(w, NT, gtile[g + 1]) - tile_prefix(w, NT, gtile[g]);
         const int64_t k = w.k[g];
         int kind;
         int64_t base, len;
@@ -503,7 +615,6 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_scan(const int64_t* __res
         w.rank[g] = k;
         w.prefix[g] = 0;
         w.mrem[g] = k;
-        w.cnt_gt[g] = 0;
         w.cpre[g] = cp;
         cp += cdiv(len, kChunk);
     }
@@ -512,55 +623,105 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_scan(const int64_t* __res
     if (dense) *status |= SGC_STATUS_DENSE_PATH;
 }
 
-// Region copy (or redo of an overflowed tile) into the ordered candidate
-// array (exact) or straight into the output (sampled, truncated at cap).
+// ----------------------------------------------------------------- gather
+// One workgroup per kGatherTiles tiles.  Exact mode: copy the regions of
+// candidate-selected groups into the ordered candidate array (indices of
+// redone, overflowed tiles carry kAccFlag: pass 1 did not zero them);
+// for groups that fall back to the dense residual, give back acc to the
+// entries pass 1 zeroed.  Sampled mode: the candidates are the output;
+// entries beyond cap get their acc back (they stay in the residual).
 __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ grad, float* __restrict__ res,
                                                   const int64_t* __restrict__ goff, const int64_t* __restrict__ gtile,
-                                                  int32_t G, int32_t mode, int32_t* __restrict__ out_idx,
-                                                  float* __restrict__ out_val, int64_t cap, CompressWs w)
+                                                  int32_t G, int64_t NT, int32_t mode,
+                                                  int32_t* __restrict__ out_idx, float* __restrict__ out_val,
+                                                  int64_t cap, CompressWs w)
 {
-    const int64_t t = blockIdx.x;
-    const uint32_t c = w.tile_cnt[t];
-    if (c == 0) return;
-    const int64_t g = tile_group(gtile, G, t);
-    int64_t dst;
-    int32_t* di;
-    float* dv;
-    int64_t lim;
+    __shared__ int64_t s_dst[kGatherTiles];   // destination of the tile's first entry (-1: restore only)
+    __shared__ uint32_t s_cnt[kGatherTiles];  // entries copied from the region
+    __shared__ uint32_t s_pre[kGatherTiles + 1];
+    __shared__ uint32_t s_z[kGatherTiles];    // zeroing bound of the tile's group
+    __shared__ uint32_t s_over;               // bit q: tile q overflowed
     const bool sampled = mode == SGC_SAMPLED;
-    if (sampled) {
-        dst = w.tile_pre[t];
-        di = out_idx;
-        dv = out_val;
-        lim = cap;
-    } else {
-        if (w.src_kind[g] != kSrcCand) return;
-        dst = w.cstart[g] + w.tile_pre[t] - w.tile_pre[gtile[g]];
-        di = w.cand_idx;
-        dv = w.cand_val;
-        lim = INT64_MAX;
-    }
-    if (dst >= lim) return;
-    if (c <= (uint32_t)kTileCap) {
-        const int32_t* ri = w.reg_idx + t * kTileCap;
-        const float* rv = w.reg_val + t * kTileCap;
-        for (uint32_t j = threadIdx.x; j < c; j += kBlock) {
-            const int64_t p = dst + j;
-            if (p >= lim) break;
-            const int32_t i = ri[j];
-            di[p] = i;
-            dv[p] = rv[j];
-            if (sampled) res[i] = 0.0f;
+    const int64_t t0 = (int64_t)blockIdx.x * kGatherTiles;
+    if (threadIdx.x < 64) {
+        const int q = threadIdx.x;
+        const int64_t t = t0 + q;
+        int64_t dst = -1;
+        uint32_t c = 0, z = kNoKey;
+        bool over = false;
+        if (q < kGatherTiles && t < NT) {
+            const int64_t g = tile_group(gtile, G, t);
+            c = w.tile_cnt[t];
+            over = c > (uint32_t)kTileCap;
+            z = w.key_z[g];
+            if (sampled) dst = tile_prefix(w, NT, t);
+            else if (w.src_kind[g] == kSrcCand)
+                dst = w.cstart[g] + tile_prefix(w, NT, t) - tile_prefix(w, NT, gtile[g]);
+            if (over) c = 0;
         }
-    } else {
-        const int64_t lo = goff[g], hi = goff[g + 1];
-        const int64_t A = (lo & ~(int64_t)3) + (t - gtile[g]) * kTile;
-        tile_candidates<false>(grad, res, lo, hi, A, w.key_lo[g], [&](uint32_t pos, int64_t i, float v) {
+        if (q < kGatherTiles) {
+            s_dst[q] = dst;
+            s_cnt[q] = c;
+            s_z[q] = z;
+        }
+        const uint64_t ob = __ballot(over);
+        if (q == 0) s_over = (uint32_t)ob;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t run = 0;
+        for (int q = 0; q < kGatherTiles; ++q) {
+            s_pre[q] = run;
+            run += s_cnt[q];
+        }
+        s_pre[kGatherTiles] = run;
+    }
+    __syncthreads();
+    const uint32_t E = s_pre[kGatherTiles];
+    for (uint32_t e = threadIdx.x; e < E; e += kBlock) {
+        int q = 0;
+        while (e >= s_pre[q + 1]) ++q;
+        const uint32_t j = e - s_pre[q];
+        const int64_t t = t0 + q;
+        const int32_t i = w.reg_idx[t * kTileCap + j];
+        const float v = w.reg_val[t * kTileCap + j];
+        const int64_t dst = s_dst[q];
+        if (dst < 0) {  // dense-path group: undo pass-1 zeroing
+            if (mag_key(v) >= s_z[q]) res[i] = v;
+        } else if (sampled) {
+            const int64_t p = dst + j;
+            if (p < cap) {
+                out_idx[p] = i;
+                out_val[p] = v;
+            } else {
+                res[i] = v;  // truncated: stays in the residual
+            }
+        } else {
+            w.cand_idx[dst + j] = i;
+            w.cand_val[dst + j] = v;
+        }
+    }
+    // overflowed tiles: redo from r (which pass 1 left as acc there)
+    const uint32_t over = s_over;
+    for (int q = 0; q < kGatherTiles; ++q) {
+        if (!(over & (1u << q))) continue;  // uniform per block
+        const int64_t t = t0 + q;
+        const int64_t dst = s_dst[q];
+        if (dst < 0) continue;
+        const int64_t g = tile_group(gtile, G, t);
+        const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
+        const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
+        tile_candidates<false>(grad, res, lo, hi, A, w.key_lo[g], kNoKey, [&](uint32_t pos, int32_t i, float v) {
             const int64_t p = dst + pos;
-            if (p < lim) {
-                di[p] = (int32_t)i;
-                dv[p] = v;
-                if (sampled) res[i] = 0.0f;
+            if (sampled) {
+                if (p < cap) {
+                    out_idx[p] = i;
+                    out_val[p] = v;
+                    res[i] = 0.0f;
+                }
+            } else {
+                w.cand_idx[p] = (int32_t)((uint32_t)i | kAccFlag);
+                w.cand_val[p] = v;
             }
         });
     }
@@ -582,22 +743,23 @@ __device__ inline ChunkView chunk_view(const CompressWs& w, int32_t G, int64_t c
     return v;
 }
 
-__device__ inline void chunk_item(const CompressWs& w, const float* res, const int64_t* goff, const ChunkView& v,
-                                  int64_t i, int32_t* idx, float* val)
+// Entry i of a chunk's source: index (with kAccFlag when r holds acc there)
+// and value.
+__device__ inline void chunk_item(const CompressWs& w, const float* res, const ChunkView& v, int64_t i,
+                                  uint32_t* idx, float* val)
 {
     if (v.kind == kSrcCand) {
-        *idx = w.cand_idx[i];
+        *idx = (uint32_t)w.cand_idx[i];
         *val = w.cand_val[i];
     } else {
-        *idx = (int32_t)i;
+        *idx = (uint32_t)i | kAccFlag;
         *val = res[i];
     }
 }
 
 __device__ inline uint32_t group_T(const CompressWs& w, int64_t g) { return w.rank[g] > 0 ? w.prefix[g] : kNoKey; }
 
-__global__ __launch_bounds__(kBlock) void k_compact_count(const float* __restrict__ res, const int64_t* goff,
-                                                         int32_t G, CompressWs w)
+__global__ __launch_bounds__(kBlock) void k_compact_count(const float* __restrict__ res, int32_t G, CompressWs w)
 {
     __shared__ uint32_t tmp[kBlock / 64 + 1];
     const int64_t nch = w.cpre[G];
@@ -609,9 +771,9 @@ __global__ __launch_bounds__(kBlock) void k_compact_count(const float* __restric
         for (int j = 0; j < kPer; ++j) {
             const int64_t i = b + j;
             if (i < v.end) {
-                int32_t id;
+                uint32_t id;
                 float x;
-                chunk_item(w, res, goff, v, i, &id, &x);
+                chunk_item(w, res, v, i, &id, &x);
                 const uint32_t key = mag_key(x);
                 gt += key > T;
                 eq += key == T;
@@ -634,8 +796,8 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_scan(int32_t G, Compress
     scan_u32_to_i64(w.ch_eq, w.ch_eq_pre, nch);
 }
 
-__global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ res, const int64_t* goff, int32_t G,
-                                                         CompressWs w, int32_t* __restrict__ out_idx,
+__global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ res, int32_t G, CompressWs w,
+                                                         int32_t* __restrict__ out_idx,
                                                          float* __restrict__ out_val, int64_t cap)
 {
     __shared__ uint32_t tmp[kBlock / 64 + 1];
@@ -643,12 +805,13 @@ __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ re
     for (int64_t c = blockIdx.x; c < nch; c += gridDim.x) {
         const ChunkView v = chunk_view(w, G, c);
         const uint32_t T = group_T(w, v.g);
+        const uint32_t kz = w.key_z[v.g];
         const int64_t quota = w.mrem[v.g];
         const int64_t c0 = w.cpre[v.g];
         const int64_t gt_before = w.ch_gt_pre[c] - w.ch_gt_pre[c0];
         const int64_t eq_before = w.ch_eq_pre[c] - w.ch_eq_pre[c0];
         const int64_t kept_before = gt_before + (eq_before < quota ? eq_before : quota);
-        int32_t id[kPer];
+        uint32_t id[kPer];
         float x[kPer];
         uint32_t key[kPer];
         uint32_t eq = 0;
@@ -658,7 +821,7 @@ __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ re
             const int64_t i = b + j;
             key[j] = kNoKey;
             if (i < v.end) {
-                chunk_item(w, res, goff, v, i, &id[j], &x[j]);
+                chunk_item(w, res, v, i, &id[j], &x[j]);
                 key[j] = mag_key(x[j]);
                 eq += key[j] == T;
             }
@@ -683,11 +846,18 @@ __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ re
         int64_t pos = w.kpre[v.g] + kept_before + kept_rank;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            if ((keep & (1u << j)) && pos < cap) {
-                out_idx[pos] = id[j];
-                out_val[pos] = x[j];
-                res[id[j]] = 0.0f;
+            if (key[j] == kNoKey) continue;
+            const uint32_t i = id[j] & ~kAccFlag;
+            const bool zeroed = !(id[j] & kAccFlag) && key[j] >= kz;  // pass 1 stored +0 here
+            if (keep & (1u << j)) {
+                if (pos < cap) {
+                    out_idx[pos] = (int32_t)i;
+                    out_val[pos] = x[j];
+                }
                 ++pos;
+                if (!zeroed) res[i] = 0.0f;
+            } else if (zeroed) {
+                res[i] = x[j];  // zeroed by pass 1 but not kept: give acc back
             }
         }
     }
@@ -703,7 +873,6 @@ __global__ void k_seg_counts(const int64_t* __restrict__ seg_off, int32_t nseg, 
             out_counts[nseg] = total;
             continue;
         }
-        // first entry >= seg_off[t] and first entry >= seg_off[t+1]
         int64_t a0 = 0, a1 = total;
         const int64_t x0 = seg_off[t];
         while (a0 < a1) {
@@ -721,27 +890,38 @@ __global__ void k_seg_counts(const int64_t* __restrict__ seg_off, int32_t nseg, 
 }
 
 template <int D>
-static int radix_select(const float* res, int32_t G, int64_t nch_max, const CompressWs& w, hipStream_t s)
+static int radix_select(const float* res, int32_t V, int64_t nch_max, const CompressWs& w, hipStream_t s)
 {
     unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>(nch_max, 1), 2048);
-    k_srs_hist<D><<<blocks, kBlock, 0, s>>>(res, G, w);
+    k_srs_hist<D><<<blocks, kBlock, 0, s>>>(res, V, w);
     SGC_LAUNCH_CHECK();
-    k_srs_resolve<D><<<(unsigned)G, kBlock, 0, s>>>(G, w);
+    k_srs_resolve<D><<<(unsigned)V, kBlock, 0, s>>>(w);
     SGC_LAUNCH_CHECK();
     return SGC_OK;
 }
 
-static int select_all(const float* res, int32_t G, int64_t nch_max, const CompressWs& w, hipStream_t s)
+static int select_all(const float* res, int32_t V, int64_t nch_max, const CompressWs& w, hipStream_t s)
 {
     int rc;
-    if ((rc = radix_select<0>(res, G, nch_max, w, s))) return rc;
-    if ((rc = radix_select<1>(res, G, nch_max, w, s))) return rc;
-    return radix_select<2>(res, G, nch_max, w, s);
+    if ((rc = radix_select<0>(res, V, nch_max, w, s))) return rc;
+    if ((rc = radix_select<1>(res, V, nch_max, w, s))) return rc;
+    return radix_select<2>(res, V, nch_max, w, s);
 }
+
+// Measurement hook: events recorded around the fused pass (benchmarks only).
+static hipEvent_t g_pass_start = nullptr, g_pass_stop = nullptr;
 
 }  // namespace sgc
 
 using namespace sgc;
+
+extern "C" int sgc_set_pass_events(void* start, void* stop)
+{
+    if ((start == nullptr) != (stop == nullptr)) return SGC_EINVAL;
+    g_pass_start = (hipEvent_t)start;
+    g_pass_stop = (hipEvent_t)stop;
+    return SGC_OK;
+}
 
 static bool opts_ok(const sgc_layout* L, const sgc_compress_opts* o)
 {
@@ -757,7 +937,7 @@ extern "C" size_t sgc_compress_workspace(const sgc_layout* L, const sgc_compress
 {
     if (!opts_ok(L, o) || cap < 0) return 0;
     if (o->mode == SGC_ACCUMULATE_ONLY) return 0;
-    CompressSizes z = compress_sizes(L, o, cap);
+    CompressSizes z = compress_sizes(L, o);
     Carver c(nullptr);
     CompressWs w;
     carve_compress(c, z, o->mode, &w);
@@ -774,7 +954,7 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
     hipStream_t s = (hipStream_t)stream;
     if (o->mode == SGC_ACCUMULATE_ONLY) {
         if (L->n == 0) return SGC_OK;
-        int64_t blocks = std::min<int64_t>(cdiv(std::max<int64_t>(L->n >> 2, 1), kBlock), 8192);
+        const int64_t blocks = cdiv(std::max<int64_t>(L->n >> 2, 1), kBlock);
         k_accumulate<<<(unsigned)blocks, kBlock, 0, s>>>(grad, residual, L->n);
         SGC_LAUNCH_CHECK();
         return SGC_OK;
@@ -788,7 +968,7 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
         for (int32_t g = 0; g < G; ++g) K += keep_count(hoff[g + 1] - hoff[g], o->keep_ppm);
         if (cap < K) return SGC_EINVAL;
     }
-    CompressSizes z = compress_sizes(L, o, cap);
+    CompressSizes z = compress_sizes(L, o);
     {
         Carver c(nullptr);
         CompressWs w0;
@@ -807,46 +987,55 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
     if (!dstatus && (rc = fill_u32(w.status, 1, 0, s))) return rc;
 
     if (L->n == 0) {
-        if ((rc = fill_u32(w.scal, 2, 0, s))) return rc;
+        if ((rc = fill_u32(w.scal, 2 * 8, 0, s))) return rc;
         k_seg_counts<<<1, kBlock, 0, s>>>(dt->seg_off, L->nseg, out_idx, w, out_counts);
         SGC_LAUNCH_CHECK();
         return SGC_OK;
     }
+    const int32_t V = 2 * G;
 
-    // 1. probe selection -> key_lo
+    // 1. probe selection -> key_lo, key_z
     k_setup<<<1, 64, 0, s>>>(gr.off, G, o->mode, o->keep_ppm, o->sample_div, o->sample_min, w);
     SGC_LAUNCH_CHECK();
-    if ((rc = fill_u32(w.hist, (int64_t)G * kBins, 0, s))) return rc;
+    if ((rc = fill_u32(w.hist, (int64_t)V * kBins, 0, s))) return rc;
     if (z.S > 0) {
         unsigned pb = (unsigned)std::min<int64_t>(cdiv(z.S, kBlock), 4096);
-        k_probe<<<pb, kBlock, 0, s>>>(grad, residual, gr.off, G, w, z.S);
+        k_probe<<<pb, kBlock, 0, s>>>(grad, residual, gr.off, G, o->mode, w, z.S);
         SGC_LAUNCH_CHECK();
     }
-    if ((rc = select_all(residual, G, cdiv(z.S, kChunk) + G + 1, w, s))) return rc;
-    k_probe_done<<<(unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(G, kBlock), 1024)), kBlock, 0, s>>>(G, w);
+    if ((rc = select_all(residual, V, 2 * cdiv(z.S, kChunk) + V + 1, w, s))) return rc;
+    k_probe_done<<<(unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(G, kBlock), 1024)), kBlock, 0, s>>>(
+        G, o->mode, w);
     SGC_LAUNCH_CHECK();
 
     // 2. pass 1
+    if (g_pass_start && hipEventRecord(g_pass_start, s) != hipSuccess) return SGC_EHIP;
     k_pass1<<<(unsigned)gr.ntiles, kBlock, 0, s>>>(grad, residual, gr.off, gr.tile, G, w);
     SGC_LAUNCH_CHECK();
+    if (g_pass_stop && hipEventRecord(g_pass_stop, s) != hipSuccess) return SGC_EHIP;
 
-    // 3. gather
-    k_tile_scan<<<1, kScanThreads, 0, s>>>(gr.off, gr.tile, G, gr.ntiles, o->mode, z.capc, cap, w, status);
+    // 3. scans
+    k_tile_scan1<<<(unsigned)z.NS, kBlock, 0, s>>>(gr.ntiles, w);
     SGC_LAUNCH_CHECK();
-    k_gather<<<(unsigned)gr.ntiles, kBlock, 0, s>>>(grad, residual, gr.off, gr.tile, G, o->mode, out_idx, out_val,
-                                                    cap, w);
+    k_tile_scan2<<<1, kScanThreads, 0, s>>>(gr.off, gr.tile, G, gr.ntiles, o->mode, z.capc, cap, w, status);
+    SGC_LAUNCH_CHECK();
+
+    // 4. gather
+    k_gather<<<(unsigned)cdiv(gr.ntiles, kGatherTiles), kBlock, 0, s>>>(grad, residual, gr.off, gr.tile, G,
+                                                                         gr.ntiles, o->mode, out_idx, out_val,
+                                                                         cap, w);
     SGC_LAUNCH_CHECK();
 
     if (o->mode == SGC_EXACT) {
-        // 4. exact selection over candidates (or the dense residual)
+        // 5. exact selection over candidates (or the dense residual)
         if ((rc = select_all(residual, G, z.nch_max, w, s))) return rc;
-        // 5. ordered compaction
+        // 6. ordered compaction
         unsigned cb = (unsigned)std::min<int64_t>(z.nch_max, 2048);
-        k_compact_count<<<cb, kBlock, 0, s>>>(residual, gr.off, G, w);
+        k_compact_count<<<cb, kBlock, 0, s>>>(residual, G, w);
         SGC_LAUNCH_CHECK();
         k_chunk_scan<<<1, kScanThreads, 0, s>>>(G, w);
         SGC_LAUNCH_CHECK();
-        k_compact_write<<<cb, kBlock, 0, s>>>(residual, gr.off, G, w, out_idx, out_val, cap);
+        k_compact_write<<<cb, kBlock, 0, s>>>(residual, G, w, out_idx, out_val, cap);
         SGC_LAUNCH_CHECK();
     }
     unsigned sb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(L->nseg + 1, kBlock), 1024));

@@ -71,15 +71,22 @@ __host__ __device__ inline int64_t sampled_count(int64_t m, uint32_t div, uint32
     return s < m ? s : m;
 }
 
-// Sample size used by the exact mode only to place a safe lower bound for
-// its candidate set (the result does not depend on it).
+// Probe of the exact mode: it only places the candidate bounds, the result
+// never depends on it.  Runs of kRun contiguous elements (one 64-byte
+// sector each) at systematic positions; a small group is read whole.
+constexpr int kRun = 16;
+__host__ __device__ inline int64_t probe_points(int64_t m)  // 0: read the whole group
+{
+    if (m <= (int64_t)kRun * 64) return 0;
+    int64_t p = m / 4096;
+    if (p < 64) p = 64;
+    if (p > 16384) p = 16384;
+    return p;
+}
 __host__ __device__ inline int64_t probe_count(int64_t m)
 {
-    if (m <= 0) return 0;
-    int64_t s = m / 256;
-    if (s < 4096) s = 4096;
-    if (s > 65536) s = 65536;
-    return s < m ? s : m;
+    const int64_t p = probe_points(m);
+    return p ? p * kRun : (m > 0 ? m : 0);
 }
 
 // Pass-1 tiles of a group [lo, hi): aligned grid starting at lo & ~3.

@@ -257,6 +257,16 @@ int sgc_decode_accumulate(const sgc_layout* layout, const sgc_message* msgs, int
                           int32_t init, const float* base, float* out,
                           uint32_t* dstatus, void* ws, size_t ws_bytes, sgc_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement hook (benchmarks only).  While set, every sgc_compress call
+ * (modes SGC_EXACT and SGC_SAMPLED) records `start` on its stream just
+ * before launching the fused residual-add + candidate pass and `stop` just
+ * after it, so the caller can time that one kernel with its own events.
+ * start / stop are hipEvent_t handles owned by the caller; NULL, NULL
+ * clears the hook.  Process-wide and not thread-safe: for single-threaded
+ * measurement only.  Returns SGC_EINVAL if exactly one handle is NULL.    */
+int sgc_set_pass_events(void* start, void* stop);
+
 #ifdef __cplusplus
 }
 #endif

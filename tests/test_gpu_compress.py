@@ -85,11 +85,13 @@ def test_ties_and_zeros(orc, scope):
 
 
 def test_probe_defeated_takes_full_pass_path(orc):
-    # Large values sit exactly where the probe samples (every 256th element from 128 at
-    # n = 2^20), so the sample overestimates the threshold and too few candidates pass.
+    # Large values sit exactly where the exact mode's probe reads (at n = 2^20: runs of 16
+    # elements starting at 2048 + 4096 j), so the probe overestimates the threshold, fewer than
+    # k candidates pass, and the selection falls back to full passes over the residual.
     n = 1 << 20
     g = np.random.default_rng(1).normal(0, 1e-4, n).astype(np.float32)
-    g[128::256] = 1.0 + np.arange(n // 256, dtype=np.float32) * 1e-3
+    runs = (2048 + 4096 * np.arange(n // 4096))[:, None] + np.arange(16)[None, :]
+    g[runs.ravel()] = 1.0 + np.arange(runs.size, dtype=np.float32) * 1e-3
     layout = sgc.Layout([n])
     r = np.zeros(n, np.float32)
     out, st = check_step(orc, layout, g, r, mode=sgc.EXACT, scope=0, ppm=10000, what="probe defeated")
