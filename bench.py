@@ -69,6 +69,9 @@ def main():
     ap.add_argument("--cpu-sample-log2", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the extra rows (e.g. under a profiler)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain elementwise copy of 2^28 fp32 (1 GiB each way) three times: "
+                         "the reference the HBM byte counters are scaled by")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no cross-GPU step in this build); "
@@ -82,6 +85,14 @@ def main():
     import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        x = torch.randn(1 << 28, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.add(x, 0.0, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": 4 << 28, "launches": 3}))
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
