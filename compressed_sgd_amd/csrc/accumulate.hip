@@ -8,18 +8,19 @@
 //
 // GPU design, per batch of messages (blockIdx.y = message):
 //  setup   validate counts / stream tables, entry and chunk prefixes;
-//  raw     copy positions and resolved values, check they ascend;
-//  span    Rice streams: one thread per 256-code chunk decodes from the
-//          chunk table and records the chunk's position span, checking
-//          that it ends exactly where the next chunk starts;
-//  scan    exclusive scan of spans -> position before every chunk;
-//  decode  decode again, writing global positions and resolved values;
-//  gaps    output-tile table entries for stretches no entry reaches.
-// Every message leaves a sorted (pos, val) list and, per 4096-element
-// output tile, the index of its first entry at or beyond the tile.  The
-// merge then gives each output tile to one workgroup: the tile is loaded
-// (or zeroed) into LDS, messages are applied in order (entries of one
-// message have distinct positions, so no atomics), and the tile is stored
+//  gaps    output-tile table entries for stretches no entry reaches;
+//  raw     check that raw positions ascend; resolve 2-bit values;
+//  decode  Rice streams: one thread per 256-code chunk starts from its
+//          chunk-table entry (bit offset, position reached), decodes from
+//          a copy of its words in LDS, writes global positions (and
+//          resolved SBC / 2-bit values), and checks that it ends exactly
+//          where the next chunk's entry says (or at the stream's bit count).
+// Every message then has a sorted position list (its own idx if raw), a
+// value list (its own val if fp32) and, per output tile, the index of its
+// first entry at or beyond the tile.  The merge then gives
+// each output tile to one workgroup: the initial tile and every message's
+// entries for it are loaded in parallel, each thread applies the messages
+// in order to the elements it owns (no atomics), and the tile is stored
 // once: the dense output is written exactly once, in a fixed order.
 #include "sgc_common.h"
 
@@ -37,8 +38,6 @@ struct MsgWs {
     int64_t* sbase;   // [S] first element of each stream
     int64_t* ssize;   // [S]
     int64_t* chpre;   // [S+1] chunk prefix
-    uint64_t* span;   // [nch] position span of each chunk
-    int64_t* cprev;   // [nch] stream-relative position before each chunk
     int32_t* pos;     // [cap] decoded global positions
     float* val;       // [cap] resolved values
     int32_t* tstart;  // [ntiles+1] first entry at or beyond each output tile
@@ -98,8 +97,6 @@ static void carve_msg(Carver& c, const sgc_layout* L, const sgc_message& m, MsgW
     w->sbase = c.take<int64_t>(S);
     w->ssize = c.take<int64_t>(S);
     w->chpre = c.take<int64_t>(S + 1);
-    w->span = c.take<uint64_t>(nch);
-    w->cprev = c.take<int64_t>(nch);
     w->pos = c.take<int32_t>(m.cap);
     w->val = c.take<float>(m.cap);
     w->tstart = c.take<int32_t>(out_tiles(L) + 1);
@@ -140,7 +137,7 @@ __global__ void k_msg_setup(Batch B, const int64_t* __restrict__ seg_off, int32_
         if (golomb) {
             const uint64_t w0 = in.word_off[s], w1 = in.word_off[s + 1];
             if (w0 != wprev || w1 < w0 || (w1 - w0) != (in.nbits[s] + 31) / 32 || w1 > (uint64_t)in.wbound) bad = 1;
-            if (cnt > 0 && in.nbits[s] == 0) bad = 1;
+            if ((cnt > 0) != (in.nbits[s] > 0)) bad = 1;  // codes take at least one bit each; no codes, no bits
             wprev = w1;
         }
         se += cnt;
@@ -184,17 +181,12 @@ __global__ __launch_bounds__(kBlock) void k_msg_raw(Batch B, int32_t nseg, int64
         const int64_t p = in.idx[j];
         const int64_t prev = j == 0 ? -1 : (int64_t)in.idx[j - 1];
         if (p < 0 || p >= n || p <= prev) { bad = true; continue; }
-        float v;
-        if (in.format == SGC_MSG_RAW_F32) {
-            v = in.val[j];
-        } else {
+        if (in.format == SGC_MSG_RAW_2BIT) {  // RAW_F32: the merge reads idx/val directly
             const uint32_t code = (in.codes[j >> 4] >> (2 * (j & 15))) & 3u;
             const int64_t t = find_bucket(w.estart, (int64_t)nseg + 1, j);
             if (code == 3u) bad = true;
-            v = code == 0u ? 0.0f : code == 1u ? in.means[2 * t] : in.means[2 * t + 1];
+            w.val[j] = code == 0u ? 0.0f : code == 1u ? in.means[2 * t] : in.means[2 * t + 1];
         }
-        w.pos[j] = (int32_t)p;
-        w.val[j] = v;
         fill_tiles(w.tstart, prev, p, j);
         if (j == total - 1) fill_tiles(w.tstart, p, n - 1, total);
     }
@@ -202,48 +194,6 @@ __global__ __launch_bounds__(kBlock) void k_msg_raw(Batch B, int32_t nseg, int64
 }
 
 // --------------------------------------------------------- Rice decoding
-struct Bits {
-    const uint32_t* w;
-    uint64_t nw, nbits;
-    __device__ uint64_t window(uint64_t bit) const
-    {
-        const uint64_t i = bit >> 5;
-        const uint32_t sh = (uint32_t)(bit & 31);
-        const uint64_t a = i < nw ? w[i] : 0, b = i + 1 < nw ? w[i + 1] : 0, c = i + 2 < nw ? w[i + 2] : 0;
-        const uint64_t lo = a | (b << 32);
-        return sh ? (lo >> sh) | (c << (64 - sh)) : lo;
-    }
-    // Decode one code at *bit; returns false on a read past nbits.
-    __device__ bool next(uint64_t* bit, uint32_t b, uint64_t* z) const
-    {
-        uint64_t q = 0, p = *bit;
-        for (;;) {
-            if (p >= nbits) return false;
-            const uint64_t win = window(p);
-            const uint64_t inv = ~win;
-            if (inv) {
-                const uint32_t ones = (uint32_t)__builtin_ctzll(inv);
-                if (p + ones >= nbits) return false;
-                q += ones;
-                p += ones + 1;
-                break;
-            }
-            q += 64;
-            p += 64;
-        }
-        uint64_t rem = 0;
-        if (b) {
-            if (p + b > nbits) return false;
-            rem = window(p) & ((1ull << b) - 1ull);
-            p += b;
-        }
-        if (q >> 33) return false;  // no stream is that long
-        *z = (q << b) | rem;
-        *bit = p;
-        return true;
-    }
-};
-
 struct ChunkAt {
     int64_t s, q0, nc;
 };
@@ -258,127 +208,234 @@ __device__ inline ChunkAt chunk_at(const MsgWs& w, int32_t S, int64_t c)
     return a;
 }
 
-__device__ inline Bits stream_bits(const MsgIn& in, int64_t s)
-{
-    Bits r;
-    r.w = in.words + in.word_off[s];
-    r.nw = in.word_off[s + 1] - in.word_off[s];
-    r.nbits = in.nbits[s];
-    return r;
-}
+// One thread per chunk, one wavefront per workgroup.  Each lane first copies
+// its chunk's words into its own LDS column (independent loads, no
+// barrier: no lane reads another lane's column), then decodes from LDS, so
+// the decode loop issues no global loads at all and never waits on memory
+// behind its own stores (one counter tracks both on this GPU).  A chunk
+// whose words do not fit the column (very long gaps) decodes from global
+// memory instead.  Positions (and, for SBC / 2-bit, resolved values) are
+// buffered kDB at a time and stored together; the output-tile table is
+// filled on the way, and the chunk is checked against its neighbours in
+// the chunk table.
+constexpr int kDB = 16;
+constexpr int kDecLanes = 64;
+constexpr int kColWords = 120;  // LDS words per lane (the chunk's words plus slack)
+constexpr int kColCodes = 17;   // 2-bit code words per lane (256 entries span at most 17)
 
-__global__ __launch_bounds__(kBlock) void k_msg_span(Batch B)
-{
-    const int m = blockIdx.y;
-    const MsgIn& in = B.in[m];
-    const MsgWs& w = B.ws[m];
-    if (in.format < SGC_MSG_GOLOMB_F32) return;
-    const int64_t nch = w.chpre[in.S];
-    bool bad = false;
-    for (int64_t c = (int64_t)blockIdx.x * kBlock + threadIdx.x; c < nch; c += (int64_t)gridDim.x * kBlock) {
-        const ChunkAt a = chunk_at(w, in.S, c);
-        const Bits bits = stream_bits(in, a.s);
-        uint64_t bit = in.chunk_off[c];
-        if (a.q0 == 0 && bit != 0) { bad = true; continue; }
-        uint64_t span = 0, z;
-        bool ok = true;
-        for (int64_t i = 0; i < a.nc; ++i) {
-            if (!bits.next(&bit, (uint32_t)in.b, &z)) { ok = false; break; }
-            span += z + 1;
-            if (span > (uint64_t)w.ssize[a.s]) { ok = false; break; }
+struct LdsWords {
+    const uint32_t* col;  // this lane's column: col[i * kDecLanes]
+    uint64_t w0, nw;      // first stream word held, words held
+    __device__ uint32_t operator()(uint64_t i) const
+    {
+        const uint64_t r = i - w0;
+        return r < nw ? col[r * kDecLanes] : 0u;
+    }
+};
+
+struct GlobalWords {
+    const uint32_t* w;
+    uint64_t nw;
+    __device__ uint32_t operator()(uint64_t i) const { return i < nw ? w[i] : 0u; }
+};
+
+// Sequential reader of one Rice stream over a word source; every read is
+// checked against nbits.
+template <typename Src>
+struct WordReader {
+    Src src;
+    uint64_t nbits, pos, buf, wi;  // buf holds bits [pos, pos + avail); wi: next word to append
+    uint32_t avail;
+    __device__ void start(Src s, uint64_t nb, uint64_t bit)
+    {
+        src = s;
+        nbits = nb;
+        pos = bit;
+        wi = (bit >> 5) + 1;
+        const uint32_t sh = (uint32_t)(bit & 31);
+        buf = (uint64_t)(src(bit >> 5) >> sh);
+        avail = 32 - sh;
+    }
+    __device__ void refill()
+    {
+        while (avail <= 32) {
+            buf |= (uint64_t)src(wi++) << avail;
+            avail += 32;
         }
-        const uint64_t want = (c + 1 < w.chpre[a.s + 1]) ? in.chunk_off[c + 1] : bits.nbits;
-        if (!ok || bit != want) bad = true;
-        w.span[c] = span;
     }
-    if (bad) atomicOr(w.bad, 1u);
+    __device__ void consume(uint32_t k)
+    {
+        buf = k >= 64 ? 0ull : buf >> k;
+        avail -= k;
+        pos += k;
+    }
+    __device__ bool next(uint32_t b, uint64_t* z)
+    {
+        uint64_t q = 0;
+        for (;;) {
+            if (pos >= nbits) return false;
+            refill();
+            const uint64_t inv = ~buf;  // buf is 0 above avail, so the count stops at avail
+            const uint32_t ones = inv ? (uint32_t)__builtin_ctzll(inv) : 64u;
+            if (ones < avail) {
+                if (pos + ones >= nbits) return false;
+                q += ones;
+                consume(ones + 1);
+                break;
+            }
+            q += avail;
+            consume(avail);
+        }
+        uint64_t rem = 0;
+        if (b) {
+            refill();
+            if (pos + b > nbits) return false;
+            rem = buf & ((1ull << b) - 1ull);
+            consume(b);
+        }
+        if (q >> 33) return false;  // no stream is that long
+        *z = (q << b) | rem;
+        return true;
+    }
+};
+
+// Decode one chunk with reader rd; returns false if the chunk is corrupt.
+template <typename Rd>
+__device__ inline bool decode_chunk(Rd& rd, const MsgIn& in, const MsgWs& w, const ChunkAt& a, int64_t c,
+                                    int32_t nseg, uint64_t reached, const uint32_t* code_col)
+{
+    const int fmt = in.format;
+    const int64_t size = w.ssize[a.s];
+    const int64_t base = w.sbase[a.s];
+    const int64_t j0 = w.sent[a.s] + a.q0;
+    int64_t prev = (int64_t)reached - 1;
+    // segment of the current entry (per-segment values), where its entries end, and its means
+    int64_t t = in.scope == SGC_PER_SEGMENT ? a.s : find_bucket(w.estart, (int64_t)nseg + 1, j0);
+    int64_t tend = in.scope == SGC_PER_SEGMENT ? INT64_MAX : w.estart[t + 1];
+    float m0 = 0.0f, m1 = 0.0f;
+    if (fmt == SGC_MSG_GOLOMB_SBC) m0 = in.means[t];
+    if (fmt == SGC_MSG_GOLOMB_2BIT) {
+        m0 = in.means[2 * t];
+        m1 = in.means[2 * t + 1];
+    }
+    const bool values = fmt != SGC_MSG_GOLOMB_F32;  // F32 values are read by the merge directly
+    int64_t gprev = base + prev;  // global position of the previous entry (tile table)
+    for (int64_t i0 = 0; i0 < a.nc; i0 += kDB) {
+        const int nb = (int)min((int64_t)kDB, a.nc - i0);
+        int32_t pb[kDB];
+        float vv[kDB];
+#pragma unroll
+        for (int q = 0; q < kDB; ++q) {
+            pb[q] = 0;
+            vv[q] = 0.0f;
+            if (q >= nb) continue;
+            uint64_t z;
+            if (!rd.next((uint32_t)in.b, &z)) return false;
+            const int64_t p = prev + 1 + (int64_t)z;
+            if (p >= size) return false;
+            prev = p;
+            const int64_t j = j0 + i0 + q;
+            while (j >= tend) {  // entered the next segment (global scope): rare
+                ++t;
+                tend = w.estart[t + 1];
+                if (fmt == SGC_MSG_GOLOMB_SBC) m0 = in.means[t];
+                if (fmt == SGC_MSG_GOLOMB_2BIT) {
+                    m0 = in.means[2 * t];
+                    m1 = in.means[2 * t + 1];
+                }
+            }
+            if (fmt == SGC_MSG_GOLOMB_SBC) {
+                vv[q] = m0;
+            } else if (fmt == SGC_MSG_GOLOMB_2BIT) {
+                const int64_t cw = (j >> 4) - (j0 >> 4);
+                const uint32_t word = code_col ? code_col[cw * kDecLanes] : in.codes[j >> 4];
+                const uint32_t code = (word >> (2 * (j & 15))) & 3u;
+                if (code == 3u) return false;
+                vv[q] = code == 0u ? 0.0f : code == 1u ? m0 : m1;
+            }
+            pb[q] = (int32_t)(base + p);
+        }
+        const int64_t jb = j0 + i0;
+        if (nb == kDB && (jb & 3) == 0) {  // whole 64-byte sectors: four 16-byte stores per array
+            typedef int32_t i4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int q = 0; q < kDB / 4; ++q) {
+                *(i4v*)(w.pos + jb + 4 * q) = i4v{pb[4 * q], pb[4 * q + 1], pb[4 * q + 2], pb[4 * q + 3]};
+                if (values) *(f4a*)(w.val + jb + 4 * q) = f4a{vv[4 * q], vv[4 * q + 1], vv[4 * q + 2], vv[4 * q + 3]};
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kDB; ++q) {
+                if (q >= nb) continue;
+                w.pos[jb + q] = pb[q];
+                if (values) w.val[jb + q] = vv[q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kDB; ++q) {
+            if (q >= nb) continue;
+            fill_tiles(w.tstart, gprev, pb[q], jb + q);
+            gprev = pb[q];
+        }
+    }
+    if (c + 1 < w.chpre[a.s + 1]) {
+        // the next chunk must start exactly where this one ended
+        if (in.chunk_off[2 * (c + 1)] != rd.pos || in.chunk_off[2 * (c + 1) + 1] != (uint64_t)(prev + 1)) return false;
+    } else {
+        if (rd.pos != rd.nbits) return false;  // no bits left over
+        // the stream's last entry covers the tiles up to the end of its range
+        fill_tiles(w.tstart, gprev, base + size - 1, w.sent[a.s + 1]);
+    }
+    return true;
 }
 
-__global__ __launch_bounds__(1024) void k_msg_scan(Batch B)
+__global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg, int64_t n)
 {
-    const int m = blockIdx.y;
-    const MsgIn& in = B.in[m];
-    const MsgWs& w = B.ws[m];
-    if (in.format < SGC_MSG_GOLOMB_F32) return;
-    __shared__ uint64_t tmp[1024 / 64 + 1];
-    // flat exclusive scan of spans, then rebase per stream
-    const int64_t nch = w.chpre[in.S];
-    const int64_t per = cdiv(nch, (int64_t)blockDim.x);
-    const int64_t b0 = threadIdx.x * per, e0 = min(b0 + per, nch);
-    uint64_t local = 0;
-    for (int64_t c = b0; c < e0; ++c) local += w.span[c];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint64_t x = local;
-    for (int d = 1; d < 64; d <<= 1) {
-        uint64_t y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
-    if (lane == 63) tmp[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t run = 0;
-        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) { uint64_t q = tmp[i]; tmp[i] = run; run += q; }
-    }
-    __syncthreads();
-    uint64_t run = tmp[wave] + x - local;
-    for (int64_t c = b0; c < e0; ++c) {
-        w.cprev[c] = (int64_t)run;  // flat prefix; chunk_prev() rebases it per stream
-        run += w.span[c];
-    }
-}
-
-// Position before chunk c, relative to its stream: -1 + (flat prefix of c) -
-// (flat prefix of the stream's first chunk).
-__device__ inline int64_t chunk_prev(const MsgWs& w, const ChunkAt& a, int64_t c)
-{
-    return -1 + w.cprev[c] - w.cprev[w.chpre[a.s]];
-}
-
-__global__ __launch_bounds__(kBlock) void k_msg_decode(Batch B, int32_t nseg, int64_t n)
-{
+    __shared__ uint32_t col[kColWords * kDecLanes];
+    __shared__ uint32_t ccol[kColCodes * kDecLanes];
     const int m = blockIdx.y;
     const MsgIn& in = B.in[m];
     const MsgWs& w = B.ws[m];
     if (in.format < SGC_MSG_GOLOMB_F32) return;
     if (w.bad[0]) return;
+    const int lane = threadIdx.x;
     const int64_t nch = w.chpre[in.S];
     bool bad = false;
-    for (int64_t c = (int64_t)blockIdx.x * kBlock + threadIdx.x; c < nch; c += (int64_t)gridDim.x * kBlock) {
+    for (int64_t c = (int64_t)blockIdx.x * kDecLanes + lane; c < nch; c += (int64_t)gridDim.x * kDecLanes) {
         const ChunkAt a = chunk_at(w, in.S, c);
-        const Bits bits = stream_bits(in, a.s);
-        uint64_t bit = in.chunk_off[c], z;
-        int64_t prev = chunk_prev(w, a, c);
-        const int64_t base = w.sbase[a.s];
-        int64_t j = w.sent[a.s] + a.q0;
-        // segment of entry j for per-segment values
-        int64_t t = in.scope == SGC_PER_SEGMENT ? a.s : find_bucket(w.estart, (int64_t)nseg + 1, j);
-        // the previous entry's global position (for the tile table)
-        int64_t gprev = prev >= 0 ? base + prev : base - 1;
-        for (int64_t i = 0; i < a.nc; ++i, ++j) {
-            if (!bits.next(&bit, (uint32_t)in.b, &z)) { bad = true; break; }
-            const int64_t p = prev + 1 + (int64_t)z;
-            if (p >= w.ssize[a.s]) { bad = true; break; }
-            prev = p;
-            const int64_t gp = base + p;
-            while (in.scope != SGC_PER_SEGMENT && j >= w.estart[t + 1]) ++t;
-            float v;
-            if (in.format == SGC_MSG_GOLOMB_F32) {
-                v = in.val[j];
-            } else if (in.format == SGC_MSG_GOLOMB_SBC) {
-                v = in.means[t];
-            } else {
-                const uint32_t code = (in.codes[j >> 4] >> (2 * (j & 15))) & 3u;
-                if (code == 3u) bad = true;
-                v = code == 0u ? 0.0f : code == 1u ? in.means[2 * t] : in.means[2 * t + 1];
-            }
-            w.pos[j] = (int32_t)gp;
-            w.val[j] = v;
-            fill_tiles(w.tstart, gprev, gp, j);
-            gprev = gp;
+        const uint64_t bit0 = in.chunk_off[2 * c], reached = in.chunk_off[2 * c + 1];
+        if ((a.q0 == 0 && (bit0 != 0 || reached != 0)) || reached > (uint64_t)w.ssize[a.s]) { bad = true; continue; }
+        const uint32_t* words = in.words + in.word_off[a.s];
+        const uint64_t nw = in.word_off[a.s + 1] - in.word_off[a.s];
+        const uint64_t nbits = in.nbits[a.s];
+        const uint64_t bit1 = (c + 1 < w.chpre[a.s + 1]) ? in.chunk_off[2 * (c + 1)] : nbits;
+        if (bit1 < bit0 || bit1 > nbits) { bad = true; continue; }
+        // 2-bit code words of the chunk's entries
+        const uint32_t* code_col = nullptr;
+        if (in.format == SGC_MSG_GOLOMB_2BIT) {
+            const int64_t j0 = w.sent[a.s] + a.q0;
+            const int64_t cw0 = j0 >> 4, cw1 = (j0 + a.nc - 1) >> 4;
+#pragma unroll 4
+            for (int64_t i = 0; i <= cw1 - cw0; ++i) ccol[i * kDecLanes + lane] = in.codes[cw0 + i];
+            code_col = ccol + lane;
         }
-        // the stream's last entry covers the tiles up to the end of its range
-        if (!bad && a.q0 + a.nc == w.scnt[a.s])
-            fill_tiles(w.tstart, gprev, base + w.ssize[a.s] - 1, w.sent[a.s + 1]);
+        // words [bit0/32, bit1/32 + 2): the chunk's bits plus a two-word window slack
+        const uint64_t wlo = bit0 >> 5;
+        const uint64_t whi = min((bit1 >> 5) + 2, nw);
+        const uint64_t nwc = whi > wlo ? whi - wlo : 0;
+        bool ok;
+        if (nwc <= (uint64_t)kColWords) {
+#pragma unroll 8
+            for (uint64_t i = 0; i < nwc; ++i) col[i * kDecLanes + lane] = words[wlo + i];
+            WordReader<LdsWords> rd;
+            rd.start(LdsWords{col + lane, wlo, nwc}, nbits, bit0);
+            ok = decode_chunk(rd, in, w, a, c, nseg, reached, code_col);
+        } else {
+            WordReader<GlobalWords> rd;
+            rd.start(GlobalWords{words, nw}, nbits, bit0);
+            ok = decode_chunk(rd, in, w, a, c, nseg, reached, code_col);
+        }
+        if (!ok) bad = true;
     }
     if (bad) atomicOr(w.bad, 1u);
 }
@@ -408,49 +465,106 @@ __global__ __launch_bounds__(kBlock) void k_msg_gaps(Batch B, int64_t n, int64_t
 }
 
 // ------------------------------------------------------------------ merge
+// One workgroup per output tile of kOutTile elements.  Round 1 (parallel):
+// the tile's initial contents (coalesced, into LDS) and every message's
+// entry range [tstart[t], tstart[t+1]).  Then the entries of all messages
+// are staged in LDS (kStage at a time, in message order) and thread t
+// applies, for each message in order, the entries that fall on the 16
+// contiguous tile elements it owns (binary search in the staged, ascending
+// positions).  No element is touched by two threads, so there are no
+// atomics and no per-message barriers; the tile is stored once, coalesced.
+constexpr int kStage = 1024;
+constexpr int kOwn = (int)(kOutTile / kBlock);  // 16 elements per thread
+
 __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t init, const float* __restrict__ base,
                                                  float* __restrict__ out, int64_t n)
 {
     __shared__ float tile[kOutTile];
+    __shared__ int32_t s_a[kMerge], s_off[kMerge + 1];
+    __shared__ uint16_t st_pos[kStage];
+    __shared__ float st_val[kStage];
     const int64_t t = blockIdx.x;
     const int64_t lo = t * kOutTile;
     const int64_t cnt = min((int64_t)kOutTile, n - lo);
     const bool full = cnt == kOutTile;
-    // initial contents
-    for (int q = 0; q < (int)(kOutTile / (4 * kBlock)); ++q) {
-        const int i = 4 * (q * kBlock + threadIdx.x);
-        f4a v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (init != SGC_INIT_ZERO) {
-            const float* src = init == SGC_INIT_BASE ? base : out;
-            if (full) {
-                v = *(const f4a*)(src + lo + i);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (i + j < cnt) v[j] = src[lo + i + j];
-            }
+    constexpr int kQ = (int)(kOutTile / (4 * kBlock));
+    if (threadIdx.x < 64) {  // wave 0: message ranges and their prefix
+        const int k = threadIdx.x;
+        int32_t a = 0, c = 0;
+        if (k < M.n && !*M.bad[k]) {
+            a = M.tstart[k][t];
+            c = M.tstart[k][t + 1] - a;
         }
-        *(f4a*)(tile + i) = v;
+        int32_t x = c;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t y = __shfl_up(x, d, 64);
+            if (k >= d) x += y;
+        }
+        if (k < kMerge) {
+            s_a[k] = a;
+            s_off[k] = x - c;
+        }
+        if (k == kMerge - 1) s_off[kMerge] = x;
+    }
+    {
+        const float* src = init == SGC_INIT_BASE ? base : out;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            const int i = 4 * (q * kBlock + threadIdx.x);
+            f4a v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (init != SGC_INIT_ZERO) {
+                if (full) {
+                    v = *(const f4a*)(src + lo + i);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (i + j < cnt) v[j] = src[lo + i + j];
+                }
+            }
+            *(f4a*)(tile + i) = v;
+        }
     }
     __syncthreads();
-    for (int k = 0; k < M.n; ++k) {
-        if (*M.bad[k]) continue;  // uniform per block
-        const int32_t a = M.tstart[k][t], e = M.tstart[k][t + 1];
-        for (int32_t j = a + threadIdx.x; j < e; j += kBlock) {
+    const int own0 = threadIdx.x * kOwn;
+    const int32_t total = s_off[kMerge];
+    for (int32_t R0 = 0; R0 < total; R0 += kStage) {  // uniform; one round in the common case
+        const int32_t R1 = min(R0 + kStage, total);
+        for (int32_t e = R0 + threadIdx.x; e < R1; e += kBlock) {
+            int k = 0;
+            while (e >= s_off[k + 1]) ++k;
+            const int32_t j = s_a[k] + (e - s_off[k]);
             const int64_t p = (int64_t)M.pos[k][j] - lo;
-            if ((uint64_t)p < (uint64_t)cnt) tile[p] = tile[p] + M.val[k][j];
+            st_pos[e - R0] = (uint16_t)((uint64_t)p < (uint64_t)cnt ? p : 0xffff);
+            st_val[e - R0] = M.val[k][j];
         }
         __syncthreads();
+        for (int k = 0; k < M.n; ++k) {
+            const int32_t e0 = max(s_off[k], R0) - R0, e1 = min(s_off[k + 1], R1) - R0;
+            if (e0 >= e1) continue;
+            // first staged entry of message k at or after own0 (positions ascend)
+            int32_t l = e0, h = e1;
+            while (l < h) {
+                const int32_t m = (l + h) >> 1;
+                if ((int32_t)st_pos[m] < own0) l = m + 1; else h = m;
+            }
+            for (int32_t e = l; e < e1; ++e) {
+                const int32_t p = st_pos[e];
+                if (p >= own0 + kOwn) break;  // also stops at the 0xffff sentinel
+                tile[p] = tile[p] + st_val[e];
+            }
+        }
+        __syncthreads();  // staging is refilled by the next round; the tile is read below
     }
-    for (int q = 0; q < (int)(kOutTile / (4 * kBlock)); ++q) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
         const int i = 4 * (q * kBlock + threadIdx.x);
-        const f4a v = *(const f4a*)(tile + i);
+        const f4a r = *(const f4a*)(tile + i);
         if (full) {
-            __builtin_nontemporal_store(v, (f4a*)(out + lo + i));
+            __builtin_nontemporal_store(r, (f4a*)(out + lo + i));
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (i + j < cnt) out[lo + i + j] = v[j];
+                if (i + j < cnt) out[lo + i + j] = r[j];
         }
     }
 }
@@ -562,12 +676,8 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         const dim3 graw((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxcap, kBlock), 4096)), (unsigned)B.n);
         k_msg_raw<<<graw, kBlock, 0, s>>>(B, L->nseg, L->n, ntiles);
         SGC_LAUNCH_CHECK();
-        const dim3 gch((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxch, kBlock), 4096)), (unsigned)B.n);
-        k_msg_span<<<gch, kBlock, 0, s>>>(B);
-        SGC_LAUNCH_CHECK();
-        k_msg_scan<<<one, 1024, 0, s>>>(B);
-        SGC_LAUNCH_CHECK();
-        k_msg_decode<<<gch, kBlock, 0, s>>>(B, L->nseg, L->n);
+        const dim3 gch((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxch, kDecLanes), 16384)), (unsigned)B.n);
+        k_msg_decode<<<gch, kDecLanes, 0, s>>>(B, L->nseg, L->n);
         SGC_LAUNCH_CHECK();
     }
     // merge in fixed message order; later batches continue in place
@@ -578,8 +688,9 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         M.n = std::min<int32_t>(kMerge, W - b0);
         for (int32_t k = 0; k < M.n; ++k) {
             const MsgWs& w = mws[(size_t)(b0 + k)];
-            M.pos[k] = w.pos;
-            M.val[k] = w.val;
+            const sgc_message& mg = msgs[b0 + k];
+            M.pos[k] = is_golomb(mg.format) ? w.pos : mg.idx;
+            M.val[k] = (mg.format == SGC_MSG_RAW_F32 || mg.format == SGC_MSG_GOLOMB_F32) ? mg.val : w.val;
             M.tstart[k] = w.tstart;
             M.bad[k] = w.bad;
         }

@@ -16,8 +16,8 @@
 //              first bit lies in the block is assembled by one thread from
 //              the codes that overlap it (binary search in LDS, plus up to
 //              32 look-ahead codes of the next block): plain stores, no
-//              atomics, no pre-zeroing; the chunk table (bit offset of every
-//              256th code) is written on the way.
+//              atomics, no pre-zeroing; the chunk table (bit offset and
+//              position reached for every 256th code) is written on the way.
 #include "sgc_common.h"
 
 namespace sgc {
@@ -225,9 +225,14 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
         const uint64_t B1 = B0 + off[nown];
         const int64_t q0 = k.e0 - w.ent[k.s];            // stream-relative index of the first code
         uint32_t* sw = words + word_off[k.s];
-        // chunk table: bit offset of every SGC_CHUNK_CODES-th code
-        for (int i = threadIdx.x * SGC_CHUNK_CODES; i < nown; i += kBlock * SGC_CHUNK_CODES)
-            chunk_off[w.chpre[k.s] + (q0 + i) / SGC_CHUNK_CODES] = B0 + off[i];
+        // chunk table: (bit offset, stream position reached before the code) of
+        // every SGC_CHUNK_CODES-th code
+        for (int i = threadIdx.x * SGC_CHUNK_CODES; i < nown; i += kBlock * SGC_CHUNK_CODES) {
+            const int64_t c = w.chpre[k.s] + (q0 + i) / SGC_CHUNK_CODES;
+            const int64_t j = k.e0 + i;
+            chunk_off[2 * c] = B0 + off[i];
+            chunk_off[2 * c + 1] = j == w.ent[k.s] ? 0 : (uint64_t)((int64_t)idx[j - 1] - w.base[k.s] + 1);
+        }
         const uint64_t wfirst = (B0 + 31) / 32, wend = (B1 + 31) / 32;
         for (uint64_t wd = wfirst + threadIdx.x; wd < wend; wd += kBlock) {
             const uint64_t W0 = wd * 32;
@@ -279,7 +284,7 @@ extern "C" int64_t sgc_encode_word_bound(const sgc_layout* L, int32_t scope, int
 extern "C" int64_t sgc_encode_chunk_bound(const sgc_layout* L, int32_t scope, int64_t cap)
 {
     if (!L || (scope != SGC_GLOBAL && scope != SGC_PER_SEGMENT) || cap < 0) return -1;
-    return cdiv(cap, (int64_t)SGC_CHUNK_CODES) + enc_streams(L, scope);
+    return 2 * (cdiv(cap, (int64_t)SGC_CHUNK_CODES) + enc_streams(L, scope));
 }
 
 extern "C" size_t sgc_encode_workspace(const sgc_layout* L, int32_t scope, int64_t cap)

@@ -203,12 +203,15 @@ int sgc_binarize(const sgc_layout* layout, int32_t mode,
  * word i / 32; each stream starts on a word boundary of out_words, pad bits
  * are 0.  out_word_off [device, nstreams+1] = first word of each stream and
  * the total; out_nbits [device, nstreams] = bits per stream;
- * out_chunk_off [device] = stream-relative bit offsets of codes 0, 256,
- * 512, ... of stream 0, then of stream 1, ... (the decoder's entry points).
- * b in [0, 30].  word_cap / chunk_cap must be at least
- * sgc_encode_word_bound / sgc_encode_chunk_bound (else SGC_ENOSPC): those
- * bounds hold for any counts with total <= cap.  Indices that are not
- * strictly ascending inside a stream set SGC_STATUS_BAD_INPUT.             */
+ * out_chunk_off [device] = the chunk table, the decoder's entry points: for
+ * codes 0, 256, 512, ... of stream 0, then of stream 1, ..., two uint64
+ * entries each: the stream-relative bit offset of the code and the stream-
+ * relative position reached before it (previous position + 1; 0 for the
+ * stream's first code).  b in [0, 30].  word_cap / chunk_cap (uint64
+ * entries) must be at least sgc_encode_word_bound / sgc_encode_chunk_bound
+ * (else SGC_ENOSPC): those bounds hold for any counts with total <= cap.
+ * Indices that are not strictly ascending inside a stream set
+ * SGC_STATUS_BAD_INPUT.                                                     */
 int64_t sgc_encode_word_bound(const sgc_layout* layout, int32_t scope, int32_t b, int64_t cap);
 int64_t sgc_encode_chunk_bound(const sgc_layout* layout, int32_t scope, int64_t cap);
 size_t sgc_encode_workspace(const sgc_layout* layout, int32_t scope, int64_t cap);
@@ -230,9 +233,9 @@ int sgc_encode(const sgc_layout* layout, int32_t scope, int32_t b,
  * entry's segment; *_2BIT -> code 0 -> +0, 1 -> means[2t], 2 -> means[2t+1].
  * The segment of entry j follows from counts (entries are ascending).  A
  * message whose stream overruns its bits, leaves bits unread, disagrees
- * with its chunk table, holds a position >= its stream's size, has raw
- * indices that are not strictly ascending or in [0, n), or a 2-bit code 3,
- * is skipped entirely and sets SGC_STATUS_CORRUPT.
+ * with either entry of its chunk table, holds a position >= its stream's
+ * size, has raw indices that are not strictly ascending or in [0, n), or a
+ * 2-bit code 3, is skipped entirely and sets SGC_STATUS_CORRUPT.
  * msgs [host, W descriptors of device pointers].  base [device, n] is read
  * for SGC_INIT_BASE only.  out [device, n].                                */
 typedef struct {
@@ -249,7 +252,7 @@ typedef struct {
     const uint32_t* words;     /* GOLOMB_*: the coded streams */
     const uint64_t* word_off;  /* GOLOMB_*: [nstreams+1] */
     const uint64_t* nbits;     /* GOLOMB_*: [nstreams] */
-    const uint64_t* chunk_off; /* GOLOMB_*: chunk table */
+    const uint64_t* chunk_off; /* GOLOMB_*: chunk table (bit offset, position reached) pairs */
 } sgc_message;
 
 size_t sgc_decode_accumulate_workspace(const sgc_layout* layout, const sgc_message* msgs, int32_t W);

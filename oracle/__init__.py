@@ -173,7 +173,7 @@ class Encoded:
     words: np.ndarray      # uint32
     word_off: np.ndarray   # uint64 [nstreams+1]
     nbits: np.ndarray      # uint64 [nstreams]
-    chunk_off: np.ndarray  # uint64
+    chunk_off: np.ndarray  # uint64 pairs: (bit offset, position reached) per 256 codes
 
 
 def encode_bound_words(seg_off, counts, scope: int, b: int) -> int:
@@ -196,9 +196,9 @@ def encode(idx, counts, seg_off, scope: int, b: int) -> Encoded:
     nstreams = 1 if scope == GLOBAL else nseg
     word_cap = encode_bound_words(seg_off, counts, scope, b) + 1
     if scope == GLOBAL:
-        chunk_cap = (int(counts[nseg]) + CHUNK_CODES - 1) // CHUNK_CODES
+        chunk_cap = 2 * ((int(counts[nseg]) + CHUNK_CODES - 1) // CHUNK_CODES)
     else:
-        chunk_cap = sum((int(c) + CHUNK_CODES - 1) // CHUNK_CODES for c in counts[:nseg])
+        chunk_cap = 2 * sum((int(c) + CHUNK_CODES - 1) // CHUNK_CODES for c in counts[:nseg])
     words = np.zeros(word_cap, np.uint32)
     word_off = np.zeros(nstreams + 1, np.uint64)
     nbits = np.zeros(nstreams, np.uint64)

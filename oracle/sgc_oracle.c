@@ -356,9 +356,11 @@ int64_t orc_binarize(const int32_t* idx, const float* val, const int64_t* counts
  * entry), i.e. the number of zeros skipped; the code of z is floor(z / 2^b)
  * one-bits, one zero-bit, then the b low bits of z least-significant first;
  * stream bit i is bit (i mod 32) of word i/32 of the stream; each stream
- * starts on a word boundary and its pad bits are 0; chunk_off records the
- * stream-relative bit offset of codes 0, C, 2C, ... (C = 256) so that a
- * decoder can start in the middle of a stream.
+ * starts on a word boundary and its pad bits are 0; the chunk table holds,
+ * for codes 0, C, 2C, ... (C = 256) of every stream, two entries: the
+ * stream-relative bit offset of the code and the stream-relative position
+ * reached before it (previous position + 1, 0 for code 0), so that a
+ * decoder can start in the middle of a stream.  chunk_cap counts entries.
  * Returns ORC_OK, ORC_EINVAL (indices not strictly ascending or out of the
  * stream) or ORC_ENOSPC (word_cap or chunk_cap too small).                */
 struct bitwriter { uint32_t* words; int64_t cap; int64_t base; uint64_t bit; int overflow; };
@@ -389,8 +391,9 @@ int32_t orc_encode(const int32_t* idx, const int64_t* counts, const int64_t* seg
         word_off[s] = (uint64_t)word_pos;
         for (int64_t q = 0; q < cnt; ++q) {
             if (q % ORC_CHUNK_CODES == 0) {
-                if (chunk_pos >= chunk_cap) return ORC_ENOSPC;
+                if (chunk_pos + 2 > chunk_cap) return ORC_ENOSPC;
                 chunk_off[chunk_pos++] = w.bit;
+                chunk_off[chunk_pos++] = (uint64_t)(prev + 1);
             }
             int64_t pos = (int64_t)idx[e0 + q] - lo;
             if (pos <= prev || pos >= hi - lo) return ORC_EINVAL;
@@ -412,8 +415,9 @@ int32_t orc_encode(const int32_t* idx, const int64_t* counts, const int64_t* seg
 /* Decode the positions of one Rice stream (the inverse of orc_encode).
  * Reads count codes starting at words[0]; pos = prev + 1 + z.  Sets
  * ORC_STATUS_CORRUPT in *status if a read passes nbits, a position reaches
- * numel, a recorded chunk offset disagrees with the decoded stream, or the
- * codes do not use exactly nbits bits.  Positions are stream-relative.    */
+ * numel, a chunk-table entry (bit offset, position reached) disagrees with
+ * the decoded stream, or the codes do not use exactly nbits bits.
+ * Positions are stream-relative.                                          */
 int32_t orc_decode_stream(const uint32_t* words, uint64_t nbits, int64_t count,
                           int32_t b, int64_t numel, const uint64_t* chunk_off,
                           int64_t* out_pos, uint32_t* status)
@@ -421,7 +425,9 @@ int32_t orc_decode_stream(const uint32_t* words, uint64_t nbits, int64_t count,
     uint64_t bit = 0;
     int64_t prev = -1;
     for (int64_t q = 0; q < count; ++q) {
-        if (chunk_off && q % ORC_CHUNK_CODES == 0 && chunk_off[q / ORC_CHUNK_CODES] != bit) {
+        if (chunk_off && q % ORC_CHUNK_CODES == 0 &&
+            (chunk_off[2 * (q / ORC_CHUNK_CODES)] != bit ||
+             chunk_off[2 * (q / ORC_CHUNK_CODES) + 1] != (uint64_t)(prev + 1))) {
             *status |= ORC_STATUS_CORRUPT;
             return ORC_OK;
         }
@@ -493,7 +499,7 @@ int32_t orc_accumulate_message(float* out, const int64_t* seg_off, int32_t nseg,
                               chunk_off ? chunk_off + c0 : NULL, pos + e0, &st);
             for (int64_t j = e0; j < e0 + counts[t]; ++j) pos[j] += seg_off[t];
             e0 += counts[t];
-            c0 += (counts[t] + ORC_CHUNK_CODES - 1) / ORC_CHUNK_CODES;
+            c0 += 2 * ((counts[t] + ORC_CHUNK_CODES - 1) / ORC_CHUNK_CODES);
         }
     }
     if (!st && vkind == ORC_VAL_2BIT)

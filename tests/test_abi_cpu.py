@@ -121,7 +121,7 @@ def test_encode_validation_and_bounds():
     wb = lib.sgc_encode_word_bound(lay.handle, 0, 6, cap)
     cb = lib.sgc_encode_chunk_bound(lay.handle, 1, cap)
     assert wb == -(-(cap * 7 + (8000 >> 6)) // 32) + 1
-    assert cb == 1 + 2
+    assert cb == 2 * (1 + 2)   # (bit offset, position reached) per chunk; one chunk per stream + ceil(cap/256)
     assert lib.sgc_encode_word_bound(lay.handle, 0, 31, cap) == -1
     need = lib.sgc_encode_workspace(lay.handle, 0, cap)
     call = lambda scope=0, b=6, wcap=wb, ccap=cb, ws=A, wsb=need, idx=A: \

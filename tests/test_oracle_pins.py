@@ -335,7 +335,7 @@ def test_worked_example_rice_b2(orc):
     enc = orc.encode(np.array([0, 5, 6, 20], np.int32), np.array([4, 4], np.int64), [0, 32], orc.GLOBAL, 2)
     assert int(enc.nbits[0]) == 16
     assert enc.words.tolist() == [0x00005C08]
-    assert enc.chunk_off.tolist() == [0]
+    assert enc.chunk_off.tolist() == [0, 0]
 
 
 def test_worked_example_rice_b3(orc):
@@ -367,9 +367,10 @@ def test_rice_matches_bit_strings(orc, data, b, nseg, scope):
         assert int(enc.nbits[s]) == len(bits)
         assert int(enc.word_off[s]) == len(words)
         words += bf.pack_bits(bits)
-        # chunk table: bit offset of codes 0, 256, 512, ...
+        # chunk table: (bit offset, position reached) of every 256th code
         for c in range(0, len(local), orc.CHUNK_CODES):
             chunks.append(len(bf.rice_bits_string(local[:c], b)))
+            chunks.append(local[c - 1] + 1 if c else 0)
         back, used = bf.parse_rice(bits, len(local), b)
         assert back == local and used == len(bits)
         # oracle decoder agrees
@@ -402,8 +403,12 @@ def test_decode_detects_corruption(orc):
     assert st & orc.STATUS_CORRUPT
     _, st = orc.decode_stream(enc.words, nb, 4, 3, 512)             # bits left over
     assert st & orc.STATUS_CORRUPT
-    _, st = orc.decode_stream(enc.words, nb, 5, 3, 512, chunk_off=np.array([1], np.uint64))
+    _, st = orc.decode_stream(enc.words, nb, 5, 3, 512, chunk_off=np.array([1, 0], np.uint64))
     assert st & orc.STATUS_CORRUPT
+    _, st = orc.decode_stream(enc.words, nb, 5, 3, 512, chunk_off=np.array([0, 1], np.uint64))
+    assert st & orc.STATUS_CORRUPT
+    _, st = orc.decode_stream(enc.words, nb, 5, 3, 512, chunk_off=np.array([0, 0], np.uint64))
+    assert st == 0
 
 
 # ------------------------------------------------------ decode + accumulate
