@@ -45,6 +45,8 @@ constexpr int kSrcSamples = 0, kSrcCand = 1, kSrcDense = 2;
 constexpr int kSuper = 4096;                     // tiles per scan super block
 constexpr int kGatherTiles = 16;                 // tiles per gather workgroup
 constexpr uint32_t kAccFlag = 0x80000000u;       // candidate index flag: r still holds acc there
+constexpr int kRep = 8;                          // global histogram replicas per (virtual) group
+constexpr int kHistBlocks = 1024;                // workgroups of a histogram pass
 
 struct CompressWs {
     int64_t* k;        // [G] keep count
@@ -61,7 +63,7 @@ struct CompressWs {
     int64_t* cpre;     // [2G+1] chunk prefix over the selection source
     uint32_t* prefix;  // [2G] radix-select prefix -> T
     int64_t* mrem;     // [2G] remaining rank -> quota of ties at T
-    uint32_t* hist;    // [2G * kBins]
+    uint32_t* hist;    // [2G * kRep * kBins] (kRep replicas spread the flush atomics)
     int64_t* cstart;   // [G] candidate array start per group
     float* samples;    // [S]
     uint32_t* tile_cnt;// [NT]
@@ -119,7 +121,7 @@ static void carve_compress(Carver& c, const CompressSizes& z, int mode, Compress
     w->cpre = c.take<int64_t>(V + 1);
     w->prefix = c.take<uint32_t>(V);
     w->mrem = c.take<int64_t>(V);
-    w->hist = c.take<uint32_t>(V * kBins);
+    w->hist = c.take<uint32_t>(V * kRep * kBins);
     w->cstart = c.take<int64_t>(G);
     w->samples = c.take<float>(z.S);
     w->tile_cnt = c.take<uint32_t>(z.NT);
@@ -258,7 +260,9 @@ __global__ __launch_bounds__(kBlock) void k_probe(const float* __restrict__ grad
 
 // ----------------------------------------------------------- radix select
 // Histogram of one digit over every selection source chunk whose (virtual)
-// group is still open and whose key matches the digits chosen so far.
+// group is still open and whose key matches the digits chosen so far.  Each
+// workgroup takes a contiguous run of chunks and accumulates in LDS across
+// them, flushing once per group it touches into one of kRep global replicas.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ res, int32_t V, CompressWs w)
 {
@@ -267,29 +271,58 @@ __global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ r
     constexpr int nb = D == 0 ? 2048 : 1024;
     __shared__ uint32_t h[nb];
     const int64_t nch = w.cpre[V];
-    for (int64_t c = blockIdx.x; c < nch; c += gridDim.x) {
-        const int64_t g = find_bucket(w.cpre, (int64_t)V + 1, c);
-        if (w.mrem[g] == 0) continue;
-        for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
+    const int64_t per = cdiv(nch, (int64_t)gridDim.x);
+    const int64_t c0 = (int64_t)blockIdx.x * per, c1 = min(c0 + per, nch);
+    for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
+    __syncthreads();
+    int64_t cur = -1;
+    bool dirty = false;
+    auto flush = [&](int64_t g) {
         __syncthreads();
+        uint32_t* gh = w.hist + (g * kRep + (blockIdx.x & (kRep - 1))) * kBins;
+        for (int b = threadIdx.x; b < nb; b += kBlock) {
+            const uint32_t v = h[b];
+            if (v) {
+                atomicAdd(&gh[b], v);
+                h[b] = 0;
+            }
+        }
+        __syncthreads();
+    };
+    for (int64_t c = c0; c < c1; ++c) {
+        const int64_t g = find_bucket(w.cpre, (int64_t)V + 1, c);  // uniform
+        if (g != cur) {
+            if (dirty) flush(cur);
+            cur = g;
+            dirty = false;
+        }
+        if (w.mrem[g] == 0) continue;
+        dirty = true;
         const int64_t base = w.src_base[g] + (c - w.cpre[g]) * kChunk;
         const int64_t end = min(base + kChunk, w.src_base[g] + w.src_len[g]);
         const int kind = w.src_kind[g];
         const float* src = kind == kSrcSamples ? w.samples : kind == kSrcCand ? w.cand_val : res;
         const uint32_t pre = w.prefix[g];
-        for (int64_t i = base + threadIdx.x; i < end; i += kBlock) {
-            const uint32_t key = mag_key(src[i]);
-            if (D == 0 || (key >> (shift + 10)) == pre) atomicAdd(&h[(key >> shift) & mask], 1u);
+        for (int64_t i0 = base + threadIdx.x; i0 < end; i0 += 4 * kBlock) {
+            float x[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {  // four independent loads in flight
+                const int64_t i = i0 + q * kBlock;
+                x[q] = i < end ? src[i] : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t key = mag_key(x[q]);
+                if (i0 + q * kBlock < end && (D == 0 || (key >> (shift + 10)) == pre))
+                    atomicAdd(&h[(key >> shift) & mask], 1u);
+            }
         }
-        __syncthreads();
-        uint32_t* gh = w.hist + g * kBins;
-        for (int b = threadIdx.x; b < nb; b += kBlock)
-            if (h[b]) atomicAdd(&gh[b], h[b]);
-        __syncthreads();
     }
+    if (dirty) flush(cur);
 }
 
-// Pick the digit holding the wanted rank (counted from the largest key).
+// Pick the digit holding the wanted rank (counted from the largest key):
+// sum the replicas, scan from the top, clear the replicas for the next digit.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_srs_resolve(CompressWs w)
 {
@@ -300,29 +333,36 @@ __global__ __launch_bounds__(kBlock) void k_srs_resolve(CompressWs w)
     const int64_t g = blockIdx.x;
     const int64_t target = w.mrem[g];
     if (target == 0) return;  // uniform per block
-    uint32_t* gh = w.hist + g * kBins;
+    uint32_t* gh = w.hist + g * kRep * kBins;
     // thread t owns bins [nb - (t+1)*per, nb - t*per): thread 0 the largest keys
     const int top = nb - threadIdx.x * per;
+    uint32_t cnt[per];
     int64_t local = 0;
 #pragma unroll
-    for (int i = 1; i <= per; ++i) local += gh[top - i];
+    for (int i = 0; i < per; ++i) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < kRep; ++r) {
+            c += gh[r * kBins + top - 1 - i];
+            gh[r * kBins + top - 1 - i] = 0;
+        }
+        cnt[i] = c;
+        local += c;
+    }
     int64_t total;
     const int64_t above = block_exclusive_scan<int64_t>(local, tmp, &total);
     if (above < target && above + local >= target) {
         int64_t run = above;
-        for (int i = 1; i <= per; ++i) {
-            const int bin = top - i;
-            const int64_t c = gh[bin];
-            if (run + c >= target) {
+        for (int i = 0; i < per; ++i) {
+            const int bin = top - 1 - i;
+            if (run + cnt[i] >= target) {
                 w.prefix[g] = (w.prefix[g] << bits) | (uint32_t)bin;
                 w.mrem[g] = target - run;
                 break;
             }
-            run += c;
+            run += cnt[i];
         }
     }
-#pragma unroll
-    for (int i = 1; i <= per; ++i) gh[top - i] = 0;
 }
 
 // After the probe selection: the candidate and zeroing bounds of each group.
@@ -759,6 +799,8 @@ __device__ inline void chunk_item(const CompressWs& w, const float* res, const C
 
 __device__ inline uint32_t group_T(const CompressWs& w, int64_t g) { return w.rank[g] > 0 ? w.prefix[g] : kNoKey; }
 
+// Item i of chunk c lives at base + j*kBlock + tid (j < kPer): coalesced
+// loads; the index order of a chunk is (j, wave, lane).
 __global__ __launch_bounds__(kBlock) void k_compact_count(const float* __restrict__ res, int32_t G, CompressWs w)
 {
     __shared__ uint32_t tmp[kBlock / 64 + 1];
@@ -767,9 +809,9 @@ __global__ __launch_bounds__(kBlock) void k_compact_count(const float* __restric
         const ChunkView v = chunk_view(w, G, c);
         const uint32_t T = group_T(w, v.g);
         uint32_t gt = 0, eq = 0;
-        const int64_t b = v.base + (int64_t)threadIdx.x * kPer;
+#pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int64_t i = b + j;
+            const int64_t i = v.base + j * kBlock + threadIdx.x;
             if (i < v.end) {
                 uint32_t id;
                 float x;
@@ -800,7 +842,10 @@ __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ re
                                                          int32_t* __restrict__ out_idx,
                                                          float* __restrict__ out_val, int64_t cap)
 {
-    __shared__ uint32_t tmp[kBlock / 64 + 1];
+    __shared__ uint32_t weq[kPer][kBlock / 64];
+    __shared__ uint32_t wkp[kPer][kBlock / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     const int64_t nch = w.cpre[G];
     for (int64_t c = blockIdx.x; c < nch; c += gridDim.x) {
         const ChunkView v = chunk_view(w, G, c);
@@ -813,53 +858,82 @@ __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ re
         const int64_t kept_before = gt_before + (eq_before < quota ? eq_before : quota);
         uint32_t id[kPer];
         float x[kPer];
-        uint32_t key[kPer];
-        uint32_t eq = 0;
-        const int64_t b = v.base + (int64_t)threadIdx.x * kPer;
+        uint32_t valid = 0, eqb = 0, gtb = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int64_t i = b + j;
-            key[j] = kNoKey;
+            const int64_t i = v.base + j * kBlock + threadIdx.x;
+            id[j] = 0;
+            x[j] = 0.0f;
             if (i < v.end) {
                 chunk_item(w, res, v, i, &id[j], &x[j]);
-                key[j] = mag_key(x[j]);
-                eq += key[j] == T;
+                const uint32_t key = mag_key(x[j]);
+                valid |= 1u << j;
+                gtb |= (uint32_t)(key > T) << j;
+                eqb |= (uint32_t)(key == T) << j;
             }
         }
-        uint32_t tot;
-        uint32_t eq_rank = block_exclusive_scan<uint32_t>(eq, tmp, &tot);
-        uint32_t keep = 0, nkeep = 0;
+        // rank of each tie among the chunk's ties, in index order
+        uint32_t rk[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            bool k = false;
-            if (key[j] != kNoKey) {
-                if (key[j] > T) k = true;
-                else if (key[j] == T) {
-                    k = eq_before + (int64_t)eq_rank < quota;
-                    ++eq_rank;
-                }
-            }
-            keep |= (uint32_t)k << j;
-            nkeep += k;
+            const uint64_t b = __ballot((eqb >> j) & 1u);
+            rk[j] = __popcll(b & below);
+            if (lane == 0) weq[j][wave] = __popcll(b);
         }
-        uint32_t kept_rank = block_exclusive_scan<uint32_t>(nkeep, tmp, &tot);
-        int64_t pos = w.kpre[v.g] + kept_before + kept_rank;
+        __syncthreads();
+        // a tie is kept while the ties before it in the group number fewer than quota
+        uint32_t keepb = gtb;
+        {
+            uint32_t run = 0;  // ties in the earlier slots j' < j of this chunk
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                uint32_t before = 0, tot = 0;
+                for (int q = 0; q < kBlock / 64; ++q) {
+                    const uint32_t cq = weq[j][q];
+                    before += q < wave ? cq : 0u;
+                    tot += cq;
+                }
+                if (((eqb >> j) & 1u) && eq_before + (int64_t)(run + before + rk[j]) < quota) keepb |= 1u << j;
+                run += tot;
+            }
+        }
+        // rank of each kept item among the chunk's kept items
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            if (key[j] == kNoKey) continue;
-            const uint32_t i = id[j] & ~kAccFlag;
-            const bool zeroed = !(id[j] & kAccFlag) && key[j] >= kz;  // pass 1 stored +0 here
-            if (keep & (1u << j)) {
-                if (pos < cap) {
-                    out_idx[pos] = (int32_t)i;
-                    out_val[pos] = x[j];
+            const uint64_t b = __ballot((keepb >> j) & 1u);
+            rk[j] = __popcll(b & below);
+            if (lane == 0) wkp[j][wave] = __popcll(b);
+        }
+        __syncthreads();
+        {
+            uint32_t run = 0;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                uint32_t before = 0, tot = 0;
+                for (int q = 0; q < kBlock / 64; ++q) {
+                    const uint32_t cq = wkp[j][q];
+                    before += q < wave ? cq : 0u;
+                    tot += cq;
                 }
-                ++pos;
-                if (!zeroed) res[i] = 0.0f;
-            } else if (zeroed) {
-                res[i] = x[j];  // zeroed by pass 1 but not kept: give acc back
+                if ((valid >> j) & 1u) {
+                    const uint32_t i = id[j] & ~kAccFlag;
+                    const uint32_t key = mag_key(x[j]);
+                    const bool zeroed = !(id[j] & kAccFlag) && key >= kz;  // pass 1 stored +0 here
+                    if ((keepb >> j) & 1u) {
+                        const int64_t pos = w.kpre[v.g] + kept_before + run + before + rk[j];
+                        if (pos < cap) {
+                            out_idx[pos] = (int32_t)i;
+                            out_val[pos] = x[j];
+                        }
+                        if (!zeroed) res[i] = 0.0f;
+                    } else if (zeroed) {
+                        res[i] = x[j];  // zeroed by pass 1 but not kept: give acc back
+                    }
+                }
+                run += tot;
             }
         }
+        __syncthreads();  // weq / wkp are rewritten by the next chunk
     }
 }
 
@@ -892,7 +966,7 @@ __global__ void k_seg_counts(const int64_t* __restrict__ seg_off, int32_t nseg, 
 template <int D>
 static int radix_select(const float* res, int32_t V, int64_t nch_max, const CompressWs& w, hipStream_t s)
 {
-    unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>(nch_max, 1), 2048);
+    unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>(nch_max, 1), kHistBlocks);
     k_srs_hist<D><<<blocks, kBlock, 0, s>>>(res, V, w);
     SGC_LAUNCH_CHECK();
     k_srs_resolve<D><<<(unsigned)V, kBlock, 0, s>>>(w);
@@ -997,7 +1071,7 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
     // 1. probe selection -> key_lo, key_z
     k_setup<<<1, 64, 0, s>>>(gr.off, G, o->mode, o->keep_ppm, o->sample_div, o->sample_min, w);
     SGC_LAUNCH_CHECK();
-    if ((rc = fill_u32(w.hist, (int64_t)V * kBins, 0, s))) return rc;
+    if ((rc = fill_u32(w.hist, (int64_t)V * kRep * kBins, 0, s))) return rc;
     if (z.S > 0) {
         unsigned pb = (unsigned)std::min<int64_t>(cdiv(z.S, kBlock), 4096);
         k_probe<<<pb, kBlock, 0, s>>>(grad, residual, gr.off, G, o->mode, w, z.S);
