@@ -27,9 +27,10 @@
 namespace sgc {
 
 typedef float f4a __attribute__((ext_vector_type(4)));
+typedef int32_t i4v __attribute__((ext_vector_type(4)));
 
 constexpr int kBatch = 8;     // messages per decode launch
-constexpr int kMerge = 32;    // messages per merge launch
+constexpr int kMerge = 16;    // messages per merge launch
 
 struct MsgWs {
     int64_t* estart;  // [nseg+1] entry prefix per segment
@@ -159,38 +160,74 @@ __global__ void k_msg_setup(Batch B, const int64_t* __restrict__ seg_off, int32_
     w.tstart[ntiles] = (int32_t)(bad ? 0 : e);
 }
 
-// Output-tile table: entry j owns tiles (tile(prev), tile(pos)] -- the tiles
-// whose first element lies after the previous entry and at or before it.
-__device__ inline void fill_tiles(int32_t* tstart, int64_t from_pos_excl, int64_t to_pos_incl, int64_t j)
+// ---------------------------------------------------- entries, tile table
+// After decoding, every message is a list of ascending global positions
+// (its own idx if raw, the decoded positions otherwise).  The output-tile
+// table holds, per tile, the first entry at or beyond the tile's first
+// element.  One thread per entry checks the order (raw input is not
+// trusted), resolves raw 2-bit values, and writes the table for the tiles
+// whose first element lies after the previous entry and at or before this
+// one -- all of them when there are at most kGapTiles, else only the last;
+// the remaining tiles (long gaps, and those after the last entry beyond
+// kGapTiles) are found by a binary search per tile.
+constexpr int64_t kGapTiles = 16;
+
+__device__ inline int64_t lower_bound_pos(const int32_t* pos, int64_t total, int64_t x)
 {
-    const int64_t t0 = from_pos_excl < 0 ? 0 : from_pos_excl / kOutTile + 1;
-    const int64_t t1 = to_pos_incl / kOutTile;
-    for (int64_t t = t0; t <= t1; ++t) tstart[t] = (int32_t)j;
+    int64_t lo = 0, hi = total;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if ((int64_t)pos[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
 }
 
-// ----------------------------------------------------------- raw messages
-__global__ __launch_bounds__(kBlock) void k_msg_raw(Batch B, int32_t nseg, int64_t n, int64_t ntiles)
+__device__ inline const int32_t* msg_positions(const MsgIn& in, const MsgWs& w)
+{
+    return in.format >= SGC_MSG_GOLOMB_F32 ? w.pos : in.idx;
+}
+
+__global__ __launch_bounds__(kBlock) void k_msg_entries(Batch B, int32_t nseg, int64_t n, int64_t ntiles)
 {
     const int m = blockIdx.y;
     const MsgIn& in = B.in[m];
     const MsgWs& w = B.ws[m];
-    if (in.format >= SGC_MSG_GOLOMB_F32) return;
+    if (w.bad[0]) return;
     const int64_t total = w.total[0];
+    const int32_t* pos = msg_positions(in, w);
     bool bad = false;
     for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < total; j += (int64_t)gridDim.x * kBlock) {
-        const int64_t p = in.idx[j];
-        const int64_t prev = j == 0 ? -1 : (int64_t)in.idx[j - 1];
-        if (p < 0 || p >= n || p <= prev) { bad = true; continue; }
-        if (in.format == SGC_MSG_RAW_2BIT) {  // RAW_F32: the merge reads idx/val directly
+        const int64_t p = pos[j];
+        const int64_t prev = j == 0 ? -1 : (int64_t)pos[j - 1];
+        if (p < 0 || p >= n || p <= prev) {
+            bad = true;
+            continue;
+        }
+        if (in.format == SGC_MSG_RAW_2BIT) {  // other formats: the merge reads the values directly
             const uint32_t code = (in.codes[j >> 4] >> (2 * (j & 15))) & 3u;
             const int64_t t = find_bucket(w.estart, (int64_t)nseg + 1, j);
             if (code == 3u) bad = true;
             w.val[j] = code == 0u ? 0.0f : code == 1u ? in.means[2 * t] : in.means[2 * t + 1];
         }
-        fill_tiles(w.tstart, prev, p, j);
-        if (j == total - 1) fill_tiles(w.tstart, p, n - 1, total);
+        const int64_t t1 = p >> kOutTileLog, t0 = prev < 0 ? 0 : (prev >> kOutTileLog) + 1;
+        for (int64_t t = max(t0, t1 - kGapTiles + 1); t <= t1; ++t) w.tstart[t] = (int32_t)j;
+        if (j == total - 1)
+            for (int64_t t = t1 + 1; t < min(ntiles, t1 + 1 + kGapTiles); ++t) w.tstart[t] = (int32_t)total;
     }
     if (bad) atomicOr(w.bad, 1u);
+}
+
+// Tiles the entry pass left unset (still negative): binary search.
+__global__ __launch_bounds__(kBlock) void k_msg_holes(Batch B, int64_t ntiles)
+{
+    const int m = blockIdx.y;
+    const MsgIn& in = B.in[m];
+    const MsgWs& w = B.ws[m];
+    if (w.bad[0]) return;
+    const int64_t total = w.total[0];
+    const int32_t* pos = msg_positions(in, w);
+    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < ntiles; t += (int64_t)gridDim.x * kBlock)
+        if (w.tstart[t] < 0) w.tstart[t] = (int32_t)lower_bound_pos(pos, total, t << kOutTileLog);
 }
 
 // --------------------------------------------------------- Rice decoding
@@ -213,307 +250,360 @@ __device__ inline ChunkAt chunk_at(const MsgWs& w, int32_t S, int64_t c)
 // barrier: no lane reads another lane's column), then decodes from LDS, so
 // the decode loop issues no global loads at all and never waits on memory
 // behind its own stores (one counter tracks both on this GPU).  A chunk
-// whose words do not fit the column (very long gaps) decodes from global
-// memory instead.  Positions (and, for SBC / 2-bit, resolved values) are
-// buffered kDB at a time and stored together; the output-tile table is
-// filled on the way, and the chunk is checked against its neighbours in
-// the chunk table.
-constexpr int kDB = 16;
+// whose words do not fit the column (very long gaps) reads global memory
+// instead.  Bit positions are 32-bit, relative to the chunk's first word:
+// a valid chunk spans less than 2^31 + 256 * 32 bits (its gaps sum to less
+// than the stream's size), and a chunk-table entry that claims more is
+// rejected.  Each code is read from a 32-bit window at its first bit; the
+// unary run and the b low bits fit the window unless the gap is far above
+// 2^b (then a loop reads further windows).
 constexpr int kDecLanes = 64;
 constexpr int kColWords = 120;  // LDS words per lane (the chunk's words plus slack)
 constexpr int kColCodes = 17;   // 2-bit code words per lane (256 entries span at most 17)
+constexpr uint32_t kMaxChunkBits = 0x80000000u + SGC_CHUNK_CODES * 32u;
 
-struct LdsWords {
-    const uint32_t* col;  // this lane's column: col[i * kDecLanes]
-    uint64_t w0, nw;      // first stream word held, words held
-    __device__ uint32_t operator()(uint64_t i) const
+// 32 stream bits starting at chunk-relative bit r, from the lane's LDS column.
+struct LdsBits {
+    const uint32_t* col;  // word i at col[i * kDecLanes]
+    __device__ uint32_t win(uint32_t r) const
     {
-        const uint64_t r = i - w0;
-        return r < nw ? col[r * kDecLanes] : 0u;
+        const uint32_t i = r >> 5;
+        const uint32_t lo = col[i * kDecLanes], hi = col[(i + 1) * kDecLanes];
+        return (uint32_t)((((uint64_t)hi << 32) | lo) >> (r & 31));
     }
 };
 
-struct GlobalWords {
+// The same from global memory; words at or past nw read as 0.
+struct GlobalBits {
     const uint32_t* w;
-    uint64_t nw;
-    __device__ uint32_t operator()(uint64_t i) const { return i < nw ? w[i] : 0u; }
-};
-
-// Sequential reader of one Rice stream over a word source; every read is
-// checked against nbits.
-template <typename Src>
-struct WordReader {
-    Src src;
-    uint64_t nbits, pos, buf, wi;  // buf holds bits [pos, pos + avail); wi: next word to append
-    uint32_t avail;
-    __device__ void start(Src s, uint64_t nb, uint64_t bit)
+    uint64_t nw, bit0;  // chunk-relative bit 0 is stream bit bit0
+    __device__ uint32_t win(uint32_t r) const
     {
-        src = s;
-        nbits = nb;
-        pos = bit;
-        wi = (bit >> 5) + 1;
-        const uint32_t sh = (uint32_t)(bit & 31);
-        buf = (uint64_t)(src(bit >> 5) >> sh);
-        avail = 32 - sh;
-    }
-    __device__ void refill()
-    {
-        while (avail <= 32) {
-            buf |= (uint64_t)src(wi++) << avail;
-            avail += 32;
-        }
-    }
-    __device__ void consume(uint32_t k)
-    {
-        buf = k >= 64 ? 0ull : buf >> k;
-        avail -= k;
-        pos += k;
-    }
-    __device__ bool next(uint32_t b, uint64_t* z)
-    {
-        uint64_t q = 0;
-        for (;;) {
-            if (pos >= nbits) return false;
-            refill();
-            const uint64_t inv = ~buf;  // buf is 0 above avail, so the count stops at avail
-            const uint32_t ones = inv ? (uint32_t)__builtin_ctzll(inv) : 64u;
-            if (ones < avail) {
-                if (pos + ones >= nbits) return false;
-                q += ones;
-                consume(ones + 1);
-                break;
-            }
-            q += avail;
-            consume(avail);
-        }
-        uint64_t rem = 0;
-        if (b) {
-            refill();
-            if (pos + b > nbits) return false;
-            rem = buf & ((1ull << b) - 1ull);
-            consume(b);
-        }
-        if (q >> 33) return false;  // no stream is that long
-        *z = (q << b) | rem;
-        return true;
+        const uint64_t a = bit0 + r, i = a >> 5;
+        const uint32_t lo = i < nw ? w[i] : 0u, hi = i + 1 < nw ? w[i + 1] : 0u;
+        return (uint32_t)((((uint64_t)hi << 32) | lo) >> (a & 31));
     }
 };
 
-// Decode one chunk with reader rd; returns false if the chunk is corrupt.
-template <typename Rd>
-__device__ inline bool decode_chunk(Rd& rd, const MsgIn& in, const MsgWs& w, const ChunkAt& a, int64_t c,
-                                    int32_t nseg, uint64_t reached, const uint32_t* code_col)
+// What one lane needs to decode its chunk.
+struct ChunkJob {
+    uint32_t b, relend;     // Rice parameter; the chunk's end bit (relative)
+    int32_t nc;             // codes in the chunk
+    int32_t j0;             // message entry of its first code
+    int32_t prev;           // stream position of the entry before it (-1 at the stream's start)
+    int32_t size, base;     // stream size and its first element
+    int32_t t, tend;        // value segment of entry j0 and where its entries end
+};
+
+template <int FMT>
+__device__ inline void seg_means(const MsgIn& in, int32_t t, float* m0, float* m1)
 {
-    const int fmt = in.format;
-    const int64_t size = w.ssize[a.s];
-    const int64_t base = w.sbase[a.s];
-    const int64_t j0 = w.sent[a.s] + a.q0;
-    int64_t prev = (int64_t)reached - 1;
-    // segment of the current entry (per-segment values), where its entries end, and its means
-    int64_t t = in.scope == SGC_PER_SEGMENT ? a.s : find_bucket(w.estart, (int64_t)nseg + 1, j0);
-    int64_t tend = in.scope == SGC_PER_SEGMENT ? INT64_MAX : w.estart[t + 1];
-    float m0 = 0.0f, m1 = 0.0f;
-    if (fmt == SGC_MSG_GOLOMB_SBC) m0 = in.means[t];
-    if (fmt == SGC_MSG_GOLOMB_2BIT) {
-        m0 = in.means[2 * t];
-        m1 = in.means[2 * t + 1];
+    if (FMT == SGC_MSG_GOLOMB_SBC) *m0 = in.means[t];
+    if (FMT == SGC_MSG_GOLOMB_2BIT) {
+        *m0 = in.means[2 * t];
+        *m1 = in.means[2 * t + 1];
     }
-    const bool values = fmt != SGC_MSG_GOLOMB_F32;  // F32 values are read by the merge directly
-    int64_t gprev = base + prev;  // global position of the previous entry (tile table)
-    for (int64_t i0 = 0; i0 < a.nc; i0 += kDB) {
-        const int nb = (int)min((int64_t)kDB, a.nc - i0);
-        int32_t pb[kDB];
-        float vv[kDB];
-#pragma unroll
-        for (int q = 0; q < kDB; ++q) {
-            pb[q] = 0;
-            vv[q] = 0.0f;
-            if (q >= nb) continue;
-            uint64_t z;
-            if (!rd.next((uint32_t)in.b, &z)) return false;
-            const int64_t p = prev + 1 + (int64_t)z;
-            if (p >= size) return false;
-            prev = p;
-            const int64_t j = j0 + i0 + q;
-            while (j >= tend) {  // entered the next segment (global scope): rare
-                ++t;
-                tend = w.estart[t + 1];
-                if (fmt == SGC_MSG_GOLOMB_SBC) m0 = in.means[t];
-                if (fmt == SGC_MSG_GOLOMB_2BIT) {
-                    m0 = in.means[2 * t];
-                    m1 = in.means[2 * t + 1];
-                }
-            }
-            if (fmt == SGC_MSG_GOLOMB_SBC) {
-                vv[q] = m0;
-            } else if (fmt == SGC_MSG_GOLOMB_2BIT) {
-                const int64_t cw = (j >> 4) - (j0 >> 4);
-                const uint32_t word = code_col ? code_col[cw * kDecLanes] : in.codes[j >> 4];
-                const uint32_t code = (word >> (2 * (j & 15))) & 3u;
-                if (code == 3u) return false;
-                vv[q] = code == 0u ? 0.0f : code == 1u ? m0 : m1;
-            }
-            pb[q] = (int32_t)(base + p);
-        }
-        const int64_t jb = j0 + i0;
-        if (nb == kDB && (jb & 3) == 0) {  // whole 64-byte sectors: four 16-byte stores per array
-            typedef int32_t i4v __attribute__((ext_vector_type(4)));
-#pragma unroll
-            for (int q = 0; q < kDB / 4; ++q) {
-                *(i4v*)(w.pos + jb + 4 * q) = i4v{pb[4 * q], pb[4 * q + 1], pb[4 * q + 2], pb[4 * q + 3]};
-                if (values) *(f4a*)(w.val + jb + 4 * q) = f4a{vv[4 * q], vv[4 * q + 1], vv[4 * q + 2], vv[4 * q + 3]};
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < kDB; ++q) {
-                if (q >= nb) continue;
-                w.pos[jb + q] = pb[q];
-                if (values) w.val[jb + q] = vv[q];
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < kDB; ++q) {
-            if (q >= nb) continue;
-            fill_tiles(w.tstart, gprev, pb[q], jb + q);
-            gprev = pb[q];
-        }
-    }
-    if (c + 1 < w.chpre[a.s + 1]) {
-        // the next chunk must start exactly where this one ended
-        if (in.chunk_off[2 * (c + 1)] != rd.pos || in.chunk_off[2 * (c + 1) + 1] != (uint64_t)(prev + 1)) return false;
-    } else {
-        if (rd.pos != rd.nbits) return false;  // no bits left over
-        // the stream's last entry covers the tiles up to the end of its range
-        fill_tiles(w.tstart, gprev, base + size - 1, w.sent[a.s + 1]);
-    }
-    return true;
 }
 
-__global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg, int64_t n)
+// Decode one chunk from src starting at relative bit rel; false if corrupt.
+// Returns the end bit and the last position through *rel_out / *prev_out.
+// Errors are collected in a flag rather than taken as branches; after one,
+// decoding goes on over garbage with every read clamped inside the chunk's
+// words, and the chunk is rejected at the end.
+template <int FMT, typename Src>
+__device__ bool decode_chunk(const Src& src, uint32_t rel, const ChunkJob& J, const MsgIn& in, const MsgWs& w,
+                             const uint32_t* code_col, uint32_t* rel_out, int32_t* prev_out)
 {
-    __shared__ uint32_t col[kColWords * kDecLanes];
-    __shared__ uint32_t ccol[kColCodes * kDecLanes];
-    const int m = blockIdx.y;
-    const MsgIn& in = B.in[m];
-    const MsgWs& w = B.ws[m];
-    if (in.format < SGC_MSG_GOLOMB_F32) return;
-    if (w.bad[0]) return;
+    const uint32_t b = J.b, mask = (1u << b) - 1u, last_rd = J.relend - 1;
+    uint32_t prev = (uint32_t)J.prev;  // stream position of the previous entry; -1 wraps to all ones
+    bool err = false;
+    float m0 = 0.0f, m1 = 0.0f;
+    int32_t t = J.t, tend = J.tend;
+    if (FMT != SGC_MSG_GOLOMB_F32) seg_means<FMT>(in, t, &m0, &m1);
+    const bool vec = (J.j0 & 3) == 0;
+    for (int32_t i0 = 0; i0 < J.nc; i0 += 4) {
+        int32_t pb[4];
+        float vb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool act = i0 + q < J.nc;  // false only in a stream's last chunk
+            err |= act && rel >= J.relend;
+            const uint32_t win = src.win(min(rel, last_rd));
+            const uint32_t ones = __builtin_ctzg(~win, 32);
+            uint32_t len = ones + 1 + b;
+            uint32_t z = (ones << b) | ((win >> min(ones, 31u) >> 1) & mask);
+            if (len > 32) {  // the unary run and the low bits leave the window: read on
+                uint64_t qq = 0;
+                uint32_t r = rel;
+                bool fin = false;
+                while (!fin && r < J.relend) {
+                    const uint32_t o = __builtin_ctzg(~src.win(r), 32);
+                    qq += o;
+                    r += o < 32 ? o + 1 : 32;
+                    fin = o < 32;
+                }
+                uint32_t rem = 0;
+                if (b) rem = src.win(min(r, last_rd)) & mask;
+                const uint64_t zz = (qq << b) | rem;
+                err |= act && (!fin || qq >> 31 || zz >= (uint64_t)J.size);
+                z = (uint32_t)zz;
+                len = r + b - rel;
+            }
+            const uint32_t pu = prev + 1 + z;  // below 2^32 unless already in error
+            err |= act && (rel + len > J.relend || pu >= (uint32_t)J.size);
+            rel = act ? rel + len : rel;
+            prev = act ? pu : prev;
+            pb[q] = (int32_t)((uint32_t)J.base + prev);
+            vb[q] = 0.0f;
+            if (FMT != SGC_MSG_GOLOMB_F32 && act) {
+                const int32_t j = J.j0 + i0 + q;
+                while (j >= tend) {  // entered the next segment (global scope): rare
+                    ++t;
+                    tend = (int32_t)w.estart[t + 1];
+                    seg_means<FMT>(in, t, &m0, &m1);
+                }
+                if (FMT == SGC_MSG_GOLOMB_SBC) {
+                    vb[q] = m0;
+                } else {
+                    const int32_t r = i0 + q + (J.j0 & 15);  // entry within the lane's code words
+                    const uint32_t code = (code_col[(r >> 4) * kDecLanes] >> (2 * (r & 15))) & 3u;
+                    err |= code == 3u;
+                    vb[q] = code == 0u ? 0.0f : code == 1u ? m0 : m1;
+                }
+            }
+        }
+        const int32_t jb = J.j0 + i0;
+        if (vec && i0 + 4 <= J.nc) {
+            *(i4v*)(w.pos + jb) = i4v{pb[0], pb[1], pb[2], pb[3]};
+            if (FMT != SGC_MSG_GOLOMB_F32) *(f4a*)(w.val + jb) = f4a{vb[0], vb[1], vb[2], vb[3]};
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (i0 + q >= J.nc) continue;
+                w.pos[jb + q] = pb[q];
+                if (FMT != SGC_MSG_GOLOMB_F32) w.val[jb + q] = vb[q];
+            }
+        }
+    }
+    *rel_out = rel;
+    *prev_out = (int32_t)prev;
+    return !err;
+}
+
+template <int FMT>
+__device__ void decode_lanes(const MsgIn& in, const MsgWs& w, int32_t nseg, uint32_t* col, uint32_t* ccol)
+{
     const int lane = threadIdx.x;
     const int64_t nch = w.chpre[in.S];
     bool bad = false;
     for (int64_t c = (int64_t)blockIdx.x * kDecLanes + lane; c < nch; c += (int64_t)gridDim.x * kDecLanes) {
         const ChunkAt a = chunk_at(w, in.S, c);
         const uint64_t bit0 = in.chunk_off[2 * c], reached = in.chunk_off[2 * c + 1];
-        if ((a.q0 == 0 && (bit0 != 0 || reached != 0)) || reached > (uint64_t)w.ssize[a.s]) { bad = true; continue; }
+        const bool last = c + 1 >= w.chpre[a.s + 1];
+        const uint64_t nbits = in.nbits[a.s];
+        const uint64_t bit1 = last ? nbits : in.chunk_off[2 * (c + 1)];
+        const int64_t size = w.ssize[a.s];
+        if ((a.q0 == 0 && (bit0 != 0 || reached != 0)) || reached > (uint64_t)size || bit1 <= bit0 ||
+            bit1 > nbits || bit1 - bit0 > kMaxChunkBits) {
+            bad = true;
+            continue;
+        }
         const uint32_t* words = in.words + in.word_off[a.s];
         const uint64_t nw = in.word_off[a.s + 1] - in.word_off[a.s];
-        const uint64_t nbits = in.nbits[a.s];
-        const uint64_t bit1 = (c + 1 < w.chpre[a.s + 1]) ? in.chunk_off[2 * (c + 1)] : nbits;
-        if (bit1 < bit0 || bit1 > nbits) { bad = true; continue; }
-        // 2-bit code words of the chunk's entries
+        ChunkJob J;
+        J.b = (uint32_t)in.b;
+        J.nc = (int32_t)a.nc;
+        J.j0 = (int32_t)(w.sent[a.s] + a.q0);
+        J.prev = (int32_t)reached - 1;
+        J.size = (int32_t)size;
+        J.base = (int32_t)w.sbase[a.s];
+        J.t = 0;
+        J.tend = INT32_MAX;
+        if (FMT != SGC_MSG_GOLOMB_F32) {
+            J.t = (int32_t)(in.scope == SGC_PER_SEGMENT ? a.s : find_bucket(w.estart, (int64_t)nseg + 1, (int64_t)J.j0));
+            J.tend = in.scope == SGC_PER_SEGMENT ? INT32_MAX : (int32_t)w.estart[J.t + 1];
+        }
         const uint32_t* code_col = nullptr;
-        if (in.format == SGC_MSG_GOLOMB_2BIT) {
-            const int64_t j0 = w.sent[a.s] + a.q0;
-            const int64_t cw0 = j0 >> 4, cw1 = (j0 + a.nc - 1) >> 4;
-#pragma unroll 4
-            for (int64_t i = 0; i <= cw1 - cw0; ++i) ccol[i * kDecLanes + lane] = in.codes[cw0 + i];
+        if (FMT == SGC_MSG_GOLOMB_2BIT) {  // the chunk's 2-bit code words
+            const int32_t cw0 = J.j0 >> 4, ncw = ((J.j0 + J.nc - 1) >> 4) - cw0 + 1;
+            for (int32_t i = 0; i < ncw; ++i) ccol[i * kDecLanes + lane] = in.codes[cw0 + i];
             code_col = ccol + lane;
         }
-        // words [bit0/32, bit1/32 + 2): the chunk's bits plus a two-word window slack
+        // words [bit0/32, bit1/32 + 1]: every window read before bit1 lies inside
         const uint64_t wlo = bit0 >> 5;
-        const uint64_t whi = min((bit1 >> 5) + 2, nw);
-        const uint64_t nwc = whi > wlo ? whi - wlo : 0;
+        const uint64_t need = (bit1 >> 5) + 2 - wlo;
+        uint32_t rel_end;
+        int32_t prev_end;
         bool ok;
-        if (nwc <= (uint64_t)kColWords) {
+        J.relend = (uint32_t)(bit1 - (wlo << 5));
+        if (need <= (uint64_t)kColWords) {
+            const uint64_t have = wlo < nw ? min(need, nw - wlo) : 0;
 #pragma unroll 8
-            for (uint64_t i = 0; i < nwc; ++i) col[i * kDecLanes + lane] = words[wlo + i];
-            WordReader<LdsWords> rd;
-            rd.start(LdsWords{col + lane, wlo, nwc}, nbits, bit0);
-            ok = decode_chunk(rd, in, w, a, c, nseg, reached, code_col);
+            for (uint64_t i = 0; i < have; ++i) col[i * kDecLanes + lane] = words[wlo + i];
+            for (uint64_t i = have; i < need; ++i) col[i * kDecLanes + lane] = 0u;
+            ok = decode_chunk<FMT>(LdsBits{col + lane}, (uint32_t)(bit0 & 31), J, in, w, code_col, &rel_end, &prev_end);
         } else {
-            WordReader<GlobalWords> rd;
-            rd.start(GlobalWords{words, nw}, nbits, bit0);
-            ok = decode_chunk(rd, in, w, a, c, nseg, reached, code_col);
+            ok = decode_chunk<FMT>(GlobalBits{words, nw, wlo << 5}, (uint32_t)(bit0 & 31), J, in, w, code_col,
+                                   &rel_end, &prev_end);
         }
-        if (!ok) bad = true;
+        if (!ok) {
+            bad = true;
+            continue;
+        }
+        if (!last) {
+            // the next chunk must start exactly where this one ended
+            if (rel_end != J.relend || in.chunk_off[2 * (c + 1) + 1] != (uint64_t)(prev_end + 1)) bad = true;
+        } else if (rel_end != J.relend) {
+            bad = true;  // bits left over
+        }
     }
     if (bad) atomicOr(w.bad, 1u);
 }
 
-// Tiles that start inside a stream without entries: the first entry at or
-// beyond them is the next stream's first entry.
-__global__ __launch_bounds__(kBlock) void k_msg_gaps(Batch B, int64_t n, int64_t ntiles)
+__global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg)
 {
+    __shared__ uint32_t col[kColWords * kDecLanes];
+    __shared__ uint32_t ccol[kColCodes * kDecLanes];
     const int m = blockIdx.y;
     const MsgIn& in = B.in[m];
     const MsgWs& w = B.ws[m];
-    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < ntiles; t += (int64_t)gridDim.x * kBlock) {
-        const int64_t p = t * kOutTile;
-        int64_t s = 0;
-        if (in.S > 1) {
-            // stream containing element p (streams are the segments, in order)
-            int64_t lo = 0, hi = in.S - 1;
-            while (lo < hi) {
-                const int64_t mid = (lo + hi + 1) >> 1;
-                if (w.sbase[mid] <= p) lo = mid; else hi = mid - 1;
-            }
-            s = lo;
-            while (s + 1 < in.S && w.ssize[s] == 0 && w.sbase[s + 1] <= p) ++s;
-        }
-        if (w.scnt[s] == 0) w.tstart[t] = (int32_t)w.sent[s];
+    if (w.bad[0]) return;
+    switch (in.format) {
+    case SGC_MSG_GOLOMB_F32: decode_lanes<SGC_MSG_GOLOMB_F32>(in, w, nseg, col, ccol); break;
+    case SGC_MSG_GOLOMB_SBC: decode_lanes<SGC_MSG_GOLOMB_SBC>(in, w, nseg, col, ccol); break;
+    case SGC_MSG_GOLOMB_2BIT: decode_lanes<SGC_MSG_GOLOMB_2BIT>(in, w, nseg, col, ccol); break;
+    default: break;
     }
 }
 
 // ------------------------------------------------------------------ merge
-// One workgroup per output tile of kOutTile elements.  Round 1 (parallel):
-// the tile's initial contents (coalesced, into LDS) and every message's
-// entry range [tstart[t], tstart[t+1]).  Then the entries of all messages
-// are staged in LDS (kStage at a time, in message order) and thread t
-// applies, for each message in order, the entries that fall on the 16
-// contiguous tile elements it owns (binary search in the staged, ascending
-// positions).  No element is touched by two threads, so there are no
-// atomics and no per-message barriers; the tile is stored once, coalesced.
-constexpr int kStage = 1024;
-constexpr int kOwn = (int)(kOutTile / kBlock);  // 16 elements per thread
+// Persistent workgroups, each over a contiguous range of output tiles
+// (kOutTile elements each); a group of threads per message (a power of two)
+// follows that message's entries, which stay in the registers of the thread
+// that loaded them.  Per tile:
+//  1  the tile's initial contents go to LDS; every entry marks its message
+//     in the 16-bit message mask of its tile position (LDS atomic or: the
+//     mask does not depend on the order);
+//  2  each entry reads its position's mask: its rank there is the number of
+//     lower messages present.  Rank-0 entries add their value in place (no
+//     other thread touches that element in this step);
+//  3  where messages meet, rank 1, 2, ... follow, one step each, with a
+//     barrier between steps (usually none is needed);
+// and the tile is stored once (coalesced).  Every element receives its
+// values in message order, so the result does not depend on scheduling.
+//
+// Software pipeline: while tile u is worked on, the entries and initial
+// contents of tile u+1 (and the entry-range bound of tile u+2) are already in
+// flight in registers.  In each iteration the stores of the previous tile are
+// issued before the next loads: loads and stores share one completion
+// counter here, so a wait for loads also waits for earlier stores, and
+// those are then long done.  A tile whose entries do not fit the prefetch (a
+// message with more than kPre * group-size entries in it, or more than
+// kPre * kBlock in all) is applied from memory instead, in rounds of
+// kPre * kBlock entries taken in message order.
+constexpr int kPre = 4;                              // entries per thread per tile (or round)
+constexpr int kRound = kPre * kBlock;                // entries per round
+constexpr int kQ = (int)(kOutTile / (4 * kBlock));  // 16-byte words per thread in a tile
+static_assert(kMerge <= 16, "message masks are 16 bits");
 
-__global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t init, const float* __restrict__ base,
-                                                 float* __restrict__ out, int64_t n)
+struct MergeLds {
+    float tile[kOutTile];
+    uint32_t mask[kOutTile / 2];  // 16-bit message mask per position, two per word
+    int32_t a[2][kMerge], cnt[2][kMerge];
+    int32_t total[3], fits[3], maxc[3];  // per tile, by tile index mod 3
+};
+
+// Tile bookkeeping for the tile with slot z: entry total, whether the
+// prefetch holds all entries, and the collision depth reset to 1.
+__device__ inline void tile_meta(MergeLds& S, int par, int z, int32_t nmsg, int32_t cap_per_msg)
 {
-    __shared__ float tile[kOutTile];
-    __shared__ int32_t s_a[kMerge], s_off[kMerge + 1];
-    __shared__ uint16_t st_pos[kStage];
-    __shared__ float st_val[kStage];
-    const int64_t t = blockIdx.x;
-    const int64_t lo = t * kOutTile;
-    const int64_t cnt = min((int64_t)kOutTile, n - lo);
-    const bool full = cnt == kOutTile;
-    constexpr int kQ = (int)(kOutTile / (4 * kBlock));
-    if (threadIdx.x < 64) {  // wave 0: message ranges and their prefix
-        const int k = threadIdx.x;
-        int32_t a = 0, c = 0;
-        if (k < M.n && !*M.bad[k]) {
-            a = M.tstart[k][t];
-            c = M.tstart[k][t + 1] - a;
-        }
-        int32_t x = c;
-        for (int d = 1; d < 64; d <<= 1) {
-            const int32_t y = __shfl_up(x, d, 64);
-            if (k >= d) x += y;
-        }
-        if (k < kMerge) {
-            s_a[k] = a;
-            s_off[k] = x - c;
-        }
-        if (k == kMerge - 1) s_off[kMerge] = x;
+    int32_t total = 0, fits = 1;
+    for (int k = 0; k < nmsg; ++k) {
+        total += S.cnt[par][k];
+        fits &= S.cnt[par][k] <= cap_per_msg;
     }
-    {
-        const float* src = init == SGC_INIT_BASE ? base : out;
+    S.total[z] = total;
+    S.fits[z] = fits && total <= kRound;
+    S.maxc[z] = 1;
+}
+
+// Apply up to kPre entries per thread: message k[i], tile position p[i]
+// (negative: no entry), value v[i].  Starts and ends with a barrier; leaves
+// the mask cleared.
+__device__ inline void apply_entries(MergeLds& S, int z, const int32_t (&k)[kPre], const int32_t (&p)[kPre],
+                                     const float (&v)[kPre])
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+        if (p[i] >= 0) atomicOr(&S.mask[p[i] >> 1], (1u << k[i]) << (16 * (p[i] & 1)));
+    __syncthreads();
+    int32_t rk[kPre];
+    int32_t deep = 1;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+        rk[i] = -1;
+        if (p[i] < 0) continue;
+        const uint32_t m = (S.mask[p[i] >> 1] >> (16 * (p[i] & 1))) & 0xffffu;
+        rk[i] = __builtin_popcount(m & ((1u << k[i]) - 1u));
+        deep = max(deep, __builtin_popcount(m));
+        if (rk[i] == 0) S.tile[p[i]] = S.tile[p[i]] + v[i];
+    }
+    if (deep > 1) atomicMax(&S.maxc[z], deep);
+    __syncthreads();
+    // every mask read is done: clear this thread's share for the next use
+    *(i4v*)&S.mask[8 * tid] = i4v{0, 0, 0, 0};
+    *(i4v*)&S.mask[8 * tid + 4] = i4v{0, 0, 0, 0};
+    const int32_t depth = S.maxc[z];  // uniform
+    for (int32_t r = 1; r < depth; ++r) {
+#pragma unroll
+        for (int i = 0; i < kPre; ++i)
+            if (rk[i] == r) S.tile[p[i]] = S.tile[p[i]] + v[i];
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, int32_t init,
+                                                 const float* __restrict__ base, float* __restrict__ out, int64_t n,
+                                                 int64_t ntiles, int64_t per)
+{
+    __shared__ __align__(16) MergeLds S;
+    const int tid = threadIdx.x;
+    const int tpm = 1 << lg_tpm;  // threads per message slot
+    const int mk = tid >> lg_tpm, ml = tid & (tpm - 1);
+    const bool live = mk < M.n && !*M.bad[mk];
+    const int32_t* posk = live ? M.pos[mk] : nullptr;
+    const float* valk = live ? M.val[mk] : nullptr;
+    const int32_t* tsk = live ? M.tstart[mk] : nullptr;
+    const float* src = init == SGC_INIT_BASE ? base : out;
+    const int64_t T0 = (int64_t)blockIdx.x * per, T1 = min(T0 + per, ntiles);
+    if (T0 >= T1) return;
+    static_assert(sizeof(S.mask) == 32 * kBlock, "mask clear: two 16-byte words per thread");
+
+    // pipeline registers: the next tile's entries (global positions) and initial contents
+    int32_t n_pos[kPre];
+    float n_val[kPre];
+    f4a ini[kQ];
+    auto ts = [&](int64_t t) -> int32_t { return (live && t <= ntiles) ? tsk[t] : 0; };
+    auto load_tile = [&](int64_t t, int32_t a, int32_t c) {
+        const int64_t lo = t * kOutTile;
+        const int32_t cnt = (int32_t)min((int64_t)kOutTile, n - lo);
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+            const int32_t r = ml + i * tpm;
+            n_pos[i] = -1;
+            n_val[i] = 0.0f;
+            if (r < c) {
+                n_pos[i] = posk[a + r];
+                n_val[i] = valk[a + r];
+            }
+        }
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            const int i = 4 * (q * kBlock + threadIdx.x);
+            const int i = 4 * (q * kBlock + tid);
             f4a v = {0.0f, 0.0f, 0.0f, 0.0f};
             if (init != SGC_INIT_ZERO) {
-                if (full) {
+                if (cnt == kOutTile) {
                     v = *(const f4a*)(src + lo + i);
                 } else {
 #pragma unroll
@@ -521,46 +611,97 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t init, co
                         if (i + j < cnt) v[j] = src[lo + i + j];
                 }
             }
-            *(f4a*)(tile + i) = v;
+            ini[q] = v;
         }
+    };
+
+    // prologue: ranges of tiles T0 and T0+1, the entries of T0 in flight
+    int32_t a_cur = ts(T0), a_nxt = ts(T0 + 1), a_nn = ts(T0 + 2);
+    if (ml == 0 && mk < kMerge) {
+        S.a[T0 & 1][mk] = a_cur;
+        S.cnt[T0 & 1][mk] = a_nxt - a_cur;
     }
+    *(i4v*)&S.mask[8 * tid] = i4v{0, 0, 0, 0};
+    *(i4v*)&S.mask[8 * tid + 4] = i4v{0, 0, 0, 0};
+    load_tile(T0, a_cur, a_nxt - a_cur);
     __syncthreads();
-    const int own0 = threadIdx.x * kOwn;
-    const int32_t total = s_off[kMerge];
-    for (int32_t R0 = 0; R0 < total; R0 += kStage) {  // uniform; one round in the common case
-        const int32_t R1 = min(R0 + kStage, total);
-        for (int32_t e = R0 + threadIdx.x; e < R1; e += kBlock) {
-            int k = 0;
-            while (e >= s_off[k + 1]) ++k;
-            const int32_t j = s_a[k] + (e - s_off[k]);
-            const int64_t p = (int64_t)M.pos[k][j] - lo;
-            st_pos[e - R0] = (uint16_t)((uint64_t)p < (uint64_t)cnt ? p : 0xffff);
-            st_val[e - R0] = M.val[k][j];
+    if (tid == 0) tile_meta(S, (int)(T0 & 1), (int)(T0 % 3), M.n, kPre * tpm);
+
+    for (int64_t u = T0; u < T1; ++u) {
+        const int b = (int)(u & 1), z = (int)(u % 3);
+        const int64_t lo = u * kOutTile;
+        const int32_t cnt = (int32_t)min((int64_t)kOutTile, n - lo);
+        // the previous tile (always whole) leaves LDS for memory; tile u's initial contents enter
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            const int i = 4 * (q * kBlock + tid);
+            const f4a pt = *(const f4a*)(S.tile + i);
+            *(f4a*)(S.tile + i) = ini[q];
+            if (u > T0) *(f4a*)(out + lo - kOutTile + i) = pt;
+        }
+        // this tile's entries, out of the pipeline registers
+        int32_t ck[kPre], cp[kPre];
+        float cv[kPre];
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+            ck[i] = mk;
+            const int32_t q = n_pos[i] - (int32_t)lo;
+            cp[i] = (n_pos[i] >= 0 && (uint32_t)q < (uint32_t)cnt) ? q : -1;  // always inside, for a clean message
+            cv[i] = n_val[i];
+        }
+        // the next tile in flight: its range bound, entries and initial contents
+        const int32_t a_n3 = ts(u + 3);
+        if (u + 1 < T1) {
+            if (ml == 0 && mk < kMerge) {
+                S.a[b ^ 1][mk] = a_nxt;
+                S.cnt[b ^ 1][mk] = a_nn - a_nxt;
+            }
+            load_tile(u + 1, a_nxt, a_nn - a_nxt);
         }
         __syncthreads();
-        for (int k = 0; k < M.n; ++k) {
-            const int32_t e0 = max(s_off[k], R0) - R0, e1 = min(s_off[k + 1], R1) - R0;
-            if (e0 >= e1) continue;
-            // first staged entry of message k at or after own0 (positions ascend)
-            int32_t l = e0, h = e1;
-            while (l < h) {
-                const int32_t m = (l + h) >> 1;
-                if ((int32_t)st_pos[m] < own0) l = m + 1; else h = m;
-            }
-            for (int32_t e = l; e < e1; ++e) {
-                const int32_t p = st_pos[e];
-                if (p >= own0 + kOwn) break;  // also stops at the 0xffff sentinel
-                tile[p] = tile[p] + st_val[e];
+        const int32_t total = S.total[z], fits = S.fits[z];  // uniform; written before the barrier above
+        if (tid == 0 && u + 1 < T1) tile_meta(S, b ^ 1, (int)((u + 1) % 3), M.n, kPre * tpm);
+        if (total == 0) {
+            // nothing to add
+        } else if (fits) {
+            apply_entries(S, z, ck, cp, cv);
+        } else {
+            // from memory, kRound entries at a time in message order
+            for (int32_t R0 = 0; R0 < total; R0 += kRound) {
+#pragma unroll
+                for (int i = 0; i < kPre; ++i) {
+                    const int32_t e = R0 + tid + i * kBlock;
+                    cp[i] = -1;
+                    ck[i] = 0;
+                    cv[i] = 0.0f;
+                    if (e >= total) continue;
+                    int32_t k = 0, off = 0;
+                    while (e >= off + S.cnt[b][k]) off += S.cnt[b][k++];
+                    const int32_t j = S.a[b][k] + (e - off);
+                    const int32_t q = M.pos[k][j] - (int32_t)lo;
+                    ck[i] = k;
+                    cp[i] = (uint32_t)q < (uint32_t)cnt ? q : -1;
+                    cv[i] = M.val[k][j];
+                }
+                apply_entries(S, z, ck, cp, cv);
+                __syncthreads();  // mask cleared, depth read: the next round may start
+                if (tid == 0) S.maxc[z] = 1;
             }
         }
-        __syncthreads();  // staging is refilled by the next round; the tile is read below
+        __syncthreads();
+        a_cur = a_nxt;
+        a_nxt = a_nn;
+        a_nn = a_n3;
     }
+    // the last tile
+    const int64_t lo = (T1 - 1) * kOutTile;
+    const int32_t cnt = (int32_t)min((int64_t)kOutTile, n - lo);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-        const int i = 4 * (q * kBlock + threadIdx.x);
-        const f4a r = *(const f4a*)(tile + i);
-        if (full) {
-            __builtin_nontemporal_store(r, (f4a*)(out + lo + i));
+        const int i = 4 * (q * kBlock + tid);
+        const f4a r = *(const f4a*)(S.tile + i);
+        if (cnt == kOutTile) {
+            *(f4a*)(out + lo + i) = r;
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -581,6 +722,16 @@ __global__ void k_fold_status(MergeBatch M, uint32_t* status)
 }  // namespace sgc
 
 using namespace sgc;
+
+// Persistent merge workgroups: as many as are resident at once on the device.
+static int64_t merge_blocks()
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_merge, kBlock, 0) != hipSuccess || cus <= 0 || per_cu <= 0)
+        return 1024;
+    return (int64_t)cus * per_cu;
+}
 
 static bool msg_ok(const sgc_layout* L, const sgc_message& m)
 {
@@ -667,17 +818,16 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
             maxcap = std::max(maxcap, m.cap);
             maxch = std::max(maxch, msg_nch(L, m));
         }
-        const dim3 one(1, (unsigned)B.n);
-        k_msg_setup<<<one, 64, 0, s>>>(B, dt->seg_off, L->nseg, ntiles);
-        SGC_LAUNCH_CHECK();
         const dim3 gtile((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(ntiles, kBlock), 2048)), (unsigned)B.n);
-        k_msg_gaps<<<gtile, kBlock, 0, s>>>(B, L->n, ntiles);
-        SGC_LAUNCH_CHECK();
-        const dim3 graw((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxcap, kBlock), 4096)), (unsigned)B.n);
-        k_msg_raw<<<graw, kBlock, 0, s>>>(B, L->nseg, L->n, ntiles);
+        k_msg_setup<<<gtile, kBlock, 0, s>>>(B, dt->seg_off, L->nseg, ntiles);
         SGC_LAUNCH_CHECK();
         const dim3 gch((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxch, kDecLanes), 16384)), (unsigned)B.n);
-        k_msg_decode<<<gch, kDecLanes, 0, s>>>(B, L->nseg, L->n);
+        k_msg_decode<<<gch, kDecLanes, 0, s>>>(B, L->nseg);
+        SGC_LAUNCH_CHECK();
+        const dim3 gent((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxcap, kBlock), 4096)), (unsigned)B.n);
+        k_msg_entries<<<gent, kBlock, 0, s>>>(B, L->nseg, L->n, ntiles);
+        SGC_LAUNCH_CHECK();
+        k_msg_holes<<<gtile, kBlock, 0, s>>>(B, ntiles);
         SGC_LAUNCH_CHECK();
     }
     // merge in fixed message order; later batches continue in place
@@ -694,7 +844,12 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
             M.tstart[k] = w.tstart;
             M.bad[k] = w.bad;
         }
-        k_merge<<<(unsigned)ntiles, kBlock, 0, s>>>(M, mb == 0 ? init : SGC_INIT_INPLACE, base, out, L->n);
+        int32_t lg_tpm = 8;  // threads per message slot: 256 / (message count rounded up to a power of two)
+        while (lg_tpm > 0 && (kBlock >> lg_tpm) < M.n) --lg_tpm;
+        const int64_t per = cdiv(ntiles, std::min<int64_t>(ntiles, merge_blocks()));
+        const int64_t grid = cdiv(ntiles, per);
+        k_merge<<<(unsigned)grid, kBlock, 0, s>>>(M, lg_tpm, mb == 0 ? init : SGC_INIT_INPLACE, base, out, L->n,
+                                                  ntiles, per);
         SGC_LAUNCH_CHECK();
         if (dstatus && M.n > 0) {
             k_fold_status<<<1, 64, 0, s>>>(M, dstatus);
