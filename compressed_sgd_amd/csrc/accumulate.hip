@@ -508,52 +508,60 @@ static_assert(kMerge <= 16, "message masks are 16 bits");
 
 struct MergeLds {
     float tile[kOutTile];
-    uint32_t mask[kOutTile / 2];  // 16-bit message mask per position, two per word
+    uint32_t mask[2][kOutTile / 2];  // per tile parity: 16-bit message mask per position, two per word
     int32_t a[2][kMerge], cnt[2][kMerge];
     int32_t total[3], fits[3], maxc[3];  // per tile, by tile index mod 3
 };
 
-// Tile bookkeeping for the tile with slot z: entry total, whether the
-// prefetch holds all entries, and the collision depth reset to 1.
+// Wave 0: bookkeeping of the tile with range parity par and slot z: entry
+// total, whether the prefetch holds all its entries, collision depth 1.
 __device__ inline void tile_meta(MergeLds& S, int par, int z, int32_t nmsg, int32_t cap_per_msg)
 {
-    int32_t total = 0, fits = 1;
-    for (int k = 0; k < nmsg; ++k) {
-        total += S.cnt[par][k];
-        fits &= S.cnt[par][k] <= cap_per_msg;
+    const int lane = threadIdx.x;
+    const int32_t c = lane < nmsg ? S.cnt[par][lane] : 0;
+    int32_t total = c;
+    for (int d = 32; d >= 1; d >>= 1) total += __shfl_xor(total, d, 64);
+    const bool over = __any(c > cap_per_msg);
+    if (lane == 0) {
+        S.total[z] = total;
+        S.fits[z] = !over && total <= kRound;
+        S.maxc[z] = 1;
     }
-    S.total[z] = total;
-    S.fits[z] = fits && total <= kRound;
-    S.maxc[z] = 1;
 }
 
-// Apply up to kPre entries per thread: message k[i], tile position p[i]
-// (negative: no entry), value v[i].  Starts and ends with a barrier; leaves
-// the mask cleared.
-__device__ inline void apply_entries(MergeLds& S, int z, const int32_t (&k)[kPre], const int32_t (&p)[kPre],
-                                     const float (&v)[kPre])
+__device__ inline void clear_mask(uint32_t* mask)
 {
-    const int tid = threadIdx.x;
+    *(i4v*)&mask[8 * threadIdx.x] = i4v{0, 0, 0, 0};
+    *(i4v*)&mask[8 * threadIdx.x + 4] = i4v{0, 0, 0, 0};
+}
+
+// Step 1: every entry (message k[i], tile position p[i] >= 0) marks its message.
+__device__ inline void mark_entries(uint32_t* mask, const int32_t (&k)[kPre], const int32_t (&p)[kPre])
+{
 #pragma unroll
     for (int i = 0; i < kPre; ++i)
-        if (p[i] >= 0) atomicOr(&S.mask[p[i] >> 1], (1u << k[i]) << (16 * (p[i] & 1)));
-    __syncthreads();
+        if (p[i] >= 0) atomicOr(&mask[p[i] >> 1], (1u << k[i]) << (16 * (p[i] & 1)));
+}
+
+// Steps 2 and 3, after a barrier that follows the marks.  Ends with a
+// barrier after the last addition; the mask is cleared afterwards.
+__device__ inline void add_entries(MergeLds& S, uint32_t* mask, int z, const int32_t (&k)[kPre],
+                                   const int32_t (&p)[kPre], const float (&v)[kPre])
+{
     int32_t rk[kPre];
     int32_t deep = 1;
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
         rk[i] = -1;
         if (p[i] < 0) continue;
-        const uint32_t m = (S.mask[p[i] >> 1] >> (16 * (p[i] & 1))) & 0xffffu;
+        const uint32_t m = (mask[p[i] >> 1] >> (16 * (p[i] & 1))) & 0xffffu;
         rk[i] = __builtin_popcount(m & ((1u << k[i]) - 1u));
         deep = max(deep, __builtin_popcount(m));
         if (rk[i] == 0) S.tile[p[i]] = S.tile[p[i]] + v[i];
     }
     if (deep > 1) atomicMax(&S.maxc[z], deep);
     __syncthreads();
-    // every mask read is done: clear this thread's share for the next use
-    *(i4v*)&S.mask[8 * tid] = i4v{0, 0, 0, 0};
-    *(i4v*)&S.mask[8 * tid + 4] = i4v{0, 0, 0, 0};
+    clear_mask(mask);  // every read of the mask is done
     const int32_t depth = S.maxc[z];  // uniform
     for (int32_t r = 1; r < depth; ++r) {
 #pragma unroll
@@ -578,7 +586,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
     const float* src = init == SGC_INIT_BASE ? base : out;
     const int64_t T0 = (int64_t)blockIdx.x * per, T1 = min(T0 + per, ntiles);
     if (T0 >= T1) return;
-    static_assert(sizeof(S.mask) == 32 * kBlock, "mask clear: two 16-byte words per thread");
+    static_assert(sizeof(S.mask[0]) == 32 * kBlock, "mask clear: two 16-byte words per thread");
 
     // pipeline registers: the next tile's entries (global positions) and initial contents
     int32_t n_pos[kPre];
@@ -621,11 +629,11 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
         S.a[T0 & 1][mk] = a_cur;
         S.cnt[T0 & 1][mk] = a_nxt - a_cur;
     }
-    *(i4v*)&S.mask[8 * tid] = i4v{0, 0, 0, 0};
-    *(i4v*)&S.mask[8 * tid + 4] = i4v{0, 0, 0, 0};
+    clear_mask(S.mask[0]);
+    clear_mask(S.mask[1]);
     load_tile(T0, a_cur, a_nxt - a_cur);
     __syncthreads();
-    if (tid == 0) tile_meta(S, (int)(T0 & 1), (int)(T0 % 3), M.n, kPre * tpm);
+    if (tid < 64) tile_meta(S, (int)(T0 & 1), (int)(T0 % 3), M.n, kPre * tpm);
 
     for (int64_t u = T0; u < T1; ++u) {
         const int b = (int)(u & 1), z = (int)(u % 3);
@@ -639,7 +647,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
             *(f4a*)(S.tile + i) = ini[q];
             if (u > T0) *(f4a*)(out + lo - kOutTile + i) = pt;
         }
-        // this tile's entries, out of the pipeline registers
+        // this tile's entries, out of the pipeline registers, mark their messages
         int32_t ck[kPre], cp[kPre];
         float cv[kPre];
 #pragma unroll
@@ -649,6 +657,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
             cp[i] = (n_pos[i] >= 0 && (uint32_t)q < (uint32_t)cnt) ? q : -1;  // always inside, for a clean message
             cv[i] = n_val[i];
         }
+        mark_entries(S.mask[b], ck, cp);
         // the next tile in flight: its range bound, entries and initial contents
         const int32_t a_n3 = ts(u + 3);
         if (u + 1 < T1) {
@@ -659,14 +668,16 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
             load_tile(u + 1, a_nxt, a_nn - a_nxt);
         }
         __syncthreads();
-        const int32_t total = S.total[z], fits = S.fits[z];  // uniform; written before the barrier above
-        if (tid == 0 && u + 1 < T1) tile_meta(S, b ^ 1, (int)((u + 1) % 3), M.n, kPre * tpm);
+        const int32_t total = S.total[z], fits = S.fits[z];  // uniform
+        if (tid < 64 && u + 1 < T1) tile_meta(S, b ^ 1, (int)((u + 1) % 3), M.n, kPre * tpm);
         if (total == 0) {
-            // nothing to add
+            // nothing to add (and nothing was marked)
         } else if (fits) {
-            apply_entries(S, z, ck, cp, cv);
+            add_entries(S, S.mask[b], z, ck, cp, cv);
         } else {
             // from memory, kRound entries at a time in message order
+            clear_mask(S.mask[b]);  // drop the marks of the prefetched share
+            __syncthreads();
             for (int32_t R0 = 0; R0 < total; R0 += kRound) {
 #pragma unroll
                 for (int i = 0; i < kPre; ++i) {
@@ -683,16 +694,18 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
                     cp[i] = (uint32_t)q < (uint32_t)cnt ? q : -1;
                     cv[i] = M.val[k][j];
                 }
-                apply_entries(S, z, ck, cp, cv);
+                mark_entries(S.mask[b], ck, cp);
+                __syncthreads();
+                add_entries(S, S.mask[b], z, ck, cp, cv);
                 __syncthreads();  // mask cleared, depth read: the next round may start
                 if (tid == 0) S.maxc[z] = 1;
             }
         }
-        __syncthreads();
         a_cur = a_nxt;
         a_nxt = a_nn;
         a_nn = a_n3;
     }
+    __syncthreads();
     // the last tile
     const int64_t lo = (T1 - 1) * kOutTile;
     const int32_t cnt = (int32_t)min((int64_t)kOutTile, n - lo);
