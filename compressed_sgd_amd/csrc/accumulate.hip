@@ -106,12 +106,18 @@ static void carve_msg(Carver& c, const sgc_layout* L, const sgc_message& m, MsgW
 }
 
 // ------------------------------------------------------------------ setup
-__global__ void k_msg_setup(Batch B, const int64_t* __restrict__ seg_off, int32_t nseg, int64_t ntiles)
+// Every thread marks output tiles as not yet known (-1: k_msg_holes fills
+// what the entry pass leaves); thread 0 of block 0 checks the message's
+// tables.
+__global__ __launch_bounds__(kBlock) void k_msg_setup(Batch B, const int64_t* __restrict__ seg_off, int32_t nseg,
+                                                     int64_t ntiles)
 {
-    if (threadIdx.x) return;
     const int m = blockIdx.y;
     const MsgIn& in = B.in[m];
     const MsgWs& w = B.ws[m];
+    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < ntiles; t += (int64_t)gridDim.x * kBlock)
+        w.tstart[t] = -1;
+    if (blockIdx.x || threadIdx.x) return;
     const int64_t n = seg_off[nseg];
     uint32_t bad = 0;
     int64_t e = 0;
@@ -592,7 +598,11 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
     int32_t n_pos[kPre];
     float n_val[kPre];
     f4a ini[kQ];
-    auto ts = [&](int64_t t) -> int32_t { return (live && t <= ntiles) ? tsk[t] : 0; };
+    // entry-range bounds, clamped to the message's entries (memory safety
+    // does not depend on the tile table being right)
+    const int32_t tot = live ? tsk[ntiles] : 0;
+    auto ts = [&](int64_t t) -> int32_t { return (live && t <= ntiles) ? min(max(tsk[t], 0), tot) : 0; };
+    auto span = [](int32_t a, int32_t e) -> int32_t { return max(e - a, 0); };
     auto load_tile = [&](int64_t t, int32_t a, int32_t c) {
         const int64_t lo = t * kOutTile;
         const int32_t cnt = (int32_t)min((int64_t)kOutTile, n - lo);
@@ -627,11 +637,11 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
     int32_t a_cur = ts(T0), a_nxt = ts(T0 + 1), a_nn = ts(T0 + 2);
     if (ml == 0 && mk < kMerge) {
         S.a[T0 & 1][mk] = a_cur;
-        S.cnt[T0 & 1][mk] = a_nxt - a_cur;
+        S.cnt[T0 & 1][mk] = span(a_cur, a_nxt);
     }
     clear_mask(S.mask[0]);
     clear_mask(S.mask[1]);
-    load_tile(T0, a_cur, a_nxt - a_cur);
+    load_tile(T0, a_cur, span(a_cur, a_nxt));
     __syncthreads();
     if (tid < 64) tile_meta(S, (int)(T0 & 1), (int)(T0 % 3), M.n, kPre * tpm);
 
@@ -663,9 +673,9 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
         if (u + 1 < T1) {
             if (ml == 0 && mk < kMerge) {
                 S.a[b ^ 1][mk] = a_nxt;
-                S.cnt[b ^ 1][mk] = a_nn - a_nxt;
+                S.cnt[b ^ 1][mk] = span(a_nxt, a_nn);
             }
-            load_tile(u + 1, a_nxt, a_nn - a_nxt);
+            load_tile(u + 1, a_nxt, span(a_nxt, a_nn));
         }
         __syncthreads();
         const int32_t total = S.total[z], fits = S.fits[z];  // uniform

@@ -6,6 +6,8 @@ scope, across ragged segment tables, ties, zeros, clustered inputs that
 overflow the per-tile candidate regions, and inputs that defeat the probe
 sample (the full-pass path).
 """
+import ctypes as C
+
 import numpy as np
 import pytest
 import torch
@@ -178,3 +180,37 @@ def test_empty_layout(orc):
     out = sgc.compress(layout, g, r, keep_ppm=10000)
     torch.cuda.synchronize()
     assert host(out.counts).tolist() == [0, 0, 0]
+
+
+@pytest.mark.parametrize("fill", [0x00, 0x7F, 0xFF])
+def test_stale_workspace(orc, fill):
+    # every workspace byte a call reads is written by that call first
+    rng = np.random.default_rng(17)
+    layout = sgc.Layout([300000, 4097, 1 << 20])
+    n = layout.n
+    seg_off = np.array(layout.seg_off, np.int64)
+    for scope in (0, 1):
+        g = rng.laplace(0, 1e-3, n).astype(np.float32)
+        r = np.zeros(n, np.float32)
+        opts = sgc.CompressOpts(sgc.EXACT, scope, 10000, 1000, 65536)
+        cap = layout.keep_total(scope, 10000)
+        nbytes = sgc.lib().sgc_compress_workspace(layout.handle, C.byref(opts), cap)
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        announce(f"compress stale workspace {fill:#x} scope={scope}")
+        rd = dev(r)
+        out = sgc.compress(layout, dev(g), rd, scope=scope, keep_ppm=10000, ws=ws)
+        ref = orc.compress_exact(g, r, seg_off, scope, 10000, cap=out.cap)
+        torch.cuda.synchronize()
+        total = int(ref.counts[-1])
+        assert_bitwise(host(out.counts), ref.counts, "counts")
+        assert_bitwise(host(out.idx)[:total], ref.idx, "idx")
+        assert_bitwise(host(rd), r, "residual")
+        b = 5
+        enb = sgc.lib().sgc_encode_workspace(layout.handle, scope, out.cap)
+        ews = torch.full((enb,), fill, dtype=torch.uint8, device="cuda")
+        enc = sgc.encode(layout, out.idx, out.counts, out.cap, scope=scope, b=b, ws=ews)
+        oenc = orc.encode(ref.idx, ref.counts, seg_off, scope, b)
+        torch.cuda.synchronize()
+        nw = int(oenc.word_off[-1])
+        assert_bitwise(host(enc.words).view(np.uint32)[:nw], oenc.words, "words")
+        assert_bitwise(host(enc.chunk_off).view(np.uint64)[:oenc.chunk_off.size], oenc.chunk_off, "chunk table")
