@@ -43,7 +43,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSrcSamples = 0, kSrcCand = 1, kSrcDense = 2;
 constexpr int kSuper = 4096;                     // tiles per scan super block
-constexpr int kGatherTiles = 16;                 // tiles per gather workgroup
+constexpr int kGatherTiles = 64;                 // tiles per gather workgroup (one wave lane each)
 constexpr uint32_t kAccFlag = 0x80000000u;       // candidate index flag: r still holds acc there
 constexpr int kRep = 8;                          // global histogram replicas per (virtual) group
 constexpr int kHistBlocks = 1024;                // workgroups of a histogram pass
@@ -379,34 +379,37 @@ __global__ void k_probe_done(int32_t G, int32_t mode, CompressWs w)
 }
 
 // ---------------------------------------------------------------- pass 1
-// Candidates of one tile in index order through `sink(pos, i, v)`.  ADD:
-// acc = r + g is formed and r is stored (acc, or +0 for key >= kz when the
-// region does not overflow); otherwise r already holds acc (redo of an
-// overflowed tile).  Returns the tile's candidate count to every thread.
-// Indices are 32-bit (n < 2^31); the tile base is uniform, so each access
-// is a scalar base plus one 32-bit lane offset.  A tile that lies entirely
-// inside its group skips every per-element range check.
-template <bool ADD, typename Sink>
+// Candidates of one tile in index order through `sink(pos, i, v)`, for a
+// workgroup of TB threads holding SL float4 slots each (TB * SL * 4 =
+// kTile).  ADD: acc = r + g is formed and r is stored (acc, or +0 for key >=
+// kz when the region does not overflow); otherwise r already holds acc
+// (redo of an overflowed tile).  Returns the tile's candidate count to every
+// thread.  Indices are 32-bit (n < 2^31); the tile base is uniform, so each
+// access is a scalar base plus one 32-bit lane offset.  A tile that lies
+// entirely inside its group skips every per-element range check.
+template <bool ADD, int TB, int SL, typename Sink>
 __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float* __restrict__ res, int32_t lo,
                                            int32_t hi, int32_t A, uint32_t klo, uint32_t kz, Sink sink)
 {
-    __shared__ uint32_t wtot[kSlots][kBlock / 64];
+    static_assert((int64_t)TB * SL * 4 == kTile, "a tile is TB threads x SL float4");
+    constexpr int NW = TB / 64;
+    __shared__ uint32_t wtot[SL][NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool full = A >= lo && A + (int32_t)kTile <= hi;  // uniform
     const f4* rb = (const f4*)(res + A);
     const f4* gb = (const f4*)(grad + A);
-    f4 acc[kSlots];
+    f4 acc[SL];
     if (full) {
 #pragma unroll
-        for (int u = 0; u < kSlots; ++u) {
-            const int o = u * kBlock + tid;
+        for (int u = 0; u < SL; ++u) {
+            const int o = u * TB + tid;
             if (ADD) acc[u] = __builtin_nontemporal_load(rb + o) + __builtin_nontemporal_load(gb + o);
             else acc[u] = rb[o];
         }
     } else {
 #pragma unroll
-        for (int u = 0; u < kSlots; ++u) {
-            const int32_t e = A + 4 * (u * kBlock + tid);
+        for (int u = 0; u < SL; ++u) {
+            const int32_t e = A + 4 * (u * TB + tid);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float a = 0.0f;
@@ -416,10 +419,10 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
         }
     }
     uint32_t flags = 0;  // 4 bits per slot
-    uint32_t pre[kSlots];
+    uint32_t pre[SL];
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
-        const int32_t e = A + 4 * (u * kBlock + tid);
+    for (int u = 0; u < SL; ++u) {
+        const int32_t e = A + 4 * (u * TB + tid);
         uint32_t f = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -436,10 +439,11 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
     // earlier slots, then of the earlier waves in slot u, then the wave prefix
     uint32_t run = 0;
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
+    for (int u = 0; u < SL; ++u) {
         const uint32_t slot_base = run;
         uint32_t before = 0;
-        for (int v = 0; v < kBlock / 64; ++v) {
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
             const uint32_t c = wtot[u][v];
             before += v < wave ? c : 0u;
             run += c;
@@ -452,17 +456,17 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
         f4* rw = (f4*)(res + A);
         if (full) {
 #pragma unroll
-            for (int u = 0; u < kSlots; ++u) {
+            for (int u = 0; u < SL; ++u) {
                 f4 st = acc[u];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (mag_key(st[j]) >= z) st[j] = 0.0f;
-                __builtin_nontemporal_store(st, rw + u * kBlock + tid);
+                __builtin_nontemporal_store(st, rw + u * TB + tid);
             }
         } else {
 #pragma unroll
-            for (int u = 0; u < kSlots; ++u) {
-                const int32_t e = A + 4 * (u * kBlock + tid);
+            for (int u = 0; u < SL; ++u) {
+                const int32_t e = A + 4 * (u * TB + tid);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (e + j >= lo && e + j < hi) res[e + j] = mag_key(acc[u][j]) >= z ? 0.0f : acc[u][j];
@@ -471,10 +475,10 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
     }
     if (flags) {
 #pragma unroll
-        for (int u = 0; u < kSlots; ++u) {
+        for (int u = 0; u < SL; ++u) {
             const uint32_t f = (flags >> (4 * u)) & 15u;
             if (!f) continue;
-            const int32_t e = A + 4 * (u * kBlock + tid);
+            const int32_t e = A + 4 * (u * TB + tid);
             uint32_t pos = pre[u];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -489,7 +493,7 @@ __device__ inline int64_t tile_group(const int64_t* gtile, int32_t G, int64_t t)
     return G == 1 ? 0 : find_bucket(gtile, (int64_t)G + 1, t);
 }
 
-__global__ __launch_bounds__(kBlock) void k_pass1(const float* __restrict__ grad, float* __restrict__ res,
+__global__ __launch_bounds__(kPassThreads) void k_pass1(const float* __restrict__ grad, float* __restrict__ res,
                                                  const int64_t* __restrict__ goff, const int64_t* __restrict__ gtile,
                                                  int32_t G, CompressWs w)
 {
@@ -499,7 +503,7 @@ __global__ __launch_bounds__(kBlock) void k_pass1(const float* __restrict__ grad
     const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
     int32_t* ridx = w.reg_idx + t * kTileCap;
     float* rval = w.reg_val + t * kTileCap;
-    const uint32_t cnt = tile_candidates<true>(grad, res, lo, hi, A, w.key_lo[g], w.key_z[g],
+    const uint32_t cnt = tile_candidates<true, kPassThreads, (int)(kTile / (4 * kPassThreads))>(grad, res, lo, hi, A, w.key_lo[g], w.key_z[g],
                                                [&](uint32_t pos, int32_t i, float v) {
                                                    if (pos < (uint32_t)kTileCap) {
                                                        ridx[pos] = i;
@@ -677,10 +681,10 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
                                                   int64_t cap, CompressWs w)
 {
     __shared__ int64_t s_dst[kGatherTiles];   // destination of the tile's first entry (-1: restore only)
-    __shared__ uint32_t s_cnt[kGatherTiles];  // entries copied from the region
-    __shared__ uint32_t s_pre[kGatherTiles + 1];
+    __shared__ uint32_t s_pre[kGatherTiles + 1];  // prefix of the entries copied from the regions
     __shared__ uint32_t s_z[kGatherTiles];    // zeroing bound of the tile's group
-    __shared__ uint32_t s_over;               // bit q: tile q overflowed
+    __shared__ uint64_t s_over;               // bit q: tile q overflowed
+    static_assert(kGatherTiles == 64, "one wave lane per tile");
     const bool sampled = mode == SGC_SAMPLED;
     const int64_t t0 = (int64_t)blockIdx.x * kGatherTiles;
     if (threadIdx.x < 64) {
@@ -689,7 +693,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
         int64_t dst = -1;
         uint32_t c = 0, z = kNoKey;
         bool over = false;
-        if (q < kGatherTiles && t < NT) {
+        if (t < NT) {
             const int64_t g = tile_group(gtile, G, t);
             c = w.tile_cnt[t];
             over = c > (uint32_t)kTileCap;
@@ -699,28 +703,24 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
                 dst = w.cstart[g] + tile_prefix(w, NT, t) - tile_prefix(w, NT, gtile[g]);
             if (over) c = 0;
         }
-        if (q < kGatherTiles) {
-            s_dst[q] = dst;
-            s_cnt[q] = c;
-            s_z[q] = z;
+        s_dst[q] = dst;
+        s_z[q] = z;
+        uint32_t x = c;  // inclusive scan over the wave
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t y = __shfl_up(x, d, 64);
+            if (q >= d) x += y;
         }
+        s_pre[q + 1] = x;
+        if (q == 0) s_pre[0] = 0;
         const uint64_t ob = __ballot(over);
-        if (q == 0) s_over = (uint32_t)ob;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t run = 0;
-        for (int q = 0; q < kGatherTiles; ++q) {
-            s_pre[q] = run;
-            run += s_cnt[q];
-        }
-        s_pre[kGatherTiles] = run;
+        if (q == 0) s_over = ob;
     }
     __syncthreads();
     const uint32_t E = s_pre[kGatherTiles];
     for (uint32_t e = threadIdx.x; e < E; e += kBlock) {
-        int q = 0;
-        while (e >= s_pre[q + 1]) ++q;
+        int q = 0;  // last tile whose entries start at or before e
+        for (int h = 32; h >= 1; h >>= 1)
+            if (e >= s_pre[q + h]) q += h;
         const uint32_t j = e - s_pre[q];
         const int64_t t = t0 + q;
         const int32_t i = w.reg_idx[t * kTileCap + j];
@@ -742,16 +742,17 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
         }
     }
     // overflowed tiles: redo from r (which pass 1 left as acc there)
-    const uint32_t over = s_over;
+    const uint64_t over = s_over;
     for (int q = 0; q < kGatherTiles; ++q) {
-        if (!(over & (1u << q))) continue;  // uniform per block
+        if (!(over & (1ull << q))) continue;  // uniform per block
         const int64_t t = t0 + q;
         const int64_t dst = s_dst[q];
         if (dst < 0) continue;
         const int64_t g = tile_group(gtile, G, t);
         const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
         const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
-        tile_candidates<false>(grad, res, lo, hi, A, w.key_lo[g], kNoKey, [&](uint32_t pos, int32_t i, float v) {
+        tile_candidates<false, kBlock, (int)(kTile / (4 * kBlock))>(grad, res, lo, hi, A, w.key_lo[g], kNoKey,
+                                                                  [&](uint32_t pos, int32_t i, float v) {
             const int64_t p = dst + pos;
             if (sampled) {
                 if (p < cap) {
@@ -1084,7 +1085,7 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
 
     // 2. pass 1
     if (g_pass_start && hipEventRecord(g_pass_start, s) != hipSuccess) return SGC_EHIP;
-    k_pass1<<<(unsigned)gr.ntiles, kBlock, 0, s>>>(grad, residual, gr.off, gr.tile, G, w);
+    k_pass1<<<(unsigned)gr.ntiles, kPassThreads, 0, s>>>(grad, residual, gr.off, gr.tile, G, w);
     SGC_LAUNCH_CHECK();
     if (g_pass_stop && hipEventRecord(g_pass_stop, s) != hipSuccess) return SGC_EHIP;
 

@@ -21,15 +21,17 @@
 namespace sgc {
 
 // ---------------------------------------------------------------- geometry
-// Pass-1 tile: 256 threads x 8 float4 slots.  Tiles never straddle a
-// selection group; inside a group they sit on a 4-element-aligned grid so
-// that every full slot is one aligned 16-byte access.
+// Pass-1 tile: 4096 elements, 256 threads x 4 float4 slots (measured on
+// gfx950: 4-slot tiles stream faster than 8- or 16-slot ones, and smaller
+// tiles lose more to their per-tile work than they gain).  Tiles never
+// straddle a selection group; inside a group they sit on a 4-element-aligned
+// grid so that every full slot is one aligned 16-byte access.
 constexpr int kBlock = 256;
-constexpr int kSlots = 8;
-constexpr int64_t kTile = (int64_t)kBlock * 4 * kSlots;  // 8192 elements
+constexpr int kPassThreads = 256;
+constexpr int64_t kTile = 4096;
 // Candidate slots per tile region; a tile with more candidates is redone
 // from the residual (which holds acc after pass 1).
-constexpr int kTileCap = 512;
+constexpr int kTileCap = 256;
 // Chunk of the selection / compaction kernels: 256 threads x 16 contiguous.
 constexpr int kPer = 16;
 constexpr int64_t kChunk = (int64_t)kBlock * kPer;  // 4096 entries
