@@ -173,9 +173,13 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const float* __restrict__
 // ----------------------------------------------------------------- setup
 // One thread walks the groups: keep counts, probe sizes, prefixes, and the
 // two ranks (lower / upper bound) each group's probe selection needs.
-__global__ void k_setup(const int64_t* __restrict__ goff, int32_t G, int32_t mode, uint32_t ppm, uint32_t div,
-                        uint32_t smin, CompressWs w)
+__global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ goff, int32_t G, int32_t mode,
+                                                 uint32_t ppm, uint32_t div, uint32_t smin, CompressWs w,
+                                                 int64_t hist_words)
 {
+    // every thread: clear the histograms (the resolve passes leave them clear)
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < hist_words; i += (int64_t)gridDim.x * kBlock)
+        w.hist[i] = 0;
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     int64_t sp = 0, kp = 0, cp = 0;
     for (int32_t g = 0; g < G; ++g) {
@@ -263,6 +267,62 @@ __global__ __launch_bounds__(kBlock) void k_probe(const float* __restrict__ grad
 // group is still open and whose key matches the digits chosen so far.  Each
 // workgroup takes a contiguous run of chunks and accumulates in LDS across
 // them, flushing once per group it touches into one of kRep global replicas.
+// Pick the digit holding the wanted rank (counted from the largest key) of
+// virtual group g: sum the replicas, scan from the top, clear the replicas for
+// the next digit.  Every thread of the block calls it (block scan inside).
+template <int D>
+__device__ inline void resolve_group(const CompressWs& w, int64_t g, int64_t* tmp)
+{
+    constexpr int nb = D == 0 ? 2048 : 1024;
+    constexpr int bits = D == 0 ? 11 : 10;
+    constexpr int per = nb / kBlock;
+    const int64_t target = w.mrem[g];
+    if (target == 0) return;  // uniform
+    uint32_t* gh = w.hist + g * kRep * kBins;
+    // thread t owns bins [nb - (t+1)*per, nb - t*per): thread 0 the largest keys
+    const int top = nb - threadIdx.x * per;
+    uint32_t cnt[per];
+    int64_t local = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < kRep; ++r) {
+            c += gh[r * kBins + top - 1 - i];
+            gh[r * kBins + top - 1 - i] = 0;
+        }
+        cnt[i] = c;
+        local += c;
+    }
+    int64_t total;
+    const int64_t above = block_exclusive_scan<int64_t>(local, tmp, &total);
+    if (above < target && above + local >= target) {
+        int64_t run = above;
+        for (int i = 0; i < per; ++i) {
+            const int bin = top - 1 - i;
+            if (run + cnt[i] >= target) {
+                w.prefix[g] = (w.prefix[g] << bits) | (uint32_t)bin;
+                w.mrem[g] = target - run;
+                break;
+            }
+            run += cnt[i];
+        }
+    }
+}
+
+// After the probe selection: the candidate and zeroing bounds of group g.
+__device__ inline void probe_bounds(const CompressWs& w, int32_t g, int32_t mode)
+{
+    if (w.rank[2 * g] > 0) w.key_lo[g] = w.prefix[2 * g];
+    if (mode == SGC_EXACT) {
+        if (w.rank[2 * g + 1] > 0) w.key_z[g] = w.prefix[2 * g + 1];
+    } else {
+        w.key_z[g] = w.key_lo[g];
+    }
+}
+
+// Histogram of digit D over every virtual group's selection source, chunks
+// split evenly over the workgroups.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ res, int32_t V, CompressWs w)
 {
@@ -321,61 +381,16 @@ __global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ r
     if (dirty) flush(cur);
 }
 
-// Pick the digit holding the wanted rank (counted from the largest key):
-// sum the replicas, scan from the top, clear the replicas for the next digit.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_srs_resolve(CompressWs w)
 {
-    constexpr int nb = D == 0 ? 2048 : 1024;
-    constexpr int bits = D == 0 ? 11 : 10;
-    constexpr int per = nb / kBlock;
     __shared__ int64_t tmp[kBlock / 64 + 1];
-    const int64_t g = blockIdx.x;
-    const int64_t target = w.mrem[g];
-    if (target == 0) return;  // uniform per block
-    uint32_t* gh = w.hist + g * kRep * kBins;
-    // thread t owns bins [nb - (t+1)*per, nb - t*per): thread 0 the largest keys
-    const int top = nb - threadIdx.x * per;
-    uint32_t cnt[per];
-    int64_t local = 0;
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int r = 0; r < kRep; ++r) {
-            c += gh[r * kBins + top - 1 - i];
-            gh[r * kBins + top - 1 - i] = 0;
-        }
-        cnt[i] = c;
-        local += c;
-    }
-    int64_t total;
-    const int64_t above = block_exclusive_scan<int64_t>(local, tmp, &total);
-    if (above < target && above + local >= target) {
-        int64_t run = above;
-        for (int i = 0; i < per; ++i) {
-            const int bin = top - 1 - i;
-            if (run + cnt[i] >= target) {
-                w.prefix[g] = (w.prefix[g] << bits) | (uint32_t)bin;
-                w.mrem[g] = target - run;
-                break;
-            }
-            run += cnt[i];
-        }
-    }
+    resolve_group<D>(w, blockIdx.x, tmp);
 }
 
-// After the probe selection: the candidate and zeroing bounds of each group.
 __global__ void k_probe_done(int32_t G, int32_t mode, CompressWs w)
 {
-    for (int32_t g = blockIdx.x * kBlock + threadIdx.x; g < G; g += gridDim.x * kBlock) {
-        if (w.rank[2 * g] > 0) w.key_lo[g] = w.prefix[2 * g];
-        if (mode == SGC_EXACT) {
-            if (w.rank[2 * g + 1] > 0) w.key_z[g] = w.prefix[2 * g + 1];
-        } else {
-            w.key_z[g] = w.key_lo[g];
-        }
-    }
+    for (int32_t g = blockIdx.x * kBlock + threadIdx.x; g < G; g += gridDim.x * kBlock) probe_bounds(w, g, mode);
 }
 
 // ---------------------------------------------------------------- pass 1
@@ -948,14 +963,15 @@ __global__ void k_seg_counts(const int64_t* __restrict__ seg_off, int32_t nseg, 
             out_counts[nseg] = total;
             continue;
         }
-        int64_t a0 = 0, a1 = total;
-        const int64_t x0 = seg_off[t];
+        // entries below x0 and below x1 (indices ascend; every index lies in [0, n))
+        const int64_t x0 = seg_off[t], x1 = seg_off[t + 1];
+        int64_t a0 = 0, a1 = x0 == 0 ? 0 : total;
         while (a0 < a1) {
             int64_t m = (a0 + a1) >> 1;
             if (out_idx[m] < x0) a0 = m + 1; else a1 = m;
         }
         int64_t b0 = a0, b1 = total;
-        const int64_t x1 = seg_off[t + 1];
+        if (x1 == seg_off[nseg]) b0 = total;
         while (b0 < b1) {
             int64_t m = (b0 + b1) >> 1;
             if (out_idx[m] < x1) b0 = m + 1; else b1 = m;
@@ -964,23 +980,31 @@ __global__ void k_seg_counts(const int64_t* __restrict__ seg_off, int32_t nseg, 
     }
 }
 
+// probe: the selection places the probe bounds of the G groups at the end.
 template <int D>
-static int radix_select(const float* res, int32_t V, int64_t nch_max, const CompressWs& w, hipStream_t s)
+static int radix_select(const float* res, int32_t V, int64_t nch_max, const CompressWs& w, hipStream_t s, bool probe,
+                        int32_t G, int32_t mode)
 {
-    unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>(nch_max, 1), kHistBlocks);
+    const unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>(nch_max, 1), kHistBlocks);
     k_srs_hist<D><<<blocks, kBlock, 0, s>>>(res, V, w);
     SGC_LAUNCH_CHECK();
     k_srs_resolve<D><<<(unsigned)V, kBlock, 0, s>>>(w);
     SGC_LAUNCH_CHECK();
+    if (probe && D == 2) {
+        k_probe_done<<<(unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(G, kBlock), 1024)), kBlock, 0, s>>>(
+            G, mode, w);
+        SGC_LAUNCH_CHECK();
+    }
     return SGC_OK;
 }
 
-static int select_all(const float* res, int32_t V, int64_t nch_max, const CompressWs& w, hipStream_t s)
+static int select_all(const float* res, int32_t V, int64_t nch_max, const CompressWs& w, hipStream_t s,
+                      bool probe = false, int32_t G = 0, int32_t mode = 0)
 {
     int rc;
-    if ((rc = radix_select<0>(res, V, nch_max, w, s))) return rc;
-    if ((rc = radix_select<1>(res, V, nch_max, w, s))) return rc;
-    return radix_select<2>(res, V, nch_max, w, s);
+    if ((rc = radix_select<0>(res, V, nch_max, w, s, probe, G, mode))) return rc;
+    if ((rc = radix_select<1>(res, V, nch_max, w, s, probe, G, mode))) return rc;
+    return radix_select<2>(res, V, nch_max, w, s, probe, G, mode);
 }
 
 // Measurement hook: events recorded around the fused pass (benchmarks only).
@@ -1070,18 +1094,16 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
     const int32_t V = 2 * G;
 
     // 1. probe selection -> key_lo, key_z
-    k_setup<<<1, 64, 0, s>>>(gr.off, G, o->mode, o->keep_ppm, o->sample_div, o->sample_min, w);
+    const int64_t hist_words = (int64_t)V * kRep * kBins;
+    k_setup<<<(unsigned)std::min<int64_t>(cdiv(hist_words, kBlock), 256), kBlock, 0, s>>>(
+        gr.off, G, o->mode, o->keep_ppm, o->sample_div, o->sample_min, w, hist_words);
     SGC_LAUNCH_CHECK();
-    if ((rc = fill_u32(w.hist, (int64_t)V * kRep * kBins, 0, s))) return rc;
     if (z.S > 0) {
         unsigned pb = (unsigned)std::min<int64_t>(cdiv(z.S, kBlock), 4096);
         k_probe<<<pb, kBlock, 0, s>>>(grad, residual, gr.off, G, o->mode, w, z.S);
         SGC_LAUNCH_CHECK();
     }
-    if ((rc = select_all(residual, V, 2 * cdiv(z.S, kChunk) + V + 1, w, s))) return rc;
-    k_probe_done<<<(unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(G, kBlock), 1024)), kBlock, 0, s>>>(
-        G, o->mode, w);
-    SGC_LAUNCH_CHECK();
+    if ((rc = select_all(residual, V, 2 * cdiv(z.S, kChunk) + V + 1, w, s, true, G, o->mode))) return rc;
 
     // 2. pass 1
     if (g_pass_start && hipEventRecord(g_pass_start, s) != hipSuccess) return SGC_EHIP;
