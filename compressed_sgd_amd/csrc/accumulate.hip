@@ -505,11 +505,13 @@ __global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg)
 // counter here, so a wait for loads also waits for earlier stores, and
 // those are then long done.  A tile whose entries do not fit the prefetch (a
 // message with more than kPre * group-size entries in it, or more than
-// kPre * kBlock in all) is applied from memory instead, in rounds of
-// kPre * kBlock entries taken in message order.
-constexpr int kPre = 4;                              // entries per thread per tile (or round)
-constexpr int kRound = kPre * kBlock;                // entries per round
-constexpr int kQ = (int)(kOutTile / (4 * kBlock));  // 16-byte words per thread in a tile
+// kRound in all) is applied from memory instead, in rounds of kRound entries
+// taken in message order.
+constexpr int kMergeThreads = 256;                          // threads per merge workgroup
+constexpr int kPre = 4;                                     // entries per thread per tile (or round)
+constexpr int kRound = kPre * kMergeThreads;                // entries per round
+constexpr int kQ = (int)(kOutTile / (4 * kMergeThreads));  // 16-byte words per thread in a tile
+constexpr int kMaskWords = (int)(kOutTile / 2) / kMergeThreads;  // mask words each thread clears
 static_assert(kMerge <= 16, "message masks are 16 bits");
 
 struct MergeLds {
@@ -537,8 +539,9 @@ __device__ inline void tile_meta(MergeLds& S, int par, int z, int32_t nmsg, int3
 
 __device__ inline void clear_mask(uint32_t* mask)
 {
-    *(i4v*)&mask[8 * threadIdx.x] = i4v{0, 0, 0, 0};
-    *(i4v*)&mask[8 * threadIdx.x + 4] = i4v{0, 0, 0, 0};
+    static_assert(kMaskWords % 4 == 0, "mask clear in 16-byte words");
+#pragma unroll
+    for (int q = 0; q < kMaskWords / 4; ++q) *(i4v*)&mask[kMaskWords * threadIdx.x + 4 * q] = i4v{0, 0, 0, 0};
 }
 
 // Step 1: every entry (message k[i], tile position p[i] >= 0) marks its message.
@@ -577,7 +580,7 @@ __device__ inline void add_entries(MergeLds& S, uint32_t* mask, int z, const int
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, int32_t init,
+__global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t lg_tpm, int32_t init,
                                                  const float* __restrict__ base, float* __restrict__ out, int64_t n,
                                                  int64_t ntiles, int64_t per)
 {
@@ -592,7 +595,6 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
     const float* src = init == SGC_INIT_BASE ? base : out;
     const int64_t T0 = (int64_t)blockIdx.x * per, T1 = min(T0 + per, ntiles);
     if (T0 >= T1) return;
-    static_assert(sizeof(S.mask[0]) == 32 * kBlock, "mask clear: two 16-byte words per thread");
 
     // pipeline registers: the next tile's entries (global positions) and initial contents
     int32_t n_pos[kPre];
@@ -618,7 +620,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
         }
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            const int i = 4 * (q * kBlock + tid);
+            const int i = 4 * (q * kMergeThreads + tid);
             f4a v = {0.0f, 0.0f, 0.0f, 0.0f};
             if (init != SGC_INIT_ZERO) {
                 if (cnt == kOutTile) {
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
         // the previous tile (always whole) leaves LDS for memory; tile u's initial contents enter
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            const int i = 4 * (q * kBlock + tid);
+            const int i = 4 * (q * kMergeThreads + tid);
             const f4a pt = *(const f4a*)(S.tile + i);
             *(f4a*)(S.tile + i) = ini[q];
             if (u > T0) *(f4a*)(out + lo - kOutTile + i) = pt;
@@ -691,7 +693,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
             for (int32_t R0 = 0; R0 < total; R0 += kRound) {
 #pragma unroll
                 for (int i = 0; i < kPre; ++i) {
-                    const int32_t e = R0 + tid + i * kBlock;
+                    const int32_t e = R0 + tid + i * kMergeThreads;
                     cp[i] = -1;
                     ck[i] = 0;
                     cv[i] = 0.0f;
@@ -721,7 +723,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(MergeBatch M, int32_t lg_tpm, 
     const int32_t cnt = (int32_t)min((int64_t)kOutTile, n - lo);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-        const int i = 4 * (q * kBlock + tid);
+        const int i = 4 * (q * kMergeThreads + tid);
         const f4a r = *(const f4a*)(S.tile + i);
         if (cnt == kOutTile) {
             *(f4a*)(out + lo + i) = r;
@@ -751,7 +753,7 @@ static int64_t merge_blocks()
 {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_merge, kBlock, 0) != hipSuccess || cus <= 0 || per_cu <= 0)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_merge, kMergeThreads, 0) != hipSuccess || cus <= 0 || per_cu <= 0)
         return 1024;
     return (int64_t)cus * per_cu;
 }
@@ -867,11 +869,13 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
             M.tstart[k] = w.tstart;
             M.bad[k] = w.bad;
         }
-        int32_t lg_tpm = 8;  // threads per message slot: 256 / (message count rounded up to a power of two)
-        while (lg_tpm > 0 && (kBlock >> lg_tpm) < M.n) --lg_tpm;
+        // threads per message slot: the workgroup / (message count rounded up to a power of two)
+        int32_t lg_tpm = 0;
+        while ((1 << (lg_tpm + 1)) <= kMergeThreads) ++lg_tpm;
+        while (lg_tpm > 0 && (kMergeThreads >> lg_tpm) < M.n) --lg_tpm;
         const int64_t per = cdiv(ntiles, std::min<int64_t>(ntiles, merge_blocks()));
         const int64_t grid = cdiv(ntiles, per);
-        k_merge<<<(unsigned)grid, kBlock, 0, s>>>(M, lg_tpm, mb == 0 ? init : SGC_INIT_INPLACE, base, out, L->n,
+        k_merge<<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, mb == 0 ? init : SGC_INIT_INPLACE, base, out, L->n,
                                                   ntiles, per);
         SGC_LAUNCH_CHECK();
         if (dstatus && M.n > 0) {
