@@ -142,9 +142,27 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     pass_ms = [a.elapsed_time(z) for a, z in ev]
     pass_avg = sum(pass_ms) / len(pass_ms)
+    # per-step times (separate run of the same steps, each bracketed by its own events)
+    st_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i, (a, z) in enumerate(st_ev):
+        a.record(stream)
+        step(args.warmup + args.steps + i)
+        z.record(stream)
+    torch.cuda.synchronize()
+    step_ms = sorted(a.elapsed_time(z) for a, z in st_ev)
     status = int(comp.status.item())
     kept = comp.total()
     nbits = int(enc.nbits[0].item())
+
+    # Rice code length at the page's parameter (b = 7) for the same message
+    enc7 = sgc.encode(layout, comp.idx, comp.counts, comp.cap, b=7)
+    nbits7 = int(enc7.nbits[0].item())
+    del enc7
+    # attainable streaming bandwidth: plain device copy of 1 GiB (2 GiB moved)
+    cx = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cy = torch.empty_like(cx)
+    copy_ms = timed(lambda: cy.copy_(cx), 5, stream)
+    del cx, cy
 
     pass_bytes = 12.0 * n                          # read g, read r, write r
     alg_bytes = 12.0 * n + 8.0 * kept + 4.0 * kept + nbits / 8.0 + 8.0 * ((kept + 255) // 256)
@@ -168,9 +186,13 @@ def main():
             "workload": "flat-2^30 gradient, exact global top-1% with residual, Rice-coded index gaps (b=6)",
             "n": n, "keep_ppm": ppm, "kept": kept, "mode": "exact", "scope": "global", "rice_b": b,
         },
+        "ms_per_step_median": step_ms[len(step_ms) // 2],
+        "ms_per_step_min": step_ms[0],
         "alg_GBps": alg_bytes / (ms / 1e3) / 1e9,
         "alg_frac_of_8TBps": alg_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
         "bits_per_position": nbits / max(kept, 1),
+        "bits_per_position_b7": nbits7 / max(kept, 1),
+        "compression_ratio_vs_dense_fp32": 32.0 * n / (nbits + 32.0 * kept),
         "status": status,
         "wall_s_timed": wall,
         "roofline": {
@@ -178,6 +200,8 @@ def main():
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
             "alg_bytes_per_launch": pass_bytes, "avg_launch_ms": pass_avg,
+            "traffic_over_alg": None if traffic is None else traffic / pass_bytes,
+            "attainable_copy_GBps": 8.0 * (1 << 28) / (copy_ms / 1e3) / 1e9,
         },
     }
 

@@ -65,7 +65,8 @@ def check_topk(acc, comp, r_after, k_expected, what, seg_off=None):
 
 
 def test_mlp_mnist_two_bit_four_workers(orc):
-    # global top-1% + 2-bit quantization + Rice (b = 6), 4 workers, 2 steps
+    # global top-1% + 2-bit quantization, 4 workers, 2 steps: raw 2-bit messages
+    # in step 0, Rice-coded positions (b = 6) in step 1
     w = W.MLP_MNIST
     layout = sgc.Layout(w.seg_numel)
     seg_off = np.array(layout.seg_off, np.int64)
@@ -83,10 +84,16 @@ def test_mlp_mnist_two_bit_four_workers(orc):
             ref = oracle_sparse(orc, comp)
             r_host = host(rd).copy()
             bn, ob = check_binarize(orc, layout, comp, ref, rd, r_host, sgc.BIN_2BIT, f"mlp s{step} w{wk}")
-            enc, oenc = check_encode(orc, layout, ref.idx, host(bn.counts), 0, b, f"mlp s{step} w{wk}")
-            gm.append(sgc.golomb_message(bn, enc))
-            om.append(orc.Message(host(bn.counts), vkind=orc.VAL_2BIT, golomb=True, scope=0, b=b,
-                                  codes=host(bn.codes).view(np.uint32), means=host(bn.means), enc=oenc))
+            codes, means = host(bn.codes).view(np.uint32), host(bn.means)
+            if step == 0:
+                gm.append(sgc.Message(sgc.MSG_RAW_2BIT, bn.counts, bn.cap, idx=comp.idx, codes=bn.codes,
+                                      means=bn.means))
+                om.append(orc.Message(host(bn.counts), vkind=orc.VAL_2BIT, idx=ref.idx, codes=codes, means=means))
+            else:
+                enc, oenc = check_encode(orc, layout, ref.idx, host(bn.counts), 0, b, f"mlp s{step} w{wk}")
+                gm.append(sgc.golomb_message(bn, enc))
+                om.append(orc.Message(host(bn.counts), vkind=orc.VAL_2BIT, golomb=True, scope=0, b=b, codes=codes,
+                                      means=means, enc=oenc))
         out = torch.empty(w.numel, dtype=torch.float32, device="cuda")
         announce(f"mlp decode_accumulate step {step}")
         st = sgc.decode_accumulate(layout, gm, out)
@@ -98,16 +105,20 @@ def test_mlp_mnist_two_bit_four_workers(orc):
 
 
 def test_nmt_rnn_global_plus_local(orc):
-    # global top-1% of 97.8M elements, 4 workers' Rice messages added to the
-    # local dense gradient
+    # global top-1% of 97.8M elements; node 0 adds the 4 workers' raw messages
+    # (its own among them) to its fresh local gradient.  The streams are also
+    # Rice coded (b = 6) and compared with the oracle: zero runs of ~10^6
+    # elements make this the long-run encoder case.
     w = W.NMT_RNN
     layout = sgc.Layout(w.seg_numel)
-    seg_off = np.array(layout.seg_off, np.int64)
     b = sgc.rice_param(w.keep_ppm / 1e6)
     k = layout.keep_total(sgc.GLOBAL, w.keep_ppm)
     msgs, sent = [], []
+    local = None
     for wk in range(w.workers):
         g = W.gradient(w, wk, 0, device="cuda")
+        if wk == 0:
+            local = g.clone()
         rd = torch.zeros(w.numel, dtype=torch.float32, device="cuda")
         acc = rd + g
         comp = sgc.compress(layout, g, rd, keep_ppm=w.keep_ppm)
@@ -115,11 +126,10 @@ def test_nmt_rnn_global_plus_local(orc):
         check_topk(acc, comp, rd, k, f"nmt w{wk}")
         total = int(host(comp.counts)[-1])
         idx = host(comp.idx)[:total]
-        enc, _ = check_encode(orc, layout, idx, host(comp.counts), 0, b, f"nmt w{wk}")
-        msgs.append(sgc.golomb_message(comp, enc))
+        check_encode(orc, layout, idx, host(comp.counts), 0, b, f"nmt w{wk}")
+        msgs.append(sgc.raw_message(comp))
         sent.append((idx.astype(np.int64), host(comp.val)[:total].copy()))
         del g, acc, rd
-    local = W.gradient(w, 99, 0, device="cuda")
     out = torch.empty(w.numel, dtype=torch.float32, device="cuda")
     announce("nmt decode_accumulate on the local gradient")
     st = sgc.decode_accumulate(layout, msgs, out, init=sgc.INIT_BASE, base=local)
@@ -129,40 +139,46 @@ def test_nmt_rnn_global_plus_local(orc):
     torch.cuda.synchronize()
     assert int(host(st)[0]) == 0
     assert_bitwise(host(out), ref, "nmt local + 4 workers")
-    assert seg_off[-1] == w.numel
 
 
 def test_resnet50_sbc_eight_workers(orc):
-    # per-tensor top-0.1% + SBC + per-tensor Rice streams, 8 workers
+    # per-tensor top-0.1% + SBC + per-tensor Rice streams (b = 9), 8 workers,
+    # 2 rounds of 7 delayed accumulations and one exchange each
     w = W.RESNET50
     layout = sgc.Layout(w.seg_numel)
     seg_off = np.array(layout.seg_off, np.int64)
     b = sgc.rice_param(w.keep_ppm / 1e6)
     k = layout.keep_total(sgc.PER_SEGMENT, w.keep_ppm)
-    gm, om = [], []
-    for wk in range(w.workers):
-        g = W.gradient(w, wk, 0, device="cuda")
-        rd = 0.25 * W.gradient(w, wk, 1, device="cuda")  # a residual carried from earlier steps
-        acc = rd + g
-        comp = sgc.compress(layout, g, rd, keep_ppm=w.keep_ppm, scope=sgc.PER_SEGMENT)
+    res = [torch.zeros(w.numel, dtype=torch.float32, device="cuda") for _ in range(w.workers)]
+    for rnd in range(2):
+        gm, om = [], []
+        for wk in range(w.workers):
+            rd = res[wk]
+            for s_ in range(w.delay - 1):  # communication delay: accumulate only
+                sgc.compress(layout, W.gradient(w, wk, rnd * w.delay + s_, device="cuda"), rd,
+                             mode=sgc.ACCUMULATE_ONLY)
+            g = W.gradient(w, wk, rnd * w.delay + w.delay - 1, device="cuda")
+            acc = rd + g
+            comp = sgc.compress(layout, g, rd, keep_ppm=w.keep_ppm, scope=sgc.PER_SEGMENT)
+            torch.cuda.synchronize()
+            check_topk(acc, comp, rd, k, f"resnet r{rnd} w{wk}", seg_off=seg_off)
+            ref = oracle_sparse(orc, comp)
+            r_host = host(rd).copy()
+            bn, ob = check_binarize(orc, layout, comp, ref, rd, r_host, sgc.BIN_SBC, f"resnet r{rnd} w{wk}")
+            cnt = host(bn.counts)
+            sidx = host(bn.idx)[:int(cnt[-1])]
+            enc, oenc = check_encode(orc, layout, sidx, cnt, 1, b, f"resnet r{rnd} w{wk}")
+            gm.append(sgc.golomb_message(bn, enc))
+            om.append(orc.Message(cnt, vkind=orc.VAL_SBC, golomb=True, scope=1, b=b, means=host(bn.means),
+                                  enc=oenc))
+        out = torch.empty(w.numel, dtype=torch.float32, device="cuda")
+        announce(f"resnet decode_accumulate round {rnd}")
+        st = sgc.decode_accumulate(layout, gm, out)
+        ref_out = np.zeros(w.numel, np.float32)
+        assert orc.decode_accumulate(om, seg_off, ref_out) == 0
         torch.cuda.synchronize()
-        check_topk(acc, comp, rd, k, f"resnet w{wk}", seg_off=seg_off)
-        ref = oracle_sparse(orc, comp)
-        r_host = host(rd).copy()
-        bn, ob = check_binarize(orc, layout, comp, ref, rd, r_host, sgc.BIN_SBC, f"resnet w{wk}")
-        cnt = host(bn.counts)
-        sidx = host(bn.idx)[:int(cnt[-1])]
-        enc, oenc = check_encode(orc, layout, sidx, cnt, 1, b, f"resnet w{wk}")
-        gm.append(sgc.golomb_message(bn, enc))
-        om.append(orc.Message(cnt, vkind=orc.VAL_SBC, golomb=True, scope=1, b=b, means=host(bn.means), enc=oenc))
-    out = torch.empty(w.numel, dtype=torch.float32, device="cuda")
-    announce("resnet decode_accumulate")
-    st = sgc.decode_accumulate(layout, gm, out)
-    ref_out = np.zeros(w.numel, np.float32)
-    assert orc.decode_accumulate(om, seg_off, ref_out) == 0
-    torch.cuda.synchronize()
-    assert int(host(st)[0]) == 0
-    assert_bitwise(host(out), ref_out, "resnet sum of 8 workers")
+        assert int(host(st)[0]) == 0
+        assert_bitwise(host(out), ref_out, f"resnet round {rnd} sum of 8 workers")
 
 
 def test_flat_1g_compress_encode_full_size(orc):
