@@ -410,7 +410,7 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
     constexpr int NW = TB / 64;
     __shared__ uint32_t wtot[SL][NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool full = A >= lo && A + (int32_t)kTile <= hi;  // uniform
+    const bool full = A >= lo && (int64_t)A + kTile <= (int64_t)hi;  // uniform; 64-bit: A + kTile may reach 2^31
     const f4* rb = (const f4*)(res + A);
     const f4* gb = (const f4*)(grad + A);
     f4 acc[SL];

@@ -238,3 +238,43 @@ def test_flat_1g_decode_accumulate_sixteen_workers(orc):
     torch.cuda.synchronize()
     assert int(host(st)[0]) == 0
     assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), "flat-1G 16-worker sum"
+
+
+@pytest.mark.parametrize("scope", [sgc.GLOBAL, sgc.PER_SEGMENT])
+def test_maximum_size(orc, scope):
+    # n = 2^31 - 1, the largest layout the int32 indices allow: top-0.1% with
+    # the last elements large, Rice coded, then accumulated onto zeros
+    sizes = [1 << 30, (1 << 30) - 1]
+    layout = sgc.Layout(sizes)
+    n = layout.n
+    assert n == (1 << 31) - 1
+    ppm = 1000
+    b = sgc.rice_param(ppm / 1e6)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77 + scope)
+    g = torch.randn(n, dtype=torch.float32, device="cuda", generator=gen).mul_(1e-4)
+    g[-5:] = torch.tensor([1.0, -2.0, 3.0, -4.0, 5.0], device="cuda")  # the very last indices are kept
+    rd = torch.zeros(n, dtype=torch.float32, device="cuda")
+    acc = rd + g
+    comp = sgc.compress(layout, g, rd, keep_ppm=ppm, scope=scope)
+    torch.cuda.synchronize()
+    del g
+    k = layout.keep_total(scope, ppm)
+    check_topk(acc, comp, rd, k, f"2^31-1 scope {scope}",
+               seg_off=None if scope == sgc.GLOBAL else np.array(layout.seg_off, np.int64))
+    del acc
+    total = int(host(comp.counts)[-1])
+    idx = host(comp.idx)[:total]
+    assert idx[-1] == n - 1
+    enc, _ = check_encode(orc, layout, idx, host(comp.counts), scope, b, f"2^31-1 scope {scope}")
+    msgs = [sgc.raw_message(comp), sgc.golomb_message(comp, enc)]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    announce(f"decode_accumulate 2^31-1 scope {scope}")
+    st = sgc.decode_accumulate(layout, msgs, out)
+    ref = torch.zeros(n, dtype=torch.float32, device="cuda")
+    sel = comp.idx[:total].long()
+    for _ in range(2):
+        ref[sel] = ref[sel] + comp.val[:total]
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) == 0
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), "2^31-1 sum"
