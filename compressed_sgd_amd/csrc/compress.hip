@@ -25,7 +25,7 @@
 //                the group is selected from its candidates or, if the probe
 //                misled (fewer than k candidates) or the candidate array is
 //                full, straight from the residual.
-//  4. gather  -- one workgroup per 16 tiles copies their regions into one
+//  4. gather  -- one workgroup per 64 tiles copies their regions into one
 //                ordered candidate array (sampled mode: into the output);
 //                an overflowed tile is redone from r (= acc there).
 //  5. select  -- exact k-th largest key per group over its candidates by a
@@ -171,13 +171,14 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const float* __restrict__
 }
 
 // ----------------------------------------------------------------- setup
-// One thread walks the groups: keep counts, probe sizes, prefixes, and the
-// two ranks (lower / upper bound) each group's probe selection needs.
+// Every thread clears the radix-select histograms (the resolve passes leave
+// them clear again); thread 0 of block 0 walks the groups: keep counts,
+// probe sizes, prefixes, and the two ranks (lower / upper bound) each
+// group's probe selection needs.
 __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ goff, int32_t G, int32_t mode,
                                                  uint32_t ppm, uint32_t div, uint32_t smin, CompressWs w,
                                                  int64_t hist_words)
 {
-    // every thread: clear the histograms (the resolve passes leave them clear)
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < hist_words; i += (int64_t)gridDim.x * kBlock)
         w.hist[i] = 0;
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
