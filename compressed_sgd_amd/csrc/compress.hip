@@ -8,26 +8,28 @@
 //
 // GPU design (one HBM pass over the gradient in the common case):
 //  1. probe   -- read a small sample of acc per group (runs of 16 elements)
-//                and radix-select two bounds from it: key_lo, a margin below
-//                the estimated k-th largest magnitude key (the candidate
-//                bound), and key_z, a margin above it (elements at or above
-//                it are almost surely kept).  Sampled mode instead takes
-//                the method's own systematic sample and threshold T, with
-//                key_lo = key_z = T.
+//                and radix-select two bounds from it (top 21 key bits):
+//                key_lo, a 6-sigma margin below the estimated k-th largest
+//                magnitude key (the candidate bound), and key_z, the
+//                estimate itself (the zeroing bound).  Sampled mode instead
+//                takes the method's own systematic sample and its exact
+//                threshold T, with key_lo = key_z = T.
 //  2. pass 1  -- stream g and r once: acc = r + g; every element with
 //                key >= key_lo goes into its tile's candidate region (wave
 //                ballots + LDS offsets, index order kept); r is stored as
-//                acc, or as +0 for key >= key_z, so that most kept entries
-//                leave the residual without a second, scattered write.  A
-//                tile whose region overflows stores plain acc everywhere.
+//                acc, or as +0 for key >= key_z, so that nearly all kept
+//                entries leave the residual without a second, scattered
+//                write.  A tile whose region overflows stores plain acc
+//                everywhere.
 //  3. scan    -- tile counts -> offsets (per 4096-tile super block, then
 //                one small scan); per group: candidate count, and whether
 //                the group is selected from its candidates or, if the probe
 //                misled (fewer than k candidates) or the candidate array is
 //                full, straight from the residual.
 //  4. gather  -- one workgroup per 64 tiles copies their regions into one
-//                ordered candidate array (sampled mode: into the output);
-//                an overflowed tile is redone from r (= acc there).
+//                ordered candidate array (sampled mode: into the output)
+//                and counts the first radix digit of every candidate; an
+//                overflowed tile is redone from r (= acc there).
 //  5. select  -- exact k-th largest key per group over its candidates by a
 //                3-digit radix select (11+10+10 bits, LDS histograms).
 //  6. compact -- keep key > T, plus the first `quota` entries with key == T
@@ -172,16 +174,18 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const float* __restrict__
 
 // ----------------------------------------------------------------- setup
 // Every thread clears the radix-select histograms (the resolve passes leave
-// them clear again); thread 0 of block 0 walks the groups: keep counts,
+// them clear again); thread 0 of block 0 clears the library's own status
+// word (when the caller passes none) and walks the groups: keep counts,
 // probe sizes, prefixes, and the two ranks (lower / upper bound) each
 // group's probe selection needs.
 __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ goff, int32_t G, int32_t mode,
                                                  uint32_t ppm, uint32_t div, uint32_t smin, CompressWs w,
-                                                 int64_t hist_words)
+                                                 int64_t hist_words, uint32_t* clear_status)
 {
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < hist_words; i += (int64_t)gridDim.x * kBlock)
         w.hist[i] = 0;
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    if (clear_status) *clear_status = 0;
     int64_t sp = 0, kp = 0, cp = 0;
     for (int32_t g = 0; g < G; ++g) {
         const int64_t m = goff[g + 1] - goff[g];
@@ -194,11 +198,16 @@ __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ go
                 if (s == m) {
                     rlo = rhi = k;  // the probe read every element: its k-th key is the threshold
                 } else {
-                    // expected sampled keys above the true threshold, 6-sigma margins either side
+                    // e: expected sampled keys above the true threshold.  The
+                    // candidate bound takes a 6-sigma margin below it (a miss
+                    // costs a dense selection); the zeroing bound sits at the
+                    // estimate itself: either way it errs, the compaction
+                    // fixes the few entries between it and the exact
+                    // threshold with scattered writes
                     const double e = (double)s * (double)k / (double)m;
                     const double d = 6.0 * sqrt(e) + 8.0;
                     const int64_t lo = (int64_t)(e + d) + 1;
-                    const int64_t hi = (int64_t)(e - d);
+                    const int64_t hi = (int64_t)(e + 0.5);
                     if (lo >= s) klo = 0;  // the bound would be the sample minimum: take every element
                     else rlo = lo;
                     if (hi >= 1) rhi = hi;
@@ -271,11 +280,16 @@ __global__ __launch_bounds__(kBlock) void k_probe(const float* __restrict__ grad
 // Pick the digit holding the wanted rank (counted from the largest key) of
 // virtual group g: sum the replicas, scan from the top, clear the replicas for
 // the next digit.  Every thread of the block calls it (block scan inside).
+// probe_last: this is the last digit of the probe selection; the resolving
+// thread also stores the bound it yields (the chosen digits, low bits zero):
+// even virtual groups give key_lo (and, in sampled mode, key_z = key_lo),
+// odd ones key_z.
 template <int D>
-__device__ inline void resolve_group(const CompressWs& w, int64_t g, int64_t* tmp)
+__device__ inline void resolve_group(const CompressWs& w, int64_t g, int64_t* tmp, bool probe_last, int32_t mode)
 {
     constexpr int nb = D == 0 ? 2048 : 1024;
     constexpr int bits = D == 0 ? 11 : 10;
+    constexpr int low = D == 0 ? 20 : D == 1 ? 10 : 0;  // key bits below this digit
     constexpr int per = nb / kBlock;
     const int64_t target = w.mrem[g];
     if (target == 0) return;  // uniform
@@ -302,8 +316,18 @@ __device__ inline void resolve_group(const CompressWs& w, int64_t g, int64_t* tm
         for (int i = 0; i < per; ++i) {
             const int bin = top - 1 - i;
             if (run + cnt[i] >= target) {
-                w.prefix[g] = (w.prefix[g] << bits) | (uint32_t)bin;
+                const uint32_t pre = (w.prefix[g] << bits) | (uint32_t)bin;
+                w.prefix[g] = pre;
                 w.mrem[g] = target - run;
+                if (probe_last) {
+                    const uint32_t key = pre << low;
+                    if (g & 1) {
+                        w.key_z[g >> 1] = key;
+                    } else {
+                        w.key_lo[g >> 1] = key;
+                        if (mode != SGC_EXACT) w.key_z[g >> 1] = key;
+                    }
+                }
                 break;
             }
             run += cnt[i];
@@ -311,21 +335,29 @@ __device__ inline void resolve_group(const CompressWs& w, int64_t g, int64_t* tm
     }
 }
 
-// After the probe selection: the candidate and zeroing bounds of group g.
-__device__ inline void probe_bounds(const CompressWs& w, int32_t g, int32_t mode)
+// LDS histogram count of one item per hitting lane.  The lanes that share
+// the first hitting lane's bin are counted with one atomic: in a narrow key
+// band most lanes of a wave fall into one bin, and same-address LDS atomics
+// serialise.
+__device__ inline void lds_count(uint32_t* h, bool hit, uint32_t bin)
 {
-    if (w.rank[2 * g] > 0) w.key_lo[g] = w.prefix[2 * g];
-    if (mode == SGC_EXACT) {
-        if (w.rank[2 * g + 1] > 0) w.key_z[g] = w.prefix[2 * g + 1];
-    } else {
-        w.key_z[g] = w.key_lo[g];
-    }
+    const uint64_t m = __ballot(hit);
+    if (m == 0) return;  // uniform
+    const int first = __builtin_ctzll(m);
+    const uint32_t b0 = __shfl(bin, first, 64);
+    const bool same = hit && bin == b0;
+    const uint64_t sm = __ballot(same);
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[b0], (uint32_t)__popcll(sm));
+    if (hit && !same) atomicAdd(&h[bin], 1u);
 }
 
 // Histogram of digit D over every virtual group's selection source, chunks
-// split evenly over the workgroups.
+// split evenly over the workgroups; a chunk is kPer loads per thread, all in
+// flight before the first is counted.  skip_cand: the digit of groups
+// selected from their candidates was counted already (by the gather).
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ res, int32_t V, CompressWs w)
+__global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ res, int32_t V, CompressWs w,
+                                                    int32_t skip_cand)
 {
     constexpr int shift = D == 0 ? 20 : D == 1 ? 10 : 0;
     constexpr uint32_t mask = D == 0 ? 0x7ffu : 0x3ffu;
@@ -334,6 +366,7 @@ __global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ r
     const int64_t nch = w.cpre[V];
     const int64_t per = cdiv(nch, (int64_t)gridDim.x);
     const int64_t c0 = (int64_t)blockIdx.x * per, c1 = min(c0 + per, nch);
+    if (c0 >= c1) return;  // uniform
     for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
     __syncthreads();
     int64_t cur = -1;
@@ -357,41 +390,33 @@ __global__ __launch_bounds__(kBlock) void k_srs_hist(const float* __restrict__ r
             cur = g;
             dirty = false;
         }
-        if (w.mrem[g] == 0) continue;
+        const int kind = w.src_kind[g];
+        if (w.mrem[g] == 0 || (skip_cand && kind == kSrcCand)) continue;
         dirty = true;
         const int64_t base = w.src_base[g] + (c - w.cpre[g]) * kChunk;
         const int64_t end = min(base + kChunk, w.src_base[g] + w.src_len[g]);
-        const int kind = w.src_kind[g];
         const float* src = kind == kSrcSamples ? w.samples : kind == kSrcCand ? w.cand_val : res;
         const uint32_t pre = w.prefix[g];
-        for (int64_t i0 = base + threadIdx.x; i0 < end; i0 += 4 * kBlock) {
-            float x[4];
+        // clamped, unconditional loads: a guarded load would be waited for
+        // before the next one is issued
+        float x[kPer];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {  // four independent loads in flight
-                const int64_t i = i0 + q * kBlock;
-                x[q] = i < end ? src[i] : 0.0f;
-            }
+        for (int j = 0; j < kPer; ++j) x[j] = src[min(base + j * kBlock + threadIdx.x, end - 1)];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t key = mag_key(x[q]);
-                if (i0 + q * kBlock < end && (D == 0 || (key >> (shift + 10)) == pre))
-                    atomicAdd(&h[(key >> shift) & mask], 1u);
-            }
+        for (int j = 0; j < kPer; ++j) {
+            const uint32_t key = mag_key(x[j]);
+            const bool hit = base + j * kBlock + threadIdx.x < end && (D == 0 || (key >> (shift + 10)) == pre);
+            lds_count(h, hit, (key >> shift) & mask);
         }
     }
     if (dirty) flush(cur);
 }
 
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_srs_resolve(CompressWs w)
+__global__ __launch_bounds__(kBlock) void k_srs_resolve(CompressWs w, int32_t probe_last, int32_t mode)
 {
     __shared__ int64_t tmp[kBlock / 64 + 1];
-    resolve_group<D>(w, blockIdx.x, tmp);
-}
-
-__global__ void k_probe_done(int32_t G, int32_t mode, CompressWs w)
-{
-    for (int32_t g = blockIdx.x * kBlock + threadIdx.x; g < G; g += gridDim.x * kBlock) probe_bounds(w, g, mode);
+    resolve_group<D>(w, blockIdx.x, tmp, probe_last != 0, mode);
 }
 
 // ---------------------------------------------------------------- pass 1
@@ -686,10 +711,14 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_scan2(const int64_t* __re
 // ----------------------------------------------------------------- gather
 // One workgroup per kGatherTiles tiles.  Exact mode: copy the regions of
 // candidate-selected groups into the ordered candidate array (indices of
-// redone, overflowed tiles carry kAccFlag: pass 1 did not zero them);
-// for groups that fall back to the dense residual, give back acc to the
-// entries pass 1 zeroed.  Sampled mode: the candidates are the output;
-// entries beyond cap get their acc back (they stay in the residual).
+// redone, overflowed tiles carry kAccFlag: pass 1 did not zero them) and
+// count the first radix digit of every copied candidate -- in LDS for the
+// group of the workgroup's first tile, straight into the global histogram
+// for any other; for groups that fall back to the dense residual, give back
+// acc to the entries pass 1 zeroed.  Sampled mode: the candidates are the
+// output; entries beyond cap get their acc back (they stay in the residual).
+constexpr int kGatherPer = 8;  // region entries per thread per round, loads all in flight
+
 __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ grad, float* __restrict__ res,
                                                   const int64_t* __restrict__ goff, const int64_t* __restrict__ gtile,
                                                   int32_t G, int64_t NT, int32_t mode,
@@ -699,28 +728,37 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
     __shared__ int64_t s_dst[kGatherTiles];   // destination of the tile's first entry (-1: restore only)
     __shared__ uint32_t s_pre[kGatherTiles + 1];  // prefix of the entries copied from the regions
     __shared__ uint32_t s_z[kGatherTiles];    // zeroing bound of the tile's group
+    __shared__ int32_t s_hg[kGatherTiles];    // group whose first digit the tile counts (-1: none)
     __shared__ uint64_t s_over;               // bit q: tile q overflowed
+    __shared__ uint32_t h[kBins];             // first-digit histogram of group s_hg[0]
     static_assert(kGatherTiles == 64, "one wave lane per tile");
     const bool sampled = mode == SGC_SAMPLED;
     const int64_t t0 = (int64_t)blockIdx.x * kGatherTiles;
+    if (!sampled)
+        for (int b = threadIdx.x; b < kBins; b += kBlock) h[b] = 0;
     if (threadIdx.x < 64) {
         const int q = threadIdx.x;
         const int64_t t = t0 + q;
         int64_t dst = -1;
         uint32_t c = 0, z = kNoKey;
+        int32_t hg = -1;
         bool over = false;
         if (t < NT) {
             const int64_t g = tile_group(gtile, G, t);
             c = w.tile_cnt[t];
             over = c > (uint32_t)kTileCap;
             z = w.key_z[g];
-            if (sampled) dst = tile_prefix(w, NT, t);
-            else if (w.src_kind[g] == kSrcCand)
+            if (sampled) {
+                dst = tile_prefix(w, NT, t);
+            } else if (w.src_kind[g] == kSrcCand) {
                 dst = w.cstart[g] + tile_prefix(w, NT, t) - tile_prefix(w, NT, gtile[g]);
+                if (w.rank[g] > 0) hg = (int32_t)g;
+            }
             if (over) c = 0;
         }
         s_dst[q] = dst;
         s_z[q] = z;
+        s_hg[q] = hg;
         uint32_t x = c;  // inclusive scan over the wave
         for (int d = 1; d < 64; d <<= 1) {
             const uint32_t y = __shfl_up(x, d, 64);
@@ -732,29 +770,52 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
         if (q == 0) s_over = ob;
     }
     __syncthreads();
+    const int32_t g_lds = s_hg[0];
+    uint32_t* const ghist = w.hist + (blockIdx.x & (kRep - 1)) * kBins;  // + group * kRep * kBins
     const uint32_t E = s_pre[kGatherTiles];
-    for (uint32_t e = threadIdx.x; e < E; e += kBlock) {
-        int q = 0;  // last tile whose entries start at or before e
-        for (int h = 32; h >= 1; h >>= 1)
-            if (e >= s_pre[q + h]) q += h;
-        const uint32_t j = e - s_pre[q];
-        const int64_t t = t0 + q;
-        const int32_t i = w.reg_idx[t * kTileCap + j];
-        const float v = w.reg_val[t * kTileCap + j];
-        const int64_t dst = s_dst[q];
-        if (dst < 0) {  // dense-path group: undo pass-1 zeroing
-            if (mag_key(v) >= s_z[q]) res[i] = v;
-        } else if (sampled) {
-            const int64_t p = dst + j;
-            if (p < cap) {
-                out_idx[p] = i;
-                out_val[p] = v;
-            } else {
-                res[i] = v;  // truncated: stays in the residual
+    for (uint32_t e0 = 0; e0 < E; e0 += kBlock * kGatherPer) {  // uniform
+        int32_t id[kGatherPer];
+        float v[kGatherPer];
+        int qs[kGatherPer];
+#pragma unroll
+        for (int u = 0; u < kGatherPer; ++u) {  // clamped, unconditional loads (all in flight)
+            const uint32_t e = min(e0 + u * kBlock + threadIdx.x, E - 1);
+            int q = 0;  // last tile whose entries start at or before e
+            for (int hb = 32; hb >= 1; hb >>= 1)
+                if (e >= s_pre[q + hb]) q += hb;
+            const int64_t at = (t0 + q) * kTileCap + (e - s_pre[q]);
+            id[u] = w.reg_idx[at];
+            v[u] = w.reg_val[at];
+            qs[u] = e0 + u * kBlock + threadIdx.x < E ? q : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherPer; ++u) {
+            const int q = qs[u];
+            const uint32_t bin = mag_key(v[u]) >> 20;
+            bool lds_hit = false;
+            if (q >= 0) {
+                const uint32_t j = e0 + u * kBlock + threadIdx.x - s_pre[q];
+                const int32_t i = id[u];
+                const int64_t dst = s_dst[q];
+                if (dst < 0) {  // dense-path group: undo pass-1 zeroing
+                    if (mag_key(v[u]) >= s_z[q]) res[i] = v[u];
+                } else if (sampled) {
+                    const int64_t p = dst + j;
+                    if (p < cap) {
+                        out_idx[p] = i;
+                        out_val[p] = v[u];
+                    } else {
+                        res[i] = v[u];  // truncated: stays in the residual
+                    }
+                } else {
+                    w.cand_idx[dst + j] = i;
+                    w.cand_val[dst + j] = v[u];
+                    const int32_t hg = s_hg[q];
+                    if (hg >= 0 && hg == g_lds) lds_hit = true;
+                    else if (hg >= 0) atomicAdd(&ghist[(int64_t)hg * kRep * kBins + bin], 1u);
+                }
             }
-        } else {
-            w.cand_idx[dst + j] = i;
-            w.cand_val[dst + j] = v;
+            if (!sampled) lds_count(h, lds_hit, bin);
         }
     }
     // overflowed tiles: redo from r (which pass 1 left as acc there)
@@ -765,6 +826,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
         const int64_t dst = s_dst[q];
         if (dst < 0) continue;
         const int64_t g = tile_group(gtile, G, t);
+        const int32_t hg = s_hg[q];
         const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
         const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
         tile_candidates<false, kBlock, (int)(kTile / (4 * kBlock))>(grad, res, lo, hi, A, w.key_lo[g], kNoKey,
@@ -779,8 +841,17 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
             } else {
                 w.cand_idx[p] = (int32_t)((uint32_t)i | kAccFlag);
                 w.cand_val[p] = v;
+                const uint32_t bin = mag_key(v) >> 20;
+                if (hg >= 0 && hg == g_lds) atomicAdd(&h[bin], 1u);
+                else if (hg >= 0) atomicAdd(&ghist[(int64_t)hg * kRep * kBins + bin], 1u);
             }
         });
+    }
+    if (sampled || g_lds < 0) return;  // uniform
+    __syncthreads();
+    for (int b = threadIdx.x; b < kBins; b += kBlock) {
+        const uint32_t c = h[b];
+        if (c) atomicAdd(&ghist[(int64_t)g_lds * kRep * kBins + b], c);
     }
 }
 
@@ -800,18 +871,32 @@ __device__ inline ChunkView chunk_view(const CompressWs& w, int32_t G, int64_t c
     return v;
 }
 
-// Entry i of a chunk's source: index (with kAccFlag when r holds acc there)
-// and value.
-__device__ inline void chunk_item(const CompressWs& w, const float* res, const ChunkView& v, int64_t i,
-                                  uint32_t* idx, float* val)
+// The kPer entries of this thread in a chunk: index (with kAccFlag when r
+// holds acc there) and value; bit j of the result: entry j exists.  Loads are
+// clamped to the chunk's last entry and unconditional, so that all of them
+// are in flight at once (a guarded load is waited for before the next).
+__device__ inline uint32_t chunk_items(const CompressWs& w, const float* res, const ChunkView& v,
+                                       uint32_t (&idx)[kPer], float (&val)[kPer])
 {
-    if (v.kind == kSrcCand) {
-        *idx = (uint32_t)w.cand_idx[i];
-        *val = w.cand_val[i];
+    uint32_t valid = 0;
+    if (v.kind == kSrcCand) {  // uniform
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int64_t i = min(v.base + j * kBlock + threadIdx.x, v.end - 1);
+            idx[j] = (uint32_t)w.cand_idx[i];
+            val[j] = w.cand_val[i];
+        }
     } else {
-        *idx = (uint32_t)i | kAccFlag;
-        *val = res[i];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int64_t i = min(v.base + j * kBlock + threadIdx.x, v.end - 1);
+            idx[j] = (uint32_t)i | kAccFlag;
+            val[j] = res[i];
+        }
     }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) valid |= (uint32_t)(v.base + j * kBlock + threadIdx.x < v.end) << j;
+    return valid;
 }
 
 __device__ inline uint32_t group_T(const CompressWs& w, int64_t g) { return w.rank[g] > 0 ? w.prefix[g] : kNoKey; }
@@ -826,17 +911,15 @@ __global__ __launch_bounds__(kBlock) void k_compact_count(const float* __restric
         const ChunkView v = chunk_view(w, G, c);
         const uint32_t T = group_T(w, v.g);
         uint32_t gt = 0, eq = 0;
+        uint32_t id[kPer];
+        float x[kPer];
+        const uint32_t valid = chunk_items(w, res, v, id, x);
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int64_t i = v.base + j * kBlock + threadIdx.x;
-            if (i < v.end) {
-                uint32_t id;
-                float x;
-                chunk_item(w, res, v, i, &id, &x);
-                const uint32_t key = mag_key(x);
-                gt += key > T;
-                eq += key == T;
-            }
+            const uint32_t key = mag_key(x[j]);
+            const bool in = (valid >> j) & 1u;
+            gt += in && key > T;
+            eq += in && key == T;
         }
         uint32_t tg, te;
         block_exclusive_scan<uint32_t>(gt, tmp, &tg);
@@ -875,20 +958,16 @@ __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ re
         const int64_t kept_before = gt_before + (eq_before < quota ? eq_before : quota);
         uint32_t id[kPer];
         float x[kPer];
-        uint32_t valid = 0, eqb = 0, gtb = 0;
+        const uint32_t valid = chunk_items(w, res, v, id, x);
+        uint32_t eqb = 0, gtb = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int64_t i = v.base + j * kBlock + threadIdx.x;
-            id[j] = 0;
-            x[j] = 0.0f;
-            if (i < v.end) {
-                chunk_item(w, res, v, i, &id[j], &x[j]);
-                const uint32_t key = mag_key(x[j]);
-                valid |= 1u << j;
-                gtb |= (uint32_t)(key > T) << j;
-                eqb |= (uint32_t)(key == T) << j;
-            }
+            const uint32_t key = mag_key(x[j]);
+            gtb |= (uint32_t)(key > T) << j;
+            eqb |= (uint32_t)(key == T) << j;
         }
+        gtb &= valid;
+        eqb &= valid;
         // rank of each tie among the chunk's ties, in index order
         uint32_t rk[kPer];
 #pragma unroll
@@ -981,31 +1060,18 @@ __global__ void k_seg_counts(const int64_t* __restrict__ seg_off, int32_t nseg, 
     }
 }
 
-// probe: the selection places the probe bounds of the G groups at the end.
+// One digit of the radix select over V virtual groups.  probe_last: the
+// digit ends the probe selection (its resolve stores the probe bounds).
+// skip_cand: the digit's histogram of candidate-selected groups is done.
 template <int D>
-static int radix_select(const float* res, int32_t V, int64_t nch_max, const CompressWs& w, hipStream_t s, bool probe,
-                        int32_t G, int32_t mode)
+static int radix_select(const float* res, int32_t V, const CompressWs& w, hipStream_t s, bool probe_last,
+                        int32_t mode, bool skip_cand)
 {
-    const unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>(nch_max, 1), kHistBlocks);
-    k_srs_hist<D><<<blocks, kBlock, 0, s>>>(res, V, w);
+    k_srs_hist<D><<<kHistBlocks, kBlock, 0, s>>>(res, V, w, skip_cand ? 1 : 0);
     SGC_LAUNCH_CHECK();
-    k_srs_resolve<D><<<(unsigned)V, kBlock, 0, s>>>(w);
+    k_srs_resolve<D><<<(unsigned)V, kBlock, 0, s>>>(w, probe_last ? 1 : 0, mode);
     SGC_LAUNCH_CHECK();
-    if (probe && D == 2) {
-        k_probe_done<<<(unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(G, kBlock), 1024)), kBlock, 0, s>>>(
-            G, mode, w);
-        SGC_LAUNCH_CHECK();
-    }
     return SGC_OK;
-}
-
-static int select_all(const float* res, int32_t V, int64_t nch_max, const CompressWs& w, hipStream_t s,
-                      bool probe = false, int32_t G = 0, int32_t mode = 0)
-{
-    int rc;
-    if ((rc = radix_select<0>(res, V, nch_max, w, s, probe, G, mode))) return rc;
-    if ((rc = radix_select<1>(res, V, nch_max, w, s, probe, G, mode))) return rc;
-    return radix_select<2>(res, V, nch_max, w, s, probe, G, mode);
 }
 
 // Measurement hook: events recorded around the fused pass (benchmarks only).
@@ -1084,9 +1150,9 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
     if (rc) return rc;
     Groups gr = groups_of(L, dt, o->scope);
     uint32_t* status = dstatus ? dstatus : w.status;
-    if (!dstatus && (rc = fill_u32(w.status, 1, 0, s))) return rc;
 
     if (L->n == 0) {
+        if (!dstatus && (rc = fill_u32(w.status, 1, 0, s))) return rc;
         if ((rc = fill_u32(w.scal, 2 * 8, 0, s))) return rc;
         k_seg_counts<<<1, kBlock, 0, s>>>(dt->seg_off, L->nseg, out_idx, w, out_counts);
         SGC_LAUNCH_CHECK();
@@ -1097,14 +1163,19 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
     // 1. probe selection -> key_lo, key_z
     const int64_t hist_words = (int64_t)V * kRep * kBins;
     k_setup<<<(unsigned)std::min<int64_t>(cdiv(hist_words, kBlock), 256), kBlock, 0, s>>>(
-        gr.off, G, o->mode, o->keep_ppm, o->sample_div, o->sample_min, w, hist_words);
+        gr.off, G, o->mode, o->keep_ppm, o->sample_div, o->sample_min, w, hist_words, dstatus ? nullptr : w.status);
     SGC_LAUNCH_CHECK();
     if (z.S > 0) {
         unsigned pb = (unsigned)std::min<int64_t>(cdiv(z.S, kBlock), 4096);
         k_probe<<<pb, kBlock, 0, s>>>(grad, residual, gr.off, G, o->mode, w, z.S);
         SGC_LAUNCH_CHECK();
     }
-    if ((rc = select_all(residual, V, 2 * cdiv(z.S, kChunk) + V + 1, w, s, true, G, o->mode))) return rc;
+    // exact mode: two digits (21 bits) place the bounds closely enough -- key_lo
+    // rounded down keeps it a lower bound; sampled mode: the method's threshold
+    // exactly, three digits
+    if ((rc = radix_select<0>(residual, V, w, s, false, o->mode, false))) return rc;
+    if ((rc = radix_select<1>(residual, V, w, s, o->mode == SGC_EXACT, o->mode, false))) return rc;
+    if (o->mode != SGC_EXACT && (rc = radix_select<2>(residual, V, w, s, true, o->mode, false))) return rc;
 
     // 2. pass 1
     if (g_pass_start && hipEventRecord(g_pass_start, s) != hipSuccess) return SGC_EHIP;
@@ -1126,7 +1197,10 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
 
     if (o->mode == SGC_EXACT) {
         // 5. exact selection over candidates (or the dense residual)
-        if ((rc = select_all(residual, G, z.nch_max, w, s))) return rc;
+        // (the gather counted the first digit of candidate-selected groups)
+        if ((rc = radix_select<0>(residual, G, w, s, false, o->mode, true))) return rc;
+        if ((rc = radix_select<1>(residual, G, w, s, false, o->mode, false))) return rc;
+        if ((rc = radix_select<2>(residual, G, w, s, false, o->mode, false))) return rc;
         // 6. ordered compaction
         unsigned cb = (unsigned)std::min<int64_t>(z.nch_max, 2048);
         k_compact_count<<<cb, kBlock, 0, s>>>(residual, G, w);

@@ -100,19 +100,30 @@ __device__ inline EncBlock enc_block(const EncWs& w, int32_t S, int64_t b)
     return k;
 }
 
-// Gap before entry j of stream s; flags malformed input (not strictly
+// Gap before entry j of stream s, from its index and the index before it
+// (loaded unconditionally from max(j-1, first entry); replaced here by the
+// stream's origin for the first entry).  Flags malformed input (not strictly
 // ascending, or outside the stream) and codes it as a zero gap.
-__device__ inline uint32_t enc_gap(const int32_t* __restrict__ idx, const EncWs& w, int64_t s, int64_t j, bool* bad)
+struct EncStream {
+    int64_t first, base, size;  // first entry, position of element 0, elements covered
+};
+
+__device__ inline EncStream enc_stream(const EncWs& w, int64_t s) { return {w.ent[s], w.base[s], w.size[s]}; }
+
+__device__ inline uint32_t enc_gap(int32_t cur, int32_t before, const EncStream& st, int64_t j, bool* bad)
 {
-    const int64_t pos = (int64_t)idx[j] - w.base[s];
-    const int64_t prev = j == w.ent[s] ? -1 : (int64_t)idx[j - 1] - w.base[s];
+    const int64_t pos = (int64_t)cur - st.base;
+    const int64_t prev = j == st.first ? -1 : (int64_t)before - st.base;
     const int64_t z = pos - prev - 1;
-    if (z < 0 || pos >= w.size[s]) {
+    if (z < 0 || pos >= st.size) {
         *bad = true;
         return 0;
     }
     return (uint32_t)z;
 }
+
+constexpr int kEncLenPer = (int)(kEncCodes / kBlock);  // codes per thread in the length pass
+static_assert(kEncLenPer * kBlock == kEncCodes, "encode block = whole rounds of the workgroup");
 
 __global__ __launch_bounds__(kBlock) void k_enc_len(const int32_t* __restrict__ idx, int32_t S, int32_t b, EncWs w)
 {
@@ -120,11 +131,24 @@ __global__ __launch_bounds__(kBlock) void k_enc_len(const int32_t* __restrict__ 
     const int64_t neb = w.ebpre[S];
     for (int64_t blk = blockIdx.x; blk < neb; blk += gridDim.x) {
         const EncBlock k = enc_block(w, S, blk);
+        const EncStream st = enc_stream(w, k.s);
+        // clamped, unconditional loads: all in flight at once
+        int32_t cur[kEncLenPer], bef[kEncLenPer];
+#pragma unroll
+        for (int q = 0; q < kEncLenPer; ++q) {
+            const int64_t j = min(k.e0 + q * kBlock + threadIdx.x, k.e1 - 1);
+            cur[q] = idx[j];
+            bef[q] = idx[j > st.first ? j - 1 : j];
+        }
         uint64_t bits = 0;
         bool bad = false;
-        for (int64_t j = k.e0 + threadIdx.x; j < k.e1; j += kBlock) {
-            const uint32_t z = enc_gap(idx, w, k.s, j, &bad);
-            bits += (uint64_t)(z >> b) + 1 + (uint64_t)b;
+#pragma unroll
+        for (int q = 0; q < kEncLenPer; ++q) {
+            const int64_t j = k.e0 + q * kBlock + threadIdx.x;
+            if (j < k.e1) {
+                const uint32_t z = enc_gap(cur[q], bef[q], st, j, &bad);
+                bits += (uint64_t)(z >> b) + 1 + (uint64_t)b;
+            }
         }
         if (bad) atomicOr(w.bad, 1u);
         uint64_t tot;
@@ -194,20 +218,32 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
     for (int64_t blk = blockIdx.x; blk < neb; blk += gridDim.x) {
         const EncBlock k = enc_block(w, S, blk);
         const int nown = (int)(k.e1 - k.e0), ntot = nown + (int)k.ahead;
-        // gaps and code lengths, thread-contiguous so the prefix is one block scan
+        // gaps into LDS (coalesced, clamped, unconditional loads), then code
+        // lengths thread-contiguous so that the prefix is one block scan
+        {
+            const EncStream st = enc_stream(w, k.s);
+            int32_t cur[kEncPer], bef[kEncPer];
+#pragma unroll
+            for (int q = 0; q < kEncPer; ++q) {
+                const int64_t j = k.e0 + min(q * kBlock + (int)threadIdx.x, ntot - 1);
+                cur[q] = idx[j];
+                bef[q] = idx[j > st.first ? j - 1 : j];
+            }
+            bool bad = false;  // flagged by the length pass already
+#pragma unroll
+            for (int q = 0; q < kEncPer; ++q) {
+                const int i = q * kBlock + threadIdx.x;
+                if (i < ntot) zs[i] = enc_gap(cur[q], bef[q], st, k.e0 + i, &bad);
+            }
+        }
+        __syncthreads();
         uint32_t len[kEncPer];
         uint32_t local = 0;
-        bool bad = false;
 #pragma unroll
         for (int q = 0; q < kEncPer; ++q) {
             const int i = threadIdx.x * kEncPer + q;
-            len[q] = 0;
-            if (i < ntot) {
-                const uint32_t z = enc_gap(idx, w, k.s, k.e0 + i, &bad);
-                zs[i] = z;
-                len[q] = (z >> b) + 1 + (uint32_t)b;
-                local += len[q];
-            }
+            len[q] = i < ntot ? (zs[i] >> b) + 1 + (uint32_t)b : 0u;
+            local += len[q];
         }
         uint32_t tot;
         uint32_t run = block_exclusive_scan<uint32_t>(local, tmp, &tot);
