@@ -193,6 +193,8 @@ __device__ inline const int32_t* msg_positions(const MsgIn& in, const MsgWs& w)
     return in.format >= SGC_MSG_GOLOMB_F32 ? w.pos : in.idx;
 }
 
+constexpr int kEntPer = 8;  // entries per thread per round, loads all in flight
+
 __global__ __launch_bounds__(kBlock) void k_msg_entries(Batch B, int32_t nseg, int64_t n, int64_t ntiles)
 {
     const int m = blockIdx.y;
@@ -202,23 +204,37 @@ __global__ __launch_bounds__(kBlock) void k_msg_entries(Batch B, int32_t nseg, i
     const int64_t total = w.total[0];
     const int32_t* pos = msg_positions(in, w);
     bool bad = false;
-    for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < total; j += (int64_t)gridDim.x * kBlock) {
-        const int64_t p = pos[j];
-        const int64_t prev = j == 0 ? -1 : (int64_t)pos[j - 1];
-        if (p < 0 || p >= n || p <= prev) {
-            bad = true;
-            continue;
+    const int64_t step = (int64_t)gridDim.x * kBlock * kEntPer;
+    for (int64_t j0 = (int64_t)blockIdx.x * kBlock * kEntPer + threadIdx.x; j0 < total; j0 += step) {
+        // clamped, unconditional loads (a guarded load is waited for at once)
+        int32_t pc[kEntPer], pp[kEntPer];
+#pragma unroll
+        for (int u = 0; u < kEntPer; ++u) {
+            const int64_t j = min(j0 + u * kBlock, total - 1);
+            pc[u] = pos[j];
+            pp[u] = pos[j > 0 ? j - 1 : 0];
         }
-        if (in.format == SGC_MSG_RAW_2BIT) {  // other formats: the merge reads the values directly
-            const uint32_t code = (in.codes[j >> 4] >> (2 * (j & 15))) & 3u;
-            const int64_t t = find_bucket(w.estart, (int64_t)nseg + 1, j);
-            if (code == 3u) bad = true;
-            w.val[j] = code == 0u ? 0.0f : code == 1u ? in.means[2 * t] : in.means[2 * t + 1];
+#pragma unroll
+        for (int u = 0; u < kEntPer; ++u) {
+            const int64_t j = j0 + u * kBlock;
+            if (j >= total) break;
+            const int64_t p = pc[u];
+            const int64_t prev = j == 0 ? -1 : (int64_t)pp[u];
+            if (p < 0 || p >= n || p <= prev) {
+                bad = true;
+                continue;
+            }
+            if (in.format == SGC_MSG_RAW_2BIT) {  // other formats: the merge reads the values directly
+                const uint32_t code = (in.codes[j >> 4] >> (2 * (j & 15))) & 3u;
+                const int64_t t = find_bucket(w.estart, (int64_t)nseg + 1, j);
+                if (code == 3u) bad = true;
+                w.val[j] = code == 0u ? 0.0f : code == 1u ? in.means[2 * t] : in.means[2 * t + 1];
+            }
+            const int64_t t1 = p >> kOutTileLog, t0 = prev < 0 ? 0 : (prev >> kOutTileLog) + 1;
+            for (int64_t t = max(t0, t1 - kGapTiles + 1); t <= t1; ++t) w.tstart[t] = (int32_t)j;
+            if (j == total - 1)
+                for (int64_t t = t1 + 1; t < min(ntiles, t1 + 1 + kGapTiles); ++t) w.tstart[t] = (int32_t)total;
         }
-        const int64_t t1 = p >> kOutTileLog, t0 = prev < 0 ? 0 : (prev >> kOutTileLog) + 1;
-        for (int64_t t = max(t0, t1 - kGapTiles + 1); t <= t1; ++t) w.tstart[t] = (int32_t)j;
-        if (j == total - 1)
-            for (int64_t t = t1 + 1; t < min(ntiles, t1 + 1 + kGapTiles); ++t) w.tstart[t] = (int32_t)total;
     }
     if (bad) atomicOr(w.bad, 1u);
 }
@@ -267,6 +283,7 @@ constexpr int kDecLanes = 64;
 constexpr int kColWords = 120;  // LDS words per lane (the chunk's words plus slack)
 constexpr int kColCodes = 17;   // 2-bit code words per lane (256 entries span at most 17)
 constexpr uint32_t kMaxChunkBits = 0x80000000u + SGC_CHUNK_CODES * 32u;
+constexpr int kCopy = 8;        // words per round of the column copy
 
 // 32 stream bits starting at chunk-relative bit r, from the lane's LDS column.
 struct LdsBits {
@@ -443,10 +460,18 @@ __device__ void decode_lanes(const MsgIn& in, const MsgWs& w, int32_t nseg, uint
         bool ok;
         J.relend = (uint32_t)(bit1 - (wlo << 5));
         if (need <= (uint64_t)kColWords) {
-            const uint64_t have = wlo < nw ? min(need, nw - wlo) : 0;
-#pragma unroll 8
-            for (uint64_t i = 0; i < have; ++i) col[i * kDecLanes + lane] = words[wlo + i];
-            for (uint64_t i = have; i < need; ++i) col[i * kDecLanes + lane] = 0u;
+            // kCopy loads at a time, clamped into the stream and all in flight;
+            // words past the stream's end read as 0 (a valid chunk has
+            // nw >= 1 and wlo < nw)
+            const uint32_t nd = (uint32_t)need;
+            for (uint32_t i0 = 0; i0 < nd; i0 += kCopy) {
+                uint32_t v[kCopy];
+#pragma unroll
+                for (int q = 0; q < kCopy; ++q) v[q] = words[min(wlo + i0 + q, nw - 1)];
+#pragma unroll
+                for (int q = 0; q < kCopy; ++q)
+                    if (i0 + q < nd) col[(i0 + q) * kDecLanes + lane] = wlo + i0 + q < nw ? v[q] : 0u;
+            }
             ok = decode_chunk<FMT>(LdsBits{col + lane}, (uint32_t)(bit0 & 31), J, in, w, code_col, &rel_end, &prev_end);
         } else {
             ok = decode_chunk<FMT>(GlobalBits{words, nw, wlo << 5}, (uint32_t)(bit0 & 31), J, in, w, code_col,
@@ -580,6 +605,10 @@ __device__ inline void add_entries(MergeLds& S, uint32_t* mask, int z, const int
     }
 }
 
+// Read by merge lanes that have no message, so that every tile-table load
+// is unconditional.
+__device__ int32_t g_zero_word = 0;
+
 __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t lg_tpm, int32_t init,
                                                  const float* __restrict__ base, float* __restrict__ out, int64_t n,
                                                  int64_t ntiles, int64_t per)
@@ -601,9 +630,15 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
     float n_val[kPre];
     f4a ini[kQ];
     // entry-range bounds, clamped to the message's entries (memory safety
-    // does not depend on the tile table being right)
-    const int32_t tot = live ? tsk[ntiles] : 0;
-    auto ts = [&](int64_t t) -> int32_t { return (live && t <= ntiles) ? min(max(tsk[t], 0), tot) : 0; };
+    // does not depend on the tile table being right).  The table load is
+    // unconditional (a lane without a message reads a zero word) and the
+    // clamp is applied where the bound is used: a guarded load would be
+    // waited for at once, together with every store issued before it.
+    const int32_t* tsl = live ? tsk : &g_zero_word;
+    auto ts_load = [&](int64_t t) -> int32_t { return tsl[live ? min(t, ntiles) : 0]; };
+    const int32_t tot = live ? ts_load(ntiles) : 0;
+    auto ts_fix = [&](int64_t t, int32_t raw) -> int32_t { return (live && t <= ntiles) ? min(max(raw, 0), tot) : 0; };
+    auto ts = [&](int64_t t) -> int32_t { return ts_fix(t, ts_load(t)); };
     auto span = [](int32_t a, int32_t e) -> int32_t { return max(e - a, 0); };
     auto load_tile = [&](int64_t t, int32_t a, int32_t c) {
         const int64_t lo = t * kOutTile;
@@ -671,7 +706,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         }
         mark_entries(S.mask[b], ck, cp);
         // the next tile in flight: its range bound, entries and initial contents
-        const int32_t a_n3 = ts(u + 3);
+        const int32_t r_n3 = ts_load(u + 3);  // clamped at the end of the iteration
         if (u + 1 < T1) {
             if (ml == 0 && mk < kMerge) {
                 S.a[b ^ 1][mk] = a_nxt;
@@ -715,7 +750,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         }
         a_cur = a_nxt;
         a_nxt = a_nn;
-        a_nn = a_n3;
+        a_nn = ts_fix(u + 3, r_n3);
     }
     __syncthreads();
     // the last tile
@@ -849,7 +884,8 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         const dim3 gch((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxch, kDecLanes), 16384)), (unsigned)B.n);
         k_msg_decode<<<gch, kDecLanes, 0, s>>>(B, L->nseg);
         SGC_LAUNCH_CHECK();
-        const dim3 gent((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxcap, kBlock), 4096)), (unsigned)B.n);
+        const dim3 gent((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxcap, kBlock * kEntPer), 4096)),
+                        (unsigned)B.n);
         k_msg_entries<<<gent, kBlock, 0, s>>>(B, L->nseg, L->n, ntiles);
         SGC_LAUNCH_CHECK();
         k_msg_holes<<<gtile, kBlock, 0, s>>>(B, ntiles);
