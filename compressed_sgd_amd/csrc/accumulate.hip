@@ -170,12 +170,13 @@ __global__ __launch_bounds__(kBlock) void k_msg_setup(Batch B, const int64_t* __
 // After decoding, every message is a list of ascending global positions
 // (its own idx if raw, the decoded positions otherwise).  The output-tile
 // table holds, per tile, the first entry at or beyond the tile's first
-// element.  One thread per entry checks the order (raw input is not
-// trusted), resolves raw 2-bit values, and writes the table for the tiles
-// whose first element lies after the previous entry and at or before this
-// one -- all of them when there are at most kGapTiles, else only the last;
-// the remaining tiles (long gaps, and those after the last entry beyond
-// kGapTiles) are found by a binary search per tile.
+// element.  Raw messages: one thread per entry checks the order (raw input
+// is not trusted), resolves raw 2-bit values, and writes the table for the
+// tiles whose first element lies after the previous entry and at or before
+// this one -- all of them when there are at most kGapTiles, else only the
+// last.  Coded messages: the decoder writes the table as it goes (at most
+// two tiles per entry).  The remaining tiles (long gaps, and those after the
+// last entry) are found by a binary search per tile.
 constexpr int64_t kGapTiles = 16;
 
 __device__ inline int64_t lower_bound_pos(const int32_t* pos, int64_t total, int64_t x)
@@ -200,9 +201,9 @@ __global__ __launch_bounds__(kBlock) void k_msg_entries(Batch B, int32_t nseg, i
     const int m = blockIdx.y;
     const MsgIn& in = B.in[m];
     const MsgWs& w = B.ws[m];
-    if (w.bad[0]) return;
+    if (in.format >= SGC_MSG_GOLOMB_F32 || w.bad[0]) return;  // the decoder writes the table of a coded message
     const int64_t total = w.total[0];
-    const int32_t* pos = msg_positions(in, w);
+    const int32_t* pos = in.idx;
     bool bad = false;
     const int64_t step = (int64_t)gridDim.x * kBlock * kEntPer;
     for (int64_t j0 = (int64_t)blockIdx.x * kBlock * kEntPer + threadIdx.x; j0 < total; j0 += step) {
@@ -316,6 +317,7 @@ struct ChunkJob {
     int32_t prev;           // stream position of the entry before it (-1 at the stream's start)
     int32_t size, base;     // stream size and its first element
     int32_t t, tend;        // value segment of entry j0 and where its entries end
+    int32_t* tstart;        // output-tile table
 };
 
 template <int FMT>
@@ -374,6 +376,22 @@ __device__ bool decode_chunk(const Src& src, uint32_t rel, const ChunkJob& J, co
             }
             const uint32_t pu = prev + 1 + z;  // below 2^32 unless already in error
             err |= act && (rel + len > J.relend || pu >= (uint32_t)J.size);
+            {
+                // output-tile table: an entry in a later tile than the entry
+                // before it starts its tile, and the one before that when the
+                // gap spans it; every other tile is left to the binary search.
+                // Global positions are below 2^31; before a stream's first
+                // entry the previous position is taken as the stream's origin
+                // minus one.  A corrupt chunk may mark wrongly: its message is
+                // dropped whole.
+                const int32_t t1 = (int32_t)(J.base + pu) >> kOutTileLog;
+                const int32_t tp = (J.base + (int32_t)prev) >> kOutTileLog;  // arithmetic: -1 stays -1
+                const int32_t j = J.j0 + i0 + q;
+                if (act && !err && t1 != tp) {
+                    J.tstart[t1] = j;
+                    if (t1 - tp >= 2) J.tstart[t1 - 1] = j;
+                }
+            }
             rel = act ? rel + len : rel;
             prev = act ? pu : prev;
             pb[q] = (int32_t)((uint32_t)J.base + prev);
@@ -442,6 +460,7 @@ __device__ void decode_lanes(const MsgIn& in, const MsgWs& w, int32_t nseg, uint
         J.base = (int32_t)w.sbase[a.s];
         J.t = 0;
         J.tend = INT32_MAX;
+        J.tstart = w.tstart;
         if (FMT != SGC_MSG_GOLOMB_F32) {
             J.t = (int32_t)(in.scope == SGC_PER_SEGMENT ? a.s : find_bucket(w.estart, (int64_t)nseg + 1, (int64_t)J.j0));
             J.tend = in.scope == SGC_PER_SEGMENT ? INT32_MAX : (int32_t)w.estart[J.t + 1];
@@ -856,6 +875,7 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         Batch B;
         B.n = std::min<int32_t>(kBatch, W - b0);
         int64_t maxcap = 0, maxch = 0;
+        bool any_raw = false;
         for (int32_t k = 0; k < B.n; ++k) {
             const sgc_message& m = msgs[b0 + k];
             MsgIn& in = B.in[k];
@@ -876,6 +896,7 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
             in.chunk_off = m.chunk_off;
             B.ws[k] = mws[(size_t)(b0 + k)];
             maxcap = std::max(maxcap, m.cap);
+            any_raw |= !is_golomb(m.format);
             maxch = std::max(maxch, msg_nch(L, m));
         }
         const dim3 gtile((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(ntiles, kBlock), 2048)), (unsigned)B.n);
@@ -884,10 +905,12 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         const dim3 gch((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxch, kDecLanes), 16384)), (unsigned)B.n);
         k_msg_decode<<<gch, kDecLanes, 0, s>>>(B, L->nseg);
         SGC_LAUNCH_CHECK();
-        const dim3 gent((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxcap, kBlock * kEntPer), 4096)),
-                        (unsigned)B.n);
-        k_msg_entries<<<gent, kBlock, 0, s>>>(B, L->nseg, L->n, ntiles);
-        SGC_LAUNCH_CHECK();
+        if (any_raw) {
+            const dim3 gent((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxcap, kBlock * kEntPer), 4096)),
+                            (unsigned)B.n);
+            k_msg_entries<<<gent, kBlock, 0, s>>>(B, L->nseg, L->n, ntiles);
+            SGC_LAUNCH_CHECK();
+        }
         k_msg_holes<<<gtile, kBlock, 0, s>>>(B, ntiles);
         SGC_LAUNCH_CHECK();
     }
