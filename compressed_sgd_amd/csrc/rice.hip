@@ -205,6 +205,8 @@ __global__ __launch_bounds__(1024) void k_enc_scan(int32_t S, int64_t word_cap, 
 
 constexpr int kEncLds = (int)kEncCodes + kEncAhead;
 constexpr int kEncPer = (kEncLds + kBlock - 1) / kBlock;  // entries per thread in the LDS prefix
+constexpr int kEncMapWords = 1024;  // words of a block whose first code is looked up in LDS
+static_assert(kEncLds <= 65536, "first-code map holds 16-bit code numbers");
 
 __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__ idx, int32_t S, int32_t b, EncWs w,
                                                     uint32_t* __restrict__ words, const uint64_t* __restrict__ word_off,
@@ -212,16 +214,22 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
 {
     __shared__ uint32_t zs[kEncLds];
     __shared__ uint32_t off[kEncLds + 1];
+    __shared__ uint16_t wmap[kEncMapWords];
     __shared__ uint32_t tmp[kBlock / 64 + 1];
     if (w.bad[0] & 2u) return;
     const int64_t neb = w.ebpre[S];
     for (int64_t blk = blockIdx.x; blk < neb; blk += gridDim.x) {
         const EncBlock k = enc_block(w, S, blk);
         const int nown = (int)(k.e1 - k.e0), ntot = nown + (int)k.ahead;
+        // per-stream and per-block values, loaded before they are needed
+        const EncStream st = enc_stream(w, k.s);
+        const uint64_t B0 = w.eboff[blk] - w.sbit0[k.s];  // stream-relative first bit of the block
+        const int64_t q0 = k.e0 - st.first;               // stream-relative index of the first code
+        const int64_t chpre = w.chpre[k.s];
+        uint32_t* sw = words + word_off[k.s];
         // gaps into LDS (coalesced, clamped, unconditional loads), then code
         // lengths thread-contiguous so that the prefix is one block scan
         {
-            const EncStream st = enc_stream(w, k.s);
             int32_t cur[kEncPer], bef[kEncPer];
 #pragma unroll
             for (int q = 0; q < kEncPer; ++q) {
@@ -257,26 +265,43 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
         }
         if (threadIdx.x == kBlock - 1) off[ntot] = tot;  // ntot <= kEncLds
         __syncthreads();
-        const uint64_t B0 = w.eboff[blk] - w.sbit0[k.s];  // stream-relative first bit of the block
         const uint64_t B1 = B0 + off[nown];
-        const int64_t q0 = k.e0 - w.ent[k.s];            // stream-relative index of the first code
-        uint32_t* sw = words + word_off[k.s];
+        const uint64_t wfirst = (B0 + 31) / 32, wend = (B1 + 31) / 32;
+        // first code of every word that starts in the block (the code holding
+        // the word's first bit), scattered by the codes themselves when the
+        // block's words fit the map; else found by binary search
+        const bool mapped = wend - wfirst <= (uint64_t)kEncMapWords;  // uniform
+        if (mapped) {
+#pragma unroll
+            for (int q = 0; q < kEncPer; ++q) {
+                const int i = threadIdx.x * kEncPer + q;
+                if (i < nown)
+                    for (uint64_t wd = (B0 + off[i] + 31) / 32; wd * 32 < B0 + off[i + 1]; ++wd)
+                        wmap[wd - wfirst] = (uint16_t)i;
+            }
+            __syncthreads();
+        }
         // chunk table: (bit offset, stream position reached before the code) of
         // every SGC_CHUNK_CODES-th code
         for (int i = threadIdx.x * SGC_CHUNK_CODES; i < nown; i += kBlock * SGC_CHUNK_CODES) {
-            const int64_t c = w.chpre[k.s] + (q0 + i) / SGC_CHUNK_CODES;
+            const int64_t c = chpre + (q0 + i) / SGC_CHUNK_CODES;
             const int64_t j = k.e0 + i;
+            const int32_t before = idx[j > st.first ? j - 1 : j];  // unconditional load
             chunk_off[2 * c] = B0 + off[i];
-            chunk_off[2 * c + 1] = j == w.ent[k.s] ? 0 : (uint64_t)((int64_t)idx[j - 1] - w.base[k.s] + 1);
+            chunk_off[2 * c + 1] = j == st.first ? 0 : (uint64_t)((int64_t)before - st.base + 1);
         }
-        const uint64_t wfirst = (B0 + 31) / 32, wend = (B1 + 31) / 32;
         for (uint64_t wd = wfirst + threadIdx.x; wd < wend; wd += kBlock) {
             const uint64_t W0 = wd * 32;
             // first code whose end lies past W0 (its start is <= W0 or it is code 0)
-            int lo = 0, hi = ntot - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (B0 + off[mid + 1] <= W0) lo = mid + 1; else hi = mid;
+            int lo = 0;
+            if (mapped) {
+                lo = wmap[wd - wfirst];
+            } else {
+                int hi = ntot - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (B0 + off[mid + 1] <= W0) lo = mid + 1; else hi = mid;
+                }
             }
             uint32_t v = 0;
             for (int i = lo; i < ntot; ++i) {
