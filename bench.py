@@ -12,8 +12,9 @@ zeroing) + sgc_encode of its indices.  The JSON line also carries, measured
 in the same run: the dominant kernel's roofline (the fused residual-add +
 candidate pass, timed with HIP events recorded on its own stream around its
 launch), the remaining rows of the path at the same scale (accumulate-only,
-SBC binarize, decode-accumulate of 16 workers' Rice messages, sampled-mode
-compress), and the CPU oracle timed on a bounded sample as a baseline.
+exact and sampled compress at 0.1% and 1%, Rice encode at both densities,
+SBC binarize, decode-accumulate of 16 workers' Rice messages), and the CPU
+oracle timed on a bounded sample as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -215,6 +216,17 @@ def main():
         rows["compress_exact_1pct"] = {"ms": t, "GBps": (12.0 * n + 8.0 * kept) / (t / 1e3) / 1e9}
         t = timed(lambda: sgc.encode(layout, comp.idx, comp.counts, comp.cap, b=b, out=enc), 5, stream)
         rows["encode_1pct"] = {"ms": t, "codes": kept}
+        # exact mode at 0.1% (compress, then Rice encode at that density's parameter)
+        c01 = sgc.compress(layout, grads[1], res, keep_ppm=1000)
+        b01 = sgc.rice_param(1000 / 1e6)
+        t = timed(lambda: sgc.compress(layout, grads[1], res, keep_ppm=1000, out=c01), 5, stream)
+        rows["compress_exact_0.1pct"] = {"ms": t, "GBps": (12.0 * n + 8.0 * c01.total()) / (t / 1e3) / 1e9,
+                                         "kept": c01.total()}
+        e01 = sgc.encode(layout, c01.idx, c01.counts, c01.cap, b=b01)
+        t = timed(lambda: sgc.encode(layout, c01.idx, c01.counts, c01.cap, b=b01, out=e01), 5, stream)
+        rows["encode_0.1pct"] = {"ms": t, "codes": c01.total(), "rice_b": b01,
+                                 "bits_per_position": int(e01.nbits[0].item()) / max(c01.total(), 1)}
+        del c01, e01
         # sampled-threshold mode at 0.1% and 1%
         for p, name in ((1000, "compress_sampled_0.1pct"), (10000, "compress_sampled_1pct")):
             cs = sgc.compress(layout, grads[0], res, keep_ppm=p, mode=sgc.SAMPLED)
