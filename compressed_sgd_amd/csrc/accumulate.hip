@@ -24,6 +24,8 @@
 // once: the dense output is written exactly once, in a fixed order.
 #include "sgc_common.h"
 
+#include <type_traits>
+
 namespace sgc {
 
 typedef float f4a __attribute__((ext_vector_type(4)));
@@ -334,9 +336,14 @@ __device__ inline void seg_means(const MsgIn& in, int32_t t, float* m0, float* m
 // Returns the end bit and the last position through *rel_out / *prev_out.
 // Errors are collected in a flag rather than taken as branches; after one,
 // decoding goes on over garbage with every read clamped inside the chunk's
-// words, and the chunk is rejected at the end.
+// words, and the chunk is rejected at the end.  Per code only the position
+// is checked (it guards the tile-table marks); a code that starts or ends
+// past the chunk's end bit shows in the end bit, which the caller compares
+// with the chunk table (bit positions only grow).  Groups of four codes run
+// without per-code activity tests except the last, partial group of a
+// stream.
 template <int FMT, typename Src>
-__device__ bool decode_chunk(const Src& src, uint32_t rel, const ChunkJob& J, const MsgIn& in, const MsgWs& w,
+__device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const ChunkJob& J, const MsgIn& in, const MsgWs& w,
                              const uint32_t* code_col, uint32_t* rel_out, int32_t* prev_out)
 {
     const uint32_t b = J.b, mask = (1u << b) - 1u, last_rd = J.relend - 1;
@@ -346,18 +353,21 @@ __device__ bool decode_chunk(const Src& src, uint32_t rel, const ChunkJob& J, co
     int32_t t = J.t, tend = J.tend;
     if (FMT != SGC_MSG_GOLOMB_F32) seg_means<FMT>(in, t, &m0, &m1);
     const bool vec = (J.j0 & 3) == 0;
-    for (int32_t i0 = 0; i0 < J.nc; i0 += 4) {
+    // output tile of the previous entry (before a stream's first entry: of the
+    // stream's origin minus one; arithmetic shift, so -1 stays -1)
+    int32_t tp = (J.base + (int32_t)prev) >> kOutTileLog;
+    auto group = [&](int32_t i0, auto full) __attribute__((always_inline)) {
+        constexpr bool kFull = decltype(full)::value;
         int32_t pb[4];
         float vb[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const bool act = i0 + q < J.nc;  // false only in a stream's last chunk
-            err |= act && rel >= J.relend;
+            const bool act = kFull || i0 + q < J.nc;
             const uint32_t win = src.win(min(rel, last_rd));
             const uint32_t ones = __builtin_ctzg(~win, 32);
             uint32_t len = ones + 1 + b;
             uint32_t z = (ones << b) | ((win >> min(ones, 31u) >> 1) & mask);
-            if (len > 32) {  // the unary run and the low bits leave the window: read on
+            if (__builtin_expect(len > 32, 0)) {  // the unary run and the low bits leave the window: read on
                 uint64_t qq = 0;
                 uint32_t r = rel;
                 bool fin = false;
@@ -375,25 +385,23 @@ __device__ bool decode_chunk(const Src& src, uint32_t rel, const ChunkJob& J, co
                 len = r + b - rel;
             }
             const uint32_t pu = prev + 1 + z;  // below 2^32 unless already in error
-            err |= act && (rel + len > J.relend || pu >= (uint32_t)J.size);
-            {
-                // output-tile table: an entry in a later tile than the entry
-                // before it starts its tile, and the one before that when the
-                // gap spans it; every other tile is left to the binary search.
-                // Global positions are below 2^31; before a stream's first
-                // entry the previous position is taken as the stream's origin
-                // minus one.  A corrupt chunk may mark wrongly: its message is
-                // dropped whole.
-                const int32_t t1 = (int32_t)(J.base + pu) >> kOutTileLog;
-                const int32_t tp = (J.base + (int32_t)prev) >> kOutTileLog;  // arithmetic: -1 stays -1
+            err |= act && pu >= (uint32_t)J.size;
+            // output-tile table: an entry in a later tile than the entry before
+            // it starts its tile, and the one before that when the gap spans
+            // it; every other tile is left to the binary search.  Global
+            // positions are below 2^31.  A corrupt chunk may mark wrongly: its
+            // message is dropped whole.
+            const int32_t t1 = (int32_t)(J.base + pu) >> kOutTileLog;
+            if (__builtin_expect(act && !err && t1 != tp, 0)) {
                 const int32_t j = J.j0 + i0 + q;
-                if (act && !err && t1 != tp) {
-                    J.tstart[t1] = j;
-                    if (t1 - tp >= 2) J.tstart[t1 - 1] = j;
-                }
+                J.tstart[t1] = j;
+                if (t1 - tp >= 2) J.tstart[t1 - 1] = j;
             }
-            rel = act ? rel + len : rel;
-            prev = act ? pu : prev;
+            if (act) {
+                rel += len;
+                prev = pu;
+                tp = t1;
+            }
             pb[q] = (int32_t)((uint32_t)J.base + prev);
             vb[q] = 0.0f;
             if (FMT != SGC_MSG_GOLOMB_F32 && act) {
@@ -414,25 +422,28 @@ __device__ bool decode_chunk(const Src& src, uint32_t rel, const ChunkJob& J, co
             }
         }
         const int32_t jb = J.j0 + i0;
-        if (vec && i0 + 4 <= J.nc) {
+        if (kFull && vec) {
             *(i4v*)(w.pos + jb) = i4v{pb[0], pb[1], pb[2], pb[3]};
             if (FMT != SGC_MSG_GOLOMB_F32) *(f4a*)(w.val + jb) = f4a{vb[0], vb[1], vb[2], vb[3]};
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (i0 + q >= J.nc) continue;
+                if (!kFull && i0 + q >= J.nc) continue;
                 w.pos[jb + q] = pb[q];
                 if (FMT != SGC_MSG_GOLOMB_F32) w.val[jb + q] = vb[q];
             }
         }
-    }
+    };
+    int32_t i0 = 0;
+    for (; i0 + 4 <= J.nc; i0 += 4) group(i0, std::true_type{});
+    if (i0 < J.nc) group(i0, std::false_type{});
     *rel_out = rel;
     *prev_out = (int32_t)prev;
     return !err;
 }
 
 template <int FMT>
-__device__ void decode_lanes(const MsgIn& in, const MsgWs& w, int32_t nseg, uint32_t* col, uint32_t* ccol)
+__device__ __forceinline__ void decode_lanes(const MsgIn& in, const MsgWs& w, int32_t nseg, uint32_t* col, uint32_t* ccol)
 {
     const int lane = threadIdx.x;
     const int64_t nch = w.chpre[in.S];
