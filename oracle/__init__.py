@@ -47,6 +47,10 @@ def lib():
         L.orc_rice_param.argtypes = [f64]
         L.orc_accumulate.restype = None
         L.orc_accumulate.argtypes = [P, P, i64]
+        L.orc_momentum_correct.restype = None
+        L.orc_momentum_correct.argtypes = [C.c_float, P, P, i64]
+        L.orc_momentum_mask.restype = None
+        L.orc_momentum_mask.argtypes = [P, P, i64]
         L.orc_compress_exact.restype = i64
         L.orc_compress_exact.argtypes = [P, P, P, i32, i32, u32, P, P, i64, P]
         L.orc_compress_sampled.restype = i64
@@ -100,6 +104,19 @@ def accumulate(g: np.ndarray, r: np.ndarray) -> None:
     lib().orc_accumulate(_p(_f32(g)), _p(r), r.size)
 
 
+def momentum_correct(beta: float, g: np.ndarray, u: np.ndarray) -> None:
+    """Momentum correction ([SBC] appendix A): u <- fp32(fp32(beta*u) + g) in place."""
+    assert u.dtype == np.float32 and u.flags.c_contiguous
+    lib().orc_momentum_correct(float(beta), _p(_f32(g)), _p(u), u.size)
+
+
+def momentum_mask(u: np.ndarray, sent_idx: np.ndarray) -> None:
+    """Momentum masking ([SBC] appendix A): u[sent] <- +0 in place."""
+    assert u.dtype == np.float32 and u.flags.c_contiguous
+    idx = np.ascontiguousarray(sent_idx, dtype=np.int32)
+    lib().orc_momentum_mask(_p(u), _p(idx), idx.size)
+
+
 def _groups_need(seg_off: np.ndarray, scope: int, ppm: int) -> int:
     if scope == GLOBAL:
         return keep_count(int(seg_off[-1]), ppm)
@@ -143,6 +160,20 @@ def compress_sampled(g, r: np.ndarray, seg_off, scope: int, ppm: int, cap: int,
     if rc < 0:
         raise ValueError(f"orc_compress_sampled failed: {rc}")
     return Sparse(idx[:rc].copy(), val[:rc].copy(), counts, int(st[0]))
+
+
+def compress_momentum(g, u: np.ndarray, r: np.ndarray, beta: float, seg_off, scope: int, ppm: int,
+                      sampled: bool = False, cap: Optional[int] = None, sample_div: int = 1000,
+                      sample_min: int = 65536) -> Sparse:
+    """One compress step with momentum correction and masking ([SBC] appendix A), in the pages'
+    order: correct the momentum, compress with it in place of the gradient, mask the sent entries."""
+    momentum_correct(beta, g, u)
+    if sampled:
+        sp = compress_sampled(u, r, seg_off, scope, ppm, cap, sample_div, sample_min)
+    else:
+        sp = compress_exact(u, r, seg_off, scope, ppm, cap)
+    momentum_mask(u, sp.idx)
+    return sp
 
 
 @dataclass

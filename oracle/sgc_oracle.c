@@ -126,6 +126,28 @@ void orc_accumulate(const float* g, float* r, int64_t n)
     for (int64_t i = 0; i < n; ++i) r[i] = r[i] + g[i];
 }
 
+/* Momentum correction.  [SBC] appendix A (Momentum Correction, Warm-up
+ * Training and Momentum Masking): the momentum-corrected gradient, not the
+ * raw gradient, is what goes into the residual.  The page gives neither the
+ * momentum coefficient nor the update order; the reading taken: the local
+ * momentum is updated first, u <- fp32(fp32(beta * u) + g), and the compress
+ * step then adds u to the residual in place of g.                         */
+void orc_momentum_correct(float beta, const float* g, float* u, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const float bu = beta * u[i];
+        u[i] = bu + g[i];
+    }
+}
+
+/* Momentum masking.  [SBC] appendix A: the momentum of the weights that were
+ * updated is set to zero, so that stale momentum does not keep pushing them.
+ * Reading: "updated" = sent; the entry becomes +0.                         */
+void orc_momentum_mask(float* u, const int32_t* sent_idx, int64_t count)
+{
+    for (int64_t j = 0; j < count; ++j) u[sent_idx[j]] = 0.0f;
+}
+
 /* Order of the exact selection: larger |acc| first; among equal magnitudes
  * the lower index first (so the lower index wins a tie at the threshold).   */
 static const float* sort_acc;

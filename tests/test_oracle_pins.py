@@ -207,6 +207,103 @@ def test_delay_one_is_plain_step_and_delay_two_sums(orc):
     assert np.array_equal(r, r_ref)
 
 
+# ------------------------------------------------------ momentum correction
+# [SBC] appendix A (Momentum Correction, Warm-up Training and Momentum Masking):
+# the momentum-corrected gradient goes into the residual; the momentum of the
+# sent entries is set to zero.  Reading: u <- fp32(fp32(beta*u) + g) first.
+fvals = st.sampled_from([0.0, 0.5, -0.5, 0.25, -0.25, 1.0, -1.0, 3.0, -2.0, 1.5e-3, -7e-5, 1e-40, 6.5e4])
+
+
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(u=st.lists(fvals, min_size=0, max_size=12), g=st.lists(fvals, min_size=0, max_size=12),
+       beta=st.sampled_from([0.0, 0.5, 0.9, 0.99, 1.0, -0.25]))
+def test_momentum_correct_matches_numpy(orc, u, g, beta):
+    n = min(len(u), len(g))
+    u = np.array(u[:n], np.float32)
+    g = np.array(g[:n], np.float32)
+    want = (np.float32(beta) * u).astype(np.float32) + g      # two IEEE fp32 roundings, no fused multiply-add
+    got = u.copy()
+    orc.momentum_correct(beta, g, got)
+    assert got.view(np.uint32).tolist() == want.astype(np.float32).view(np.uint32).tolist()
+
+
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(u=st.lists(fvals, min_size=0, max_size=12), g=vec, rv=vec, beta=st.sampled_from([0.5, 0.9]),
+       ppm=st.sampled_from([0, 100000, 250000, 500000, 1000000]), scope=st.sampled_from([0, 1]))
+def test_momentum_step_matches_rank_count(orc, u, g, rv, beta, ppm, scope):
+    n = min(len(u), len(g), len(rv))
+    u = np.array(u[:n], np.float32)
+    g = np.array(g[:n], np.float32)
+    r = np.array(rv[:n], np.float32)
+    seg_off = np.array([0, n // 2, n], np.int64)
+    u1 = ((np.float32(beta) * u).astype(np.float32) + g).astype(np.float32)
+    acc = (r + u1).astype(np.float32)
+    groups = [(0, n)] if scope == 0 else [(int(seg_off[t]), int(seg_off[t + 1])) for t in range(2)]
+    want = []
+    for lo, hi in groups:
+        want += bf.kept_by_rank(acc, lo, hi, bf.ceil_frac((hi - lo) * ppm, 10**6))
+    want = sorted(want)
+    u2, r2 = u.copy(), r.copy()
+    sp = orc.compress_momentum(g, u2, r2, beta, seg_off, scope, ppm)
+    assert sp.idx.tolist() == want
+    assert sp.val.view(np.uint32).tolist() == acc[want].view(np.uint32).tolist()
+    er, eu = acc.copy(), u1.copy()
+    er[want] = 0.0
+    eu[want] = 0.0
+    assert r2.view(np.uint32).tolist() == er.view(np.uint32).tolist()
+    assert u2.view(np.uint32).tolist() == eu.view(np.uint32).tolist()
+
+
+def test_worked_example_momentum(orc):
+    # beta = 0.5: u' = 0.5*[2, -2, 0, 4] + [1, 1, 1, -3] = [2, 0, 1, -1]; acc = r + u' with
+    # r = [0, 0.5, 0, 0] gives [2, 0.5, 1, -1]; keep 2 of 4: 2, then the |1| tie goes to index 2.
+    u = np.array([2, -2, 0, 4], np.float32)
+    g = np.array([1, 1, 1, -3], np.float32)
+    r = np.array([0, 0.5, 0, 0], np.float32)
+    sp = orc.compress_momentum(g, u, r, 0.5, [0, 4], orc.GLOBAL, 500000)
+    assert sp.idx.tolist() == [0, 2] and sp.val.tolist() == [2.0, 1.0]
+    assert r.tolist() == [0.0, 0.5, 0.0, -1.0]
+    assert u.tolist() == [0.0, 0.0, 0.0, -1.0]
+
+
+def test_momentum_zero_beta_is_plain_step(orc):
+    # beta = 0: u' = g (no negative zeros here), so the step is the plain one and u holds g masked
+    rng = np.random.default_rng(5)
+    n = 20000
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    u = rng.normal(0, 1, n).astype(np.float32)
+    r = rng.laplace(0, 1e-3, n).astype(np.float32)
+    r_ref = r.copy()
+    sp = orc.compress_momentum(g, u, r, 0.0, [0, n], orc.GLOBAL, 10000)
+    sp_ref = orc.compress_exact(g, r_ref, [0, n], orc.GLOBAL, 10000)
+    assert np.array_equal(sp.idx, sp_ref.idx) and np.array_equal(sp.val.view(np.uint32), sp_ref.val.view(np.uint32))
+    assert np.array_equal(r.view(np.uint32), r_ref.view(np.uint32))
+    want_u = g.copy()
+    want_u[sp.idx] = 0.0
+    assert np.array_equal(u.view(np.uint32), want_u.view(np.uint32))
+
+
+def test_momentum_invariants_over_steps(orc):
+    # every step: residual + sent == fp32(residual + u'), bitwise; u == u' outside the sent set
+    rng = np.random.default_rng(6)
+    n = 30000
+    u = np.zeros(n, np.float32)
+    r = np.zeros(n, np.float32)
+    for step in range(4):
+        g = rng.laplace(0, 1e-3, n).astype(np.float32)
+        u1 = ((np.float32(0.9) * u).astype(np.float32) + g).astype(np.float32)
+        acc = (r + u1).astype(np.float32)
+        sp = orc.compress_momentum(g, u, r, 0.9, [0, n], orc.GLOBAL, 10000)
+        assert sp.idx.size == orc.keep_count(n, 10000)
+        rebuilt = r.copy()
+        rebuilt[sp.idx] = rebuilt[sp.idx] + sp.val
+        assert np.array_equal(rebuilt.view(np.uint32), acc.view(np.uint32))
+        keep = np.zeros(n, bool)
+        keep[sp.idx] = True
+        assert np.array_equal(u[~keep].view(np.uint32), u1[~keep].view(np.uint32))
+        assert np.all(u[keep].view(np.uint32) == 0)
+
+
 # ------------------------------------------------------------ sampled mode
 def test_sampled_full_sample_is_superlevel_set(orc):
     rng = np.random.default_rng(11)
