@@ -12,7 +12,8 @@ zeroing) + sgc_encode of its indices.  The JSON line also carries, measured
 in the same run: the dominant kernel's roofline (the fused residual-add +
 candidate pass, timed with HIP events recorded on its own stream around its
 launch), the remaining rows of the path at the same scale (accumulate-only,
-exact and sampled compress at 0.1% and 1%, Rice encode at both densities,
+exact and sampled compress at 0.1% and 1%, exact compress with momentum
+correction, Rice encode at both densities,
 SBC binarize, decode-accumulate of 16 workers' Rice messages), and the CPU
 oracle timed on a bounded sample as a baseline.
 
@@ -227,6 +228,13 @@ def main():
         rows["encode_0.1pct"] = {"ms": t, "codes": c01.total(), "rice_b": b01,
                                  "bits_per_position": int(e01.nbits[0].item()) / max(c01.total(), 1)}
         del c01, e01
+        # momentum correction + masking, exact top-1%: 20 B/elem (g, r, u read; r, u written)
+        mom = torch.zeros(n, dtype=torch.float32, device=dev)
+        cm = sgc.compress_momentum(layout, grads[0], mom, res, 0.9, keep_ppm=ppm)
+        t = timed(lambda: sgc.compress_momentum(layout, grads[1], mom, res, 0.9, keep_ppm=ppm, out=cm), 5, stream)
+        rows["compress_momentum_exact_1pct"] = {"ms": t, "GBps": (20.0 * n + 12.0 * kept) / (t / 1e3) / 1e9,
+                                                "beta": 0.9}
+        del mom, cm
         # sampled-threshold mode at 0.1% and 1%
         for p, name in ((1000, "compress_sampled_0.1pct"), (10000, "compress_sampled_1pct")):
             cs = sgc.compress(layout, grads[0], res, keep_ppm=p, mode=sgc.SAMPLED)

@@ -34,7 +34,7 @@ CHUNK_CODES = 256
 EXPORTED = (
     "sgc_layout_create", "sgc_layout_destroy", "sgc_layout_numel", "sgc_layout_nseg",
     "sgc_keep_count", "sgc_rice_param", "sgc_strerror", "sgc_abi_version",
-    "sgc_compress_workspace", "sgc_compress",
+    "sgc_compress_workspace", "sgc_compress", "sgc_compress_momentum_workspace", "sgc_compress_momentum",
     "sgc_binarize_workspace", "sgc_binarize",
     "sgc_encode_word_bound", "sgc_encode_chunk_bound", "sgc_encode_workspace", "sgc_encode",
     "sgc_decode_accumulate_workspace", "sgc_decode_accumulate", "sgc_set_pass_events",
@@ -91,6 +91,10 @@ def lib():
         L.sgc_compress_workspace.restype = sz
         L.sgc_compress.argtypes = [P, P, P, P, P, P, i64, P, P, P, sz, P]
         L.sgc_compress.restype = C.c_int
+        L.sgc_compress_momentum_workspace.argtypes = [P, P, i64]
+        L.sgc_compress_momentum_workspace.restype = sz
+        L.sgc_compress_momentum.argtypes = [P, P, C.c_float, P, P, P, P, P, i64, P, P, P, sz, P]
+        L.sgc_compress_momentum.restype = C.c_int
         L.sgc_binarize_workspace.argtypes = [P, i64]
         L.sgc_binarize_workspace.restype = sz
         L.sgc_binarize.argtypes = [P, i32, P, P, P, i64, P, P, P, P, P, P, sz, P]
@@ -242,6 +246,45 @@ def compress(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode
     _check(lib().sgc_compress(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), _ptr(out.idx),
                               _ptr(out.val), cap, _ptr(out.counts), _ptr(out.status), _ptr(ws), ws.numel(), st),
            "sgc_compress")
+    return out
+
+
+def compress_momentum(layout: Layout, grad: torch.Tensor, momentum: torch.Tensor, residual: torch.Tensor,
+                      beta: float, *, mode: int = EXACT, scope: int = GLOBAL, keep_ppm: int = 10000,
+                      sample_div: int = 1000, sample_min: int = 65536, cap: Optional[int] = None,
+                      out: Optional[Compressed] = None, ws: Optional[torch.Tensor] = None,
+                      stream=None) -> Optional[Compressed]:
+    """One step with momentum correction: momentum = beta*momentum + grad, residual += momentum,
+    select, emit, zero residual and momentum at the sent entries.
+
+    mode ACCUMULATE_ONLY only updates momentum and residual and returns None.
+    """
+    for t, name in ((grad, "grad"), (momentum, "momentum"), (residual, "residual")):
+        _require_gpu(t, name)
+        if t.dtype != torch.float32 or t.numel() != layout.n:
+            raise ValueError(f"{name} must be float32 with {layout.n} elements")
+    dev = grad.device
+    opts = CompressOpts(mode, scope, keep_ppm, sample_div, sample_min)
+    st = _stream(dev, stream)
+    if mode == ACCUMULATE_ONLY:
+        _check(lib().sgc_compress_momentum(layout.handle, C.byref(opts), float(beta), _ptr(grad), _ptr(momentum),
+                                           _ptr(residual), None, None, 0, None, None, None, 0, st),
+               "sgc_compress_momentum")
+        return None
+    if cap is None:
+        k = layout.keep_total(scope, keep_ppm)
+        cap = k if mode == EXACT else min(layout.n, 2 * k + 4096)
+    if out is None:
+        out = Compressed(torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+                         torch.empty(max(cap, 1), dtype=torch.float32, device=dev),
+                         torch.empty(layout.nseg + 1, dtype=torch.int64, device=dev),
+                         torch.zeros(1, dtype=torch.int32, device=dev), cap)
+    nbytes = lib().sgc_compress_momentum_workspace(layout.handle, C.byref(opts), cap)
+    if ws is None:
+        ws = workspace(nbytes, dev, "compress_momentum")
+    _check(lib().sgc_compress_momentum(layout.handle, C.byref(opts), float(beta), _ptr(grad), _ptr(momentum),
+                                       _ptr(residual), _ptr(out.idx), _ptr(out.val), cap, _ptr(out.counts),
+                                       _ptr(out.status), _ptr(ws), ws.numel(), st), "sgc_compress_momentum")
     return out
 
 

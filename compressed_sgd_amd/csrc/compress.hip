@@ -39,6 +39,8 @@
 //                selection did not keep.
 #include "sgc_common.h"
 
+#include <cmath>
+
 namespace sgc {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -49,6 +51,27 @@ constexpr int kGatherTiles = 64;                 // tiles per gather workgroup (
 constexpr uint32_t kAccFlag = 0x80000000u;       // candidate index flag: r still holds acc there
 constexpr int kRep = 8;                          // global histogram replicas per (virtual) group
 constexpr int kHistBlocks = 1024;                // workgroups of a histogram pass
+
+// Momentum correction of one compress call ([SBC] appendix A): off, or on
+// with coefficient beta and the momentum vector u (u <- beta*u + g is what
+// goes into the residual; u <- +0 where an entry is sent).
+struct NoMom {
+    static constexpr bool on = false;
+    float beta;
+    float* u;
+};
+struct Mom {
+    static constexpr bool on = true;
+    float beta;
+    float* u;
+};
+
+// u' = fp32(fp32(beta * u) + g), two roundings (the build disables contraction)
+__device__ inline float mom_update(float beta, float u, float g)
+{
+    const float bu = beta * u;
+    return bu + g;
+}
 
 struct CompressWs {
     int64_t* k;        // [G] keep count
@@ -73,8 +96,10 @@ struct CompressWs {
     int64_t* sup_pre;  // [NS+1] super block prefix
     int32_t* reg_idx;  // [NT * kTileCap]
     float* reg_val;    // [NT * kTileCap]
+    float* reg_mom;    // [NT * kTileCap] u' of each candidate (momentum correction only)
     int32_t* cand_idx; // [capc]
     float* cand_val;   // [capc]
+    float* cand_mom;   // [capc] (momentum correction only)
     uint32_t* ch_gt;   // [nch_max]
     uint32_t* ch_eq;   // [nch_max]
     int64_t* ch_gt_pre;// [nch_max+1]
@@ -107,7 +132,7 @@ static CompressSizes compress_sizes(const sgc_layout* L, const sgc_compress_opts
     return z;
 }
 
-static void carve_compress(Carver& c, const CompressSizes& z, int mode, CompressWs* w)
+static void carve_compress(Carver& c, const CompressSizes& z, int mode, bool mom, CompressWs* w)
 {
     const int64_t G = z.G, V = 2 * (int64_t)z.G;
     w->k = c.take<int64_t>(G);
@@ -131,9 +156,12 @@ static void carve_compress(Carver& c, const CompressSizes& z, int mode, Compress
     w->sup_pre = c.take<int64_t>(z.NS + 1);
     w->reg_idx = c.take<int32_t>(z.NT * kTileCap);
     w->reg_val = c.take<float>(z.NT * kTileCap);
+    w->reg_mom = mom ? c.take<float>(z.NT * kTileCap) : nullptr;
+    w->cand_mom = nullptr;
     if (mode == SGC_EXACT) {
         w->cand_idx = c.take<int32_t>(z.capc);
         w->cand_val = c.take<float>(z.capc);
+        if (mom) w->cand_mom = c.take<float>(z.capc);
         w->ch_gt = c.take<uint32_t>(z.nch_max);
         w->ch_eq = c.take<uint32_t>(z.nch_max);
         w->ch_gt_pre = c.take<int64_t>(z.nch_max + 1);
@@ -155,7 +183,11 @@ __device__ inline int64_t tile_prefix(const CompressWs& w, int64_t NT, int64_t t
 }
 
 // ------------------------------------------------------------ accumulate
-__global__ __launch_bounds__(kBlock) void k_accumulate(const float* __restrict__ g, float* __restrict__ r, int64_t n)
+// Communication delay: r <- r + g, or with momentum correction u <- beta*u + g
+// and r <- r + u.
+template <typename M>
+__global__ __launch_bounds__(kBlock) void k_accumulate(const float* __restrict__ g, float* __restrict__ r, int64_t n,
+                                                      M m)
 {
     const int64_t n4 = n >> 2;
     const f4* g4 = (const f4*)g;
@@ -164,11 +196,25 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const float* __restrict__
     if (i < n4) {
         f4 a = __builtin_nontemporal_load(r4 + i);
         f4 b = __builtin_nontemporal_load(g4 + i);
+        if constexpr (M::on) {
+            f4* u4 = (f4*)m.u;
+            const f4 uo = __builtin_nontemporal_load(u4 + i);
+            f4 up;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) up[j] = mom_update(m.beta, uo[j], b[j]);
+            __builtin_nontemporal_store(up, u4 + i);
+            b = up;
+        }
         __builtin_nontemporal_store(a + b, r4 + i);
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
         const int64_t j = (n4 << 2) + threadIdx.x;
-        r[j] = r[j] + g[j];
+        float gj = g[j];
+        if constexpr (M::on) {
+            gj = mom_update(m.beta, m.u[j], gj);
+            m.u[j] = gj;
+        }
+        r[j] = r[j] + gj;
     }
 }
 
@@ -242,13 +288,15 @@ __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ go
     w.cpre[2 * G] = cp;
 }
 
-// Probe: acc = r + g at the sample positions.  Exact mode: runs of kRun
+// Probe: acc = r + g (g replaced by u' = beta*u + g with momentum correction;
+// u is only read here) at the sample positions.  Exact mode: runs of kRun
 // contiguous elements at systematic unit positions (the whole group if it
 // is small).  Sampled mode: the method's systematic single-element sample
 // floor((2j+1) m / (2s)).
+template <typename M>
 __global__ __launch_bounds__(kBlock) void k_probe(const float* __restrict__ grad, const float* __restrict__ res,
                                                  const int64_t* __restrict__ goff, int32_t G, int32_t mode,
-                                                 CompressWs w, int64_t S)
+                                                 CompressWs w, int64_t S, M mom)
 {
     for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < S; j += (int64_t)gridDim.x * kBlock) {
         const int64_t g = find_bucket(w.spre, (int64_t)G + 1, j);
@@ -268,7 +316,8 @@ __global__ __launch_bounds__(kBlock) void k_probe(const float* __restrict__ grad
         } else {
             pos = goff[g] + (int64_t)(((2 * jj + 1) * (uint64_t)m) / (2 * (uint64_t)s));
         }
-        w.samples[j] = res[pos] + grad[pos];
+        const float gp = M::on ? mom_update(mom.beta, mom.u[pos], grad[pos]) : grad[pos];
+        w.samples[j] = res[pos] + gp;
     }
 }
 
@@ -420,17 +469,19 @@ __global__ __launch_bounds__(kBlock) void k_srs_resolve(CompressWs w, int32_t pr
 }
 
 // ---------------------------------------------------------------- pass 1
-// Candidates of one tile in index order through `sink(pos, i, v)`, for a
+// Candidates of one tile in index order through `sink(pos, i, v, u')`, for a
 // workgroup of TB threads holding SL float4 slots each (TB * SL * 4 =
 // kTile).  ADD: acc = r + g is formed and r is stored (acc, or +0 for key >=
 // kz when the region does not overflow); otherwise r already holds acc
-// (redo of an overflowed tile).  Returns the tile's candidate count to every
+// (redo of an overflowed tile).  With momentum correction g is replaced by
+// u' = beta*u + g, and u is stored like r (u', or +0 where r gets +0); a redo
+// reads u' back from u.  Returns the tile's candidate count to every
 // thread.  Indices are 32-bit (n < 2^31); the tile base is uniform, so each
 // access is a scalar base plus one 32-bit lane offset.  A tile that lies
 // entirely inside its group skips every per-element range check.
-template <bool ADD, int TB, int SL, typename Sink>
+template <bool ADD, int TB, int SL, typename M, typename Sink>
 __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float* __restrict__ res, int32_t lo,
-                                           int32_t hi, int32_t A, uint32_t klo, uint32_t kz, Sink sink)
+                                           int32_t hi, int32_t A, uint32_t klo, uint32_t kz, M m, Sink sink)
 {
     static_assert((int64_t)TB * SL * 4 == kTile, "a tile is TB threads x SL float4");
     constexpr int NW = TB / 64;
@@ -439,13 +490,27 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
     const bool full = A >= lo && (int64_t)A + kTile <= (int64_t)hi;  // uniform; 64-bit: A + kTile may reach 2^31
     const f4* rb = (const f4*)(res + A);
     const f4* gb = (const f4*)(grad + A);
+    const f4* ub = M::on ? (const f4*)(m.u + A) : nullptr;  // momentum correction only
     f4 acc[SL];
+    f4 um[SL];  // u' (momentum correction only; r or u already hold acc / u' when !ADD)
     if (full) {
 #pragma unroll
         for (int u = 0; u < SL; ++u) {
             const int o = u * TB + tid;
-            if (ADD) acc[u] = __builtin_nontemporal_load(rb + o) + __builtin_nontemporal_load(gb + o);
-            else acc[u] = rb[o];
+            if (ADD) {
+                const f4 rv = __builtin_nontemporal_load(rb + o);
+                f4 gv = __builtin_nontemporal_load(gb + o);
+                if constexpr (M::on) {
+                    const f4 uo = __builtin_nontemporal_load(ub + o);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) gv[j] = mom_update(m.beta, uo[j], gv[j]);
+                    um[u] = gv;
+                }
+                acc[u] = rv + gv;
+            } else {
+                acc[u] = rb[o];
+                if constexpr (M::on) um[u] = ub[o];
+            }
         }
     } else {
 #pragma unroll
@@ -453,9 +518,20 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
             const int32_t e = A + 4 * (u * TB + tid);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float a = 0.0f;
-                if (e + j >= lo && e + j < hi) a = ADD ? res[e + j] + grad[e + j] : res[e + j];
+                float a = 0.0f, up = 0.0f;
+                if (e + j >= lo && e + j < hi) {
+                    if (ADD) {
+                        float gv = grad[e + j];
+                        if constexpr (M::on) gv = mom_update(m.beta, m.u[e + j], gv);
+                        up = gv;
+                        a = res[e + j] + gv;
+                    } else {
+                        a = res[e + j];
+                        if constexpr (M::on) up = m.u[e + j];
+                    }
+                }
                 acc[u][j] = a;
+                if constexpr (M::on) um[u][j] = up;
             }
         }
     }
@@ -495,14 +571,20 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
     if (ADD) {
         const uint32_t z = run <= (uint32_t)kTileCap ? kz : kNoKey;  // overflow: keep acc everywhere
         f4* rw = (f4*)(res + A);
+        f4* uw = M::on ? (f4*)(m.u + A) : nullptr;
         if (full) {
 #pragma unroll
             for (int u = 0; u < SL; ++u) {
-                f4 st = acc[u];
+                f4 st = acc[u], su;
+                if constexpr (M::on) su = um[u];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (mag_key(st[j]) >= z) st[j] = 0.0f;
+                    if (mag_key(st[j]) >= z) {
+                        st[j] = 0.0f;
+                        if constexpr (M::on) su[j] = 0.0f;  // momentum masking
+                    }
                 __builtin_nontemporal_store(st, rw + u * TB + tid);
+                if constexpr (M::on) __builtin_nontemporal_store(su, uw + u * TB + tid);
             }
         } else {
 #pragma unroll
@@ -510,7 +592,11 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
                 const int32_t e = A + 4 * (u * TB + tid);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (e + j >= lo && e + j < hi) res[e + j] = mag_key(acc[u][j]) >= z ? 0.0f : acc[u][j];
+                    if (e + j >= lo && e + j < hi) {
+                        const bool zero = mag_key(acc[u][j]) >= z;
+                        res[e + j] = zero ? 0.0f : acc[u][j];
+                        if constexpr (M::on) m.u[e + j] = zero ? 0.0f : um[u][j];
+                    }
             }
         }
     }
@@ -523,7 +609,7 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
             uint32_t pos = pre[u];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (f & (1u << j)) sink(pos++, e + j, acc[u][j]);
+                if (f & (1u << j)) sink(pos++, e + j, acc[u][j], M::on ? um[u][j] : 0.0f);
         }
     }
     return run;
@@ -534,9 +620,10 @@ __device__ inline int64_t tile_group(const int64_t* gtile, int32_t G, int64_t t)
     return G == 1 ? 0 : find_bucket(gtile, (int64_t)G + 1, t);
 }
 
+template <typename M>
 __global__ __launch_bounds__(kPassThreads) void k_pass1(const float* __restrict__ grad, float* __restrict__ res,
                                                  const int64_t* __restrict__ goff, const int64_t* __restrict__ gtile,
-                                                 int32_t G, CompressWs w)
+                                                 int32_t G, CompressWs w, M m)
 {
     const int64_t t = blockIdx.x;
     const int64_t g = tile_group(gtile, G, t);
@@ -544,13 +631,15 @@ __global__ __launch_bounds__(kPassThreads) void k_pass1(const float* __restrict_
     const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
     int32_t* ridx = w.reg_idx + t * kTileCap;
     float* rval = w.reg_val + t * kTileCap;
-    const uint32_t cnt = tile_candidates<true, kPassThreads, (int)(kTile / (4 * kPassThreads))>(grad, res, lo, hi, A, w.key_lo[g], w.key_z[g],
-                                               [&](uint32_t pos, int32_t i, float v) {
-                                                   if (pos < (uint32_t)kTileCap) {
-                                                       ridx[pos] = i;
-                                                       rval[pos] = v;
-                                                   }
-                                               });
+    float* rmom = M::on ? w.reg_mom + t * kTileCap : nullptr;
+    const uint32_t cnt = tile_candidates<true, kPassThreads, (int)(kTile / (4 * kPassThreads))>(
+        grad, res, lo, hi, A, w.key_lo[g], w.key_z[g], m, [&](uint32_t pos, int32_t i, float v, float up) {
+            if (pos < (uint32_t)kTileCap) {
+                ridx[pos] = i;
+                rval[pos] = v;
+                if constexpr (M::on) rmom[pos] = up;
+            }
+        });
     if (threadIdx.x == 0) w.tile_cnt[t] = cnt;
 }
 
@@ -717,13 +806,17 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_scan2(const int64_t* __re
 // for any other; for groups that fall back to the dense residual, give back
 // acc to the entries pass 1 zeroed.  Sampled mode: the candidates are the
 // output; entries beyond cap get their acc back (they stay in the residual).
+// With momentum correction u' travels with each candidate and is given back
+// to u wherever acc is given back to r; a redone entry that is sent has its
+// momentum zeroed here (sampled) or in the compaction (exact).
 constexpr int kGatherPer = 8;  // region entries per thread per round, loads all in flight
 
+template <typename M>
 __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ grad, float* __restrict__ res,
                                                   const int64_t* __restrict__ goff, const int64_t* __restrict__ gtile,
                                                   int32_t G, int64_t NT, int32_t mode,
                                                   int32_t* __restrict__ out_idx, float* __restrict__ out_val,
-                                                  int64_t cap, CompressWs w)
+                                                  int64_t cap, CompressWs w, M m)
 {
     __shared__ int64_t s_dst[kGatherTiles];   // destination of the tile's first entry (-1: restore only)
     __shared__ uint32_t s_pre[kGatherTiles + 1];  // prefix of the entries copied from the regions
@@ -775,7 +868,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
     const uint32_t E = s_pre[kGatherTiles];
     for (uint32_t e0 = 0; e0 < E; e0 += kBlock * kGatherPer) {  // uniform
         int32_t id[kGatherPer];
-        float v[kGatherPer];
+        float v[kGatherPer], um[kGatherPer];
         int qs[kGatherPer];
 #pragma unroll
         for (int u = 0; u < kGatherPer; ++u) {  // clamped, unconditional loads (all in flight)
@@ -786,6 +879,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
             const int64_t at = (t0 + q) * kTileCap + (e - s_pre[q]);
             id[u] = w.reg_idx[at];
             v[u] = w.reg_val[at];
+            um[u] = M::on ? w.reg_mom[at] : 0.0f;
             qs[u] = e0 + u * kBlock + threadIdx.x < E ? q : -1;
         }
 #pragma unroll
@@ -798,18 +892,23 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
                 const int32_t i = id[u];
                 const int64_t dst = s_dst[q];
                 if (dst < 0) {  // dense-path group: undo pass-1 zeroing
-                    if (mag_key(v[u]) >= s_z[q]) res[i] = v[u];
+                    if (mag_key(v[u]) >= s_z[q]) {
+                        res[i] = v[u];
+                        if constexpr (M::on) m.u[i] = um[u];
+                    }
                 } else if (sampled) {
                     const int64_t p = dst + j;
                     if (p < cap) {
                         out_idx[p] = i;
                         out_val[p] = v[u];
                     } else {
-                        res[i] = v[u];  // truncated: stays in the residual
+                        res[i] = v[u];  // truncated: stays in the residual (and keeps its momentum)
+                        if constexpr (M::on) m.u[i] = um[u];
                     }
                 } else {
                     w.cand_idx[dst + j] = i;
                     w.cand_val[dst + j] = v[u];
+                    if constexpr (M::on) w.cand_mom[dst + j] = um[u];
                     const int32_t hg = s_hg[q];
                     if (hg >= 0 && hg == g_lds) lds_hit = true;
                     else if (hg >= 0) atomicAdd(&ghist[(int64_t)hg * kRep * kBins + bin], 1u);
@@ -829,18 +928,20 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
         const int32_t hg = s_hg[q];
         const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
         const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
-        tile_candidates<false, kBlock, (int)(kTile / (4 * kBlock))>(grad, res, lo, hi, A, w.key_lo[g], kNoKey,
-                                                                  [&](uint32_t pos, int32_t i, float v) {
+        tile_candidates<false, kBlock, (int)(kTile / (4 * kBlock))>(grad, res, lo, hi, A, w.key_lo[g], kNoKey, m,
+                                                                  [&](uint32_t pos, int32_t i, float v, float up) {
             const int64_t p = dst + pos;
             if (sampled) {
                 if (p < cap) {
                     out_idx[p] = i;
                     out_val[p] = v;
                     res[i] = 0.0f;
+                    if constexpr (M::on) m.u[i] = 0.0f;
                 }
             } else {
                 w.cand_idx[p] = (int32_t)((uint32_t)i | kAccFlag);
                 w.cand_val[p] = v;
+                if constexpr (M::on) w.cand_mom[p] = up;
                 const uint32_t bin = mag_key(v) >> 20;
                 if (hg >= 0 && hg == g_lds) atomicAdd(&h[bin], 1u);
                 else if (hg >= 0) atomicAdd(&ghist[(int64_t)hg * kRep * kBins + bin], 1u);
@@ -938,9 +1039,10 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_scan(int32_t G, Compress
     scan_u32_to_i64(w.ch_eq, w.ch_eq_pre, nch);
 }
 
+template <typename M>
 __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ res, int32_t G, CompressWs w,
                                                          int32_t* __restrict__ out_idx,
-                                                         float* __restrict__ out_val, int64_t cap)
+                                                         float* __restrict__ out_val, int64_t cap, M m)
 {
     __shared__ uint32_t weq[kPer][kBlock / 64];
     __shared__ uint32_t wkp[kPer][kBlock / 64];
@@ -1021,9 +1123,13 @@ __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ re
                             out_idx[pos] = (int32_t)i;
                             out_val[pos] = x[j];
                         }
-                        if (!zeroed) res[i] = 0.0f;
+                        if (!zeroed) {
+                            res[i] = 0.0f;
+                            if constexpr (M::on) m.u[i] = 0.0f;  // momentum masking
+                        }
                     } else if (zeroed) {
-                        res[i] = x[j];  // zeroed by pass 1 but not kept: give acc back
+                        res[i] = x[j];  // zeroed by pass 1 but not kept: give acc (and u') back
+                        if constexpr (M::on) m.u[i] = w.cand_mom[v.base + j * kBlock + threadIdx.x];
                     }
                 }
                 run += tot;
@@ -1099,29 +1205,39 @@ static bool opts_ok(const sgc_layout* L, const sgc_compress_opts* o)
     return true;
 }
 
+static size_t workspace_bytes(const sgc_layout* L, const sgc_compress_opts* o, bool mom)
+{
+    CompressSizes z = compress_sizes(L, o);
+    Carver c(nullptr);
+    CompressWs w;
+    carve_compress(c, z, o->mode, mom, &w);
+    return c.off;
+}
+
 extern "C" size_t sgc_compress_workspace(const sgc_layout* L, const sgc_compress_opts* o, int64_t cap)
 {
     if (!opts_ok(L, o) || cap < 0) return 0;
     if (o->mode == SGC_ACCUMULATE_ONLY) return 0;
-    CompressSizes z = compress_sizes(L, o);
-    Carver c(nullptr);
-    CompressWs w;
-    carve_compress(c, z, o->mode, &w);
-    return c.off;
+    return workspace_bytes(L, o, false);
 }
 
-extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, const float* grad, float* residual,
-                            int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts, uint32_t* dstatus,
-                            void* ws, size_t ws_bytes, sgc_stream_t stream)
+extern "C" size_t sgc_compress_momentum_workspace(const sgc_layout* L, const sgc_compress_opts* o, int64_t cap)
 {
-    sgc_layout* L = const_cast<sgc_layout*>(Lc);
-    if (!opts_ok(L, o)) return SGC_EINVAL;
-    if ((L->n > 0 && (!grad || !residual)) || !aligned16(grad) || !aligned16(residual)) return SGC_EINVAL;
-    hipStream_t s = (hipStream_t)stream;
+    if (!opts_ok(L, o) || cap < 0) return 0;
+    if (o->mode == SGC_ACCUMULATE_ONLY) return 0;
+    return workspace_bytes(L, o, true);
+}
+
+// The compress step, plain (NoMom) or with momentum correction (Mom).
+template <typename M>
+static int compress_impl(sgc_layout* L, const sgc_compress_opts* o, M m, const float* grad, float* residual,
+                         int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts, uint32_t* dstatus,
+                         void* ws, size_t ws_bytes, hipStream_t s)
+{
     if (o->mode == SGC_ACCUMULATE_ONLY) {
         if (L->n == 0) return SGC_OK;
         const int64_t blocks = cdiv(std::max<int64_t>(L->n >> 2, 1), kBlock);
-        k_accumulate<<<(unsigned)blocks, kBlock, 0, s>>>(grad, residual, L->n);
+        k_accumulate<M><<<(unsigned)blocks, kBlock, 0, s>>>(grad, residual, L->n, m);
         SGC_LAUNCH_CHECK();
         return SGC_OK;
     }
@@ -1135,15 +1251,10 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
         if (cap < K) return SGC_EINVAL;
     }
     CompressSizes z = compress_sizes(L, o);
-    {
-        Carver c(nullptr);
-        CompressWs w0;
-        carve_compress(c, z, o->mode, &w0);
-        if (!ws || ws_bytes < c.off) return SGC_ENOSPC;
-    }
+    if (!ws || ws_bytes < workspace_bytes(L, o, M::on)) return SGC_ENOSPC;
     Carver c(ws);
     CompressWs w;
-    carve_compress(c, z, o->mode, &w);
+    carve_compress(c, z, o->mode, M::on, &w);
 
     DevTables* dt = nullptr;
     int rc = device_tables(L, &dt);
@@ -1167,7 +1278,7 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
     SGC_LAUNCH_CHECK();
     if (z.S > 0) {
         unsigned pb = (unsigned)std::min<int64_t>(cdiv(z.S, kBlock), 4096);
-        k_probe<<<pb, kBlock, 0, s>>>(grad, residual, gr.off, G, o->mode, w, z.S);
+        k_probe<M><<<pb, kBlock, 0, s>>>(grad, residual, gr.off, G, o->mode, w, z.S, m);
         SGC_LAUNCH_CHECK();
     }
     // exact mode: two digits (21 bits) place the bounds closely enough -- key_lo
@@ -1179,7 +1290,7 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
 
     // 2. pass 1
     if (g_pass_start && hipEventRecord(g_pass_start, s) != hipSuccess) return SGC_EHIP;
-    k_pass1<<<(unsigned)gr.ntiles, kPassThreads, 0, s>>>(grad, residual, gr.off, gr.tile, G, w);
+    k_pass1<M><<<(unsigned)gr.ntiles, kPassThreads, 0, s>>>(grad, residual, gr.off, gr.tile, G, w, m);
     SGC_LAUNCH_CHECK();
     if (g_pass_stop && hipEventRecord(g_pass_stop, s) != hipSuccess) return SGC_EHIP;
 
@@ -1190,9 +1301,9 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
     SGC_LAUNCH_CHECK();
 
     // 4. gather
-    k_gather<<<(unsigned)cdiv(gr.ntiles, kGatherTiles), kBlock, 0, s>>>(grad, residual, gr.off, gr.tile, G,
-                                                                         gr.ntiles, o->mode, out_idx, out_val,
-                                                                         cap, w);
+    k_gather<M><<<(unsigned)cdiv(gr.ntiles, kGatherTiles), kBlock, 0, s>>>(grad, residual, gr.off, gr.tile, G,
+                                                                            gr.ntiles, o->mode, out_idx, out_val,
+                                                                            cap, w, m);
     SGC_LAUNCH_CHECK();
 
     if (o->mode == SGC_EXACT) {
@@ -1207,11 +1318,36 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
         SGC_LAUNCH_CHECK();
         k_chunk_scan<<<1, kScanThreads, 0, s>>>(G, w);
         SGC_LAUNCH_CHECK();
-        k_compact_write<<<cb, kBlock, 0, s>>>(residual, G, w, out_idx, out_val, cap);
+        k_compact_write<M><<<cb, kBlock, 0, s>>>(residual, G, w, out_idx, out_val, cap, m);
         SGC_LAUNCH_CHECK();
     }
     unsigned sb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(L->nseg + 1, kBlock), 1024));
     k_seg_counts<<<sb, kBlock, 0, s>>>(dt->seg_off, L->nseg, out_idx, w, out_counts);
     SGC_LAUNCH_CHECK();
     return SGC_OK;
+}
+
+extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, const float* grad, float* residual,
+                            int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts, uint32_t* dstatus,
+                            void* ws, size_t ws_bytes, sgc_stream_t stream)
+{
+    sgc_layout* L = const_cast<sgc_layout*>(Lc);
+    if (!opts_ok(L, o)) return SGC_EINVAL;
+    if ((L->n > 0 && (!grad || !residual)) || !aligned16(grad) || !aligned16(residual)) return SGC_EINVAL;
+    return compress_impl(L, o, NoMom{0.0f, nullptr}, grad, residual, out_idx, out_val, cap, out_counts, dstatus, ws,
+                         ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" int sgc_compress_momentum(const sgc_layout* Lc, const sgc_compress_opts* o, float beta, const float* grad,
+                                     float* momentum, float* residual, int32_t* out_idx, float* out_val, int64_t cap,
+                                     int64_t* out_counts, uint32_t* dstatus, void* ws, size_t ws_bytes,
+                                     sgc_stream_t stream)
+{
+    sgc_layout* L = const_cast<sgc_layout*>(Lc);
+    if (!opts_ok(L, o) || !std::isfinite(beta)) return SGC_EINVAL;
+    if ((L->n > 0 && (!grad || !residual || !momentum)) || !aligned16(grad) || !aligned16(residual) ||
+        !aligned16(momentum))
+        return SGC_EINVAL;
+    return compress_impl(L, o, Mom{beta, momentum}, grad, residual, out_idx, out_val, cap, out_counts, dstatus, ws,
+                         ws_bytes, (hipStream_t)stream);
 }

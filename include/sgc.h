@@ -161,6 +161,32 @@ int sgc_compress(const sgc_layout* layout, const sgc_compress_opts* opt,
                  uint32_t* dstatus, void* ws, size_t ws_bytes, sgc_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Compress one step with momentum correction and momentum masking ([SBC]
+ * appendix A Momentum Correction, Warm-up Training and Momentum Masking:
+ * the momentum-corrected gradient is added to the residual, and the
+ * momentum of the updated weights is set to zero).  The page gives no
+ * coefficient and no order; this call takes beta from the caller and
+ * updates the momentum first:
+ *
+ *   u   = fp32(fp32(beta * momentum) + grad)       (two roundings, no FMA)
+ *   then exactly sgc_compress with u in place of grad (acc = fp32(residual
+ *   + u), the same selection, outputs, counts and status);
+ *   momentum <- u, with +0.0 at every sent entry (entries kept but past cap
+ *   in SGC_SAMPLED mode are not sent and keep u, like their residual).
+ *   SGC_ACCUMULATE_ONLY: momentum <- u; residual <- fp32(residual + u).
+ *
+ * momentum [device, n fp32, 16-byte aligned] is updated in place; beta must
+ * be finite (else SGC_EINVAL); other arguments and errors as sgc_compress.
+ * The workspace is larger than sgc_compress's (candidates also carry u):
+ * size it with sgc_compress_momentum_workspace.  beta = 0 gives
+ * sgc_compress's selection with momentum <- grad (masked).               */
+size_t sgc_compress_momentum_workspace(const sgc_layout* layout, const sgc_compress_opts* opt, int64_t cap);
+int sgc_compress_momentum(const sgc_layout* layout, const sgc_compress_opts* opt, float beta,
+                          const float* grad, float* momentum, float* residual,
+                          int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts,
+                          uint32_t* dstatus, void* ws, size_t ws_bytes, sgc_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Binarize the kept values of each segment ([SBC] §II Sparse Binarization;
  * [SBC] appendix C: the mean is the unique least-squares single value;
  * [AH17] Abstract: dropping combined with quantization).

@@ -98,6 +98,24 @@ def test_compress_validation():
     assert lib.sgc_compress_workspace(lay.handle, C.byref(sgc.CompressOpts(9, 0, 1, 1, 1)), 5) == 0
 
 
+def test_compress_momentum_validation():
+    lib = sgc.lib()
+    lay = sgc.Layout([1000, 24])
+    k = lay.keep_total(sgc.GLOBAL, 10000)
+    o = sgc.CompressOpts(sgc.EXACT, sgc.GLOBAL, 10000, 1000, 65536)
+    need = lib.sgc_compress_momentum_workspace(lay.handle, C.byref(o), k)
+    assert need > lib.sgc_compress_workspace(lay.handle, C.byref(o), k) > 0
+    call = lambda beta=0.9, u=A, wsb=need, opt=o: lib.sgc_compress_momentum(
+        lay.handle, C.byref(opt), beta, A, u, A, A, A, k, A, None, A, wsb, None)
+    assert call(beta=float("nan")) == sgc.EINVAL
+    assert call(beta=float("-inf")) == sgc.EINVAL
+    assert call(u=None) == sgc.EINVAL
+    assert call(u=MIS) == sgc.EINVAL
+    assert call(opt=sgc.CompressOpts(7, 0, 10000, 1000, 1)) == sgc.EINVAL
+    assert call(wsb=need - 1) == sgc.ENOSPC
+    assert lib.sgc_compress_momentum_workspace(lay.handle, C.byref(sgc.CompressOpts(9, 0, 1, 1, 1)), 5) == 0
+
+
 def test_binarize_validation():
     lib = sgc.lib()
     lay = sgc.Layout([100, 100])
