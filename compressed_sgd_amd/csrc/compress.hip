@@ -94,9 +94,9 @@ struct CompressWs {
     uint32_t* tile_cnt;// [NT]
     int64_t* tile_loc; // [NT] exclusive prefix inside the super block
     int64_t* sup_pre;  // [NS+1] super block prefix
-    int32_t* reg_idx;  // [NT * kTileCap]
-    float* reg_val;    // [NT * kTileCap]
-    float* reg_mom;    // [NT * kTileCap] u' of each candidate (momentum correction only)
+    int32_t* reg_idx;  // [NT * tcap]
+    float* reg_val;    // [NT * tcap]
+    float* reg_mom;    // [NT * tcap] u' of each candidate (momentum correction only)
     int32_t* cand_idx; // [capc]
     float* cand_val;   // [capc]
     float* cand_mom;   // [capc] (momentum correction only)
@@ -106,11 +106,12 @@ struct CompressWs {
     int64_t* ch_eq_pre;// [nch_max+1]
     int64_t* scal;     // [8]: 0 output total, 1 candidate total
     uint32_t* status;  // [1] used when the caller passes no dstatus
+    uint32_t tcap;     // candidate slots per tile region (a power of two)
 };
 
 struct CompressSizes {
     int32_t G;
-    int64_t NT, NS, S, capc, nch_max;
+    int64_t NT, NS, S, capc, nch_max, tcap;
 };
 
 static CompressSizes compress_sizes(const sgc_layout* L, const sgc_compress_opts* o)
@@ -120,6 +121,7 @@ static CompressSizes compress_sizes(const sgc_layout* L, const sgc_compress_opts
     z.G = (int32_t)off.size() - 1;
     z.NT = (o->scope == SGC_GLOBAL) ? group_tiles(0, L->n) : L->seg_tile[L->nseg];
     z.NS = cdiv(z.NT, kSuper);
+    z.tcap = region_capacity(o->keep_ppm);
     z.S = 0;
     int64_t K = 0;
     for (int32_t g = 0; g < z.G; ++g) {
@@ -154,9 +156,10 @@ static void carve_compress(Carver& c, const CompressSizes& z, int mode, bool mom
     w->tile_cnt = c.take<uint32_t>(z.NT);
     w->tile_loc = c.take<int64_t>(z.NT);
     w->sup_pre = c.take<int64_t>(z.NS + 1);
-    w->reg_idx = c.take<int32_t>(z.NT * kTileCap);
-    w->reg_val = c.take<float>(z.NT * kTileCap);
-    w->reg_mom = mom ? c.take<float>(z.NT * kTileCap) : nullptr;
+    w->tcap = (uint32_t)z.tcap;
+    w->reg_idx = c.take<int32_t>(z.NT * z.tcap);
+    w->reg_val = c.take<float>(z.NT * z.tcap);
+    w->reg_mom = mom ? c.take<float>(z.NT * z.tcap) : nullptr;
     w->cand_mom = nullptr;
     if (mode == SGC_EXACT) {
         w->cand_idx = c.take<int32_t>(z.capc);
@@ -472,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void k_srs_resolve(CompressWs w, int32_t pr
 // Candidates of one tile in index order through `sink(pos, i, v, u')`, for a
 // workgroup of TB threads holding SL float4 slots each (TB * SL * 4 =
 // kTile).  ADD: acc = r + g is formed and r is stored (acc, or +0 for key >=
-// kz when the region does not overflow); otherwise r already holds acc
+// kz when the tile's candidates fit its tcap-slot region); otherwise r already holds acc
 // (redo of an overflowed tile).  With momentum correction g is replaced by
 // u' = beta*u + g, and u is stored like r (u', or +0 where r gets +0); a redo
 // reads u' back from u.  Returns the tile's candidate count to every
@@ -481,7 +484,8 @@ __global__ __launch_bounds__(kBlock) void k_srs_resolve(CompressWs w, int32_t pr
 // entirely inside its group skips every per-element range check.
 template <bool ADD, int TB, int SL, typename M, typename Sink>
 __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float* __restrict__ res, int32_t lo,
-                                           int32_t hi, int32_t A, uint32_t klo, uint32_t kz, M m, Sink sink)
+                                           int32_t hi, int32_t A, uint32_t klo, uint32_t kz, uint32_t tcap, M m,
+                                           Sink sink)
 {
     static_assert((int64_t)TB * SL * 4 == kTile, "a tile is TB threads x SL float4");
     constexpr int NW = TB / 64;
@@ -569,7 +573,7 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
     }
     __syncthreads();  // wtot is reused by the next call in this block
     if (ADD) {
-        const uint32_t z = run <= (uint32_t)kTileCap ? kz : kNoKey;  // overflow: keep acc everywhere
+        const uint32_t z = run <= tcap ? kz : kNoKey;  // overflow: keep acc everywhere
         f4* rw = (f4*)(res + A);
         f4* uw = M::on ? (f4*)(m.u + A) : nullptr;
         if (full) {
@@ -629,12 +633,12 @@ __global__ __launch_bounds__(kPassThreads) void k_pass1(const float* __restrict_
     const int64_t g = tile_group(gtile, G, t);
     const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
     const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
-    int32_t* ridx = w.reg_idx + t * kTileCap;
-    float* rval = w.reg_val + t * kTileCap;
-    float* rmom = M::on ? w.reg_mom + t * kTileCap : nullptr;
+    int32_t* ridx = w.reg_idx + t * w.tcap;
+    float* rval = w.reg_val + t * w.tcap;
+    float* rmom = M::on ? w.reg_mom + t * w.tcap : nullptr;
     const uint32_t cnt = tile_candidates<true, kPassThreads, (int)(kTile / (4 * kPassThreads))>(
-        grad, res, lo, hi, A, w.key_lo[g], w.key_z[g], m, [&](uint32_t pos, int32_t i, float v, float up) {
-            if (pos < (uint32_t)kTileCap) {
+        grad, res, lo, hi, A, w.key_lo[g], w.key_z[g], w.tcap, m, [&](uint32_t pos, int32_t i, float v, float up) {
+            if (pos < w.tcap) {
                 ridx[pos] = i;
                 rval[pos] = v;
                 if constexpr (M::on) rmom[pos] = up;
@@ -839,7 +843,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
         if (t < NT) {
             const int64_t g = tile_group(gtile, G, t);
             c = w.tile_cnt[t];
-            over = c > (uint32_t)kTileCap;
+            over = c > w.tcap;
             z = w.key_z[g];
             if (sampled) {
                 dst = tile_prefix(w, NT, t);
@@ -876,7 +880,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
             int q = 0;  // last tile whose entries start at or before e
             for (int hb = 32; hb >= 1; hb >>= 1)
                 if (e >= s_pre[q + hb]) q += hb;
-            const int64_t at = (t0 + q) * kTileCap + (e - s_pre[q]);
+            const int64_t at = (t0 + q) * w.tcap + (e - s_pre[q]);
             id[u] = w.reg_idx[at];
             v[u] = w.reg_val[at];
             um[u] = M::on ? w.reg_mom[at] : 0.0f;
@@ -928,7 +932,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
         const int32_t hg = s_hg[q];
         const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
         const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
-        tile_candidates<false, kBlock, (int)(kTile / (4 * kBlock))>(grad, res, lo, hi, A, w.key_lo[g], kNoKey, m,
+        tile_candidates<false, kBlock, (int)(kTile / (4 * kBlock))>(grad, res, lo, hi, A, w.key_lo[g], kNoKey, w.tcap, m,
                                                                   [&](uint32_t pos, int32_t i, float v, float up) {
             const int64_t p = dst + pos;
             if (sampled) {

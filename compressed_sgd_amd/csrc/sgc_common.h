@@ -29,9 +29,20 @@ namespace sgc {
 constexpr int kBlock = 256;
 constexpr int kPassThreads = 256;
 constexpr int64_t kTile = 4096;
-// Candidate slots per tile region; a tile with more candidates is redone
-// from the residual (which holds acc after pass 1).
-constexpr int kTileCap = 256;
+// Candidate slots per tile region: a power of two from kTileCapMin up to a
+// whole tile, chosen per call as about 1.5 times the expected candidates of
+// a tile (the kept fraction plus the probe's band) -- a power-of-two region
+// stride keeps pass 1's region writes at full speed.  A tile with more
+// candidates than its region is redone from the residual (which holds acc
+// there after pass 1).
+constexpr int kTileCapMin = 256;
+inline int64_t region_capacity(uint32_t ppm)
+{
+    const double expect = (double)kTile * (double)ppm / 1e6 * 1.15;
+    int64_t cap = kTileCapMin;
+    while (cap < kTile && (double)cap < 1.5 * expect + 64.0) cap *= 2;
+    return cap;
+}
 // Chunk of the selection / compaction kernels: 256 threads x 16 contiguous.
 constexpr int kPer = 16;
 constexpr int64_t kChunk = (int64_t)kBlock * kPer;  // 4096 entries
