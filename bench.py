@@ -12,7 +12,8 @@ zeroing) + sgc_encode of its indices.  The JSON line also carries, measured
 in the same run: the dominant kernel's roofline (the fused residual-add +
 candidate pass, timed with HIP events recorded on its own stream around its
 launch), the remaining rows of the path at the same scale (accumulate-only,
-exact and sampled compress at 0.1% and 1%, exact compress with momentum
+exact and sampled compress at 0.1% and 1%, exact compress + encode at 5%,
+10% and 25% (the warm-up densities), exact compress with momentum
 correction, Rice encode at both densities,
 SBC binarize, decode-accumulate of 16 workers' Rice messages), and the CPU
 oracle timed on a bounded sample as a baseline.
@@ -228,6 +229,18 @@ def main():
         rows["encode_0.1pct"] = {"ms": t, "codes": c01.total(), "rice_b": b01,
                                  "bits_per_position": int(e01.nbits[0].item()) / max(c01.total(), 1)}
         del c01, e01
+        # density sweep (warm-up sparsity runs from 25% down to 0.1%): exact compress + Rice encode
+        for p in (250000, 100000, 50000):
+            cp = sgc.compress(layout, grads[1], res, keep_ppm=p)
+            tp = timed(lambda: sgc.compress(layout, grads[1], res, keep_ppm=p, out=cp), 3, stream)
+            bp = sgc.rice_param(p / 1e6)
+            ep = sgc.encode(layout, cp.idx, cp.counts, cp.cap, b=bp)
+            te = timed(lambda: sgc.encode(layout, cp.idx, cp.counts, cp.cap, b=bp, out=ep), 3, stream)
+            rows[f"compress_encode_exact_{p / 1e4:g}pct"] = {
+                "compress_ms": tp, "encode_ms": te, "kept": cp.total(), "rice_b": bp,
+                "compress_GBps": (12.0 * n + 8.0 * cp.total()) / (tp / 1e3) / 1e9,
+                "bits_per_position": int(ep.nbits[0].item()) / max(cp.total(), 1)}
+            del cp, ep
         # momentum correction + masking, exact top-1%: 20 B/elem (g, r, u read; r, u written)
         mom = torch.zeros(n, dtype=torch.float32, device=dev)
         cm = sgc.compress_momentum(layout, grads[0], mom, res, 0.9, keep_ppm=ppm)
