@@ -116,6 +116,23 @@ def test_clustered_overflowing_tiles(orc):
         check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=scope, ppm=10000, cap=n, what=f"clustered sampled{scope}")
 
 
+@pytest.mark.parametrize("ppm", [60000, 150000, 400000])
+def test_clustered_overflow_at_larger_regions(orc, ppm):
+    # At these kept fractions the regions hold 512, 1024 and 4096 slots (a power of two near 1.5x
+    # the expected candidates of a tile); runs of huge values still overflow the smaller ones.
+    n = 1 << 21
+    rng = np.random.default_rng(6)
+    g = rng.normal(0, 1e-5, n).astype(np.float32)
+    for start in (7000, 400001):
+        g[start:start + 20000] = rng.laplace(0, 1.0, 20000).astype(np.float32)
+    layout = sgc.Layout([n // 3, n - n // 3])
+    for scope in (0, 1):
+        r = np.zeros(n, np.float32)
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=ppm, what=f"clustered {ppm} scope{scope}")
+        check_step(orc, layout, g * np.float32(0.25), r, mode=sgc.EXACT, scope=scope, ppm=ppm,
+                   what=f"clustered {ppm} scope{scope} step 2")
+
+
 @pytest.mark.parametrize("scope", [0, 1])
 @pytest.mark.parametrize("ppm", [1000, 10000])
 def test_sampled_matches_oracle(orc, scope, ppm):
