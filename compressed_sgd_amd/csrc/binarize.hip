@@ -100,10 +100,15 @@ __global__ __launch_bounds__(kBlock) void k_bin_sums(const float* __restrict__ v
         uint32_t cp = 0, cn = 0;
         double sp = 0.0, sn = 0.0;
         const int64_t b = base + (int64_t)threadIdx.x * kPer;
+        // clamped, unconditional loads: all in flight at once (a guarded load
+        // would be waited for before the next is issued)
+        float vv[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) vv[j] = val[min(b + j, end - 1)];
+#pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int64_t i = b + j;
-            if (i < end) {
-                const float v = val[i];
+            if (b + j < end) {
+                const float v = vv[j];
                 if (v > 0.0f) { ++cp; sp += (double)v; }
                 else if (v < 0.0f) { ++cn; sn += -(double)v; }
             }
@@ -227,11 +232,20 @@ __global__ __launch_bounds__(kBlock) void k_bin_apply_sbc(const int32_t* __restr
         const int64_t base = w.estart[t] + (c - w.cpre[t]) * kChunk;
         const int64_t end = min(base + kChunk, w.estart[t + 1]);
         const int64_t b = base + (int64_t)threadIdx.x * kPer;
-        uint32_t sel = 0, cnt = 0;
+        // clamped, unconditional loads (see k_bin_sums)
+        float vv[kPer];
+        int32_t ii[kPer];
+#pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int64_t i = b + j;
-            if (i < end) {
-                const float v = val[i];
+            const int64_t i = min(b + j, end - 1);
+            vv[j] = val[i];
+            ii[j] = idx[i];
+        }
+        uint32_t sel = 0, cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (b + j < end) {
+                const float v = vv[j];
                 const bool s = (side > 0 && v > 0.0f) || (side < 0 && v < 0.0f);
                 sel |= (uint32_t)s << j;
                 cnt += s;
@@ -239,11 +253,11 @@ __global__ __launch_bounds__(kBlock) void k_bin_apply_sbc(const int32_t* __restr
         }
         uint32_t tot;
         int64_t pos = w.cout[c] + block_exclusive_scan<uint32_t>(cnt, tmp, &tot);
+#pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int64_t i = b + j;
-            if (i < end) {
-                const float v = val[i];
-                const int32_t id = idx[i];
+            if (b + j < end) {
+                const float v = vv[j];
+                const int32_t id = ii[j];
                 if ((uint32_t)id >= (uint32_t)n) continue;
                 if (sel & (1u << j)) {
                     if (pos < cap) out_idx[pos] = id;
@@ -267,15 +281,31 @@ __global__ __launch_bounds__(kBlock) void k_bin_apply_2bit(const int32_t* __rest
     for (int64_t wd = (int64_t)blockIdx.x * kBlock + threadIdx.x; wd < nwords; wd += (int64_t)gridDim.x * kBlock) {
         const int64_t j0 = wd * 16;
         int64_t t = find_bucket(w.estart, (int64_t)nseg + 1, j0);
+        // clamped, unconditional loads (see k_bin_sums)
+        float vv[16];
+        int32_t ii[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int64_t j = min(j0 + q, total - 1);
+            vv[q] = val[j];
+            ii[q] = idx[j];
+        }
+        int64_t tend = w.estart[t + 1];
+        float mp = w.mpos[t], mn = w.mneg[t];
         uint32_t word = 0;
         for (int q = 0; q < 16; ++q) {
             const int64_t j = j0 + q;
             if (j >= total) break;
-            while (j >= w.estart[t + 1]) ++t;
-            const float v = val[j];
+            while (j >= tend) {  // the next segment (rare)
+                ++t;
+                tend = w.estart[t + 1];
+                mp = w.mpos[t];
+                mn = w.mneg[t];
+            }
+            const float v = vv[q];
             const uint32_t code = v > 0.0f ? 1u : v < 0.0f ? 2u : 0u;
-            const float qv = code == 1u ? w.mpos[t] : code == 2u ? -w.mneg[t] : 0.0f;
-            const int32_t id = idx[j];
+            const float qv = code == 1u ? mp : code == 2u ? -mn : 0.0f;
+            const int32_t id = ii[q];
             if ((uint32_t)id < (uint32_t)n) res[id] = v - qv;
             if (out_idx) out_idx[j] = id;
             word |= code << (2 * q);
