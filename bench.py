@@ -258,6 +258,11 @@ def main():
         rsave = res.clone()
         t = timed(lambda: sgc.binarize(layout, comp, res, sgc.BIN_SBC), 5, stream)
         rows["binarize_sbc_1pct"] = {"ms": t, "entries": kept}
+        # the same after compress with the hold flag: only the sent side is written
+        res.copy_(rsave)
+        sgc.compress(layout, grads[0], res, keep_ppm=ppm, out=comp, hold=True)
+        t = timed(lambda: sgc.binarize(layout, comp, res, sgc.BIN_SBC, held=True), 5, stream)
+        rows["binarize_sbc_1pct_held"] = {"ms": t, "entries": kept}
         res.copy_(rsave)
         del rsave
         # a7: decode-accumulate of 16 workers' Rice messages into 4 GiB, onto zeros

@@ -25,8 +25,10 @@ LIB_PATH = os.path.join(HERE, "libsgc.so")
 OK, EINVAL, ENOSPC, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4
 STATUS_TRUNCATED, STATUS_CORRUPT, STATUS_DENSE_PATH, STATUS_BAD_INPUT = 1, 2, 4, 8
 EXACT, SAMPLED, ACCUMULATE_ONLY = 0, 1, 2
+HOLD_KEPT = 0x10
 GLOBAL, PER_SEGMENT = 0, 1
 BIN_SBC, BIN_2BIT = 0, 1
+BIN_HELD = 0x10
 MSG_RAW_F32, MSG_RAW_2BIT, MSG_GOLOMB_F32, MSG_GOLOMB_SBC, MSG_GOLOMB_2BIT = 0, 1, 2, 3, 4
 INIT_ZERO, INIT_BASE, INIT_INPLACE = 0, 1, 2
 CHUNK_CODES = 256
@@ -216,17 +218,18 @@ class Compressed:
 def compress(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode: int = EXACT,
              scope: int = GLOBAL, keep_ppm: int = 10000, sample_div: int = 1000, sample_min: int = 65536,
              cap: Optional[int] = None, out: Optional[Compressed] = None, ws: Optional[torch.Tensor] = None,
-             stream=None) -> Optional[Compressed]:
+             hold: bool = False, stream=None) -> Optional[Compressed]:
     """One step: residual += grad, select, emit, zero the residual at kept entries.
 
     mode ACCUMULATE_ONLY only adds (communication delay) and returns None.
+    hold: the kept entries keep acc in the residual (for binarize(..., held=True) next).
     """
     for t, name in ((grad, "grad"), (residual, "residual")):
         _require_gpu(t, name)
         if t.dtype != torch.float32 or t.numel() != layout.n:
             raise ValueError(f"{name} must be float32 with {layout.n} elements")
     dev = grad.device
-    opts = CompressOpts(mode, scope, keep_ppm, sample_div, sample_min)
+    opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min)
     st = _stream(dev, stream)
     if mode == ACCUMULATE_ONLY:
         _check(lib().sgc_compress(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), None, None, 0, None,
@@ -300,8 +303,12 @@ class Binarized:
 
 
 def binarize(layout: Layout, comp: Compressed, residual: torch.Tensor, mode: int = BIN_SBC, *,
-             ws: Optional[torch.Tensor] = None, stream=None) -> Binarized:
-    """Sparse binarization (SBC) or 2-bit quantization of a compress result."""
+             ws: Optional[torch.Tensor] = None, held: bool = False, stream=None) -> Binarized:
+    """Sparse binarization (SBC) or 2-bit quantization of a compress result.
+
+    held: the residual holds acc at the kept entries (compress(..., hold=True)); same result,
+    fewer writes.
+    """
     _require_gpu(residual, "residual")
     dev = residual.device
     cap = comp.cap
@@ -314,7 +321,8 @@ def binarize(layout: Layout, comp: Compressed, residual: torch.Tensor, mode: int
     nbytes = lib().sgc_binarize_workspace(layout.handle, cap)
     if ws is None:
         ws = workspace(nbytes, dev, "binarize")
-    _check(lib().sgc_binarize(layout.handle, mode, _ptr(comp.idx), _ptr(comp.val), _ptr(comp.counts), cap,
+    _check(lib().sgc_binarize(layout.handle, mode | (BIN_HELD if held else 0), _ptr(comp.idx), _ptr(comp.val),
+                              _ptr(comp.counts), cap,
                               _ptr(residual), _ptr(out.idx), _ptr(out.counts), _ptr(out.means), _ptr(out.codes),
                               _ptr(ws), ws.numel(), _stream(dev, stream)), "sgc_binarize")
     return out

@@ -219,9 +219,12 @@ __global__ __launch_bounds__(1024) void k_bin_resolve(int32_t nseg, int32_t mode
     }
 }
 
+// held: the residual holds val at the kept entries already (only the sent
+// side is written).
 __global__ __launch_bounds__(kBlock) void k_bin_apply_sbc(const int32_t* __restrict__ idx, const float* __restrict__ val,
                                                          int32_t nseg, BinWs w, float* __restrict__ res,
-                                                         int64_t n, int32_t* __restrict__ out_idx, int64_t cap)
+                                                         int64_t n, int32_t* __restrict__ out_idx, int64_t cap,
+                                                         int32_t held)
 {
     __shared__ uint32_t tmp[kBlock / 64 + 1];
     const int64_t nch = w.cpre[nseg];
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kBlock) void k_bin_apply_sbc(const int32_t* __restr
                     if (pos < cap) out_idx[pos] = id;
                     ++pos;
                     res[id] = v - mean;
-                } else {
+                } else if (!held) {
                     res[id] = v;
                 }
             }
@@ -274,7 +277,8 @@ __global__ __launch_bounds__(kBlock) void k_bin_apply_sbc(const int32_t* __restr
 // One thread per output word of 16 two-bit codes.
 __global__ __launch_bounds__(kBlock) void k_bin_apply_2bit(const int32_t* __restrict__ idx, const float* __restrict__ val,
                                                           int32_t nseg, BinWs w, float* __restrict__ res, int64_t n,
-                                                          int32_t* __restrict__ out_idx, uint32_t* __restrict__ codes)
+                                                          int32_t* __restrict__ out_idx, uint32_t* __restrict__ codes,
+                                                          int32_t held)
 {
     const int64_t total = w.estart[nseg];
     const int64_t nwords = cdiv(total, 16);
@@ -306,7 +310,8 @@ __global__ __launch_bounds__(kBlock) void k_bin_apply_2bit(const int32_t* __rest
             const uint32_t code = v > 0.0f ? 1u : v < 0.0f ? 2u : 0u;
             const float qv = code == 1u ? mp : code == 2u ? -mn : 0.0f;
             const int32_t id = ii[q];
-            if ((uint32_t)id < (uint32_t)n) res[id] = v - qv;
+            // code 0: v - (+0) is v itself, already there when held
+            if ((uint32_t)id < (uint32_t)n && (code != 0u || !held)) res[id] = v - qv;
             if (out_idx) out_idx[j] = id;
             word |= code << (2 * q);
         }
@@ -333,6 +338,8 @@ extern "C" int sgc_binarize(const sgc_layout* Lc, int32_t mode, const int32_t* i
                             sgc_stream_t stream)
 {
     sgc_layout* L = const_cast<sgc_layout*>(Lc);
+    const int32_t held = (mode & SGC_BIN_HELD) ? 1 : 0;
+    mode &= ~(int32_t)SGC_BIN_HELD;
     if (!L || (mode != SGC_BIN_SBC && mode != SGC_BIN_2BIT)) return SGC_EINVAL;
     if (cap < 0 || cap >= ((int64_t)1 << 31)) return SGC_EINVAL;
     if (!counts || !out_counts || !out_means || (L->n > 0 && !residual)) return SGC_EINVAL;
@@ -359,10 +366,10 @@ extern "C" int sgc_binarize(const sgc_layout* Lc, int32_t mode, const int32_t* i
     k_bin_resolve<<<1, 1024, 0, s>>>(nseg, mode, w, out_counts, out_means);
     SGC_LAUNCH_CHECK();
     if (mode == SGC_BIN_SBC) {
-        k_bin_apply_sbc<<<cb, kBlock, 0, s>>>(idx, val, nseg, w, residual, L->n, out_idx, cap);
+        k_bin_apply_sbc<<<cb, kBlock, 0, s>>>(idx, val, nseg, w, residual, L->n, out_idx, cap, held);
     } else {
         const unsigned wb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(cdiv(cap, 16), kBlock), 4096));
-        k_bin_apply_2bit<<<wb, kBlock, 0, s>>>(idx, val, nseg, w, residual, L->n, out_idx, out_codes);
+        k_bin_apply_2bit<<<wb, kBlock, 0, s>>>(idx, val, nseg, w, residual, L->n, out_idx, out_codes, held);
     }
     SGC_LAUNCH_CHECK();
     return SGC_OK;

@@ -107,6 +107,7 @@ struct CompressWs {
     int64_t* scal;     // [8]: 0 output total, 1 candidate total
     uint32_t* status;  // [1] used when the caller passes no dstatus
     uint32_t tcap;     // candidate slots per tile region (a power of two)
+    uint32_t hold;     // SGC_HOLD_KEPT: kept entries keep acc in the residual (nothing is zeroed)
 };
 
 struct CompressSizes {
@@ -245,7 +246,8 @@ __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ go
         if (mode == SGC_EXACT) {
             if (k > 0) {
                 if (s == m) {
-                    rlo = rhi = k;  // the probe read every element: its k-th key is the threshold
+                    rlo = k;  // the probe read every element: its k-th key is the threshold
+                    rhi = w.hold ? 0 : k;
                 } else {
                     // e: expected sampled keys above the true threshold.  The
                     // candidate bound takes a 6-sigma margin below it (a miss
@@ -260,6 +262,7 @@ __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ go
                     if (lo >= s) klo = 0;  // the bound would be the sample minimum: take every element
                     else rlo = lo;
                     if (hi >= 1) rhi = hi;
+                    if (w.hold) rhi = 0;  // no zeroing bound: nothing is zeroed
                 }
             }
         } else {
@@ -377,7 +380,7 @@ __device__ inline void resolve_group(const CompressWs& w, int64_t g, int64_t* tm
                         w.key_z[g >> 1] = key;
                     } else {
                         w.key_lo[g >> 1] = key;
-                        if (mode != SGC_EXACT) w.key_z[g >> 1] = key;
+                        if (mode != SGC_EXACT && !w.hold) w.key_z[g >> 1] = key;
                     }
                 }
                 break;
@@ -939,7 +942,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
                 if (p < cap) {
                     out_idx[p] = i;
                     out_val[p] = v;
-                    res[i] = 0.0f;
+                    if (!w.hold) res[i] = 0.0f;
                     if constexpr (M::on) m.u[i] = 0.0f;
                 }
             } else {
@@ -1127,7 +1130,7 @@ __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ re
                             out_idx[pos] = (int32_t)i;
                             out_val[pos] = x[j];
                         }
-                        if (!zeroed) {
+                        if (!zeroed && !w.hold) {
                             res[i] = 0.0f;
                             if constexpr (M::on) m.u[i] = 0.0f;  // momentum masking
                         }
@@ -1199,14 +1202,27 @@ extern "C" int sgc_set_pass_events(void* start, void* stop)
     return SGC_OK;
 }
 
+// The selection mode without the SGC_HOLD_KEPT flag.
+static int32_t base_mode(const sgc_compress_opts* o) { return o->mode & ~(int32_t)SGC_HOLD_KEPT; }
+
 static bool opts_ok(const sgc_layout* L, const sgc_compress_opts* o)
 {
     if (!L || !o) return false;
-    if (o->mode != SGC_EXACT && o->mode != SGC_SAMPLED && o->mode != SGC_ACCUMULATE_ONLY) return false;
+    const int32_t bm = base_mode(o);
+    if (bm != SGC_EXACT && bm != SGC_SAMPLED && bm != SGC_ACCUMULATE_ONLY) return false;
+    if ((o->mode & SGC_HOLD_KEPT) && bm == SGC_ACCUMULATE_ONLY) return false;
     if (o->scope != SGC_GLOBAL && o->scope != SGC_PER_SEGMENT) return false;
     if (o->keep_ppm > 1000000) return false;
-    if (o->mode == SGC_SAMPLED && o->sample_div == 0) return false;
+    if (bm == SGC_SAMPLED && o->sample_div == 0) return false;
     return true;
+}
+
+// The options with the flag taken out of the mode (the kernels see it in CompressWs::hold).
+static sgc_compress_opts plain_opts(const sgc_compress_opts* o)
+{
+    sgc_compress_opts p = *o;
+    p.mode = base_mode(o);
+    return p;
 }
 
 static size_t workspace_bytes(const sgc_layout* L, const sgc_compress_opts* o, bool mom)
@@ -1221,22 +1237,23 @@ static size_t workspace_bytes(const sgc_layout* L, const sgc_compress_opts* o, b
 extern "C" size_t sgc_compress_workspace(const sgc_layout* L, const sgc_compress_opts* o, int64_t cap)
 {
     if (!opts_ok(L, o) || cap < 0) return 0;
-    if (o->mode == SGC_ACCUMULATE_ONLY) return 0;
-    return workspace_bytes(L, o, false);
+    const sgc_compress_opts p = plain_opts(o);
+    if (p.mode == SGC_ACCUMULATE_ONLY) return 0;
+    return workspace_bytes(L, &p, false);
 }
 
 extern "C" size_t sgc_compress_momentum_workspace(const sgc_layout* L, const sgc_compress_opts* o, int64_t cap)
 {
-    if (!opts_ok(L, o) || cap < 0) return 0;
+    if (!opts_ok(L, o) || cap < 0 || (o->mode & SGC_HOLD_KEPT)) return 0;
     if (o->mode == SGC_ACCUMULATE_ONLY) return 0;
     return workspace_bytes(L, o, true);
 }
 
 // The compress step, plain (NoMom) or with momentum correction (Mom).
 template <typename M>
-static int compress_impl(sgc_layout* L, const sgc_compress_opts* o, M m, const float* grad, float* residual,
-                         int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts, uint32_t* dstatus,
-                         void* ws, size_t ws_bytes, hipStream_t s)
+static int compress_impl(sgc_layout* L, const sgc_compress_opts* o, bool hold, M m, const float* grad,
+                         float* residual, int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts,
+                         uint32_t* dstatus, void* ws, size_t ws_bytes, hipStream_t s)
 {
     if (o->mode == SGC_ACCUMULATE_ONLY) {
         if (L->n == 0) return SGC_OK;
@@ -1259,6 +1276,7 @@ static int compress_impl(sgc_layout* L, const sgc_compress_opts* o, M m, const f
     Carver c(ws);
     CompressWs w;
     carve_compress(c, z, o->mode, M::on, &w);
+    w.hold = hold ? 1u : 0u;
 
     DevTables* dt = nullptr;
     int rc = device_tables(L, &dt);
@@ -1338,8 +1356,9 @@ extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, co
     sgc_layout* L = const_cast<sgc_layout*>(Lc);
     if (!opts_ok(L, o)) return SGC_EINVAL;
     if ((L->n > 0 && (!grad || !residual)) || !aligned16(grad) || !aligned16(residual)) return SGC_EINVAL;
-    return compress_impl(L, o, NoMom{0.0f, nullptr}, grad, residual, out_idx, out_val, cap, out_counts, dstatus, ws,
-                         ws_bytes, (hipStream_t)stream);
+    const sgc_compress_opts p = plain_opts(o);
+    return compress_impl(L, &p, (o->mode & SGC_HOLD_KEPT) != 0, NoMom{0.0f, nullptr}, grad, residual, out_idx,
+                         out_val, cap, out_counts, dstatus, ws, ws_bytes, (hipStream_t)stream);
 }
 
 extern "C" int sgc_compress_momentum(const sgc_layout* Lc, const sgc_compress_opts* o, float beta, const float* grad,
@@ -1349,9 +1368,10 @@ extern "C" int sgc_compress_momentum(const sgc_layout* Lc, const sgc_compress_op
 {
     sgc_layout* L = const_cast<sgc_layout*>(Lc);
     if (!opts_ok(L, o) || !std::isfinite(beta)) return SGC_EINVAL;
+    if (o->mode & SGC_HOLD_KEPT) return SGC_EUNSUPPORTED;  // momentum masking writes the sent entries anyway
     if ((L->n > 0 && (!grad || !residual || !momentum)) || !aligned16(grad) || !aligned16(residual) ||
         !aligned16(momentum))
         return SGC_EINVAL;
-    return compress_impl(L, o, Mom{beta, momentum}, grad, residual, out_idx, out_val, cap, out_counts, dstatus, ws,
-                         ws_bytes, (hipStream_t)stream);
+    return compress_impl(L, o, false, Mom{beta, momentum}, grad, residual, out_idx, out_val, cap, out_counts, dstatus,
+                         ws, ws_bytes, (hipStream_t)stream);
 }

@@ -68,6 +68,7 @@ extern "C" {
 #define SGC_EXACT 0           /* exact top-k, lower index wins ties */
 #define SGC_SAMPLED 1         /* threshold estimated from a systematic sample, every |acc| >= T kept */
 #define SGC_ACCUMULATE_ONLY 2 /* communication delay: r <- r + g only */
+#define SGC_HOLD_KEPT 0x10    /* flag for SGC_EXACT / SGC_SAMPLED: kept entries keep acc in the residual */
 
 /* Selection / stream scope. */
 #define SGC_GLOBAL 0      /* one selection (one Rice stream) over the whole vector */
@@ -76,6 +77,7 @@ extern "C" {
 /* Binarize modes. */
 #define SGC_BIN_SBC 0  /* sparse binarization: one signed mean per segment, one sign side sent */
 #define SGC_BIN_2BIT 1 /* ternary 2-bit codes {0, +mean_pos, -mean_neg} per kept value */
+#define SGC_BIN_HELD 0x10 /* flag: the residual holds acc (= val) at the kept entries, not +0 */
 
 /* Received message formats. */
 #define SGC_MSG_RAW_F32 0     /* idx[] + val[] */
@@ -141,6 +143,12 @@ int32_t sgc_abi_version(void);
  *   then the total.
  *   SGC_ACCUMULATE_ONLY: residual <- fp32(residual + grad); the out_*, ws
  *   and dstatus arguments are ignored and may be NULL.
+ *   SGC_HOLD_KEPT (or-ed into SGC_EXACT or SGC_SAMPLED): the kept entries
+ *   keep acc in the residual instead of +0; everything else is unchanged.
+ *   For a caller that binarizes next (sgc_binarize with SGC_BIN_HELD), which
+ *   then writes only the residual entries binarization changes -- half the
+ *   scattered writes of the two calls without the flags.  Not accepted by
+ *   sgc_compress_momentum (SGC_EUNSUPPORTED).
  *
  * grad [device, n fp32] is read; residual [device, n fp32] is updated in
  * place.  cap = capacity of out_idx/out_val; SGC_EXACT requires cap >= the
@@ -209,8 +217,11 @@ int sgc_compress_momentum(const sgc_layout* layout, const sgc_compress_opts* opt
  *     counts; out_idx (may be NULL) receives a copy of idx.
  *     residual[i] <- fp32(v - value).
  * residual [device, n] must hold +0 at the kept positions (as compress
- * leaves it).  Means match a sequential double-precision sum within 1 ulp
- * of fp32 (the summation order differs).                                   */
+ * leaves it), or -- with SGC_BIN_HELD or-ed into mode -- acc, that is val,
+ * at the kept positions (as compress with SGC_HOLD_KEPT leaves it); the
+ * result is the same, and only the entries whose value changes are written
+ * (SBC: the sent side; 2-bit: codes 1 and 2).  Means match a sequential
+ * double-precision sum within 1 ulp of fp32 (the summation order differs). */
 size_t sgc_binarize_workspace(const sgc_layout* layout, int64_t cap);
 int sgc_binarize(const sgc_layout* layout, int32_t mode,
                  const int32_t* idx, const float* val, const int64_t* counts, int64_t cap,

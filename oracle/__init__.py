@@ -131,6 +131,11 @@ class Sparse:
     status: int = 0
 
 
+def hold_kept(sp: Sparse, r: np.ndarray) -> None:
+    """The residual as a compress with the hold flag leaves it: the sent entries keep acc."""
+    r[sp.idx] = sp.val
+
+
 def compress_exact(g, r: np.ndarray, seg_off, scope: int, ppm: int, cap: Optional[int] = None) -> Sparse:
     g = _f32(g)
     seg_off = np.ascontiguousarray(seg_off, dtype=np.int64)
@@ -182,6 +187,13 @@ class Binarized:
     counts: np.ndarray
     means: np.ndarray
     codes: Optional[np.ndarray]
+
+
+def binarize_held(sp: Sparse, nseg: int, mode: int, r: np.ndarray) -> Binarized:
+    """Binarize when the residual holds acc (= val) at the kept entries: by definition the same as
+    zeroing them first and binarizing as usual."""
+    r[sp.idx] = 0.0
+    return binarize(sp, nseg, mode, r)
 
 
 def binarize(sp: Sparse, nseg: int, mode: int, r: np.ndarray) -> Binarized:

@@ -114,6 +114,26 @@ def test_compress_momentum_validation():
     assert call(opt=sgc.CompressOpts(7, 0, 10000, 1000, 1)) == sgc.EINVAL
     assert call(wsb=need - 1) == sgc.ENOSPC
     assert lib.sgc_compress_momentum_workspace(lay.handle, C.byref(sgc.CompressOpts(9, 0, 1, 1, 1)), 5) == 0
+    held = sgc.CompressOpts(sgc.EXACT | sgc.HOLD_KEPT, sgc.GLOBAL, 10000, 1000, 65536)
+    assert call(opt=held) == sgc.EUNSUPPORTED
+    assert lib.sgc_compress_momentum_workspace(lay.handle, C.byref(held), k) == 0
+
+
+def test_hold_flag_validation():
+    lib = sgc.lib()
+    lay = sgc.Layout([1000, 24])
+    k = lay.keep_total(sgc.GLOBAL, 10000)
+    plain = sgc.CompressOpts(sgc.EXACT, sgc.GLOBAL, 10000, 1000, 65536)
+    held = sgc.CompressOpts(sgc.EXACT | sgc.HOLD_KEPT, sgc.GLOBAL, 10000, 1000, 65536)
+    held_s = sgc.CompressOpts(sgc.SAMPLED | sgc.HOLD_KEPT, sgc.GLOBAL, 10000, 1000, 65536)
+    bad = sgc.CompressOpts(sgc.ACCUMULATE_ONLY | sgc.HOLD_KEPT, sgc.GLOBAL, 10000, 1000, 65536)
+    need = lib.sgc_compress_workspace(lay.handle, C.byref(plain), k)
+    assert lib.sgc_compress_workspace(lay.handle, C.byref(held), k) == need
+    assert lib.sgc_compress_workspace(lay.handle, C.byref(held_s), k) > 0
+    assert lib.sgc_compress_workspace(lay.handle, C.byref(bad), k) == 0
+    assert lib.sgc_compress(lay.handle, C.byref(bad), A, A, A, A, k, A, None, A, need, None) == sgc.EINVAL
+    bneed = lib.sgc_binarize_workspace(lay.handle, 10)
+    assert lib.sgc_binarize(lay.handle, 2 | sgc.BIN_HELD, A, A, A, 10, A, A, A, A, A, A, bneed, None) == sgc.EINVAL
 
 
 def test_binarize_validation():

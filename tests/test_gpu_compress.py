@@ -231,3 +231,43 @@ def test_stale_workspace(orc, fill):
         nw = int(oenc.word_off[-1])
         assert_bitwise(host(enc.words).view(np.uint32)[:nw], oenc.words, "words")
         assert_bitwise(host(enc.chunk_off).view(np.uint64)[:oenc.chunk_off.size], oenc.chunk_off, "chunk table")
+
+
+@pytest.mark.parametrize("mode", [sgc.EXACT, sgc.SAMPLED])
+@pytest.mark.parametrize("bmode", [sgc.BIN_SBC, sgc.BIN_2BIT])
+@pytest.mark.parametrize("scope", [0, 1])
+def test_hold_then_held_binarize(orc, mode, bmode, scope):
+    # compress with the hold flag leaves acc at the kept entries; binarize with the held flag then
+    # gives exactly what compress + binarize without the flags give, writing half as much
+    rng = np.random.default_rng(41)
+    layout = sgc.Layout([1 << 20, 300001, 4096, 77])
+    n = layout.n
+    seg_off = np.array(layout.seg_off, np.int64)
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    r0 = rng.laplace(0, 1e-3, n).astype(np.float32)
+    cap = None if mode == sgc.EXACT else 40000
+    announce(f"hold/held mode={mode} bmode={bmode} scope={scope}")
+    outs = []
+    for hold in (False, True):
+        rd = dev(r0)
+        comp = sgc.compress(layout, dev(g), rd, mode=mode, scope=scope, keep_ppm=10000, cap=cap, hold=hold)
+        torch.cuda.synchronize()
+        if hold:  # the residual after compress: acc at the sent entries
+            r_ref = r0.copy()
+            ref = (orc.compress_exact(g, r_ref, seg_off, scope, 10000, cap=comp.cap) if mode == sgc.EXACT else
+                   orc.compress_sampled(g, r_ref, seg_off, scope, 10000, comp.cap))
+            orc.hold_kept(ref, r_ref)
+            assert_bitwise(host(rd), r_ref, "held residual after compress")
+        bn = sgc.binarize(layout, comp, rd, bmode, held=hold)
+        torch.cuda.synchronize()
+        outs.append((host(rd), host(bn.counts), host(bn.means),
+                     host(bn.idx)[:int(host(bn.counts)[-1])] if bn.idx is not None else None,
+                     host(bn.codes) if bn.codes is not None else None))
+    (r1, c1, m1, i1, k1), (r2, c2, m2, i2, k2) = outs
+    assert_bitwise(r2, r1, "residual after binarize")
+    assert_bitwise(c2, c1, "counts")
+    assert_bitwise(m2, m1, "means")
+    if i1 is not None:
+        assert_bitwise(i2, i1, "sent indices")
+    if k1 is not None:
+        assert_bitwise(k2, k1, "2-bit codes")
