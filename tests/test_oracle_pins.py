@@ -304,6 +304,28 @@ def test_momentum_invariants_over_steps(orc):
         assert np.all(u[keep].view(np.uint32) == 0)
 
 
+def test_hold_kept_then_held_binarize_equals_plain_pair(orc):
+    # the hold flag only defers the residual write of the sent entries: with acc held there, the
+    # held binarize must give the residual the plain pair gives, and the held residual itself is
+    # acc at the sent entries and the plain residual elsewhere
+    rng = np.random.default_rng(8)
+    n = 40000
+    seg_off = np.array([0, 15000, 15001, n], np.int64)
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    r0 = rng.laplace(0, 1e-3, n).astype(np.float32)
+    acc = (r0 + g).astype(np.float32)
+    for mode in (orc.BIN_SBC, orc.BIN_2BIT):
+        ra, rb = r0.copy(), r0.copy()
+        spa = orc.compress_exact(g, ra, seg_off, orc.PER_SEGMENT, 10000)
+        spb = orc.compress_exact(g, rb, seg_off, orc.PER_SEGMENT, 10000)
+        orc.hold_kept(spb, rb)
+        assert np.array_equal(rb.view(np.uint32), acc.view(np.uint32))
+        ba = orc.binarize(spa, 3, mode, ra)
+        bb = orc.binarize_held(spb, 3, mode, rb)
+        assert np.array_equal(ra.view(np.uint32), rb.view(np.uint32))
+        assert np.array_equal(ba.means.view(np.uint32), bb.means.view(np.uint32))
+
+
 # ------------------------------------------------------------ sampled mode
 def test_sampled_full_sample_is_superlevel_set(orc):
     rng = np.random.default_rng(11)
