@@ -552,10 +552,20 @@ __global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg)
 //     barrier between steps (usually none is needed);
 // and the tile is stored once (coalesced).  Every element receives its
 // values in message order, so the result does not depend on scheduling.
+// One mask serves every tile: it is cleared after its last read, and a
+// barrier separates that clear from the next tile's marks.
+//
+// Tiles are 8192 elements: the fixed cost per tile (its barriers and
+// bookkeeping) is what bounds the merge at low densities, and halving the
+// tile count took 16 x 0.1% onto zeros from 1.09 to 0.93 ms.  kPre = 8 holds
+// a message's share of a tile at 1% (82 entries on average) in 16 threads.
+// The kernel is built twice: without initial contents to load (sums onto
+// zeros) it needs no registers for them and runs three workgroups per CU
+// (the LDS limit); with them, two.
 //
 // Software pipeline: while tile u is worked on, the entries and initial
-// contents of tile u+1 (and the entry-range bound of tile u+2) are already in
-// flight in registers.  In each iteration the stores of the previous tile are
+// contents of tile u+1 (LOAD only; and the entry-range bound of tile u+2) are
+// already in flight in registers.  In each iteration the stores of the previous tile are
 // issued before the next loads: loads and stores share one completion
 // counter here, so a wait for loads also waits for earlier stores, and
 // those are then long done.  A tile whose entries do not fit the prefetch (a
@@ -563,7 +573,7 @@ __global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg)
 // kRound in all) is applied from memory instead, in rounds of kRound entries
 // taken in message order.
 constexpr int kMergeThreads = 256;                          // threads per merge workgroup
-constexpr int kPre = 4;                                     // entries per thread per tile (or round)
+constexpr int kPre = 8;                                     // entries per thread per tile (or round)
 constexpr int kRound = kPre * kMergeThreads;                // entries per round
 constexpr int kQ = (int)(kOutTile / (4 * kMergeThreads));  // 16-byte words per thread in a tile
 constexpr int kMaskWords = (int)(kOutTile / 2) / kMergeThreads;  // mask words each thread clears
@@ -571,7 +581,7 @@ static_assert(kMerge <= 16, "message masks are 16 bits");
 
 struct MergeLds {
     float tile[kOutTile];
-    uint32_t mask[2][kOutTile / 2];  // per tile parity: 16-bit message mask per position, two per word
+    uint32_t mask[kOutTile / 2];  // 16-bit message mask per position, two per word
     int32_t a[2][kMerge], cnt[2][kMerge];
     int32_t total[3], fits[3], maxc[3];  // per tile, by tile index mod 3
 };
@@ -607,8 +617,9 @@ __device__ inline void mark_entries(uint32_t* mask, const int32_t (&k)[kPre], co
         if (p[i] >= 0) atomicOr(&mask[p[i] >> 1], (1u << k[i]) << (16 * (p[i] & 1)));
 }
 
-// Steps 2 and 3, after a barrier that follows the marks.  Ends with a
-// barrier after the last addition; the mask is cleared afterwards.
+// Steps 2 and 3, after a barrier that follows the marks.  The mask is
+// cleared after the barrier that ends its reads; the function ends with a
+// barrier after both the last addition and the clear.
 __device__ inline void add_entries(MergeLds& S, uint32_t* mask, int z, const int32_t (&k)[kPre],
                                    const int32_t (&p)[kPre], const float (&v)[kPre])
 {
@@ -627,6 +638,7 @@ __device__ inline void add_entries(MergeLds& S, uint32_t* mask, int z, const int
     __syncthreads();
     clear_mask(mask);  // every read of the mask is done
     const int32_t depth = S.maxc[z];  // uniform
+    if (depth == 1) __syncthreads();  // the clear ends before the next marks
     for (int32_t r = 1; r < depth; ++r) {
 #pragma unroll
         for (int i = 0; i < kPre; ++i)
@@ -639,6 +651,7 @@ __device__ inline void add_entries(MergeLds& S, uint32_t* mask, int z, const int
 // is unconditional.
 __device__ int32_t g_zero_word = 0;
 
+template <bool LOAD>
 __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t lg_tpm, int32_t init,
                                                  const float* __restrict__ base, float* __restrict__ out, int64_t n,
                                                  int64_t ntiles, int64_t per)
@@ -687,7 +700,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         for (int q = 0; q < kQ; ++q) {
             const int i = 4 * (q * kMergeThreads + tid);
             f4a v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (init != SGC_INIT_ZERO) {
+            if (LOAD) {
                 if (cnt == kOutTile) {
                     v = *(const f4a*)(src + lo + i);
                 } else {
@@ -706,8 +719,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         S.a[T0 & 1][mk] = a_cur;
         S.cnt[T0 & 1][mk] = span(a_cur, a_nxt);
     }
-    clear_mask(S.mask[0]);
-    clear_mask(S.mask[1]);
+    clear_mask(S.mask);
     load_tile(T0, a_cur, span(a_cur, a_nxt));
     __syncthreads();
     if (tid < 64) tile_meta(S, (int)(T0 & 1), (int)(T0 % 3), M.n, kPre * tpm);
@@ -734,7 +746,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
             cp[i] = (n_pos[i] >= 0 && (uint32_t)q < (uint32_t)cnt) ? q : -1;  // always inside, for a clean message
             cv[i] = n_val[i];
         }
-        mark_entries(S.mask[b], ck, cp);
+        mark_entries(S.mask, ck, cp);
         // the next tile in flight: its range bound, entries and initial contents
         const int32_t r_n3 = ts_load(u + 3);  // clamped at the end of the iteration
         if (u + 1 < T1) {
@@ -750,10 +762,10 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         if (total == 0) {
             // nothing to add (and nothing was marked)
         } else if (fits) {
-            add_entries(S, S.mask[b], z, ck, cp, cv);
+            add_entries(S, S.mask, z, ck, cp, cv);
         } else {
             // from memory, kRound entries at a time in message order
-            clear_mask(S.mask[b]);  // drop the marks of the prefetched share
+            clear_mask(S.mask);  // drop the marks of the prefetched share
             __syncthreads();
             for (int32_t R0 = 0; R0 < total; R0 += kRound) {
 #pragma unroll
@@ -771,9 +783,9 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
                     cp[i] = (uint32_t)q < (uint32_t)cnt ? q : -1;
                     cv[i] = M.val[k][j];
                 }
-                mark_entries(S.mask[b], ck, cp);
+                mark_entries(S.mask, ck, cp);
                 __syncthreads();
-                add_entries(S, S.mask[b], z, ck, cp, cv);
+                add_entries(S, S.mask, z, ck, cp, cv);
                 __syncthreads();  // mask cleared, depth read: the next round may start
                 if (tid == 0) S.maxc[z] = 1;
             }
@@ -814,11 +826,12 @@ __global__ void k_fold_status(MergeBatch M, uint32_t* status)
 using namespace sgc;
 
 // Persistent merge workgroups: as many as are resident at once on the device.
+template <bool LOAD>
 static int64_t merge_blocks()
 {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_merge, kMergeThreads, 0) != hipSuccess || cus <= 0 || per_cu <= 0)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_merge<LOAD>, kMergeThreads, 0) != hipSuccess || cus <= 0 || per_cu <= 0)
         return 1024;
     return (int64_t)cus * per_cu;
 }
@@ -943,10 +956,14 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         int32_t lg_tpm = 0;
         while ((1 << (lg_tpm + 1)) <= kMergeThreads) ++lg_tpm;
         while (lg_tpm > 0 && (kMergeThreads >> lg_tpm) < M.n) --lg_tpm;
-        const int64_t per = cdiv(ntiles, std::min<int64_t>(ntiles, merge_blocks()));
+        const int32_t im = mb == 0 ? init : SGC_INIT_INPLACE;
+        const bool load = im != SGC_INIT_ZERO;
+        const int64_t per = cdiv(ntiles, std::min<int64_t>(ntiles, load ? merge_blocks<true>() : merge_blocks<false>()));
         const int64_t grid = cdiv(ntiles, per);
-        k_merge<<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, mb == 0 ? init : SGC_INIT_INPLACE, base, out, L->n,
-                                                  ntiles, per);
+        if (load)
+            k_merge<true><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles, per);
+        else
+            k_merge<false><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles, per);
         SGC_LAUNCH_CHECK();
         if (dstatus && M.n > 0) {
             k_fold_status<<<1, 64, 0, s>>>(M, dstatus);

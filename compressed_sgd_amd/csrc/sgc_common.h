@@ -52,8 +52,8 @@ constexpr int kBins = 2048;
 constexpr int64_t kEncCodes = 2048;
 constexpr int kEncAhead = 32;
 // Dense output tile of decode-accumulate.
-constexpr int64_t kOutTile = 4096;
-constexpr int kOutTileLog = 12;
+constexpr int64_t kOutTile = 8192;
+constexpr int kOutTileLog = 13;
 static_assert(kOutTile == (int64_t)1 << kOutTileLog, "output tile size");
 
 constexpr uint32_t kNoKey = 0x80000000u;  // above every 31-bit magnitude key
