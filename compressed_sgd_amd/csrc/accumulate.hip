@@ -559,6 +559,8 @@ __global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg)
 // bookkeeping) is what bounds the merge at low densities, and halving the
 // tile count took 16 x 0.1% onto zeros from 1.09 to 0.93 ms.  kPre = 8 holds
 // a message's share of a tile at 1% (82 entries on average) in 16 threads.
+// The output and the initial contents are streamed with non-temporal
+// stores and loads (each is touched once; 3-5% faster than plain ones).
 // The kernel is built twice: without initial contents to load (sums onto
 // zeros) it needs no registers for them and runs three workgroups per CU
 // (the LDS limit); with them, two.
@@ -702,7 +704,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
             f4a v = {0.0f, 0.0f, 0.0f, 0.0f};
             if (LOAD) {
                 if (cnt == kOutTile) {
-                    v = *(const f4a*)(src + lo + i);
+                    v = __builtin_nontemporal_load((const f4a*)(src + lo + i));
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
@@ -734,7 +736,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
             const int i = 4 * (q * kMergeThreads + tid);
             const f4a pt = *(const f4a*)(S.tile + i);
             *(f4a*)(S.tile + i) = ini[q];
-            if (u > T0) *(f4a*)(out + lo - kOutTile + i) = pt;
+            if (u > T0) __builtin_nontemporal_store(pt, (f4a*)(out + lo - kOutTile + i));
         }
         // this tile's entries, out of the pipeline registers, mark their messages
         int32_t ck[kPre], cp[kPre];
@@ -803,7 +805,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         const int i = 4 * (q * kMergeThreads + tid);
         const f4a r = *(const f4a*)(S.tile + i);
         if (cnt == kOutTile) {
-            *(f4a*)(out + lo + i) = r;
+            __builtin_nontemporal_store(r, (f4a*)(out + lo + i));
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)

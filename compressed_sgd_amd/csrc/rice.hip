@@ -12,12 +12,13 @@
 //  1. lengths: per block the sum of code lengths;
 //  2. scan:    block bit offsets (flat scan), stream bit counts and word
 //              offsets (streams start on word boundaries);
-//  3. pack:    per block, code offsets in LDS, then every output word whose
-//              first bit lies in the block is assembled by one thread from
-//              the codes that overlap it (binary search in LDS, plus up to
-//              32 look-ahead codes of the next block): plain stores, no
-//              atomics, no pre-zeroing; the chunk table (bit offset and
-//              position reached for every 256th code) is written on the way.
+//  3. pack:    per block, code offsets by one block scan; every code ORs
+//              its bits into an LDS copy of the output words whose first
+//              bit lies in the block (plus up to 32 look-ahead codes of the
+//              next block, which complete the last word), and the words are
+//              stored once, coalesced: no global atomics, no pre-zeroing.
+//              The chunk table (bit offset and position reached for every
+//              256th code) is written on the way.
 #include "sgc_common.h"
 
 namespace sgc {
@@ -205,8 +206,45 @@ __global__ __launch_bounds__(1024) void k_enc_scan(int32_t S, int64_t word_cap, 
 
 constexpr int kEncLds = (int)kEncCodes + kEncAhead;
 constexpr int kEncPer = (kEncLds + kBlock - 1) / kBlock;  // entries per thread in the LDS prefix
-constexpr int kEncMapWords = 1024;  // words of a block whose first code is looked up in LDS
-static_assert(kEncLds <= 65536, "first-code map holds 16-bit code numbers");
+constexpr int kEncBufWords = 2048;  // LDS words a block assembles its output words in
+static_assert(kEncBufWords % (4 * kBlock) == 0, "the word buffer is cleared in 16-byte stores");
+
+typedef uint32_t u4e __attribute__((ext_vector_type(4)));
+
+// OR v into buffer word k unless it is zero or not the block's.
+__device__ inline void enc_or(uint32_t* buf, int64_t k, int32_t nbuf, uint32_t v)
+{
+    if (v && k >= 0 && k < nbuf) atomicOr(&buf[k], v);
+}
+
+// The code of gap z placed at aligned bit a: buffer word k holds aligned bits
+// [32 (k + m0), 32 (k + m0) + 32).  A code of at most 33 bits is one shifted
+// 64-bit pattern over two words; a longer one (long unary run) fills its
+// words one by one, clamped to the block's words.
+__device__ inline void enc_put(uint32_t* buf, uint64_t a, uint32_t z, uint32_t b, int32_t m0, int32_t nbuf)
+{
+    const uint32_t q = z >> b;
+    const uint64_t rem = z & ((1u << b) - 1u);
+    const int64_t m = (int64_t)(a >> 5) - m0;
+    if (q + 1 + b <= 33) {
+        const uint64_t p = (((1ull << q) - 1ull) | (rem << (q + 1))) << (uint32_t)(a & 31);
+        enc_or(buf, m, nbuf, (uint32_t)p);
+        enc_or(buf, m + 1, nbuf, (uint32_t)(p >> 32));
+        return;
+    }
+    const uint64_t e = a + q;  // one-bits [a, e), the zero at e, the low bits after it
+    const int64_t k0 = max(m, (int64_t)0), k1 = min((int64_t)((e - 1) >> 5) - m0, (int64_t)nbuf - 1);
+    for (int64_t k = k0; k <= k1; ++k) {
+        const uint64_t w0 = (uint64_t)(k + m0) * 32;
+        const uint64_t lo = a > w0 ? a : w0, hi = e < w0 + 32 ? e : w0 + 32;
+        const uint32_t nb = (uint32_t)(hi - lo);
+        atomicOr(&buf[k], (nb >= 32 ? 0xffffffffu : ((1u << nb) - 1u)) << (uint32_t)(lo - w0));
+    }
+    const uint64_t p = rem << (uint32_t)((e + 1) & 31);
+    const int64_t mr = (int64_t)((e + 1) >> 5) - m0;
+    enc_or(buf, mr, nbuf, (uint32_t)p);
+    enc_or(buf, mr + 1, nbuf, (uint32_t)(p >> 32));
+}
 
 __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__ idx, int32_t S, int32_t b, EncWs w,
                                                     uint32_t* __restrict__ words, const uint64_t* __restrict__ word_off,
@@ -214,7 +252,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
 {
     __shared__ uint32_t zs[kEncLds];
     __shared__ uint32_t off[kEncLds + 1];
-    __shared__ uint16_t wmap[kEncMapWords];
+    __shared__ __align__(16) uint32_t buf[kEncBufWords];
     __shared__ uint32_t tmp[kBlock / 64 + 1];
     if (w.bad[0] & 2u) return;
     const int64_t neb = w.ebpre[S];
@@ -227,6 +265,10 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
         const int64_t q0 = k.e0 - st.first;               // stream-relative index of the first code
         const int64_t chpre = w.chpre[k.s];
         uint32_t* sw = words + word_off[k.s];
+        // the word buffer starts clear (the previous block's last barrier has passed)
+#pragma unroll
+        for (int q = 0; q < kEncBufWords / (4 * kBlock); ++q)
+            *(u4e*)&buf[4 * (q * kBlock + threadIdx.x)] = u4e{0u, 0u, 0u, 0u};
         // gaps into LDS (coalesced, clamped, unconditional loads), then code
         // lengths thread-contiguous so that the prefix is one block scan
         {
@@ -245,41 +287,73 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
             }
         }
         __syncthreads();
-        uint32_t len[kEncPer];
+        uint32_t zq[kEncPer], oq[kEncPer];
         uint32_t local = 0;
 #pragma unroll
         for (int q = 0; q < kEncPer; ++q) {
             const int i = threadIdx.x * kEncPer + q;
-            len[q] = i < ntot ? (zs[i] >> b) + 1 + (uint32_t)b : 0u;
-            local += len[q];
+            zq[q] = i < ntot ? zs[i] : 0u;
+            oq[q] = local;
+            local += i < ntot ? (zq[q] >> b) + 1 + (uint32_t)b : 0u;
         }
         uint32_t tot;
-        uint32_t run = block_exclusive_scan<uint32_t>(local, tmp, &tot);
+        const uint32_t run = block_exclusive_scan<uint32_t>(local, tmp, &tot);
 #pragma unroll
         for (int q = 0; q < kEncPer; ++q) {
             const int i = threadIdx.x * kEncPer + q;
-            if (i < ntot) {
-                off[i] = run;
-                run += len[q];
-            }
+            oq[q] += run;
+            if (i < ntot) off[i] = oq[q];
         }
         if (threadIdx.x == kBlock - 1) off[ntot] = tot;  // ntot <= kEncLds
         __syncthreads();
         const uint64_t B1 = B0 + off[nown];
         const uint64_t wfirst = (B0 + 31) / 32, wend = (B1 + 31) / 32;
-        // first code of every word that starts in the block (the code holding
-        // the word's first bit), scattered by the codes themselves when the
-        // block's words fit the map; else found by binary search
-        const bool mapped = wend - wfirst <= (uint64_t)kEncMapWords;  // uniform
-        if (mapped) {
+        // The block writes every word whose first bit lies in it (the next
+        // block's first codes complete the last one).  Usually each code ORs
+        // its bits into those words in LDS and the words are stored once;
+        // a block whose words exceed the buffer has each word assembled by
+        // one thread from the codes that overlap it instead.
+        if (wend - wfirst <= (uint64_t)kEncBufWords) {  // uniform
+            const uint32_t h = (uint32_t)(B0 & 31);  // aligned bit 0 is stream bit B0 - h
+            const int32_t m0 = h ? 1 : 0, nbuf = (int32_t)(wend - wfirst);
 #pragma unroll
-            for (int q = 0; q < kEncPer; ++q) {
-                const int i = threadIdx.x * kEncPer + q;
-                if (i < nown)
-                    for (uint64_t wd = (B0 + off[i] + 31) / 32; wd * 32 < B0 + off[i + 1]; ++wd)
-                        wmap[wd - wfirst] = (uint16_t)i;
-            }
+            for (int q = 0; q < kEncPer; ++q)
+                if (threadIdx.x * kEncPer + q < ntot) enc_put(buf, (uint64_t)oq[q] + h, zq[q], (uint32_t)b, m0, nbuf);
             __syncthreads();
+            for (int32_t i = threadIdx.x; i < nbuf; i += kBlock) sw[wfirst + i] = buf[i];
+        } else {
+            for (uint64_t wd = wfirst + threadIdx.x; wd < wend; wd += kBlock) {
+                const uint64_t W0 = wd * 32;
+                // first code whose end lies past W0 (its start is <= W0 or it is code 0)
+                int lo = 0, hi = ntot - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (B0 + off[mid + 1] <= W0) lo = mid + 1; else hi = mid;
+                }
+                uint32_t v = 0;
+                for (int i = lo; i < ntot; ++i) {
+                    const uint64_t o = B0 + off[i];
+                    if (o >= W0 + 32) break;
+                    const uint32_t z = zs[i];
+                    const uint64_t q = z >> b;
+                    // unary one-bits [o, o+q)
+                    const uint64_t a0 = o > W0 ? o : W0;
+                    const uint64_t a1 = (o + q) < (W0 + 32) ? (o + q) : (W0 + 32);
+                    if (a0 < a1) {
+                        const uint32_t nbit = (uint32_t)(a1 - a0);
+                        const uint32_t m = nbit >= 32 ? 0xffffffffu : ((1u << nbit) - 1u);
+                        v |= m << (uint32_t)(a0 - W0);
+                    }
+                    // remainder bits start after the terminating zero
+                    if (b > 0) {
+                        const int64_t sh = (int64_t)(o + q + 1) - (int64_t)W0;
+                        const uint64_t rem = (uint64_t)(z & ((1u << b) - 1u));
+                        if (sh >= 0 && sh < 32) v |= (uint32_t)(rem << sh);
+                        else if (sh < 0 && -sh < b) v |= (uint32_t)(rem >> (-sh));
+                    }
+                }
+                sw[wd] = v;
+            }
         }
         // chunk table: (bit offset, stream position reached before the code) of
         // every SGC_CHUNK_CODES-th code
@@ -289,43 +363,6 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
             const int32_t before = idx[j > st.first ? j - 1 : j];  // unconditional load
             chunk_off[2 * c] = B0 + off[i];
             chunk_off[2 * c + 1] = j == st.first ? 0 : (uint64_t)((int64_t)before - st.base + 1);
-        }
-        for (uint64_t wd = wfirst + threadIdx.x; wd < wend; wd += kBlock) {
-            const uint64_t W0 = wd * 32;
-            // first code whose end lies past W0 (its start is <= W0 or it is code 0)
-            int lo = 0;
-            if (mapped) {
-                lo = wmap[wd - wfirst];
-            } else {
-                int hi = ntot - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (B0 + off[mid + 1] <= W0) lo = mid + 1; else hi = mid;
-                }
-            }
-            uint32_t v = 0;
-            for (int i = lo; i < ntot; ++i) {
-                const uint64_t o = B0 + off[i];
-                if (o >= W0 + 32) break;
-                const uint32_t z = zs[i];
-                const uint64_t q = z >> b;
-                // unary one-bits [o, o+q)
-                const uint64_t a0 = o > W0 ? o : W0;
-                const uint64_t a1 = (o + q) < (W0 + 32) ? (o + q) : (W0 + 32);
-                if (a0 < a1) {
-                    const uint32_t nbit = (uint32_t)(a1 - a0);
-                    const uint32_t m = nbit >= 32 ? 0xffffffffu : ((1u << nbit) - 1u);
-                    v |= m << (uint32_t)(a0 - W0);
-                }
-                // remainder bits start after the terminating zero
-                if (b > 0) {
-                    const int64_t sh = (int64_t)(o + q + 1) - (int64_t)W0;
-                    const uint64_t rem = (uint64_t)(z & ((1u << b) - 1u));
-                    if (sh >= 0 && sh < 32) v |= (uint32_t)(rem << sh);
-                    else if (sh < 0 && -sh < b) v |= (uint32_t)(rem >> (-sh));
-                }
-            }
-            sw[wd] = v;
         }
         __syncthreads();  // LDS reuse by the next block of this workgroup
     }
