@@ -158,36 +158,66 @@ __global__ __launch_bounds__(kBlock) void k_enc_len(const int32_t* __restrict__ 
     }
 }
 
+constexpr int kEncScanU = 4;  // 64-entry steps per batch of loads in the block scan
+
+// Exclusive prefix of the encode blocks' bit counts.  Each wave owns a
+// contiguous range, a multiple of 64 entries long, and reads it 64
+// consecutive entries per load (coalesced; a per-thread range would put
+// every lane of a load on its own cache line); the range total first, then,
+// after the wave offsets are known, a shuffle scan per step with a running
+// carry.
 __global__ __launch_bounds__(1024) void k_enc_scan(int32_t S, int64_t word_cap, EncWs w,
                                                   uint64_t* __restrict__ word_off, uint64_t* __restrict__ nbits,
                                                   uint32_t* status)
 {
     __shared__ uint64_t tmp[1024 / 64 + 1];
+    constexpr int NW = 1024 / 64;
     const int64_t neb = w.ebpre[S];
-    const int64_t per = cdiv(neb, (int64_t)blockDim.x);
-    const int64_t b = threadIdx.x * per, e = min(b + per, neb);
-    uint64_t local = 0;
-    for (int64_t i = b; i < e; ++i) local += w.ebits[i];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint64_t x = local;
-    for (int d = 1; d < 64; d <<= 1) {
-        uint64_t y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
+    const int64_t L = cdiv(cdiv(neb, (int64_t)NW), (int64_t)64) * 64;
+    const int64_t b = min(wave * L, neb), e = min(b + L, neb);
+    // clamped, unconditional loads, kEncScanU steps at a time
+    auto load = [&](int64_t i0, uint64_t (&v)[kEncScanU]) {
+#pragma unroll
+        for (int u = 0; u < kEncScanU; ++u) {
+            const int64_t i = i0 + u * 64 + lane;
+            v[u] = w.ebits[min(i, e - 1)];
+            if (i >= e) v[u] = 0;
+        }
+    };
+    uint64_t local = 0;
+    for (int64_t i0 = b; i0 < e; i0 += kEncScanU * 64) {
+        uint64_t v[kEncScanU];
+        load(i0, v);
+#pragma unroll
+        for (int u = 0; u < kEncScanU; ++u) local += v[u];
     }
-    if (lane == 63) tmp[wave] = x;
+    for (int d = 32; d >= 1; d >>= 1) local += __shfl_xor(local, d, 64);
+    if (lane == 0) tmp[wave] = local;
     __syncthreads();
     if (threadIdx.x == 0) {
         uint64_t run = 0;
-        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) { uint64_t q = tmp[i]; tmp[i] = run; run += q; }
-        tmp[blockDim.x >> 6] = run;
+        for (int i = 0; i < NW; ++i) { uint64_t q = tmp[i]; tmp[i] = run; run += q; }
+        tmp[NW] = run;
     }
     __syncthreads();
-    uint64_t run = tmp[wave] + x - local;
-    for (int64_t i = b; i < e; ++i) {
-        w.eboff[i] = run;
-        run += w.ebits[i];
+    uint64_t carry = tmp[wave];
+    for (int64_t i0 = b; i0 < e; i0 += kEncScanU * 64) {
+        uint64_t v[kEncScanU];
+        load(i0, v);
+#pragma unroll
+        for (int u = 0; u < kEncScanU; ++u) {
+            uint64_t x = v[u];
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint64_t y = __shfl_up(x, d, 64);
+                if (lane >= d) x += y;
+            }
+            const int64_t i = i0 + u * 64 + lane;
+            if (i < e) w.eboff[i] = carry + x - v[u];
+            carry += __shfl(x, 63, 64);
+        }
     }
-    if (threadIdx.x == 0) w.eboff[neb] = tmp[blockDim.x >> 6];
+    if (threadIdx.x == 0) w.eboff[neb] = tmp[NW];
     __syncthreads();
     if (threadIdx.x != 0) return;
     uint64_t words = 0;
@@ -220,27 +250,29 @@ __device__ inline void enc_or(uint32_t* buf, int64_t k, int32_t nbuf, uint32_t v
 // The code of gap z placed at aligned bit a: buffer word k holds aligned bits
 // [32 (k + m0), 32 (k + m0) + 32).  A code of at most 33 bits is one shifted
 // 64-bit pattern over two words; a longer one (long unary run) fills its
-// words one by one, clamped to the block's words.
-__device__ inline void enc_put(uint32_t* buf, uint64_t a, uint32_t z, uint32_t b, int32_t m0, int32_t nbuf)
+// words one by one, clamped to the block's words.  32-bit positions: a
+// block's codes, look-ahead included, span less than 2^31 + 2080 * 31 bits
+// (the gaps of a stream sum to less than 2^31), and a < that + 32.
+__device__ inline void enc_put(uint32_t* buf, uint32_t a, uint32_t z, uint32_t b, int32_t m0, int32_t nbuf)
 {
     const uint32_t q = z >> b;
     const uint64_t rem = z & ((1u << b) - 1u);
     const int64_t m = (int64_t)(a >> 5) - m0;
     if (q + 1 + b <= 33) {
-        const uint64_t p = (((1ull << q) - 1ull) | (rem << (q + 1))) << (uint32_t)(a & 31);
+        const uint64_t p = (((1ull << q) - 1ull) | (rem << (q + 1))) << (a & 31);
         enc_or(buf, m, nbuf, (uint32_t)p);
         enc_or(buf, m + 1, nbuf, (uint32_t)(p >> 32));
         return;
     }
-    const uint64_t e = a + q;  // one-bits [a, e), the zero at e, the low bits after it
-    const int64_t k0 = max(m, (int64_t)0), k1 = min((int64_t)((e - 1) >> 5) - m0, (int64_t)nbuf - 1);
-    for (int64_t k = k0; k <= k1; ++k) {
-        const uint64_t w0 = (uint64_t)(k + m0) * 32;
-        const uint64_t lo = a > w0 ? a : w0, hi = e < w0 + 32 ? e : w0 + 32;
-        const uint32_t nb = (uint32_t)(hi - lo);
-        atomicOr(&buf[k], (nb >= 32 ? 0xffffffffu : ((1u << nb) - 1u)) << (uint32_t)(lo - w0));
+    const uint32_t e = a + q;  // one-bits [a, e), the zero at e, the low bits after it
+    const int32_t k0 = (int32_t)max(m, (int64_t)0), k1 = (int32_t)min((int64_t)((e - 1) >> 5) - m0, (int64_t)nbuf - 1);
+    for (int32_t k = k0; k <= k1; ++k) {
+        const uint32_t w0 = (uint32_t)(k + m0) * 32;
+        const uint32_t lo = a > w0 ? a : w0, hi = e - w0 < 32 ? e : w0 + 32;
+        const uint32_t nb = hi - lo;
+        atomicOr(&buf[k], (nb >= 32 ? 0xffffffffu : ((1u << nb) - 1u)) << (lo - w0));
     }
-    const uint64_t p = rem << (uint32_t)((e + 1) & 31);
+    const uint64_t p = rem << ((e + 1) & 31);
     const int64_t mr = (int64_t)((e + 1) >> 5) - m0;
     enc_or(buf, mr, nbuf, (uint32_t)p);
     enc_or(buf, mr + 1, nbuf, (uint32_t)(p >> 32));
@@ -272,12 +304,19 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
         // gaps into LDS (coalesced, clamped, unconditional loads), then code
         // lengths thread-contiguous so that the prefix is one block scan
         {
+            // pointers rebased to the block (uniform) and small unsigned
+            // offsets: scalar base + 32-bit lane offset per load.  The entry
+            // before code l is pb[l] inside a stream, and for a block that
+            // starts its stream pb[max(l - 1, 0)] (code 0 has none)
+            const int32_t* pc = idx + k.e0;
+            const uint32_t sft = k.e0 > st.first ? 1u : 0u;
+            const int32_t* pb = pc - sft;
             int32_t cur[kEncPer], bef[kEncPer];
 #pragma unroll
             for (int q = 0; q < kEncPer; ++q) {
-                const int64_t j = k.e0 + min(q * kBlock + (int)threadIdx.x, ntot - 1);
-                cur[q] = idx[j];
-                bef[q] = idx[j > st.first ? j - 1 : j];
+                const uint32_t l = (uint32_t)min(q * kBlock + (int)threadIdx.x, ntot - 1);
+                cur[q] = pc[l];
+                bef[q] = pb[sft ? l : (l ? l - 1 : 0u)];
             }
             bool bad = false;  // flagged by the length pass already
 #pragma unroll
@@ -318,7 +357,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_pack(const int32_t* __restrict__
             const int32_t m0 = h ? 1 : 0, nbuf = (int32_t)(wend - wfirst);
 #pragma unroll
             for (int q = 0; q < kEncPer; ++q)
-                if (threadIdx.x * kEncPer + q < ntot) enc_put(buf, (uint64_t)oq[q] + h, zq[q], (uint32_t)b, m0, nbuf);
+                if (threadIdx.x * kEncPer + q < ntot) enc_put(buf, oq[q] + h, zq[q], (uint32_t)b, m0, nbuf);
             __syncthreads();
             for (int32_t i = threadIdx.x; i < nbuf; i += kBlock) sw[wfirst + i] = buf[i];
         } else {
