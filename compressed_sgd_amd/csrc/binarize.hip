@@ -99,15 +99,16 @@ __global__ __launch_bounds__(kBlock) void k_bin_sums(const float* __restrict__ v
         const int64_t end = min(base + kChunk, w.estart[t + 1]);
         uint32_t cp = 0, cn = 0;
         double sp = 0.0, sn = 0.0;
-        const int64_t b = base + (int64_t)threadIdx.x * kPer;
-        // clamped, unconditional loads: all in flight at once (a guarded load
+        // entry j*kBlock + tid of the chunk: coalesced loads.  Clamped and
+        // unconditional, so that all are in flight at once (a guarded load
         // would be waited for before the next is issued)
+        const int64_t b = base + threadIdx.x;
         float vv[kPer];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) vv[j] = val[min(b + j, end - 1)];
+        for (int j = 0; j < kPer; ++j) vv[j] = val[min(b + j * kBlock, end - 1)];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            if (b + j < end) {
+            if (b + j * kBlock < end) {
                 const float v = vv[j];
                 if (v > 0.0f) { ++cp; sp += (double)v; }
                 else if (v < 0.0f) { ++cn; sn += -(double)v; }
@@ -220,13 +221,20 @@ __global__ __launch_bounds__(1024) void k_bin_resolve(int32_t nseg, int32_t mode
 }
 
 // held: the residual holds val at the kept entries already (only the sent
-// side is written).
+// side is written).  Entry j*kBlock + tid of a chunk belongs to thread tid
+// (slot j): the loads are coalesced, and the 64 residual writes of one
+// store instruction go to 64 consecutive kept entries, close together in
+// memory.  Output offsets inside the chunk follow the entry order (slot,
+// wave, lane): wave ballots give the lane prefix, LDS the wave totals.
 __global__ __launch_bounds__(kBlock) void k_bin_apply_sbc(const int32_t* __restrict__ idx, const float* __restrict__ val,
                                                          int32_t nseg, BinWs w, float* __restrict__ res,
                                                          int64_t n, int32_t* __restrict__ out_idx, int64_t cap,
                                                          int32_t held)
 {
-    __shared__ uint32_t tmp[kBlock / 64 + 1];
+    constexpr int NW = kBlock / 64;
+    __shared__ uint32_t wcnt[kPer][NW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     const int64_t nch = w.cpre[nseg];
     for (int64_t c = blockIdx.x; c < nch; c += gridDim.x) {
         const int64_t t = find_bucket(w.cpre, (int64_t)nseg + 1, c);
@@ -234,43 +242,52 @@ __global__ __launch_bounds__(kBlock) void k_bin_apply_sbc(const int32_t* __restr
         const float mean = side > 0 ? w.mpos[t] : side < 0 ? -w.mneg[t] : 0.0f;
         const int64_t base = w.estart[t] + (c - w.cpre[t]) * kChunk;
         const int64_t end = min(base + kChunk, w.estart[t + 1]);
-        const int64_t b = base + (int64_t)threadIdx.x * kPer;
         // clamped, unconditional loads (see k_bin_sums)
         float vv[kPer];
         int32_t ii[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int64_t i = min(b + j, end - 1);
+            const int64_t i = min(base + j * kBlock + threadIdx.x, end - 1);
             vv[j] = val[i];
             ii[j] = idx[i];
         }
-        uint32_t sel = 0, cnt = 0;
+        uint32_t sel = 0, valid = 0;
+        uint32_t pre[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            if (b + j < end) {
-                const float v = vv[j];
-                const bool s = (side > 0 && v > 0.0f) || (side < 0 && v < 0.0f);
-                sel |= (uint32_t)s << j;
-                cnt += s;
-            }
+            const bool in = base + j * kBlock + threadIdx.x < end;
+            const float v = vv[j];
+            const bool s = in && ((side > 0 && v > 0.0f) || (side < 0 && v < 0.0f));
+            valid |= (uint32_t)in << j;
+            sel |= (uint32_t)s << j;
+            const uint64_t b = __ballot(s);
+            pre[j] = (uint32_t)__popcll(b & below);
+            if (lane == 0) wcnt[j][wave] = (uint32_t)__popcll(b);
         }
-        uint32_t tot;
-        int64_t pos = w.cout[c] + block_exclusive_scan<uint32_t>(cnt, tmp, &tot);
+        __syncthreads();
+        int64_t run = w.cout[c];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            if (b + j < end) {
-                const float v = vv[j];
-                const int32_t id = ii[j];
-                if ((uint32_t)id >= (uint32_t)n) continue;
-                if (sel & (1u << j)) {
-                    if (pos < cap) out_idx[pos] = id;
-                    ++pos;
-                    res[id] = v - mean;
-                } else if (!held) {
-                    res[id] = v;
-                }
+            uint32_t before = 0, all = 0;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                const uint32_t q = wcnt[j][v];
+                before += v < wave ? q : 0u;
+                all += q;
+            }
+            const int64_t pos = run + before + pre[j];
+            run += all;
+            if (!((valid >> j) & 1u)) continue;
+            const int32_t id = ii[j];
+            if ((uint32_t)id >= (uint32_t)n) continue;
+            if ((sel >> j) & 1u) {
+                if (pos < cap) out_idx[pos] = id;
+                res[id] = vv[j] - mean;
+            } else if (!held) {
+                res[id] = vv[j];
             }
         }
+        __syncthreads();  // wcnt is rewritten by the next chunk
     }
 }
 

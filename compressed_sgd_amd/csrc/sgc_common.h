@@ -21,13 +21,14 @@
 namespace sgc {
 
 // ---------------------------------------------------------------- geometry
-// Pass-1 tile: 4096 elements, 256 threads x 4 float4 slots (measured on
-// gfx950: 4-slot tiles stream faster than 8- or 16-slot ones, and smaller
-// tiles lose more to their per-tile work than they gain).  Tiles never
+// Pass-1 tile: 4096 elements, 512 threads x 2 float4 slots (measured on
+// gfx950: about 1% faster than 256 x 4, while 1024 x 1, 256 x 8 and
+// 8192-element tiles are slower, and smaller tiles lose more to their
+// per-tile work than they gain).  Tiles never
 // straddle a selection group; inside a group they sit on a 4-element-aligned
 // grid so that every full slot is one aligned 16-byte access.
 constexpr int kBlock = 256;
-constexpr int kPassThreads = 256;
+constexpr int kPassThreads = 512;
 constexpr int64_t kTile = 4096;
 // Candidate slots per tile region: a power of two from kTileCapMin up to a
 // whole tile, chosen per call as about 1.5 times the expected candidates of
