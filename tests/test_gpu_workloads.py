@@ -208,6 +208,33 @@ def test_flat_1g_compress_encode_full_size(orc):
                        f"flat-1G step {step} chunk table")
 
 
+def test_flat_1g_sampled_full_size(orc):
+    # sampled-threshold top-0.1%, then top-1% on the residual it leaves, over
+    # all 2^30 elements: indices, values, counts, status and the whole
+    # residual bit for bit against the oracle (its own sample of the same acc)
+    w = W.FLAT_1G
+    layout = sgc.Layout(w.seg_numel)
+    seg_off = np.array(layout.seg_off, np.int64)
+    rd = torch.zeros(w.numel, dtype=torch.float32, device="cuda")
+    r = np.zeros(w.numel, np.float32)
+    for step, ppm in enumerate((1000, 10000)):
+        announce(f"flat-1G sampled step {step} ppm={ppm}")
+        g = W.gradient(w, 0, step, device="cuda")
+        comp = sgc.compress(layout, g, rd, mode=sgc.SAMPLED, keep_ppm=ppm)
+        torch.cuda.synchronize()
+        gh = host(g)
+        del g
+        ref = orc.compress_sampled(gh, r, seg_off, sgc.GLOBAL, ppm, comp.cap)
+        del gh
+        counts = host(comp.counts)
+        total = int(counts[-1])
+        assert_bitwise(counts, ref.counts, f"flat-1G sampled step {step} counts")
+        assert_bitwise(host(comp.idx)[:total], ref.idx, f"flat-1G sampled step {step} idx")
+        assert_bitwise(host(comp.val)[:total], ref.val, f"flat-1G sampled step {step} val")
+        assert (int(host(comp.status)[0]) & sgc.STATUS_TRUNCATED) == (ref.status & 1)
+        assert_bitwise(host(rd), r, f"flat-1G sampled step {step} residual")
+
+
 def test_flat_1g_decode_accumulate_sixteen_workers(orc):
     # 16 workers' top-0.1% Rice messages (b = 9) summed into 2^30 elements
     w = W.FLAT_1G
