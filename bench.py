@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 METRIC = "gradient elems/sec (GB/s, % of HBM peak) for top-1% compress+encode at 1 GPU"
 PEAK_HBM_GBS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "pass1_flat1G_top1pct_pmc.txt")
-PASS_SRC = os.path.join(ROOT, "compressed_sgd_amd", "csrc", "compress.hip")
+# sources the fused pass is compiled from (its tile geometry lives in the header)
+PASS_SRCS = [os.path.join(ROOT, "compressed_sgd_amd", "csrc", f) for f in ("compress.hip", "sgc_common.h")]
 
 
 def pass_traffic():
@@ -46,7 +47,10 @@ def pass_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    want = hashlib.sha256(open(PASS_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in PASS_SRCS:
+        h.update(open(f, "rb").read())
+    want = h.hexdigest()
     if vals.get("source_sha256") != want or "traffic_bytes_per_launch" not in vals:
         return None
     return float(vals["traffic_bytes_per_launch"])
