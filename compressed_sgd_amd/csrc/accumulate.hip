@@ -283,7 +283,12 @@ __device__ inline ChunkAt chunk_at(const MsgWs& w, int32_t S, int64_t c)
 // unary run and the b low bits fit the window unless the gap is far above
 // 2^b (then a loop reads further windows).
 constexpr int kDecLanes = 64;
-constexpr int kColWords = 120;  // LDS words per lane (the chunk's words plus slack)
+constexpr int kColWords = 120;  // LDS words per lane (the chunk's words plus slack), largest column
+// Column sizes: a chunk of 256 Rice codes with parameter b takes about
+// 256 * (b + 2) bits when b suits the density; the smallest column that
+// holds that with slack is used, so that more waves fit in LDS (a chunk
+// that does not fit reads global memory instead).
+__host__ __device__ constexpr int col_words_for(int b) { return b <= 6 ? 80 : b <= 9 ? 104 : kColWords; }
 constexpr int kColCodes = 17;   // 2-bit code words per lane (256 entries span at most 17)
 constexpr uint32_t kMaxChunkBits = 0x80000000u + SGC_CHUNK_CODES * 32u;
 constexpr int kCopy = 8;        // words per round of the column copy
@@ -442,7 +447,7 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
     return !err;
 }
 
-template <int FMT>
+template <int FMT, int COLW>
 __device__ __forceinline__ void decode_lanes(const MsgIn& in, const MsgWs& w, int32_t nseg, uint32_t* col, uint32_t* ccol)
 {
     const int lane = threadIdx.x;
@@ -489,7 +494,7 @@ __device__ __forceinline__ void decode_lanes(const MsgIn& in, const MsgWs& w, in
         int32_t prev_end;
         bool ok;
         J.relend = (uint32_t)(bit1 - (wlo << 5));
-        if (need <= (uint64_t)kColWords) {
+        if (need <= (uint64_t)COLW) {
             // kCopy loads at a time, clamped into the stream and all in flight;
             // words past the stream's end read as 0 (a valid chunk has
             // nw >= 1 and wlo < nw)
@@ -521,20 +526,34 @@ __device__ __forceinline__ void decode_lanes(const MsgIn& in, const MsgWs& w, in
     if (bad) atomicOr(w.bad, 1u);
 }
 
+// COLW: column words per lane; CODES: the batch holds 2-bit messages (their
+// code words get a column of their own).  LDS per workgroup is what limits
+// how many decoding waves a CU holds.
+template <int COLW, bool CODES>
 __global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg)
 {
-    __shared__ uint32_t col[kColWords * kDecLanes];
-    __shared__ uint32_t ccol[kColCodes * kDecLanes];
+    __shared__ uint32_t col[COLW * kDecLanes];
+    __shared__ uint32_t ccol[(CODES ? kColCodes : 1) * kDecLanes];
     const int m = blockIdx.y;
     const MsgIn& in = B.in[m];
     const MsgWs& w = B.ws[m];
     if (w.bad[0]) return;
     switch (in.format) {
-    case SGC_MSG_GOLOMB_F32: decode_lanes<SGC_MSG_GOLOMB_F32>(in, w, nseg, col, ccol); break;
-    case SGC_MSG_GOLOMB_SBC: decode_lanes<SGC_MSG_GOLOMB_SBC>(in, w, nseg, col, ccol); break;
-    case SGC_MSG_GOLOMB_2BIT: decode_lanes<SGC_MSG_GOLOMB_2BIT>(in, w, nseg, col, ccol); break;
+    case SGC_MSG_GOLOMB_F32: decode_lanes<SGC_MSG_GOLOMB_F32, COLW>(in, w, nseg, col, ccol); break;
+    case SGC_MSG_GOLOMB_SBC: decode_lanes<SGC_MSG_GOLOMB_SBC, COLW>(in, w, nseg, col, ccol); break;
+    case SGC_MSG_GOLOMB_2BIT:
+        if constexpr (CODES) decode_lanes<SGC_MSG_GOLOMB_2BIT, COLW>(in, w, nseg, col, ccol);
+        break;
     default: break;
     }
+}
+
+template <bool CODES>
+static void launch_decode(int colw, dim3 grid, const Batch& B, int32_t nseg, hipStream_t s)
+{
+    if (colw == col_words_for(6)) k_msg_decode<col_words_for(6), CODES><<<grid, kDecLanes, 0, s>>>(B, nseg);
+    else if (colw == col_words_for(9)) k_msg_decode<col_words_for(9), CODES><<<grid, kDecLanes, 0, s>>>(B, nseg);
+    else k_msg_decode<kColWords, CODES><<<grid, kDecLanes, 0, s>>>(B, nseg);
 }
 
 // ------------------------------------------------------------------ merge
@@ -901,7 +920,8 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         Batch B;
         B.n = std::min<int32_t>(kBatch, W - b0);
         int64_t maxcap = 0, maxch = 0;
-        bool any_raw = false;
+        bool any_raw = false, any_2bit = false;
+        int colw = 0;
         for (int32_t k = 0; k < B.n; ++k) {
             const sgc_message& m = msgs[b0 + k];
             MsgIn& in = B.in[k];
@@ -923,13 +943,16 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
             B.ws[k] = mws[(size_t)(b0 + k)];
             maxcap = std::max(maxcap, m.cap);
             any_raw |= !is_golomb(m.format);
+            any_2bit |= m.format == SGC_MSG_GOLOMB_2BIT;
+            if (is_golomb(m.format)) colw = std::max(colw, col_words_for(m.rice_b));
             maxch = std::max(maxch, msg_nch(L, m));
         }
         const dim3 gtile((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(ntiles, kBlock), 2048)), (unsigned)B.n);
         k_msg_setup<<<gtile, kBlock, 0, s>>>(B, dt->seg_off, L->nseg, ntiles);
         SGC_LAUNCH_CHECK();
         const dim3 gch((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxch, kDecLanes), 16384)), (unsigned)B.n);
-        k_msg_decode<<<gch, kDecLanes, 0, s>>>(B, L->nseg);
+        if (any_2bit) launch_decode<true>(colw, gch, B, L->nseg, s);
+        else launch_decode<false>(colw, gch, B, L->nseg, s);
         SGC_LAUNCH_CHECK();
         if (any_raw) {
             const dim3 gent((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxcap, kBlock * kEntPer), 4096)),
