@@ -228,9 +228,12 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const float* __restrict__
 // word (when the caller passes none) and walks the groups: keep counts,
 // probe sizes, prefixes, and the two ranks (lower / upper bound) each
 // group's probe selection needs.
+// counts_out (or NULL): exact mode with one segment per group -- the
+// per-segment output counts are the groups' keep counts, written here.
 __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ goff, int32_t G, int32_t mode,
                                                  uint32_t ppm, uint32_t div, uint32_t smin, CompressWs w,
-                                                 int64_t hist_words, uint32_t* clear_status)
+                                                 int64_t hist_words, uint32_t* clear_status,
+                                                 int64_t* __restrict__ counts_out)
 {
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < hist_words; i += (int64_t)gridDim.x * kBlock)
         w.hist[i] = 0;
@@ -269,6 +272,7 @@ __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ go
             rlo = keep_count(s, ppm);  // the method's threshold; zeroing uses the same key
         }
         w.k[g] = k;
+        if (counts_out) counts_out[g] = k;
         w.s[g] = s;
         w.spre[g] = sp;
         w.kpre[g] = kp;
@@ -292,6 +296,7 @@ __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ go
     w.spre[G] = sp;
     w.kpre[G] = kp;
     w.cpre[2 * G] = cp;
+    if (counts_out) counts_out[G] = kp;
 }
 
 // Probe: acc = r + g (g replaced by u' = beta*u + g with momentum correction;
@@ -1295,8 +1300,12 @@ static int compress_impl(sgc_layout* L, const sgc_compress_opts* o, bool hold, M
 
     // 1. probe selection -> key_lo, key_z
     const int64_t hist_words = (int64_t)V * kRep * kBins;
+    // exact mode, one segment per selection group: each segment keeps exactly
+    // its group's k, so the output counts need no search over the indices
+    const bool counts_known = o->mode == SGC_EXACT && (o->scope == SGC_PER_SEGMENT || L->nseg == 1);
     k_setup<<<(unsigned)std::min<int64_t>(cdiv(hist_words, kBlock), 256), kBlock, 0, s>>>(
-        gr.off, G, o->mode, o->keep_ppm, o->sample_div, o->sample_min, w, hist_words, dstatus ? nullptr : w.status);
+        gr.off, G, o->mode, o->keep_ppm, o->sample_div, o->sample_min, w, hist_words, dstatus ? nullptr : w.status,
+        counts_known ? out_counts : nullptr);
     SGC_LAUNCH_CHECK();
     if (z.S > 0) {
         unsigned pb = (unsigned)std::min<int64_t>(cdiv(z.S, kBlock), 4096);
@@ -1343,6 +1352,7 @@ static int compress_impl(sgc_layout* L, const sgc_compress_opts* o, bool hold, M
         k_compact_write<M><<<cb, kBlock, 0, s>>>(residual, G, w, out_idx, out_val, cap, m);
         SGC_LAUNCH_CHECK();
     }
+    if (counts_known) return SGC_OK;
     unsigned sb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(L->nseg + 1, kBlock), 1024));
     k_seg_counts<<<sb, kBlock, 0, s>>>(dt->seg_off, L->nseg, out_idx, w, out_counts);
     SGC_LAUNCH_CHECK();
