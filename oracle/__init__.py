@@ -8,6 +8,11 @@ pages each function follows and which reading it takes where they are silent.
 Every function works on host numpy arrays, returns fresh arrays and never
 touches a GPU.  ``compress_*`` and ``binarize`` update the residual passed in
 place (like the method does).
+
+Parity unpinned: the statistics of ``compress_sampled`` beyond the properties
+any sample satisfies, and the reading that the local node's own message is
+summed as well as its dense gradient in the global+local combination (pinned
+by linearity only).
 """
 from __future__ import annotations
 

@@ -24,6 +24,15 @@
  *           with minimal Communication" (Sattler et al., arXiv 1805.08768)
  *
  * Where the pages leave a step open, the reading taken is stated at the step.
+ *
+ * Parity unpinned (nothing printed on the pages, no closed form): the
+ * statistics of the sampled-threshold mode (orc_compress_sampled) -- its
+ * sample design is a reading, and the tests pin only what holds for any
+ * sample (the kept set is the superlevel set at its own threshold, a
+ * superset of exact top-k when every element is sampled, the count inside a
+ * binomial band); and, in the global+local combination, the reading that the
+ * local node's own sparse message is summed as well as its dense gradient
+ * (pinned by linearity only).
  */
 #include <math.h>
 #include <stdint.h>
