@@ -15,8 +15,11 @@ launch), the remaining rows of the path at the same scale (accumulate-only,
 exact and sampled compress at 0.1% and 1%, exact compress + encode at 5%,
 10% and 25% (the warm-up densities), exact compress with momentum
 correction, Rice encode at both densities,
-SBC binarize, decode-accumulate of 16 workers' Rice messages), and the CPU
-oracle timed on a bounded sample as a baseline.
+SBC binarize, decode-accumulate of 16 workers' Rice messages), every other
+workload on its own shapes (flat 2^20; the MLP with 2-bit messages; the
+NMT-style model with its global+local sum; ResNet-50 per tensor with delay,
+SBC and Rice: worker step exact and sampled, and the receive step), and the
+CPU oracle timed on a bounded sample as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -69,6 +72,122 @@ def timed(fn, reps, stream):
     return e0.elapsed_time(e1) / reps
 
 
+def workload_rows(sgc, W, torch, dev, stream, reps=10):
+    """Every workload besides the 2^30 one, on its own shapes: the worker step
+    (compress exact and sampled, plus the binarize / Rice / delay steps the
+    workload uses) and the receive step (decode-accumulate of its workers'
+    messages).  Working sets of 4-204 MB fit the 256 MB last-level cache, so
+    these report elements/s only, no roofline; the Python binding's launch
+    cost is included (small steps can be host-bound)."""
+    rows = {}
+
+    def el(n, t):
+        return n / (t / 1e3)
+
+    # flat-1M: exact / sampled global top-1%, residual carried over 3 gradients in turn
+    w = W.FLAT_1M
+    L = sgc.Layout(w.seg_numel)
+    n = w.numel
+    gs = [W.gradient(w, 0, s, device=dev) for s in range(w.steps)]
+    row = {}
+    for mode, tag in ((sgc.EXACT, "exact"), (sgc.SAMPLED, "sampled")):
+        r = torch.zeros(n, dtype=torch.float32, device=dev)
+        c = sgc.compress(L, gs[0], r, mode=mode, keep_ppm=w.keep_ppm)
+        it = [0]
+
+        def step():
+            sgc.compress(L, gs[it[0] % len(gs)], r, mode=mode, keep_ppm=w.keep_ppm, out=c)
+            it[0] += 1
+        t = timed(step, reps, stream)
+        row[f"compress_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "kept": c.total()}
+    rows[w.name] = row
+
+    # mlp-mnist: global top-1% + 2-bit per worker; 4 raw 2-bit messages summed into zeros
+    w = W.MLP_MNIST
+    L = sgc.Layout(w.seg_numel)
+    n = w.numel
+    gs = [W.gradient(w, k, 0, device=dev) for k in range(w.workers)]
+    rs = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(w.workers)]
+    msgs = []
+    for k in range(w.workers):
+        c = sgc.compress(L, gs[k], rs[k], keep_ppm=w.keep_ppm)
+        bn = sgc.binarize(L, c, rs[k], sgc.BIN_2BIT)
+        msgs.append(sgc.Message(sgc.MSG_RAW_2BIT, bn.counts, bn.cap, idx=c.idx, codes=bn.codes, means=bn.means))
+    row = {}
+    for mode, tag in ((sgc.EXACT, "exact"), (sgc.SAMPLED, "sampled")):
+        ct = sgc.compress(L, gs[0], rs[0], mode=mode, keep_ppm=w.keep_ppm)
+
+        def step():
+            sgc.compress(L, gs[1], rs[0], mode=mode, keep_ppm=w.keep_ppm, out=ct)
+            sgc.binarize(L, ct, rs[0], sgc.BIN_2BIT)
+        t = timed(step, reps, stream)
+        row[f"worker_step_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "steps": "compress + 2-bit"}
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    t = timed(lambda: sgc.decode_accumulate(L, msgs, out), reps, stream)
+    row["receive"] = {"ms": t, "elements_per_s": el(n, t), "messages": len(msgs), "format": "raw 2-bit"}
+    rows[w.name] = row
+    del gs, rs, msgs, out
+
+    # nmt-rnn: global top-1% per worker; 4 raw messages added onto the local gradient
+    w = W.NMT_RNN
+    L = sgc.Layout(w.seg_numel)
+    n = w.numel
+    gs = [W.gradient(w, k, 0, device=dev) for k in range(w.workers)]
+    msgs = []
+    r = torch.zeros(n, dtype=torch.float32, device=dev)
+    for k in range(w.workers):
+        r.zero_()
+        msgs.append(sgc.raw_message(sgc.compress(L, gs[k], r, keep_ppm=w.keep_ppm)))
+    row = {}
+    for mode, tag in ((sgc.EXACT, "exact"), (sgc.SAMPLED, "sampled")):
+        ct = sgc.compress(L, gs[0], r, mode=mode, keep_ppm=w.keep_ppm)
+        t = timed(lambda: sgc.compress(L, gs[1], r, mode=mode, keep_ppm=w.keep_ppm, out=ct), reps, stream)
+        row[f"compress_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "GBps": 12.0 * n / (t / 1e3) / 1e9}
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    t = timed(lambda: sgc.decode_accumulate(L, msgs, out, init=sgc.INIT_BASE, base=gs[0]), reps, stream)
+    row["receive_on_local"] = {"ms": t, "elements_per_s": el(n, t), "messages": len(msgs), "format": "raw fp32"}
+    rows[w.name] = row
+    del gs, msgs, r, out
+
+    # resnet50: 7 delayed accumulations + per-tensor top-0.1% + SBC + per-tensor Rice (b = 9)
+    # per worker round; 8 workers' messages summed into zeros
+    w = W.RESNET50
+    L = sgc.Layout(w.seg_numel)
+    n = w.numel
+    b = sgc.rice_param(w.keep_ppm / 1e6)
+    gs = [W.gradient(w, 0, s, device=dev) for s in range(2)]
+    msgs = []
+    r = torch.zeros(n, dtype=torch.float32, device=dev)
+    for k in range(w.workers):
+        r.zero_()
+        c = sgc.compress(L, gs[k % 2], r, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm)
+        bn = sgc.binarize(L, c, r, sgc.BIN_SBC)
+        e = sgc.encode(L, bn.idx, bn.counts, bn.cap, scope=sgc.PER_SEGMENT, b=b)
+        msgs.append(sgc.golomb_message(bn, e))
+    row = {}
+    for mode, tag in ((sgc.EXACT, "exact"), (sgc.SAMPLED, "sampled")):
+        ct = sgc.compress(L, gs[0], r, mode=mode, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm)
+
+        def exchange():
+            sgc.compress(L, gs[1], r, mode=mode, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm, out=ct)
+            bt = sgc.binarize(L, ct, r, sgc.BIN_SBC)
+            sgc.encode(L, bt.idx, bt.counts, bt.cap, scope=sgc.PER_SEGMENT, b=b)
+
+        def rnd():
+            for s_ in range(w.delay - 1):
+                sgc.compress(L, gs[s_ % 2], r, mode=sgc.ACCUMULATE_ONLY)
+            exchange()
+        t = timed(exchange, reps, stream)
+        tr = timed(rnd, reps, stream)
+        row[f"exchange_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "steps": "compress + SBC + Rice"}
+        row[f"round_{tag}"] = {"ms": tr, "steps": f"{w.delay - 1} accumulations + exchange"}
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    t = timed(lambda: sgc.decode_accumulate(L, msgs, out), reps, stream)
+    row["receive"] = {"ms": t, "elements_per_s": el(n, t), "messages": len(msgs), "format": "Rice + SBC mean"}
+    rows[w.name] = row
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,7 +195,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-sample-log2", type=int, default=26)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-rows", action="store_true", help="skip the extra rows (e.g. under a profiler)")
+    ap.add_argument("--no-rows", action="store_true", help="skip the extra rows and workloads (e.g. under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of 2^28 fp32 (1 GiB each way) three times: "
                          "the reference the HBM byte counters are scaled by")
@@ -294,6 +413,8 @@ def main():
             del msgs
         out["rows"] = rows
         del r16, outd
+        print("[bench] the other workloads", file=sys.stderr, flush=True)
+        out["workloads"] = workload_rows(sgc, W, torch, dev, stream)
 
     if not args.no_cpu_baseline:
         import oracle as orc

@@ -106,6 +106,8 @@ struct CompressWs {
     int64_t* ch_eq_pre;// [nch_max+1]
     int64_t* scal;     // [8]: 0 output total, 1 candidate total
     uint32_t* status;  // [1] used when the caller passes no dstatus
+    int32_t* over;     // [NT] tiles whose region overflowed (any order)
+    uint32_t* nover;   // [1] entries in over
     uint32_t tcap;     // candidate slots per tile region (a power of two)
     uint32_t hold;     // SGC_HOLD_KEPT: kept entries keep acc in the residual (nothing is zeroed)
 };
@@ -178,6 +180,8 @@ static void carve_compress(Carver& c, const CompressSizes& z, int mode, bool mom
     }
     w->scal = c.take<int64_t>(8);
     w->status = c.take<uint32_t>(1);
+    w->over = c.take<int32_t>(z.NT);
+    w->nover = c.take<uint32_t>(1);
 }
 
 // Global exclusive prefix of tile t (t == NT gives the total).
@@ -239,6 +243,7 @@ __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ go
         w.hist[i] = 0;
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     if (clear_status) *clear_status = 0;
+    *w.nover = 0;
     int64_t sp = 0, kp = 0, cp = 0;
     for (int32_t g = 0; g < G; ++g) {
         const int64_t m = goff[g + 1] - goff[g];
@@ -738,6 +743,8 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan1(int64_t NT, CompressWs w)
     for (int q = 0; q < per; ++q) {
         if (t0 + q < NT) w.tile_loc[t0 + q] = run;
         run += c[q];
+        // a tile whose region overflowed is redone by the gather, from this list
+        if (c[q] > w.tcap) w.over[atomicAdd(w.nover, 1u)] = (int32_t)(t0 + q);
     }
     if (threadIdx.x == 0) w.sup_pre[blockIdx.x] = total;  // block sum; k_tile_scan2 makes it a prefix
 }
@@ -834,7 +841,6 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
     __shared__ uint32_t s_pre[kGatherTiles + 1];  // prefix of the entries copied from the regions
     __shared__ uint32_t s_z[kGatherTiles];    // zeroing bound of the tile's group
     __shared__ int32_t s_hg[kGatherTiles];    // group whose first digit the tile counts (-1: none)
-    __shared__ uint64_t s_over;               // bit q: tile q overflowed
     __shared__ uint32_t h[kBins];             // first-digit histogram of group s_hg[0]
     static_assert(kGatherTiles == 64, "one wave lane per tile");
     const bool sampled = mode == SGC_SAMPLED;
@@ -871,8 +877,6 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
         }
         s_pre[q + 1] = x;
         if (q == 0) s_pre[0] = 0;
-        const uint64_t ob = __ballot(over);
-        if (q == 0) s_over = ob;
     }
     __syncthreads();
     const int32_t g_lds = s_hg[0];
@@ -929,15 +933,24 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
             if (!sampled) lds_count(h, lds_hit, bin);
         }
     }
-    // overflowed tiles: redo from r (which pass 1 left as acc there)
-    const uint64_t over = s_over;
-    for (int q = 0; q < kGatherTiles; ++q) {
-        if (!(over & (1ull << q))) continue;  // uniform per block
-        const int64_t t = t0 + q;
-        const int64_t dst = s_dst[q];
-        if (dst < 0) continue;
+    // overflowed tiles: redo from r (which pass 1 left as acc there).  The
+    // tile scan listed them; every workgroup takes its share of the list, so
+    // that clustered inputs (many overflowed tiles side by side) spread the
+    // redo over the whole grid instead of a few workgroups.
+    const uint32_t nover = *w.nover;
+    for (uint32_t j = blockIdx.x; j < nover; j += gridDim.x) {  // uniform per block
+        const int64_t t = w.over[j];
         const int64_t g = tile_group(gtile, G, t);
-        const int32_t hg = s_hg[q];
+        int64_t dst;
+        int32_t hg = -1;
+        if (sampled) {
+            dst = tile_prefix(w, NT, t);
+        } else if (w.src_kind[g] == kSrcCand) {
+            dst = w.cstart[g] + tile_prefix(w, NT, t) - tile_prefix(w, NT, gtile[g]);
+            if (w.rank[g] > 0) hg = (int32_t)g;
+        } else {
+            continue;  // dense-path group: pass 1 left acc everywhere in this tile
+        }
         const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
         const int32_t A = (lo & ~3) + (int32_t)(t - gtile[g]) * (int32_t)kTile;
         tile_candidates<false, kBlock, (int)(kTile / (4 * kBlock))>(grad, res, lo, hi, A, w.key_lo[g], kNoKey, w.tcap, m,
