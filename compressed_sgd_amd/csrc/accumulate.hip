@@ -109,8 +109,10 @@ static void carve_msg(Carver& c, const sgc_layout* L, const sgc_message& m, MsgW
 
 // ------------------------------------------------------------------ setup
 // Every thread marks output tiles as not yet known (-1: k_msg_holes fills
-// what the entry pass leaves); thread 0 of block 0 checks the message's
-// tables.
+// what the entry pass leaves); workgroup 0 of each message checks its
+// tables, one thread per segment / stream in rounds (workgroup scans for the
+// prefixes, an OR over the workgroup for the verdict).  A message that fails
+// any check is skipped whole: its stream tables are cleared.
 __global__ __launch_bounds__(kBlock) void k_msg_setup(Batch B, const int64_t* __restrict__ seg_off, int32_t nseg,
                                                      int64_t ntiles)
 {
@@ -119,51 +121,78 @@ __global__ __launch_bounds__(kBlock) void k_msg_setup(Batch B, const int64_t* __
     const MsgWs& w = B.ws[m];
     for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < ntiles; t += (int64_t)gridDim.x * kBlock)
         w.tstart[t] = -1;
-    if (blockIdx.x || threadIdx.x) return;
+    if (blockIdx.x) return;
+    __shared__ int64_t tmp[kBlock / 64 + 1];
     const int64_t n = seg_off[nseg];
-    uint32_t bad = 0;
+    bool bad = false;
+    // entry prefix per segment; every count within [0, the room left below cap]
     int64_t e = 0;
-    for (int32_t t = 0; t < nseg; ++t) {
-        w.estart[t] = e;
-        int64_t c = in.counts[t];
-        if (c < 0 || c > in.cap - e) bad = 1;
-        else e += c;
+    for (int64_t t0 = 0; t0 < nseg; t0 += kBlock) {
+        const int64_t t = t0 + threadIdx.x;
+        const bool on = t < nseg;
+        const int64_t raw = on ? in.counts[t] : 0;
+        const int64_t c = raw < 0 ? 0 : (raw > in.cap ? in.cap : raw);
+        int64_t te;
+        const int64_t xe = e + block_scan_excl<kBlock, int64_t>(c, tmp, &te);
+        bad |= on && (raw < 0 || raw > in.cap - xe);
+        if (on) w.estart[t] = xe;
+        e += te;
     }
-    w.estart[nseg] = e;
-    if (bad || in.counts[nseg] != e) bad = 1;
+    bad = __syncthreads_or(bad);  // also makes every estart entry visible to the workgroup
+    if (threadIdx.x == 0) w.estart[nseg] = e;
+    if (bad || in.counts[nseg] != e) bad = true;
     const bool golomb = in.format >= SGC_MSG_GOLOMB_F32;
-    int64_t ch = 0, se = 0;
-    uint64_t wprev = 0;
-    for (int32_t s = 0; s < in.S && !bad; ++s) {
-        const bool glob = !golomb || in.scope == SGC_GLOBAL;
-        const int64_t cnt = glob ? e : w.estart[s + 1] - w.estart[s];
-        w.scnt[s] = cnt;
-        w.sent[s] = se;
-        w.sbase[s] = glob ? 0 : seg_off[s];
-        w.ssize[s] = glob ? n : seg_off[s + 1] - seg_off[s];
-        w.chpre[s] = ch;
-        if (cnt > w.ssize[s]) bad = 1;
-        if (golomb) {
-            const uint64_t w0 = in.word_off[s], w1 = in.word_off[s + 1];
-            if (w0 != wprev || w1 < w0 || (w1 - w0) != (in.nbits[s] + 31) / 32 || w1 > (uint64_t)in.wbound) bad = 1;
-            if ((cnt > 0) != (in.nbits[s] > 0)) bad = 1;  // codes take at least one bit each; no codes, no bits
-            wprev = w1;
+    const bool glob = !golomb || in.scope == SGC_GLOBAL;
+    int64_t se = 0, ch = 0;
+    if (!bad) {  // uniform
+        for (int64_t s0 = 0; s0 < in.S; s0 += kBlock) {
+            const int64_t s = s0 + threadIdx.x;
+            const bool on = s < in.S;
+            int64_t cnt = 0;
+            bool sbad = false;
+            if (on) {
+                cnt = glob ? e : w.estart[s + 1] - w.estart[s];
+                const int64_t size = glob ? n : seg_off[s + 1] - seg_off[s];
+                w.scnt[s] = cnt;
+                w.sbase[s] = glob ? 0 : seg_off[s];
+                w.ssize[s] = size;
+                sbad = cnt > size;
+                if (golomb) {
+                    const uint64_t w0 = in.word_off[s], w1 = in.word_off[s + 1];
+                    // streams follow one another from word 0; each has the words its bits need
+                    if ((s == 0 && w0 != 0) || w1 < w0 || (w1 - w0) != (in.nbits[s] + 31) / 32 ||
+                        w1 > (uint64_t)in.wbound)
+                        sbad = true;
+                    if ((cnt > 0) != (in.nbits[s] > 0)) sbad = true;  // codes take at least one bit each
+                }
+            }
+            int64_t tse, tch;
+            const int64_t xse = se + block_scan_excl<kBlock, int64_t>(cnt, tmp, &tse);
+            const int64_t xch =
+                ch + block_scan_excl<kBlock, int64_t>(golomb ? cdiv(cnt, (int64_t)SGC_CHUNK_CODES) : 0, tmp, &tch);
+            if (on) {
+                w.sent[s] = xse;
+                w.chpre[s] = xch;
+            }
+            bad |= sbad;
+            se += tse;
+            ch += tch;
         }
-        se += cnt;
-        ch += golomb ? cdiv(cnt, (int64_t)SGC_CHUNK_CODES) : 0;
     }
+    bad = __syncthreads_or(bad);
     if (bad) {
-        for (int32_t s = 0; s < in.S; ++s) {
+        for (int64_t s = threadIdx.x; s < in.S; s += kBlock) {
             w.scnt[s] = 0;
             w.sent[s] = 0;
             w.chpre[s] = 0;
         }
-        ch = 0;
         se = 0;
+        ch = 0;
     }
+    if (threadIdx.x != 0) return;
     w.sent[in.S] = se;
     w.chpre[in.S] = ch;
-    w.bad[0] = bad;
+    w.bad[0] = bad ? 1u : 0u;
     w.total[0] = bad ? 0 : e;
     w.tstart[ntiles] = (int32_t)(bad ? 0 : e);
 }

@@ -54,22 +54,35 @@ static void carve_bin(Carver& c, const sgc_layout* L, int64_t cap, BinWs* w)
     w->segsn = c.take<double>(ns);
 }
 
-// Entry and chunk prefixes.  Counts are clamped into [0, cap] so that a
-// malformed count table can never move a read outside the inputs.
-__global__ void k_bin_setup(const int64_t* __restrict__ counts, int32_t nseg, int64_t cap, BinWs w)
+// Entry and chunk prefixes, one thread per segment in rounds (workgroup
+// scans).  Counts are clamped into [0, cap] so that a malformed count table
+// can never move a read outside the inputs: entry prefix = min(cap, prefix of
+// the clamped counts), the same as clamping each count to the room left.
+__global__ __launch_bounds__(kBlock) void k_bin_setup(const int64_t* __restrict__ counts, int32_t nseg, int64_t cap,
+                                                     BinWs w)
 {
-    if (threadIdx.x || blockIdx.x) return;
-    int64_t e = 0, c = 0;
-    for (int32_t t = 0; t < nseg; ++t) {
-        w.estart[t] = e;
-        w.cpre[t] = c;
-        int64_t m = counts[t];
-        m = m < 0 ? 0 : (m > cap - e ? cap - e : m);
-        e += m;
-        c += cdiv(m, kChunk);
+    __shared__ int64_t tmp[kBlock / 64 + 1];
+    int64_t P = 0, C = 0;  // prefixes carried from round to round
+    for (int64_t t0 = 0; t0 < nseg; t0 += kBlock) {
+        const int64_t t = t0 + threadIdx.x;
+        const bool in = t < nseg;
+        int64_t c = in ? counts[t] : 0;
+        c = c < 0 ? 0 : (c > cap ? cap : c);
+        int64_t tp, tc;
+        const int64_t xp = P + block_scan_excl<kBlock, int64_t>(c, tmp, &tp);
+        const int64_t e0 = xp < cap ? xp : cap, e1 = xp + c < cap ? xp + c : cap;
+        const int64_t xc = C + block_scan_excl<kBlock, int64_t>(cdiv(e1 - e0, kChunk), tmp, &tc);
+        if (in) {
+            w.estart[t] = e0;
+            w.cpre[t] = xc;
+        }
+        P += tp;
+        C += tc;
     }
-    w.estart[nseg] = e;
-    w.cpre[nseg] = c;
+    if (threadIdx.x == 0) {
+        w.estart[nseg] = P < cap ? P : cap;
+        w.cpre[nseg] = C;
+    }
 }
 
 // Deterministic block sum (fixed shuffle tree, then waves in order).
@@ -159,6 +172,8 @@ __global__ __launch_bounds__(kBlock) void k_bin_segsum(int32_t nseg, BinWs w)
 __global__ __launch_bounds__(1024) void k_bin_resolve(int32_t nseg, int32_t mode, BinWs w,
                                                      int64_t* __restrict__ out_counts, float* __restrict__ out_means)
 {
+    __shared__ int64_t tmp[1024 / 64 + 1];
+    int64_t sent = 0;  // this thread's share of the output total
     for (int64_t t = threadIdx.x; t < nseg; t += blockDim.x) {
         const int64_t cp = w.segcp[t], cn = w.segcn[t];
         const float mp = cp ? (float)(w.segsp[t] / (double)cp) : 0.0f;
@@ -171,25 +186,18 @@ __global__ __launch_bounds__(1024) void k_bin_resolve(int32_t nseg, int32_t mode
         if (mode == SGC_BIN_SBC) {
             out_means[t] = side > 0 ? mp : side < 0 ? -mn : 0.0f;
             out_counts[t] = side > 0 ? cp : side < 0 ? cn : 0;
+            sent += side > 0 ? cp : side < 0 ? cn : 0;
         } else {
             out_means[2 * t] = mp;
             out_means[2 * t + 1] = -mn;
             out_counts[t] = w.estart[t + 1] - w.estart[t];
         }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int64_t run = 0;
-        if (mode == SGC_BIN_SBC) {
-            for (int32_t t = 0; t < nseg; ++t) run += out_counts[t];
-        } else {
-            run = w.estart[nseg];
-        }
-        out_counts[nseg] = run;
-    }
+    int64_t total;
+    block_scan_excl<1024, int64_t>(sent, tmp, &total);  // (also the barrier before w.side is read below)
+    if (threadIdx.x == 0) out_counts[nseg] = mode == SGC_BIN_SBC ? total : w.estart[nseg];
     if (mode != SGC_BIN_SBC) return;
     // chunk output offsets: flat exclusive scan of the chosen count per chunk
-    __shared__ int64_t tmp[1024 / 64 + 1];
     const int64_t nch = w.cpre[nseg];
     const int64_t per = cdiv(nch, (int64_t)blockDim.x);
     const int64_t b = threadIdx.x * per, e = min(b + per, nch);
@@ -374,7 +382,7 @@ extern "C" int sgc_binarize(const sgc_layout* Lc, int32_t mode, const int32_t* i
     const int32_t nseg = L->nseg;
     const int64_t nch_max = bin_nch_max(L, cap);
     const unsigned cb = (unsigned)std::min<int64_t>(nch_max, 2048);
-    k_bin_setup<<<1, 64, 0, s>>>(counts, nseg, cap, w);
+    k_bin_setup<<<1, kBlock, 0, s>>>(counts, nseg, cap, w);
     SGC_LAUNCH_CHECK();
     k_bin_sums<<<cb, kBlock, 0, s>>>(val, nseg, w);
     SGC_LAUNCH_CHECK();

@@ -228,12 +228,13 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const float* __restrict__
 
 // ----------------------------------------------------------------- setup
 // Every thread clears the radix-select histograms (the resolve passes leave
-// them clear again); thread 0 of block 0 clears the library's own status
-// word (when the caller passes none) and walks the groups: keep counts,
-// probe sizes, prefixes, and the two ranks (lower / upper bound) each
-// group's probe selection needs.
-// counts_out (or NULL): exact mode with one segment per group -- the
-// per-segment output counts are the groups' keep counts, written here.
+// them clear again); workgroup 0 clears the library's own status word (when
+// the caller passes none) and the overflow-list count, and goes over the
+// groups in rounds of kBlock, one thread per group: keep counts, probe
+// sizes, the two ranks (lower / upper bound) each group's probe selection
+// needs, and their prefixes (workgroup scans).  counts_out (or NULL):
+// exact mode with one segment per group -- the per-segment output counts
+// are the groups' keep counts, written here.
 __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ goff, int32_t G, int32_t mode,
                                                  uint32_t ppm, uint32_t div, uint32_t smin, CompressWs w,
                                                  int64_t hist_words, uint32_t* clear_status,
@@ -241,67 +242,84 @@ __global__ __launch_bounds__(kBlock) void k_setup(const int64_t* __restrict__ go
 {
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < hist_words; i += (int64_t)gridDim.x * kBlock)
         w.hist[i] = 0;
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    if (clear_status) *clear_status = 0;
-    *w.nover = 0;
-    int64_t sp = 0, kp = 0, cp = 0;
-    for (int32_t g = 0; g < G; ++g) {
-        const int64_t m = goff[g + 1] - goff[g];
-        const int64_t k = keep_count(m, ppm);
-        const int64_t s = (mode == SGC_EXACT) ? probe_count(m) : sampled_count(m, div, smin);
-        int64_t rlo = 0, rhi = 0;
-        uint32_t klo = kNoKey, kz = kNoKey;
-        if (mode == SGC_EXACT) {
-            if (k > 0) {
-                if (s == m) {
-                    rlo = k;  // the probe read every element: its k-th key is the threshold
-                    rhi = w.hold ? 0 : k;
-                } else {
-                    // e: expected sampled keys above the true threshold.  The
-                    // candidate bound takes a 6-sigma margin below it (a miss
-                    // costs a dense selection); the zeroing bound sits at the
-                    // estimate itself: either way it errs, the compaction
-                    // fixes the few entries between it and the exact
-                    // threshold with scattered writes
-                    const double e = (double)s * (double)k / (double)m;
-                    const double d = 6.0 * sqrt(e) + 8.0;
-                    const int64_t lo = (int64_t)(e + d) + 1;
-                    const int64_t hi = (int64_t)(e + 0.5);
-                    if (lo >= s) klo = 0;  // the bound would be the sample minimum: take every element
-                    else rlo = lo;
-                    if (hi >= 1) rhi = hi;
-                    if (w.hold) rhi = 0;  // no zeroing bound: nothing is zeroed
-                }
-            }
-        } else {
-            rlo = keep_count(s, ppm);  // the method's threshold; zeroing uses the same key
-        }
-        w.k[g] = k;
-        if (counts_out) counts_out[g] = k;
-        w.s[g] = s;
-        w.spre[g] = sp;
-        w.kpre[g] = kp;
-        w.key_lo[g] = klo;
-        w.key_z[g] = kz;
-        for (int v = 0; v < 2; ++v) {
-            const int64_t vg = 2 * (int64_t)g + v;
-            const int64_t r = v == 0 ? rlo : rhi;
-            w.rank[vg] = r;
-            w.src_kind[vg] = kSrcSamples;
-            w.src_base[vg] = sp;
-            w.src_len[vg] = r > 0 ? s : 0;
-            w.cpre[vg] = cp;
-            w.prefix[vg] = 0;
-            w.mrem[vg] = r;
-            cp += cdiv(w.src_len[vg], kChunk);
-        }
-        sp += s;
-        kp += k;
+    if (blockIdx.x != 0) return;
+    if (threadIdx.x == 0) {
+        if (clear_status) *clear_status = 0;
+        *w.nover = 0;
     }
-    w.spre[G] = sp;
-    w.kpre[G] = kp;
-    w.cpre[2 * G] = cp;
-    if (counts_out) counts_out[G] = kp;
+    __shared__ int64_t tmp[kBlock / 64 + 1];
+    int64_t sp = 0, kp = 0, cp = 0;  // prefixes carried from round to round
+    for (int64_t g0 = 0; g0 < G; g0 += kBlock) {
+        const int64_t g = g0 + threadIdx.x;
+        const bool in = g < G;
+        int64_t k = 0, sz = 0, rlo = 0, rhi = 0;
+        uint32_t klo = kNoKey, kz = kNoKey;
+        if (in) {
+            const int64_t m = goff[g + 1] - goff[g];
+            k = keep_count(m, ppm);
+            sz = (mode == SGC_EXACT) ? probe_count(m) : sampled_count(m, div, smin);
+            if (mode == SGC_EXACT) {
+                if (k > 0) {
+                    if (sz == m) {
+                        rlo = k;  // the probe read every element: its k-th key is the threshold
+                        rhi = w.hold ? 0 : k;
+                    } else {
+                        // e: expected sampled keys above the true threshold.  The
+                        // candidate bound takes a 6-sigma margin below it (a miss
+                        // costs a dense selection); the zeroing bound sits at the
+                        // estimate itself: either way it errs, the compaction
+                        // fixes the few entries between it and the exact
+                        // threshold with scattered writes
+                        const double e = (double)sz * (double)k / (double)m;
+                        const double d = 6.0 * sqrt(e) + 8.0;
+                        const int64_t lo = (int64_t)(e + d) + 1;
+                        const int64_t hi = (int64_t)(e + 0.5);
+                        if (lo >= sz) klo = 0;  // the bound would be the sample minimum: take every element
+                        else rlo = lo;
+                        if (hi >= 1) rhi = hi;
+                        if (w.hold) rhi = 0;  // no zeroing bound: nothing is zeroed
+                    }
+                }
+            } else {
+                rlo = keep_count(sz, ppm);  // the method's threshold; zeroing uses the same key
+            }
+        }
+        const int64_t len0 = rlo > 0 ? sz : 0, len1 = rhi > 0 ? sz : 0;
+        const int64_t c0 = cdiv(len0, kChunk), c1 = cdiv(len1, kChunk);
+        int64_t ts, tk, tc;
+        const int64_t xs = sp + block_scan_excl<kBlock, int64_t>(sz, tmp, &ts);
+        const int64_t xk = kp + block_scan_excl<kBlock, int64_t>(k, tmp, &tk);
+        const int64_t xc = cp + block_scan_excl<kBlock, int64_t>(c0 + c1, tmp, &tc);
+        if (in) {
+            w.k[g] = k;
+            if (counts_out) counts_out[g] = k;
+            w.s[g] = sz;
+            w.spre[g] = xs;
+            w.kpre[g] = xk;
+            w.key_lo[g] = klo;
+            w.key_z[g] = kz;
+            for (int v = 0; v < 2; ++v) {
+                const int64_t vg = 2 * g + v;
+                const int64_t r = v == 0 ? rlo : rhi;
+                w.rank[vg] = r;
+                w.src_kind[vg] = kSrcSamples;
+                w.src_base[vg] = xs;
+                w.src_len[vg] = v == 0 ? len0 : len1;
+                w.cpre[vg] = v == 0 ? xc : xc + c0;
+                w.prefix[vg] = 0;
+                w.mrem[vg] = r;
+            }
+        }
+        sp += ts;
+        kp += tk;
+        cp += tc;
+    }
+    if (threadIdx.x == 0) {
+        w.spre[G] = sp;
+        w.kpre[G] = kp;
+        w.cpre[2 * G] = cp;
+        if (counts_out) counts_out[G] = kp;
+    }
 }
 
 // Probe: acc = r + g (g replaced by u' = beta*u + g with momentum correction;
@@ -770,47 +788,63 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_scan2(const int64_t* __re
         w.sup_pre[i] = run;
         run += v;
     }
-    __syncthreads();
-    if (threadIdx.x != 0) return;
-    w.sup_pre[NS] = total;
-    w.scal[1] = total;
-    if (mode == SGC_SAMPLED) {
-        w.scal[0] = total < cap ? total : cap;
-        if (total > cap) *status |= SGC_STATUS_TRUNCATED;
-        return;
-    }
-    int64_t used = 0, cp = 0;
-    bool dense = false;
-    for (int32_t g = 0; g < G; ++g) {
-        const int64_t cg = tile_prefix(w, NT, gtile[g + 1]) - tile_prefix(w, NT, gtile[g]);
-        const int64_t k = w.k[g];
-        int kind;
-        int64_t base, len;
-        if (k == 0) {
-            kind = kSrcCand;
-            base = used;
-            len = 0;
-        } else if (cg >= k && used + cg <= capc) {
-            kind = kSrcCand;
-            base = used;
-            len = cg;
-            used += cg;
-        } else {
-            kind = kSrcDense;
-            base = goff[g];
-            len = goff[g + 1] - goff[g];
-            dense = true;
+    if (threadIdx.x == 0) {
+        w.sup_pre[NS] = total;
+        w.scal[1] = total;
+        if (mode == SGC_SAMPLED) {
+            w.scal[0] = total < cap ? total : cap;
+            if (total > cap) *status |= SGC_STATUS_TRUNCATED;
         }
-        w.cstart[g] = base;
-        w.src_kind[g] = kind;
-        w.src_base[g] = base;
-        w.src_len[g] = len;
-        w.rank[g] = k;
-        w.prefix[g] = 0;
-        w.mrem[g] = k;
-        w.cpre[g] = cp;
-        cp += cdiv(len, kChunk);
     }
+    __syncthreads();  // every block prefix, the total included, is visible to the whole workgroup
+    if (mode == SGC_SAMPLED) return;  // uniform
+    // Per group, one thread each, in rounds: a group is selected from its
+    // candidates when it has at least k of them and they fit the candidate
+    // array after those of every earlier group that has at least its k
+    // (a group that does not fit leaves a hole: nothing reads it); otherwise
+    // straight from the residual.  Either way gives the same result.
+    int64_t used = 0, cp = 0;  // prefixes carried from round to round
+    bool dense = false;
+    for (int64_t g0 = 0; g0 < G; g0 += kScanThreads) {
+        const int64_t g = g0 + threadIdx.x;
+        const bool in = g < G;
+        int64_t cg = 0, k = 0;
+        if (in) {
+            cg = tile_prefix(w, NT, gtile[g + 1]) - tile_prefix(w, NT, gtile[g]);
+            k = w.k[g];
+        }
+        const bool elig = in && k > 0 && cg >= k;
+        int64_t tu;
+        const int64_t xu = used + block1024_exclusive_scan<int64_t>(elig ? cg : 0, tmp, &tu);
+        int kind = kSrcCand;
+        int64_t base = xu, len = 0;
+        if (in && k > 0) {
+            if (elig && xu + cg <= capc) {
+                len = cg;
+            } else {
+                kind = kSrcDense;
+                base = goff[g];
+                len = goff[g + 1] - goff[g];
+                dense = true;
+            }
+        }
+        int64_t tc;
+        const int64_t xc = cp + block1024_exclusive_scan<int64_t>(in ? cdiv(len, kChunk) : 0, tmp, &tc);
+        if (in) {
+            w.cstart[g] = base;
+            w.src_kind[g] = kind;
+            w.src_base[g] = base;
+            w.src_len[g] = len;
+            w.rank[g] = k;
+            w.prefix[g] = 0;
+            w.mrem[g] = k;
+            w.cpre[g] = xc;
+        }
+        used += tu;
+        cp += tc;
+    }
+    dense = __syncthreads_or(dense);
+    if (threadIdx.x != 0) return;
     w.cpre[G] = cp;
     w.scal[0] = w.kpre[G];
     if (dense) *status |= SGC_STATUS_DENSE_PATH;

@@ -59,32 +59,49 @@ static void carve_enc(Carver& c, const sgc_layout* L, int32_t scope, int64_t cap
     w->st = c.take<uint32_t>(1);
 }
 
-__global__ void k_enc_setup(const int64_t* __restrict__ counts, const int64_t* __restrict__ seg_off, int32_t nseg,
-                            int32_t scope, int64_t cap, EncWs w)
+// Per-stream tables, one thread per stream in rounds (workgroup scans).
+// Counts are clamped to the room left below cap (entry prefix = min(cap,
+// prefix of the clamped counts)), so that malformed counts never move a
+// read past cap entries; they are flagged.
+__global__ __launch_bounds__(kBlock) void k_enc_setup(const int64_t* __restrict__ counts,
+                                                     const int64_t* __restrict__ seg_off, int32_t nseg,
+                                                     int32_t scope, int64_t cap, EncWs w)
 {
-    if (threadIdx.x || blockIdx.x) return;
+    __shared__ int64_t tmp[kBlock / 64 + 1];
     const int32_t S = scope == SGC_GLOBAL ? 1 : nseg;
-    int64_t e = 0, eb = 0, ch = 0;
-    w.bad[0] = 0;
-    for (int32_t s = 0; s < S; ++s) {
-        int64_t m = scope == SGC_GLOBAL ? counts[nseg] : counts[s];
-        if (m < 0 || m > cap - e) {  // malformed counts: never read past cap entries
-            w.bad[0] = 1;
-            m = m < 0 ? 0 : cap - e;
+    int64_t P = 0, EB = 0, CH = 0;  // prefixes carried from round to round
+    bool bad = false;
+    for (int64_t s0 = 0; s0 < S; s0 += kBlock) {
+        const int64_t s = s0 + threadIdx.x;
+        const bool in = s < S;
+        const int64_t raw = in ? (scope == SGC_GLOBAL ? counts[nseg] : counts[s]) : 0;
+        const int64_t c = raw < 0 ? 0 : (raw > cap ? cap : raw);
+        int64_t tp, teb, tch;
+        const int64_t xp = P + block_scan_excl<kBlock, int64_t>(c, tmp, &tp);
+        const int64_t e0 = xp < cap ? xp : cap, e1 = xp + c < cap ? xp + c : cap;
+        const int64_t m = e1 - e0;
+        bad |= in && (raw < 0 || raw > cap - e0);
+        const int64_t xeb = EB + block_scan_excl<kBlock, int64_t>(cdiv(m, kEncCodes), tmp, &teb);
+        const int64_t xch = CH + block_scan_excl<kBlock, int64_t>(cdiv(m, (int64_t)SGC_CHUNK_CODES), tmp, &tch);
+        if (in) {
+            w.cnt[s] = m;
+            w.ent[s] = e0;
+            w.base[s] = scope == SGC_GLOBAL ? 0 : seg_off[s];
+            w.size[s] = scope == SGC_GLOBAL ? seg_off[nseg] : seg_off[s + 1] - seg_off[s];
+            w.ebpre[s] = xeb;
+            w.chpre[s] = xch;
         }
-        w.cnt[s] = m;
-        w.ent[s] = e;
-        w.base[s] = scope == SGC_GLOBAL ? 0 : seg_off[s];
-        w.size[s] = scope == SGC_GLOBAL ? seg_off[nseg] : seg_off[s + 1] - seg_off[s];
-        w.ebpre[s] = eb;
-        w.chpre[s] = ch;
-        e += m;
-        eb += cdiv(m, kEncCodes);
-        ch += cdiv(m, (int64_t)SGC_CHUNK_CODES);
+        P += tp;
+        EB += teb;
+        CH += tch;
     }
-    w.ent[S] = e;
-    w.ebpre[S] = eb;
-    w.chpre[S] = ch;
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) {
+        w.bad[0] = bad ? 1u : 0u;
+        w.ent[S] = P < cap ? P : cap;
+        w.ebpre[S] = EB;
+        w.chpre[S] = CH;
+    }
 }
 
 struct EncBlock {
@@ -219,16 +236,23 @@ __global__ __launch_bounds__(1024) void k_enc_scan(int32_t S, int64_t word_cap, 
     }
     if (threadIdx.x == 0) w.eboff[neb] = tmp[NW];
     __syncthreads();
-    if (threadIdx.x != 0) return;
-    uint64_t words = 0;
-    for (int32_t s = 0; s < S; ++s) {
-        const uint64_t b0 = w.eboff[w.ebpre[s]];
-        const uint64_t nb = w.eboff[w.ebpre[s + 1]] - b0;
-        w.sbit0[s] = b0;
-        word_off[s] = words;
-        nbits[s] = nb;
-        words += (nb + 31) / 32;
+    // per stream, one thread each in rounds: first bit, word offset, bit count
+    uint64_t words = 0;  // carried from round to round
+    for (int64_t s0 = 0; s0 < S; s0 += 1024) {
+        const int64_t s = s0 + threadIdx.x;
+        const bool in = s < S;
+        const uint64_t b0 = in ? w.eboff[w.ebpre[s]] : 0;
+        const uint64_t nb = in ? w.eboff[w.ebpre[s + 1]] - b0 : 0;
+        uint64_t tw;
+        const uint64_t xw = words + block_scan_excl<1024, uint64_t>((nb + 31) / 32, tmp, &tw);
+        if (in) {
+            w.sbit0[s] = b0;
+            word_off[s] = xw;
+            nbits[s] = nb;
+        }
+        words += tw;
     }
+    if (threadIdx.x != 0) return;
     word_off[S] = words;
     if (words > (uint64_t)word_cap) w.bad[0] |= 2u;  // only reachable with malformed input
     if (w.bad[0]) *status |= SGC_STATUS_BAD_INPUT;
@@ -457,7 +481,7 @@ extern "C" int sgc_encode(const sgc_layout* Lc, int32_t scope, int32_t b, const 
     hipStream_t s = (hipStream_t)stream;
     const int32_t S = enc_streams(L, scope);
     uint32_t* status = dstatus ? dstatus : w.st;
-    k_enc_setup<<<1, 64, 0, s>>>(counts, dt->seg_off, L->nseg, scope, cap, w);
+    k_enc_setup<<<1, kBlock, 0, s>>>(counts, dt->seg_off, L->nseg, scope, cap, w);
     SGC_LAUNCH_CHECK();
     const unsigned gb = (unsigned)std::min<int64_t>(enc_neb_max(L, scope, cap), 4096);
     k_enc_len<<<gb, kBlock, 0, s>>>(idx, S, b, w);

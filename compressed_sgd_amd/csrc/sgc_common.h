@@ -156,6 +156,34 @@ __device__ inline T block_exclusive_scan(T v, T* tmp, T* total)
     return res;
 }
 
+// Exclusive scan over a workgroup of NTH threads (a multiple of 64, at most
+// 1024); tmp holds NTH/64 + 1 entries.  Every thread gets its exclusive
+// prefix and the total; the trailing barrier lets the caller reuse tmp.
+template <int NTH, typename T>
+__device__ inline T block_scan_excl(T v, T* tmp, T* total)
+{
+    static_assert(NTH % 64 == 0 && NTH <= 1024, "whole waves");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    T x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        T y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        T run = 0;
+        for (int w = 0; w < NTH / 64; ++w) { T t = tmp[w]; tmp[w] = run; run += t; }
+        tmp[NTH / 64] = run;
+    }
+    __syncthreads();
+    T res = tmp[wave] + x - v;
+    *total = tmp[NTH / 64];
+    __syncthreads();
+    return res;
+}
+
 // ------------------------------------------------------------- layout
 struct DevTables {
     int64_t* seg_off = nullptr;   // [nseg+1]
