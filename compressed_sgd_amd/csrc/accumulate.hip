@@ -586,8 +586,11 @@ static void launch_decode(int colw, dim3 grid, const Batch& B, int32_t nseg, hip
 }
 
 // ------------------------------------------------------------------ merge
-// Persistent workgroups, each over a contiguous range of output tiles
-// (kOutTile elements each); a group of threads per message (a power of two)
+// Persistent workgroups over the output tiles (kOutTile elements each),
+// workgroup i taking tiles i, i + G, i + 2G, ... for a grid of G: clustered
+// entries (runs of dense tiles, as the rows of a Zipf-sampled embedding
+// give) spread over every workgroup instead of loading the few that a
+// contiguous range would give them to.  A group of threads per message (a power of two)
 // follows that message's entries, which stay in the registers of the thread
 // that loaded them.  Per tile:
 //  1  the tile's initial contents go to LDS; every entry marks its message
@@ -613,9 +616,9 @@ static void launch_decode(int colw, dim3 grid, const Batch& B, int32_t nseg, hip
 // zeros) it needs no registers for them and runs three workgroups per CU
 // (the LDS limit); with them, two.
 //
-// Software pipeline: while tile u is worked on, the entries and initial
-// contents of tile u+1 (LOAD only; and the entry-range bound of tile u+2) are
-// already in flight in registers.  In each iteration the stores of the previous tile are
+// Software pipeline: while tile j of the sequence is worked on, the entries
+// and initial contents of tile j+1 (LOAD only; and the entry-range bounds of
+// tile j+2) are already in flight in registers.  In each iteration the stores of the previous tile are
 // issued before the next loads: loads and stores share one completion
 // counter here, so a wait for loads also waits for earlier stores, and
 // those are then long done.  A tile whose entries do not fit the prefetch (a
@@ -704,7 +707,7 @@ __device__ int32_t g_zero_word = 0;
 template <bool LOAD>
 __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t lg_tpm, int32_t init,
                                                  const float* __restrict__ base, float* __restrict__ out, int64_t n,
-                                                 int64_t ntiles, int64_t per)
+                                                 int64_t ntiles)
 {
     __shared__ __align__(16) MergeLds S;
     const int tid = threadIdx.x;
@@ -715,8 +718,11 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
     const float* valk = live ? M.val[mk] : nullptr;
     const int32_t* tsk = live ? M.tstart[mk] : nullptr;
     const float* src = init == SGC_INIT_BASE ? base : out;
-    const int64_t T0 = (int64_t)blockIdx.x * per, T1 = min(T0 + per, ntiles);
-    if (T0 >= T1) return;
+    // this workgroup's tiles: blockIdx.x, + gridDim.x, + 2 gridDim.x, ... (j-th: tile(j))
+    if ((int64_t)blockIdx.x >= ntiles) return;
+    const int64_t G = gridDim.x;
+    const int64_t J = (ntiles - (int64_t)blockIdx.x + G - 1) / G;
+    auto tile = [&](int64_t j) -> int64_t { return (int64_t)blockIdx.x + j * G; };
 
     // pipeline registers: the next tile's entries (global positions) and initial contents
     int32_t n_pos[kPre];
@@ -763,19 +769,22 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         }
     };
 
-    // prologue: ranges of tiles T0 and T0+1, the entries of T0 in flight
-    int32_t a_cur = ts(T0), a_nxt = ts(T0 + 1), a_nn = ts(T0 + 2);
+    // prologue: entry ranges of tiles 0 and 1 of the sequence, the entries of
+    // tile 0 in flight.  A tile's range is [ts(t), ts(t + 1)).
+    const int32_t a0 = ts(tile(0)), e0 = ts(tile(0) + 1);
+    int32_t a_nxt = ts(tile(1)), e_nxt = ts(tile(1) + 1);  // tile 1 (past the end: empty)
     if (ml == 0 && mk < kMerge) {
-        S.a[T0 & 1][mk] = a_cur;
-        S.cnt[T0 & 1][mk] = span(a_cur, a_nxt);
+        S.a[0][mk] = a0;
+        S.cnt[0][mk] = span(a0, e0);
     }
     clear_mask(S.mask);
-    load_tile(T0, a_cur, span(a_cur, a_nxt));
+    load_tile(tile(0), a0, span(a0, e0));
     __syncthreads();
-    if (tid < 64) tile_meta(S, (int)(T0 & 1), (int)(T0 % 3), M.n, kPre * tpm);
+    if (tid < 64) tile_meta(S, 0, 0, M.n, kPre * tpm);
 
-    for (int64_t u = T0; u < T1; ++u) {
-        const int b = (int)(u & 1), z = (int)(u % 3);
+    for (int64_t j = 0; j < J; ++j) {
+        const int64_t u = tile(j);
+        const int b = (int)(j & 1), z = (int)(j % 3);
         const int64_t lo = u * kOutTile;
         const int32_t cnt = (int32_t)min((int64_t)kOutTile, n - lo);
         // the previous tile (always whole) leaves LDS for memory; tile u's initial contents enter
@@ -784,7 +793,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
             const int i = 4 * (q * kMergeThreads + tid);
             const f4a pt = *(const f4a*)(S.tile + i);
             *(f4a*)(S.tile + i) = ini[q];
-            if (u > T0) __builtin_nontemporal_store(pt, (f4a*)(out + lo - kOutTile + i));
+            if (j > 0) __builtin_nontemporal_store(pt, (f4a*)(out + tile(j - 1) * kOutTile + i));
         }
         // this tile's entries, out of the pipeline registers, mark their messages
         int32_t ck[kPre], cp[kPre];
@@ -797,18 +806,20 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
             cv[i] = n_val[i];
         }
         mark_entries(S.mask, ck, cp);
-        // the next tile in flight: its range bound, entries and initial contents
-        const int32_t r_n3 = ts_load(u + 3);  // clamped at the end of the iteration
-        if (u + 1 < T1) {
+        // the next tile in flight (its entries and initial contents), and the
+        // range bounds of the one after it (clamped at the end of the iteration)
+        const int64_t t2 = tile(j + 2);
+        const int32_t r2a = ts_load(t2), r2e = ts_load(t2 + 1);
+        if (j + 1 < J) {
             if (ml == 0 && mk < kMerge) {
                 S.a[b ^ 1][mk] = a_nxt;
-                S.cnt[b ^ 1][mk] = span(a_nxt, a_nn);
+                S.cnt[b ^ 1][mk] = span(a_nxt, e_nxt);
             }
-            load_tile(u + 1, a_nxt, span(a_nxt, a_nn));
+            load_tile(tile(j + 1), a_nxt, span(a_nxt, e_nxt));
         }
         __syncthreads();
         const int32_t total = S.total[z], fits = S.fits[z];  // uniform
-        if (tid < 64 && u + 1 < T1) tile_meta(S, b ^ 1, (int)((u + 1) % 3), M.n, kPre * tpm);
+        if (tid < 64 && j + 1 < J) tile_meta(S, b ^ 1, (int)((j + 1) % 3), M.n, kPre * tpm);
         if (total == 0) {
             // nothing to add (and nothing was marked)
         } else if (fits) {
@@ -840,13 +851,12 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
                 if (tid == 0) S.maxc[z] = 1;
             }
         }
-        a_cur = a_nxt;
-        a_nxt = a_nn;
-        a_nn = ts_fix(u + 3, r_n3);
+        a_nxt = ts_fix(t2, r2a);
+        e_nxt = ts_fix(t2 + 1, r2e);
     }
     __syncthreads();
     // the last tile
-    const int64_t lo = (T1 - 1) * kOutTile;
+    const int64_t lo = tile(J - 1) * kOutTile;
     const int32_t cnt = (int32_t)min((int64_t)kOutTile, n - lo);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
@@ -1012,12 +1022,11 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         while (lg_tpm > 0 && (kMergeThreads >> lg_tpm) < M.n) --lg_tpm;
         const int32_t im = mb == 0 ? init : SGC_INIT_INPLACE;
         const bool load = im != SGC_INIT_ZERO;
-        const int64_t per = cdiv(ntiles, std::min<int64_t>(ntiles, load ? merge_blocks<true>() : merge_blocks<false>()));
-        const int64_t grid = cdiv(ntiles, per);
+        const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(ntiles, load ? merge_blocks<true>() : merge_blocks<false>()));
         if (load)
-            k_merge<true><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles, per);
+            k_merge<true><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles);
         else
-            k_merge<false><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles, per);
+            k_merge<false><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles);
         SGC_LAUNCH_CHECK();
         if (dstatus && M.n > 0) {
             k_fold_status<<<1, 64, 0, s>>>(M, dstatus);
