@@ -48,8 +48,9 @@ def random_values(rng, n):
     return g
 
 
-def one_message(orc, layout, rng, what):
-    """One worker step on both sides; returns the GPU and oracle messages."""
+def one_message(orc, layout, rng, what, **fixed):
+    """One worker step on both sides; returns the GPU and oracle messages.
+    fixed: any of ppm, scope, mode, kind, b, enc_scope, instead of a random draw."""
     n = layout.n
     seg_off = np.array(layout.seg_off, np.int64)
     ppm = int(rng.choice(PPMS))
@@ -58,6 +59,12 @@ def one_message(orc, layout, rng, what):
     kind = KINDS[int(rng.integers(0, len(KINDS)))]
     b = int(rng.integers(0, 15))
     enc_scope = int(rng.integers(0, 2))
+    ppm = fixed.get("ppm", ppm)
+    scope = fixed.get("scope", scope)
+    mode = fixed.get("mode", mode)
+    kind = fixed.get("kind", kind)
+    b = fixed.get("b", b)
+    enc_scope = fixed.get("enc_scope", enc_scope)
     g = random_values(rng, n)
     r = (rng.normal(0, 3e-4, n) * (rng.random(n) < 0.5)).astype(np.float32)
     announce(f"{what}: n={n} nseg={layout.nseg} ppm={ppm} scope={scope} mode={mode} kind={kind} b={b} "
@@ -132,3 +139,38 @@ def test_random_pipeline(orc, seed):
     ost = orc.decode_accumulate(om, np.array(layout.seg_off, np.int64), ref)
     assert ost == 0 and int(host(st)[0]) == 0, f"seed {seed}: status {ost} / {int(host(st)[0])}"
     assert_bitwise(host(out), ref, f"seed {seed}: dense sum")
+
+
+@pytest.mark.parametrize("nseg", [300, 1500, 2100])
+def test_many_segments(orc, nseg):
+    # more segments than one round of the per-segment bookkeeping (256 or
+    # 1024 threads, one segment each): prefixes carried across rounds in the
+    # compress set-up and tile scan, binarize set-up, encode set-up and
+    # stream offsets, and the message set-up; every stage against the oracle
+    rng = np.random.default_rng(9100 + nseg)
+    sizes = [int(x) for x in rng.integers(0, 3000, nseg)]
+    for t in range(0, nseg, 7):
+        sizes[t] = 0
+    layout = sgc.Layout(sizes)
+    n = layout.n
+    combos = [
+        dict(scope=1, mode=sgc.EXACT, kind="golomb_sbc", enc_scope=1, ppm=20000),
+        dict(scope=1, mode=sgc.SAMPLED, kind="golomb_f32", enc_scope=1, ppm=5000),
+        dict(scope=0, mode=sgc.EXACT, kind="golomb_2bit", enc_scope=1, ppm=100000),
+        dict(scope=1, mode=sgc.EXACT, kind="raw_2bit", ppm=1000),
+        dict(scope=0, mode=sgc.SAMPLED, kind="raw_f32", ppm=20000),
+        dict(scope=1, mode=sgc.EXACT, kind="golomb_f32", enc_scope=0, ppm=400000),
+    ]
+    gm, om = [], []
+    for wk, fixed in enumerate(combos):
+        a, o = one_message(orc, layout, rng, f"nseg {nseg} worker {wk}", **fixed)
+        gm.append(a)
+        om.append(o)
+    out = torch.zeros(n, dtype=torch.float32, device="cuda")
+    announce(f"nseg {nseg}: decode_accumulate W={len(gm)}")
+    st = sgc.decode_accumulate(layout, gm, out)
+    torch.cuda.synchronize()
+    ref = np.zeros(n, np.float32)
+    ost = orc.decode_accumulate(om, np.array(layout.seg_off, np.int64), ref)
+    assert ost == 0 and int(host(st)[0]) == 0
+    assert_bitwise(host(out), ref, f"nseg {nseg}: dense sum")
