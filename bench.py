@@ -72,6 +72,28 @@ def timed(fn, reps, stream):
     return e0.elapsed_time(e1) / reps
 
 
+def graph_timed(fn, reps, stream):
+    """fn captured once in a HIP graph (after an eager warm-up call) and
+    replayed: the launch cost of its kernels leaves the timed region."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / reps
+
+
 def workload_rows(sgc, W, torch, dev, stream, reps=10):
     """Every workload besides the 2^30 one, on its own shapes: the worker step
     (compress exact and sampled, plus the binarize / Rice / delay steps the
@@ -100,6 +122,19 @@ def workload_rows(sgc, W, torch, dev, stream, reps=10):
             it[0] += 1
         t = timed(step, reps, stream)
         row[f"compress_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "kept": c.total()}
+    # the same step with its Rice encode, replayed from a HIP graph (no launch cost)
+    r = torch.zeros(n, dtype=torch.float32, device=dev)
+    g_in = gs[0].clone()
+    c = sgc.compress(L, g_in, r, keep_ppm=w.keep_ppm)
+    bf = sgc.rice_param(w.keep_ppm / 1e6)
+    e = sgc.encode(L, c.idx, c.counts, c.cap, b=bf)
+
+    def step_enc():
+        sgc.compress(L, g_in, r, keep_ppm=w.keep_ppm, out=c)
+        sgc.encode(L, c.idx, c.counts, c.cap, b=bf, out=e)
+    t = timed(step_enc, reps, stream)
+    tg = graph_timed(step_enc, reps, stream)
+    row["compress_encode_exact"] = {"ms": t, "ms_graph": tg, "elements_per_s_graph": el(n, tg)}
     rows[w.name] = row
 
     # mlp-mnist: global top-1% + 2-bit per worker; 4 raw 2-bit messages summed into zeros
@@ -181,6 +216,9 @@ def workload_rows(sgc, W, torch, dev, stream, reps=10):
         tr = timed(rnd, reps, stream)
         row[f"exchange_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "steps": "compress + SBC + Rice"}
         row[f"round_{tag}"] = {"ms": tr, "steps": f"{w.delay - 1} accumulations + exchange"}
+        if mode == sgc.EXACT:  # the same, replayed from a HIP graph
+            row[f"exchange_{tag}"]["ms_graph"] = graph_timed(exchange, reps, stream)
+            row[f"round_{tag}"]["ms_graph"] = graph_timed(rnd, reps, stream)
     out = torch.empty(n, dtype=torch.float32, device=dev)
     t = timed(lambda: sgc.decode_accumulate(L, msgs, out), reps, stream)
     row["receive"] = {"ms": t, "elements_per_s": el(n, t), "messages": len(msgs), "format": "Rice + SBC mean"}
