@@ -100,6 +100,27 @@ def test_probe_defeated_takes_full_pass_path(orc):
     assert st & sgc.STATUS_DENSE_PATH
 
 
+def test_candidate_array_full(orc):
+    # Segments of equal magnitudes make every element a candidate (the candidate bound is that
+    # magnitude).  At 1% the array holds 4K + 2^18 = 280,144 entries.  Per tensor: the first
+    # segment's 100,000 fit, the second's 300,000 do not (full passes over the residual), and
+    # the small normal segment after them is also taken by full passes.  Globally: 400,000
+    # candidates, full passes.  Ties go to the lowest indices either way.
+    rng = np.random.default_rng(12)
+    sizes = [100000, 300000, 50000]
+    n = sum(sizes)
+    g = np.empty(n, np.float32)
+    g[:100000] = 1.0
+    g[100000:400000] = -1.0  # the same magnitude: one run of 400,000 tied candidates in global scope
+    g[400000:] = rng.normal(0, 1e-3, 50000).astype(np.float32)
+    layout = sgc.Layout(sizes)
+    for scope in (1, 0):
+        r = np.zeros(n, np.float32)
+        out, st = check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=10000,
+                             what=f"candidate array full scope{scope}")
+        assert st & sgc.STATUS_DENSE_PATH
+
+
 def test_clustered_overflowing_tiles(orc):
     # All large values in a few contiguous runs: some tiles hold far more candidates than
     # their region, and those tiles are redone from the residual.
