@@ -299,7 +299,11 @@ __global__ __launch_bounds__(kBlock) void k_bin_apply_sbc(const int32_t* __restr
     }
 }
 
-// One thread per output word of 16 two-bit codes.
+// One lane per entry, 16 consecutive lanes per output word of 16 two-bit
+// codes (their codes OR-ed together by shuffles): coalesced loads and
+// stores, and every entry of the message in flight at once.  Each wave
+// takes 4 words (64 entries) at a time; the segment of its first entry is
+// found once and the lanes step forward over segment ends (rare).
 __global__ __launch_bounds__(kBlock) void k_bin_apply_2bit(const int32_t* __restrict__ idx, const float* __restrict__ val,
                                                           int32_t nseg, BinWs w, float* __restrict__ res, int64_t n,
                                                           int32_t* __restrict__ out_idx, uint32_t* __restrict__ codes,
@@ -307,40 +311,26 @@ __global__ __launch_bounds__(kBlock) void k_bin_apply_2bit(const int32_t* __rest
 {
     const int64_t total = w.estart[nseg];
     const int64_t nwords = cdiv(total, 16);
-    for (int64_t wd = (int64_t)blockIdx.x * kBlock + threadIdx.x; wd < nwords; wd += (int64_t)gridDim.x * kBlock) {
-        const int64_t j0 = wd * 16;
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t)gridDim.x * (kBlock / 64);
+    for (int64_t w0 = ((int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * 4; w0 < nwords; w0 += waves * 4) {
+        const int64_t j0 = w0 * 16, j = j0 + lane;  // uniform per wave
+        const bool in = j < total;
+        const int64_t jc = in ? j : total - 1;  // clamped, unconditional loads
+        const float v = val[jc];
+        const int32_t id = idx[jc];
         int64_t t = find_bucket(w.estart, (int64_t)nseg + 1, j0);
-        // clamped, unconditional loads (see k_bin_sums)
-        float vv[16];
-        int32_t ii[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int64_t j = min(j0 + q, total - 1);
-            vv[q] = val[j];
-            ii[q] = idx[j];
-        }
-        int64_t tend = w.estart[t + 1];
-        float mp = w.mpos[t], mn = w.mneg[t];
-        uint32_t word = 0;
-        for (int q = 0; q < 16; ++q) {
-            const int64_t j = j0 + q;
-            if (j >= total) break;
-            while (j >= tend) {  // the next segment (rare)
-                ++t;
-                tend = w.estart[t + 1];
-                mp = w.mpos[t];
-                mn = w.mneg[t];
-            }
-            const float v = vv[q];
-            const uint32_t code = v > 0.0f ? 1u : v < 0.0f ? 2u : 0u;
-            const float qv = code == 1u ? mp : code == 2u ? -mn : 0.0f;
-            const int32_t id = ii[q];
-            // code 0: v - (+0) is v itself, already there when held
-            if ((uint32_t)id < (uint32_t)n && (code != 0u || !held)) res[id] = v - qv;
-            if (out_idx) out_idx[j] = id;
-            word |= code << (2 * q);
-        }
-        codes[wd] = word;
+        while (t + 1 < nseg && jc >= w.estart[t + 1]) ++t;  // a later segment (rare)
+        const float mp = w.mpos[t], mn = w.mneg[t];
+        const uint32_t code = !in ? 0u : v > 0.0f ? 1u : v < 0.0f ? 2u : 0u;
+        const float qv = code == 1u ? mp : code == 2u ? -mn : 0.0f;
+        // code 0: v - (+0) is v itself, already there when held
+        if (in && (uint32_t)id < (uint32_t)n && (code != 0u || !held)) res[id] = v - qv;
+        if (in && out_idx) out_idx[j] = id;
+        uint32_t word = code << (2 * (lane & 15));
+        for (int d = 1; d < 16; d <<= 1) word |= __shfl_xor(word, d, 64);
+        const int64_t wd = w0 + (lane >> 4);
+        if ((lane & 15) == 0 && wd < nwords) codes[wd] = word;
     }
 }
 
@@ -393,7 +383,7 @@ extern "C" int sgc_binarize(const sgc_layout* Lc, int32_t mode, const int32_t* i
     if (mode == SGC_BIN_SBC) {
         k_bin_apply_sbc<<<cb, kBlock, 0, s>>>(idx, val, nseg, w, residual, L->n, out_idx, cap, held);
     } else {
-        const unsigned wb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(cdiv(cap, 16), kBlock), 4096));
+        const unsigned wb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(cap, kBlock), 4096));
         k_bin_apply_2bit<<<wb, kBlock, 0, s>>>(idx, val, nseg, w, residual, L->n, out_idx, out_codes, held);
     }
     SGC_LAUNCH_CHECK();
