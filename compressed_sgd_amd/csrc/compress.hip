@@ -1198,30 +1198,48 @@ __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ re
     }
 }
 
-// Per-segment counts of the (ascending) output by binary search.
-__global__ void k_seg_counts(const int64_t* __restrict__ seg_off, int32_t nseg, const int32_t* __restrict__ out_idx,
-                             CompressWs w, int64_t* __restrict__ out_counts)
+// First entry at or after position x among the ascending a[lo, hi), found
+// by a whole wave: 64 evenly spaced probes per round narrow the interval
+// about 64-fold (a handful of dependent loads instead of one per halving);
+// every lane returns the same answer (hi when every entry is below x).
+__device__ inline int64_t wave_lower_bound(const int32_t* __restrict__ a, int64_t lo, int64_t hi, int64_t x)
+{
+    const int lane = threadIdx.x & 63;
+    while (hi - lo > 64) {  // uniform
+        const int64_t step = (hi - lo + 63) / 64;
+        const int64_t p = lo + lane * step;
+        const bool below = p < hi && (int64_t)a[p < hi ? p : hi - 1] < x;
+        const int c = __popcll(__ballot(below));  // the probes below x are a prefix of the lanes
+        if (c == 0) return lo;
+        const int64_t nhi = lo + (int64_t)c * step;
+        lo = lo + (int64_t)(c - 1) * step + 1;
+        hi = nhi < hi ? nhi : hi;
+    }
+    if (lo >= hi) return lo;
+    const int64_t p = lo + lane;
+    const bool below = p < hi && (int64_t)a[p < hi ? p : hi - 1] < x;
+    return lo + __popcll(__ballot(below));
+}
+
+// Per-segment counts of the (ascending) output: one wave per segment, two
+// searches for the entries below its first and past its last element.
+__global__ __launch_bounds__(kBlock) void k_seg_counts(const int64_t* __restrict__ seg_off, int32_t nseg,
+                                                      const int32_t* __restrict__ out_idx, CompressWs w,
+                                                      int64_t* __restrict__ out_counts)
 {
     const int64_t total = w.scal[0];
-    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t <= nseg; t += (int64_t)gridDim.x * kBlock) {
-        if (t == nseg) {
-            out_counts[nseg] = total;
+    const int64_t waves = (int64_t)gridDim.x * (kBlock / 64);
+    const bool lead = (threadIdx.x & 63) == 0;
+    for (int64_t t = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6); t <= nseg; t += waves) {
+        if (t == nseg) {  // uniform per wave
+            if (lead) out_counts[nseg] = total;
             continue;
         }
-        // entries below x0 and below x1 (indices ascend; every index lies in [0, n))
+        // every index lies in [0, n): nothing below element 0, everything below n
         const int64_t x0 = seg_off[t], x1 = seg_off[t + 1];
-        int64_t a0 = 0, a1 = x0 == 0 ? 0 : total;
-        while (a0 < a1) {
-            int64_t m = (a0 + a1) >> 1;
-            if (out_idx[m] < x0) a0 = m + 1; else a1 = m;
-        }
-        int64_t b0 = a0, b1 = total;
-        if (x1 == seg_off[nseg]) b0 = total;
-        while (b0 < b1) {
-            int64_t m = (b0 + b1) >> 1;
-            if (out_idx[m] < x1) b0 = m + 1; else b1 = m;
-        }
-        out_counts[t] = b0 - a0;
+        const int64_t a = x0 == 0 ? 0 : wave_lower_bound(out_idx, 0, total, x0);
+        const int64_t b = x1 == seg_off[nseg] ? total : wave_lower_bound(out_idx, a, total, x1);
+        if (lead) out_counts[t] = b - a;
     }
 }
 
@@ -1400,7 +1418,7 @@ static int compress_impl(sgc_layout* L, const sgc_compress_opts* o, bool hold, M
         SGC_LAUNCH_CHECK();
     }
     if (counts_known) return SGC_OK;
-    unsigned sb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(L->nseg + 1, kBlock), 1024));
+    unsigned sb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(L->nseg + 1, kBlock / 64), 1024));
     k_seg_counts<<<sb, kBlock, 0, s>>>(dt->seg_off, L->nseg, out_idx, w, out_counts);
     SGC_LAUNCH_CHECK();
     return SGC_OK;
