@@ -863,6 +863,7 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_scan2(const int64_t* __re
 // to u wherever acc is given back to r; a redone entry that is sent has its
 // momentum zeroed here (sampled) or in the compaction (exact).
 constexpr int kGatherPer = 8;  // region entries per thread per round, loads all in flight
+constexpr uint32_t kWaveGatherCap = 1024;  // regions this large (or larger) are copied a tile per wave
 
 template <typename M>
 __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ grad, float* __restrict__ res,
@@ -915,56 +916,87 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float* __restrict__ gra
     __syncthreads();
     const int32_t g_lds = s_hg[0];
     uint32_t* const ghist = w.hist + (blockIdx.x & (kRep - 1)) * kBins;  // + group * kRep * kBins
-    const uint32_t E = s_pre[kGatherTiles];
-    for (uint32_t e0 = 0; e0 < E; e0 += kBlock * kGatherPer) {  // uniform
-        int32_t id[kGatherPer];
-        float v[kGatherPer], um[kGatherPer];
-        int qs[kGatherPer];
-#pragma unroll
-        for (int u = 0; u < kGatherPer; ++u) {  // clamped, unconditional loads (all in flight)
-            const uint32_t e = min(e0 + u * kBlock + threadIdx.x, E - 1);
-            int q = 0;  // last tile whose entries start at or before e
-            for (int hb = 32; hb >= 1; hb >>= 1)
-                if (e >= s_pre[q + hb]) q += hb;
-            const int64_t at = (t0 + q) * w.tcap + (e - s_pre[q]);
-            id[u] = w.reg_idx[at];
-            v[u] = w.reg_val[at];
-            um[u] = M::on ? w.reg_mom[at] : 0.0f;
-            qs[u] = e0 + u * kBlock + threadIdx.x < E ? q : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kGatherPer; ++u) {
-            const int q = qs[u];
-            const uint32_t bin = mag_key(v[u]) >> 20;
-            bool lds_hit = false;
-            if (q >= 0) {
-                const uint32_t j = e0 + u * kBlock + threadIdx.x - s_pre[q];
-                const int32_t i = id[u];
-                const int64_t dst = s_dst[q];
-                if (dst < 0) {  // dense-path group: undo pass-1 zeroing
-                    if (mag_key(v[u]) >= s_z[q]) {
-                        res[i] = v[u];
-                        if constexpr (M::on) m.u[i] = um[u];
-                    }
-                } else if (sampled) {
-                    const int64_t p = dst + j;
-                    if (p < cap) {
-                        out_idx[p] = i;
-                        out_val[p] = v[u];
-                    } else {
-                        res[i] = v[u];  // truncated: stays in the residual (and keeps its momentum)
-                        if constexpr (M::on) m.u[i] = um[u];
-                    }
+    // entry j of tile q (value v, index i, u' um) where it belongs: the
+    // candidate array (counting its first digit), the output (sampled), or
+    // back into the residual (dense-path groups); every lane of the wave
+    // calls it (the digit count takes wave ballots), ok = the entry exists
+    auto place = [&](int q, uint32_t j, int32_t i, float v, float um, bool ok) {
+        const uint32_t bin = mag_key(v) >> 20;
+        bool lds_hit = false;
+        if (ok) {
+            const int64_t dst = s_dst[q];
+            if (dst < 0) {  // dense-path group: undo pass-1 zeroing
+                if (mag_key(v) >= s_z[q]) {
+                    res[i] = v;
+                    if constexpr (M::on) m.u[i] = um;
+                }
+            } else if (sampled) {
+                const int64_t p = dst + j;
+                if (p < cap) {
+                    out_idx[p] = i;
+                    out_val[p] = v;
                 } else {
-                    w.cand_idx[dst + j] = i;
-                    w.cand_val[dst + j] = v[u];
-                    if constexpr (M::on) w.cand_mom[dst + j] = um[u];
-                    const int32_t hg = s_hg[q];
-                    if (hg >= 0 && hg == g_lds) lds_hit = true;
-                    else if (hg >= 0) atomicAdd(&ghist[(int64_t)hg * kRep * kBins + bin], 1u);
+                    res[i] = v;  // truncated: stays in the residual (and keeps its momentum)
+                    if constexpr (M::on) m.u[i] = um;
+                }
+            } else {
+                w.cand_idx[dst + j] = i;
+                w.cand_val[dst + j] = v;
+                if constexpr (M::on) w.cand_mom[dst + j] = um;
+                const int32_t hg = s_hg[q];
+                if (hg >= 0 && hg == g_lds) lds_hit = true;
+                else if (hg >= 0) atomicAdd(&ghist[(int64_t)hg * kRep * kBins + bin], 1u);
+            }
+        }
+        if (!sampled) lds_count(h, lds_hit, bin);
+    };
+    if (w.tcap >= kWaveGatherCap) {  // uniform
+        // full regions (high kept fractions): each wave copies whole tiles, 64
+        // consecutive entries per load -- no search for the tile of an entry
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        for (int q = wave; q < kGatherTiles; q += kBlock / 64) {
+            const uint32_t c = s_pre[q + 1] - s_pre[q];  // 0 for an overflowed tile (redone below)
+            const int64_t rb = (t0 + q) * w.tcap;
+            for (uint32_t j0 = 0; j0 < c; j0 += 64 * kGatherPer) {  // uniform per wave
+                int32_t id[kGatherPer];
+                float v[kGatherPer], um[kGatherPer];
+#pragma unroll
+                for (int u = 0; u < kGatherPer; ++u) {  // clamped, unconditional loads (all in flight)
+                    const int64_t at = rb + min(j0 + u * 64 + lane, c - 1);
+                    id[u] = w.reg_idx[at];
+                    v[u] = w.reg_val[at];
+                    um[u] = M::on ? w.reg_mom[at] : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < kGatherPer; ++u) {
+                    const uint32_t j = j0 + u * 64 + lane;
+                    place(q, j, id[u], v[u], um[u], j < c);
                 }
             }
-            if (!sampled) lds_count(h, lds_hit, bin);
+        }
+    } else {
+        const uint32_t E = s_pre[kGatherTiles];
+        for (uint32_t e0 = 0; e0 < E; e0 += kBlock * kGatherPer) {  // uniform
+            int32_t id[kGatherPer];
+            float v[kGatherPer], um[kGatherPer];
+            int qs[kGatherPer];
+#pragma unroll
+            for (int u = 0; u < kGatherPer; ++u) {  // clamped, unconditional loads (all in flight)
+                const uint32_t e = min(e0 + u * kBlock + threadIdx.x, E - 1);
+                int q = 0;  // last tile whose entries start at or before e
+                for (int hb = 32; hb >= 1; hb >>= 1)
+                    if (e >= s_pre[q + hb]) q += hb;
+                const int64_t at = (t0 + q) * w.tcap + (e - s_pre[q]);
+                id[u] = w.reg_idx[at];
+                v[u] = w.reg_val[at];
+                um[u] = M::on ? w.reg_mom[at] : 0.0f;
+                qs[u] = e0 + u * kBlock + threadIdx.x < E ? q : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kGatherPer; ++u) {
+                const int q = qs[u] < 0 ? 0 : qs[u];
+                place(q, e0 + u * kBlock + threadIdx.x - s_pre[q], id[u], v[u], um[u], qs[u] >= 0);
+            }
         }
     }
     // overflowed tiles: redo from r (which pass 1 left as acc there).  The
