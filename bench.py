@@ -18,8 +18,10 @@ correction, Rice encode at both densities,
 SBC binarize, decode-accumulate of 16 workers' Rice messages), every other
 workload on its own shapes (flat 2^20; the MLP with 2-bit messages; the
 NMT-style model with its global+local sum; ResNet-50 per tensor with delay,
-SBC and Rice: worker step exact and sampled, and the receive step), and the
-CPU oracle timed on a bounded sample as a baseline.
+SBC and Rice: worker step exact and sampled, and the receive step), a grid
+of communication delay (1, 10, 100) against kept fraction (25% to 0.1%)
+with time and bits per element per iteration, and the CPU oracle timed on a
+bounded sample as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -92,6 +94,42 @@ def graph_timed(fn, reps, stream):
     torch.cuda.synchronize()
     del graph
     return e0.elapsed_time(e1) / reps
+
+
+def sparsity_grid(sgc, W, torch, dev, stream, log2n=26, reps=5):
+    """Temporal versus gradient sparsity: communication delay n (n - 1
+    accumulate-only steps, then one exchange: exact top-p compress + Rice)
+    crossed with the kept fraction p, on the first 2^log2n elements of the
+    flat gradient.  Per cell: time per training iteration, ((n - 1) x the
+    measured accumulate step + the measured exchange) / n, and the bits sent
+    per element per iteration, (Rice position bits + 32 value bits per kept
+    entry) / (n x elements)."""
+    w = W.FLAT_1G
+    N = 1 << log2n
+    L = sgc.Layout([N])
+    g = W.gradient(w, 0, 0, device=dev, numel=N)
+    r = torch.zeros(N, dtype=torch.float32, device=dev)
+    t_acc = timed(lambda: sgc.compress(L, g, r, mode=sgc.ACCUMULATE_ONLY), reps, stream)
+    exch = {}
+    for p in (250000, 100000, 10000, 1000):
+        b = sgc.rice_param(p / 1e6)
+        c = sgc.compress(L, g, r, keep_ppm=p)
+        e = sgc.encode(L, c.idx, c.counts, c.cap, b=b)
+
+        def step():
+            sgc.compress(L, g, r, keep_ppm=p, out=c)
+            sgc.encode(L, c.idx, c.counts, c.cap, b=b, out=e)
+        t = timed(step, reps, stream)
+        exch[p] = (t, int(e.nbits[0].item()), c.total(), b)
+        del c, e
+    cells = []
+    for n_delay in (1, 10, 100):
+        for p, (t, nbits, kept, b) in exch.items():
+            cells.append({"delay": n_delay, "keep_pct": p / 1e4, "rice_b": b,
+                          "ms_per_iteration": ((n_delay - 1) * t_acc + t) / n_delay,
+                          "bits_per_element_per_iteration": (nbits + 32.0 * kept) / (n_delay * N)})
+    return {"elements": N, "accumulate_ms": t_acc,
+            "exchange_ms": {f"{p / 1e4:g}pct": v[0] for p, v in exch.items()}, "cells": cells}
 
 
 def workload_rows(sgc, W, torch, dev, stream, reps=10):
@@ -454,6 +492,8 @@ def main():
         del r16, outd
         print("[bench] the other workloads", file=sys.stderr, flush=True)
         out["workloads"] = workload_rows(sgc, W, torch, dev, stream)
+        print("[bench] temporal x gradient sparsity grid", file=sys.stderr, flush=True)
+        out["sparsity_grid"] = sparsity_grid(sgc, W, torch, dev, stream)
 
     if not args.no_cpu_baseline:
         import oracle as orc
