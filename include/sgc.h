@@ -38,6 +38,12 @@
  *   device can see are OR-ed into *dstatus (device uint32, may be NULL).
  * - Results are deterministic: no floating-point atomics; every sum has a
  *   fixed order.
+ * - Graph capture: once a layout has been used on a device (its first use
+ *   there uploads its tables synchronously), a call queues only kernel
+ *   launches on `stream` -- no allocation, memset or synchronous copy -- so
+ *   a sequence of calls can be captured into a HIP graph and replayed.  The
+ *   sgc_layout_* calls and a layout's first use on a device cannot be
+ *   captured.
  */
 #ifndef SGC_H
 #define SGC_H
