@@ -151,7 +151,8 @@ __global__ __launch_bounds__(kBlock) void k_msg_setup(Batch B, const int64_t* __
             int64_t cnt = 0;
             bool sbad = false;
             if (on) {
-                cnt = glob ? e : w.estart[s + 1] - w.estart[s];
+                // the total e stands for estart[nseg] (thread 0 stores it, unsynchronised)
+                cnt = glob ? e : (s + 1 == nseg ? e : w.estart[s + 1]) - w.estart[s];
                 const int64_t size = glob ? n : seg_off[s + 1] - seg_off[s];
                 w.scnt[s] = cnt;
                 w.sbase[s] = glob ? 0 : seg_off[s];
