@@ -33,9 +33,17 @@ struct EncWs {
     uint64_t* ebits; // [neb] bits per encode block
     uint64_t* eboff; // [neb+1] flat exclusive prefix of ebits
     uint64_t* sbit0; // [S] flat bit offset of each stream's first block
+    uint64_t* part;  // [neb_max / kScanPart + 1] bit totals per scan part (split scan only)
     uint32_t* bad;   // [1] malformed-input flags
     uint32_t* st;    // [1] status target when the caller passes none
 };
+
+// The block-offset scan runs in one workgroup up to kScanSplit encode
+// blocks; beyond that (kept fractions of ~5% and up at 2^30 elements) one
+// workgroup does too much shuffle work, and it is split over workgroups of
+// kScanPart blocks each.
+constexpr int64_t kScanPart = 4096;
+constexpr int64_t kScanSplit = 16384;
 
 static int32_t enc_streams(const sgc_layout* L, int32_t scope) { return scope == SGC_GLOBAL ? 1 : L->nseg; }
 static int64_t enc_neb_max(const sgc_layout* L, int32_t scope, int64_t cap)
@@ -55,6 +63,7 @@ static void carve_enc(Carver& c, const sgc_layout* L, int32_t scope, int64_t cap
     w->ebits = c.take<uint64_t>(neb);
     w->eboff = c.take<uint64_t>(neb + 1);
     w->sbit0 = c.take<uint64_t>(S);
+    w->part = c.take<uint64_t>(cdiv(neb, kScanPart) + 1);
     w->bad = c.take<uint32_t>(1);
     w->st = c.take<uint32_t>(1);
 }
@@ -183,13 +192,53 @@ constexpr int kEncScanU = 4;  // 64-entry steps per batch of loads in the block 
 // every lane of a load on its own cache line); the range total first, then,
 // after the wave offsets are known, a shuffle scan per step with a running
 // carry.
+// Split scan, part 1: the bit total of each part of kScanPart encode blocks
+// (coalesced reads; parts past the end give 0).
+__global__ __launch_bounds__(kBlock) void k_enc_scan_part(int32_t S, EncWs w)
+{
+    __shared__ uint64_t tmp[kBlock / 64 + 1];
+    const int64_t neb = w.ebpre[S];
+    const int64_t b0 = (int64_t)blockIdx.x * kScanPart, b1 = min(b0 + kScanPart, neb);
+    uint64_t local = 0;
+    for (int64_t i = b0 + threadIdx.x; i < b1; i += kBlock) local += w.ebits[i];
+    uint64_t total;
+    block_scan_excl<kBlock, uint64_t>(local, tmp, &total);
+    if (threadIdx.x == 0) w.part[blockIdx.x] = total;
+}
+
+// Split scan, part 2: each workgroup adds up the parts before its own (a few
+// dozen at most) and scans its part in rounds of kBlock, coalesced; the
+// workgroup holding the last block writes the flat total.
+__global__ __launch_bounds__(kBlock) void k_enc_scan_apply(int32_t S, EncWs w)
+{
+    __shared__ uint64_t tmp[kBlock / 64 + 1];
+    const int64_t neb = w.ebpre[S];
+    const int64_t b0 = (int64_t)blockIdx.x * kScanPart, b1 = min(b0 + kScanPart, neb);
+    uint64_t before = 0;
+    for (int64_t q = threadIdx.x; q < (int64_t)blockIdx.x; q += kBlock) before += w.part[q];
+    uint64_t carry;
+    block_scan_excl<kBlock, uint64_t>(before, tmp, &carry);
+    for (int64_t r0 = b0; r0 < b1; r0 += kBlock) {  // uniform
+        const int64_t i = r0 + threadIdx.x;
+        const uint64_t v = i < b1 ? w.ebits[i] : 0;
+        uint64_t t;
+        const uint64_t x = block_scan_excl<kBlock, uint64_t>(v, tmp, &t);
+        if (i < b1) w.eboff[i] = carry + x;
+        carry += t;
+    }
+    const bool last = b0 < neb ? b1 == neb : (blockIdx.x == 0 && neb == 0);
+    if (last && threadIdx.x == 0) w.eboff[neb] = carry;
+}
+
+// split: the flat prefix (eboff) is done already (k_enc_scan_part and
+// k_enc_scan_apply); only the per-stream tables are left.
 __global__ __launch_bounds__(1024) void k_enc_scan(int32_t S, int64_t word_cap, EncWs w,
                                                   uint64_t* __restrict__ word_off, uint64_t* __restrict__ nbits,
-                                                  uint32_t* status)
+                                                  uint32_t* status, int32_t split)
 {
     __shared__ uint64_t tmp[1024 / 64 + 1];
     constexpr int NW = 1024 / 64;
-    const int64_t neb = w.ebpre[S];
+    const int64_t neb = split ? 0 : w.ebpre[S];  // split: the flat scan below does nothing
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t L = cdiv(cdiv(neb, (int64_t)NW), (int64_t)64) * 64;
     const int64_t b = min(wave * L, neb), e = min(b + L, neb);
@@ -234,7 +283,7 @@ __global__ __launch_bounds__(1024) void k_enc_scan(int32_t S, int64_t word_cap, 
             carry += __shfl(x, 63, 64);
         }
     }
-    if (threadIdx.x == 0) w.eboff[neb] = tmp[NW];
+    if (threadIdx.x == 0 && !split) w.eboff[neb] = tmp[NW];
     __syncthreads();
     // per stream, one thread each in rounds: first bit, word offset, bit count
     uint64_t words = 0;  // carried from round to round
@@ -486,7 +535,16 @@ extern "C" int sgc_encode(const sgc_layout* Lc, int32_t scope, int32_t b, const 
     const unsigned gb = (unsigned)std::min<int64_t>(enc_neb_max(L, scope, cap), 4096);
     k_enc_len<<<gb, kBlock, 0, s>>>(idx, S, b, w);
     SGC_LAUNCH_CHECK();
-    k_enc_scan<<<1, 1024, 0, s>>>(S, word_cap, w, out_word_off, out_nbits, status);
+    const int64_t nebm = enc_neb_max(L, scope, cap);
+    const int32_t split = nebm > kScanSplit ? 1 : 0;
+    if (split) {
+        const unsigned pb = (unsigned)cdiv(nebm, kScanPart);
+        k_enc_scan_part<<<pb, kBlock, 0, s>>>(S, w);
+        SGC_LAUNCH_CHECK();
+        k_enc_scan_apply<<<pb, kBlock, 0, s>>>(S, w);
+        SGC_LAUNCH_CHECK();
+    }
+    k_enc_scan<<<1, 1024, 0, s>>>(S, word_cap, w, out_word_off, out_nbits, status, split);
     SGC_LAUNCH_CHECK();
     k_enc_pack<<<gb, kBlock, 0, s>>>(idx, S, b, w, out_words, out_word_off, out_chunk_off);
     SGC_LAUNCH_CHECK();

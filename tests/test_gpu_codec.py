@@ -83,6 +83,21 @@ def test_encode_ragged(orc, b, scope):
         check_encode(orc, layout, idx, counts, scope, b, f"ragged d={density}")
 
 
+@pytest.mark.parametrize("scope", [0, 1])
+def test_encode_split_offset_scan(orc, scope):
+    # About 36M codes: more than 16,384 encode blocks of 2048, so the block-offset scan is
+    # split over workgroups (part totals, then a prefix per part); two streams per message
+    # in per-segment scope.  Words, offsets, bit counts and the chunk table bitwise.
+    rng = np.random.default_rng(77 + scope)
+    n = 1 << 28
+    layout = sgc.Layout([n // 2, n // 2])
+    idx = np.flatnonzero(rng.random(n, dtype=np.float32) < 0.134).astype(np.int32)
+    half = int(np.searchsorted(idx, n // 2))
+    counts = np.array([half, idx.size - half, idx.size], np.int64)
+    assert idx.size > 16384 * 2048
+    check_encode(orc, layout, idx, counts, scope, 3, f"split scan scope{scope}")
+
+
 def test_encode_long_runs(orc):
     # embedding-like clusters: gaps of up to millions of elements (long unary runs)
     rng = np.random.default_rng(41)
