@@ -277,7 +277,7 @@ def main():
                          "the reference the HBM byte counters are scaled by")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the path has no cross-GPU step in this build); "
+        print(f"bench.py measures one GPU only (the library has no cross-GPU step); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 

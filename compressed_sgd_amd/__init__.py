@@ -69,8 +69,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                               "(python -c 'import __graft_entry__ as g; g.build()')")
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "'python compressed_sgd_amd/build.py' (hipcc, gfx950)")
         L = C.CDLL(LIB_PATH)
         P, i32, i64, u32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32, C.c_size_t
         L.sgc_layout_create.argtypes = [P, i32, C.POINTER(P)]
