@@ -51,6 +51,11 @@ constexpr int kGatherTiles = 64;                 // tiles per gather workgroup (
 constexpr uint32_t kAccFlag = 0x80000000u;       // candidate index flag: r still holds acc there
 constexpr int kRep = 8;                          // global histogram replicas per (virtual) group
 constexpr int kHistBlocks = 1024;                // workgroups of a histogram pass
+// The compaction's chunk-count scan runs in one workgroup unless the kept
+// total exceeds kChunkSplit chunks' worth (kept fractions of ~10% and up at
+// 2^30 elements); then it is split over workgroups of kChunkPart chunks.
+constexpr int64_t kChunkPart = 4096;
+constexpr int64_t kChunkSplit = 16384;
 
 // Momentum correction of one compress call ([SBC] appendix A): off, or on
 // with coefficient beta and the momentum vector u (u <- beta*u + g is what
@@ -104,6 +109,7 @@ struct CompressWs {
     uint32_t* ch_eq;   // [nch_max]
     int64_t* ch_gt_pre;// [nch_max+1]
     int64_t* ch_eq_pre;// [nch_max+1]
+    int64_t* cpart;    // [2 * (nch_max / kChunkPart + 1)] (gt, eq) totals per part (split chunk scan)
     int64_t* scal;     // [8]: 0 output total, 1 candidate total
     uint32_t* status;  // [1] used when the caller passes no dstatus
     int32_t* over;     // [NT] tiles whose region overflowed (any order)
@@ -172,11 +178,13 @@ static void carve_compress(Carver& c, const CompressSizes& z, int mode, bool mom
         w->ch_eq = c.take<uint32_t>(z.nch_max);
         w->ch_gt_pre = c.take<int64_t>(z.nch_max + 1);
         w->ch_eq_pre = c.take<int64_t>(z.nch_max + 1);
+        w->cpart = c.take<int64_t>(2 * (cdiv(z.nch_max, kChunkPart) + 1));
     } else {
         w->cand_idx = nullptr;
         w->cand_val = nullptr;
         w->ch_gt = w->ch_eq = nullptr;
         w->ch_gt_pre = w->ch_eq_pre = nullptr;
+        w->cpart = nullptr;
     }
     w->scal = c.take<int64_t>(8);
     w->status = c.take<uint32_t>(1);
@@ -1130,6 +1138,63 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_scan(int32_t G, Compress
     scan_u32_to_i64(w.ch_eq, w.ch_eq_pre, nch);
 }
 
+// Split chunk scan, part 1: the (gt, eq) totals of each part of kChunkPart
+// chunks (coalesced reads; parts past the end give 0).
+__global__ __launch_bounds__(kBlock) void k_chunk_part(int32_t G, CompressWs w)
+{
+    __shared__ int64_t tmp[kBlock / 64 + 1];
+    const int64_t nch = w.cpre[G];
+    const int64_t c0 = (int64_t)blockIdx.x * kChunkPart, c1 = min(c0 + kChunkPart, nch);
+    int64_t gt = 0, eq = 0;
+    for (int64_t c = c0 + threadIdx.x; c < c1; c += kBlock) {
+        gt += w.ch_gt[c];
+        eq += w.ch_eq[c];
+    }
+    int64_t tg, te;
+    block_scan_excl<kBlock, int64_t>(gt, tmp, &tg);
+    block_scan_excl<kBlock, int64_t>(eq, tmp, &te);
+    if (threadIdx.x == 0) {
+        w.cpart[2 * blockIdx.x] = tg;
+        w.cpart[2 * blockIdx.x + 1] = te;
+    }
+}
+
+// Split chunk scan, part 2: each workgroup adds up the parts before its own
+// and scans its chunks in rounds of kBlock, coalesced; the workgroup holding
+// the last chunk writes the totals.
+__global__ __launch_bounds__(kBlock) void k_chunk_apply(int32_t G, CompressWs w)
+{
+    __shared__ int64_t tmp[kBlock / 64 + 1];
+    const int64_t nch = w.cpre[G];
+    const int64_t c0 = (int64_t)blockIdx.x * kChunkPart, c1 = min(c0 + kChunkPart, nch);
+    int64_t bg = 0, be = 0;
+    for (int64_t q = threadIdx.x; q < (int64_t)blockIdx.x; q += kBlock) {
+        bg += w.cpart[2 * q];
+        be += w.cpart[2 * q + 1];
+    }
+    int64_t rg, re;
+    block_scan_excl<kBlock, int64_t>(bg, tmp, &rg);
+    block_scan_excl<kBlock, int64_t>(be, tmp, &re);
+    for (int64_t r0 = c0; r0 < c1; r0 += kBlock) {  // uniform
+        const int64_t c = r0 + threadIdx.x;
+        const int64_t g = c < c1 ? (int64_t)w.ch_gt[c] : 0, e = c < c1 ? (int64_t)w.ch_eq[c] : 0;
+        int64_t tg, te;
+        const int64_t xg = block_scan_excl<kBlock, int64_t>(g, tmp, &tg);
+        const int64_t xe = block_scan_excl<kBlock, int64_t>(e, tmp, &te);
+        if (c < c1) {
+            w.ch_gt_pre[c] = rg + xg;
+            w.ch_eq_pre[c] = re + xe;
+        }
+        rg += tg;
+        re += te;
+    }
+    const bool last = c0 < nch ? c1 == nch : (blockIdx.x == 0 && nch == 0);
+    if (last && threadIdx.x == 0) {
+        w.ch_gt_pre[nch] = rg;
+        w.ch_eq_pre[nch] = re;
+    }
+}
+
 template <typename M>
 __global__ __launch_bounds__(kBlock) void k_compact_write(float* __restrict__ res, int32_t G, CompressWs w,
                                                          int32_t* __restrict__ out_idx,
@@ -1444,8 +1509,18 @@ static int compress_impl(sgc_layout* L, const sgc_compress_opts* o, bool hold, M
         unsigned cb = (unsigned)std::min<int64_t>(z.nch_max, 2048);
         k_compact_count<<<cb, kBlock, 0, s>>>(residual, G, w);
         SGC_LAUNCH_CHECK();
-        k_chunk_scan<<<1, kScanThreads, 0, s>>>(G, w);
-        SGC_LAUNCH_CHECK();
+        int64_t K = 0;  // the kept total, an estimate of the candidates the scan will see
+        for (int32_t g = 0; g < G; ++g) K += keep_count(hoff[g + 1] - hoff[g], o->keep_ppm);
+        if (cdiv(K, kChunk) > kChunkSplit) {
+            const unsigned pb = (unsigned)(cdiv(z.nch_max, kChunkPart));  // covers any chunk count
+            k_chunk_part<<<pb, kBlock, 0, s>>>(G, w);
+            SGC_LAUNCH_CHECK();
+            k_chunk_apply<<<pb, kBlock, 0, s>>>(G, w);
+            SGC_LAUNCH_CHECK();
+        } else {
+            k_chunk_scan<<<1, kScanThreads, 0, s>>>(G, w);
+            SGC_LAUNCH_CHECK();
+        }
         k_compact_write<M><<<cb, kBlock, 0, s>>>(residual, G, w, out_idx, out_val, cap, m);
         SGC_LAUNCH_CHECK();
     }

@@ -208,6 +208,24 @@ def test_flat_1g_compress_encode_full_size(orc):
                        f"flat-1G step {step} chunk table")
 
 
+@pytest.mark.parametrize("ppm", [260000, 300000])
+def test_high_density_split_chunk_scan(ppm):
+    # 2^28 elements at 26% and 30% kept: more than 16,384 chunks of kept entries, so the
+    # compaction's chunk-count scan is split over workgroups; exact top-k through its
+    # defining properties (the oracle's full sort is too slow at this size)
+    w = W.FLAT_1G
+    n = 1 << 28
+    layout = sgc.Layout([n])
+    g = W.gradient(w, 0, 0, device="cuda", numel=n)
+    rd = torch.zeros(n, dtype=torch.float32, device="cuda")
+    acc = rd + g
+    k = layout.keep_total(sgc.GLOBAL, ppm)
+    assert (k + 4095) // 4096 > 16384
+    comp = sgc.compress(layout, g, rd, keep_ppm=ppm)
+    torch.cuda.synchronize()
+    check_topk(acc, comp, rd, k, f"2^28 at {ppm / 1e4:g}%")
+
+
 def test_flat_1g_sampled_full_size(orc):
     # sampled-threshold top-0.1%, then top-1% on the residual it leaves, over
     # all 2^30 elements: indices, values, counts, status and the whole
