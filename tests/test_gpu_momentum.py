@@ -69,6 +69,19 @@ def test_sampled_steps(orc, scope):
     run_steps(orc, layout, grads, 0.9, mode=sgc.SAMPLED, scope=scope, ppm=10000, what="sampled")
 
 
+@pytest.mark.parametrize("mode", [sgc.EXACT, sgc.SAMPLED])
+def test_many_segments_per_tensor(orc, mode):
+    # 2100 tensors (every seventh empty), per-tensor selection: the per-segment bookkeeping
+    # runs in several rounds of its workgroup; three steps carry residual and momentum
+    rng = np.random.default_rng(23)
+    sizes = [int(x) for x in rng.integers(0, 3000, 2100)]
+    for t in range(0, len(sizes), 7):
+        sizes[t] = 0
+    layout = sgc.Layout(sizes)
+    grads = [rng.laplace(0, 1e-3, layout.n).astype(np.float32) for _ in range(3)]
+    run_steps(orc, layout, grads, 0.9, mode=mode, scope=1, ppm=20000, what="2100 tensors")
+
+
 def test_sampled_truncation_keeps_momentum(orc):
     rng = np.random.default_rng(23)
     n = 500000
