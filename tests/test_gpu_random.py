@@ -160,6 +160,7 @@ def test_many_segments(orc, nseg):
         dict(scope=1, mode=sgc.EXACT, kind="raw_2bit", ppm=1000),
         dict(scope=0, mode=sgc.SAMPLED, kind="raw_f32", ppm=20000),
         dict(scope=1, mode=sgc.EXACT, kind="golomb_f32", enc_scope=0, ppm=400000),
+        dict(scope=1, mode=sgc.EXACT, kind="golomb_sbc", enc_scope=0, ppm=50000),
     ]
     gm, om = [], []
     for wk, fixed in enumerate(combos):

@@ -40,7 +40,20 @@ def test_random_steps(orc, seed):
     sizes = [int(x) for x in rng.integers(0, 90000, nseg)]
     if sum(sizes) == 0:
         sizes[0] = 3000
-    layout = sgc.Layout(sizes)
+    run_sequence(orc, rng, sgc.Layout(sizes), seed)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_steps_many_segments(orc, seed):
+    # 1500 segments: the per-segment bookkeeping in several rounds, under every kind of step
+    rng = np.random.default_rng(8300 + seed)
+    sizes = [int(x) for x in rng.integers(0, 2500, 1500)]
+    for t in range(0, len(sizes), 5):
+        sizes[t] = 0
+    run_sequence(orc, rng, sgc.Layout(sizes), seed)
+
+
+def run_sequence(orc, rng, layout, seed):
     n = layout.n
     seg_off = np.array(layout.seg_off, np.int64)
     mom = rng.random() < 0.4
