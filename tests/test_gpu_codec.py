@@ -6,6 +6,8 @@ relative (the GPU sums in a different, fixed order); the GPU residual must
 then equal fp32(v - mean_gpu) exactly, and the sent index set must match
 the oracle's except on a segment whose two means are a near-tie.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -185,6 +187,58 @@ def test_corrupt_message_is_skipped(orc):
     torch.cuda.synchronize()
     assert int(host(st2)[0]) & sgc.STATUS_CORRUPT
     assert_bitwise(host(out2), ref2, "non-ascending raw skipped")
+
+
+def test_corrupt_per_segment_stream_is_skipped(orc):
+    # per-tensor Rice streams over 1500 tensors, one message corrupted at a
+    # tensor past the first 1024 (the set-up's later rounds); each corruption
+    # keeps every read inside the message's buffers (same chunk counts and
+    # total), so only the checks decide: a shifted stream offset (set-up), a
+    # stream two bits short, and one code moved from an earlier tensor's count
+    # to this one's (decoder: one stream ends early, the other has bits left).  The message is skipped and the others summed exactly.
+    rng = np.random.default_rng(73)
+    sizes = [int(x) for x in rng.integers(0, 2500, 1500)]
+    for t in range(0, len(sizes), 5):
+        sizes[t] = 0
+    layout = sgc.Layout(sizes)
+    gm, om = make_messages(orc, layout, rng, ["golomb_f32_seg", "golomb_f32_seg", "golomb_sbc"])
+    ref = np.zeros(layout.n, np.float32)
+    orc.decode_accumulate([om[0], om[2]], np.array(layout.seg_off, np.int64), ref)
+    good = gm[1]
+    cnt = host(good.counts).astype(np.int64)
+    s = max(t for t in range(1025, layout.nseg) if cnt[t] >= 2 and cnt[t] % sgc.CHUNK_CODES != 0)
+    s2 = min(t for t in range(layout.nseg) if cnt[t] >= 2 and cnt[t] % sgc.CHUNK_CODES != 1)
+    e = good.enc
+
+    def variant(what, words=None, word_off=None, nbits=None, counts=None):
+        enc = sgc.Encoded(e.words if words is None else words, e.word_off if word_off is None else word_off,
+                          e.nbits if nbits is None else nbits, e.chunk_off, e.status, e.scope, e.b, e.cap)
+        bad = dataclasses.replace(good, counts=good.counts if counts is None else counts, enc=enc)
+        out = torch.zeros(layout.n, dtype=torch.float32, device="cuda")
+        announce(f"corrupt per-tensor stream: {what} at tensor {s}")
+        st = sgc.decode_accumulate(layout, [gm[0], bad, gm[2]], out)
+        torch.cuda.synchronize()
+        assert int(host(st)[0]) & sgc.STATUS_CORRUPT, what
+        assert_bitwise(host(out), ref, f"{what}: corrupt message skipped")
+
+    wo = e.word_off.clone()
+    wo[s] += 1
+    variant("stream offset shifted", word_off=wo)
+    nb = e.nbits.clone()
+    nb[s] -= 2
+    variant("stream two bits short", nbits=nb)
+    c2 = good.counts.clone()
+    c2[s] += 1
+    c2[s2] -= 1
+    variant(f"one code moved from tensor {s2}", counts=c2)
+    # and the untouched message decodes
+    out = torch.zeros(layout.n, dtype=torch.float32, device="cuda")
+    st = sgc.decode_accumulate(layout, gm, out)
+    full = np.zeros(layout.n, np.float32)
+    orc.decode_accumulate(om, np.array(layout.seg_off, np.int64), full)
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) == 0
+    assert_bitwise(host(out), full, "uncorrupted")
 
 
 def test_zero_messages_initialises(orc):
