@@ -1,4 +1,5 @@
-"""Worker steps captured in a HIP graph (torch's graph API) and replayed.
+"""Worker steps and the receive side captured in a HIP graph (torch's graph
+API) and replayed.
 
 The library allocates nothing and queues no memset or synchronous call once
 a layout's tables are on the device, so a whole step can be captured after
@@ -13,7 +14,8 @@ import torch
 
 import compressed_sgd_amd as sgc
 import workloads as W
-from gpu_util import announce, assert_bitwise, host
+from codec_util import make_messages
+from gpu_util import announce, assert_bitwise, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +110,57 @@ def test_graph_per_tensor_sbc_round():
         nw = int(host(ee.word_off)[-1])
         assert_bitwise(host(enc.words)[:nw], host(ee.words)[:nw], f"replay {it} words")
         assert_bitwise(host(enc.word_off), host(ee.word_off), f"replay {it} word offsets")
+
+
+def _tensors(m):
+    """The device tensors a message reads, in a fixed order."""
+    e = m.enc
+    ts = [m.counts, m.idx, m.val, m.codes, m.means]
+    if e is not None:
+        ts += [e.words, e.word_off, e.nbits, e.chunk_off]
+    return [t for t in ts if t is not None]
+
+
+def test_graph_receive(orc):
+    # decode + ordered sum of four message kinds onto a local gradient,
+    # captured once; before each replay a new set of messages (same shapes:
+    # exact selection keeps the counts' totals and so the capacities) is
+    # copied into the captured buffers; the workspace and status are the
+    # test's own, so no later call can reallocate what the graph points at
+    rng = np.random.default_rng(77)
+    layout = sgc.Layout([300000, 7, 120000, 0, 65536, 1000])
+    n = layout.n
+    seg_off = np.array(layout.seg_off, np.int64)
+    kinds = ["raw_f32", "golomb_f32_seg", "golomb_sbc", "golomb_2bit"]
+    sets = [make_messages(orc, layout, rng, kinds) for _ in range(4)]
+    cap_msgs = sets[0][0]
+    for gm, _ in sets[1:]:
+        for a, b in zip(cap_msgs, gm):
+            assert [t.shape for t in _tensors(a)] == [t.shape for t in _tensors(b)]
+    base_h = rng.normal(0, 1e-3, n).astype(np.float32)
+    base = dev(base_h)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    arr = (sgc.MessageDesc * len(cap_msgs))(*[m.desc() for m in cap_msgs])
+    ws = torch.empty(max(int(sgc.lib().sgc_decode_accumulate_workspace(layout.handle, arr, len(cap_msgs))), 256),
+                     dtype=torch.uint8, device="cuda")
+    sgc.decode_accumulate(layout, cap_msgs, out, init=sgc.INIT_BASE, base=base, status=status, ws=ws)  # eager
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sgc.decode_accumulate(layout, cap_msgs, out, init=sgc.INIT_BASE, base=base, status=status, ws=ws)
+    torch.cuda.synchronize()
+    for it, (gm, om) in enumerate(sets[1:]):
+        for a, b in zip(cap_msgs, gm):
+            for dst, src in zip(_tensors(a), _tensors(b)):
+                dst.copy_(src)
+        status.zero_()
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        announce(f"graph replay {it}: receive of {len(gm)} messages ({', '.join(kinds)})")
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = base_h.copy()
+        ost = orc.decode_accumulate(om, seg_off, ref)
+        assert ost == 0 and int(host(status)[0]) == 0, f"replay {it}: status {ost} / {int(host(status)[0])}"
+        assert_bitwise(host(out), ref, f"replay {it}: dense sum")
