@@ -193,6 +193,8 @@ def workspace(nbytes: int, device: torch.device, slot: str = "default") -> torch
     """A cached uint8 device buffer of at least nbytes (one per device and slot).
 
     Calls that share a slot must not overlap in time (same stream is fine).
+    A later call that needs more replaces (and frees) the cached buffer, so a
+    call captured into a HIP graph should be given a workspace of its own.
     """
     key = (device.index if device.index is not None else torch.cuda.current_device(), slot)
     buf = _ws_cache.get(key)
