@@ -157,6 +157,37 @@ def test_decode_accumulate_many_workers(orc):
     assert_bitwise(host(out), ref, "36 workers")
 
 
+@pytest.mark.parametrize("init", [sgc.INIT_BASE, sgc.INIT_INPLACE])
+def test_decode_accumulate_many_kinds_batches(orc, init):
+    # 35 messages of all six kinds on a ragged layout: three merge batches
+    # (the later ones add in place) onto a base or onto out itself; message
+    # 19 (second merge batch, third decode batch) is two bits short and must
+    # be the only one left out
+    rng = np.random.default_rng(67 + init)
+    layout = sgc.Layout([40000, 0, 13, 70000, 4096])
+    n = layout.n
+    kinds = ["raw_f32", "golomb_f32", "golomb_f32_seg", "golomb_sbc", "raw_2bit", "golomb_2bit"] * 6
+    kinds = kinds[:35]
+    gm, om = make_messages(orc, layout, rng, kinds, ppm=30000)
+    assert kinds[19] == "golomb_f32"
+    e = gm[19].enc
+    nb = e.nbits.clone()
+    nb[0] -= 2
+    gm[19] = dataclasses.replace(gm[19], enc=sgc.Encoded(e.words, e.word_off, nb, e.chunk_off, e.status, e.scope,
+                                                         e.b, e.cap))
+    start = rng.normal(0, 1e-3, n).astype(np.float32)
+    base = rng.normal(0, 1e-3, n).astype(np.float32)
+    out = dev(start)
+    announce(f"35 messages, six kinds, init={init}, message 19 corrupt")
+    st = sgc.decode_accumulate(layout, gm, out, init=init, base=dev(base))
+    ref = (base if init == sgc.INIT_BASE else start).copy()
+    ost = orc.decode_accumulate(om[:19] + om[20:], np.array(layout.seg_off, np.int64), ref)
+    torch.cuda.synchronize()
+    assert ost == 0
+    assert int(host(st)[0]) & sgc.STATUS_CORRUPT
+    assert_bitwise(host(out), ref, f"35 messages init={init}")
+
+
 def test_corrupt_message_is_skipped(orc):
     rng = np.random.default_rng(71)
     layout = sgc.Layout([60000])
