@@ -133,6 +133,15 @@ def _stream(device: torch.device, stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
+def _zeros(stream, *shape, **kw) -> torch.Tensor:
+    """A zero-filled tensor whose fill runs on the stream the call's kernels
+    use (torch fills on its current stream, which an explicit stream may not be)."""
+    if stream is None:
+        return torch.zeros(*shape, **kw)
+    with torch.cuda.stream(stream):
+        return torch.zeros(*shape, **kw)
+
+
 def _require_gpu(t: torch.Tensor, name: str):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device (HIP) tensor")
@@ -244,7 +253,7 @@ def compress(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode
         out = Compressed(torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
                          torch.empty(max(cap, 1), dtype=torch.float32, device=dev),
                          torch.empty(layout.nseg + 1, dtype=torch.int64, device=dev),
-                         torch.zeros(1, dtype=torch.int32, device=dev), cap)
+                         _zeros(stream, 1, dtype=torch.int32, device=dev), cap)
     nbytes = lib().sgc_compress_workspace(layout.handle, C.byref(opts), cap)
     if ws is None:
         ws = workspace(nbytes, dev, "compress")
@@ -283,7 +292,7 @@ def compress_momentum(layout: Layout, grad: torch.Tensor, momentum: torch.Tensor
         out = Compressed(torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
                          torch.empty(max(cap, 1), dtype=torch.float32, device=dev),
                          torch.empty(layout.nseg + 1, dtype=torch.int64, device=dev),
-                         torch.zeros(1, dtype=torch.int32, device=dev), cap)
+                         _zeros(stream, 1, dtype=torch.int32, device=dev), cap)
     nbytes = lib().sgc_compress_momentum_workspace(layout.handle, C.byref(opts), cap)
     if ws is None:
         ws = workspace(nbytes, dev, "compress_momentum")
@@ -318,7 +327,7 @@ def binarize(layout: Layout, comp: Compressed, residual: torch.Tensor, mode: int
                     torch.empty(layout.nseg + 1, dtype=torch.int64, device=dev),
                     torch.empty(layout.nseg if mode == BIN_SBC else 2 * layout.nseg, dtype=torch.float32,
                                 device=dev),
-                    torch.zeros(max((cap + 15) // 16, 1), dtype=torch.int32, device=dev) if mode == BIN_2BIT
+                    _zeros(stream, max((cap + 15) // 16, 1), dtype=torch.int32, device=dev) if mode == BIN_2BIT
                     else None, mode, cap)
     nbytes = lib().sgc_binarize_workspace(layout.handle, cap)
     if ws is None:
@@ -367,7 +376,7 @@ def encode(layout: Layout, idx: torch.Tensor, counts: torch.Tensor, cap: int, *,
                       torch.empty(nstreams + 1, dtype=torch.int64, device=dev),
                       torch.empty(nstreams, dtype=torch.int64, device=dev),
                       torch.empty(max(ccap, 1), dtype=torch.int64, device=dev),
-                      torch.zeros(1, dtype=torch.int32, device=dev), scope, b, cap)
+                      _zeros(stream, 1, dtype=torch.int32, device=dev), scope, b, cap)
     out.scope, out.b, out.cap = scope, b, cap
     nbytes = lib().sgc_encode_workspace(layout.handle, scope, cap)
     if ws is None:
@@ -432,7 +441,7 @@ def decode_accumulate(layout: Layout, msgs: Sequence[Message], out: torch.Tensor
     if ws is None:
         ws = workspace(nbytes, dev, "decode")
     if status is None:
-        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        status = _zeros(stream, 1, dtype=torch.int32, device=dev)
     _check(lib().sgc_decode_accumulate(layout.handle, arr, W, init, _ptr(base), _ptr(out), _ptr(status), _ptr(ws),
                                        ws.numel(), _stream(dev, stream)), "sgc_decode_accumulate")
     return status
