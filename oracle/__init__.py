@@ -9,10 +9,10 @@ Every function works on host numpy arrays, returns fresh arrays and never
 touches a GPU.  ``compress_*`` and ``binarize`` update the residual passed in
 place (like the method does).
 
-Parity unpinned: the statistics of ``compress_sampled`` beyond the properties
-any sample satisfies, and the reading that the local node's own message is
-summed as well as its dense gradient in the global+local combination (pinned
-by linearity only).
+The sampled-threshold mode follows a reading (its defining page is cut
+short), pinned by hand-worked literal examples of that reading.  Parity
+unpinned: the reading that the local node's own message is summed as well as
+its dense gradient in the global+local combination (pinned by linearity only).
 """
 from __future__ import annotations
 

@@ -12,7 +12,9 @@
  * or reordering beyond what the definition states.  fp32 arithmetic is plain
  * scalar C float arithmetic (x86-64 SSE, round-to-nearest-even, no fused
  * multiply-add: build with -ffp-contract=off); means are accumulated in
- * double precision.  Not thread-safe (qsort comparators read file statics).
+ * double precision.  Calls on distinct arrays may run in parallel threads:
+ * the one file-scope variable (the array a qsort comparator reads) is
+ * thread-local.
  *
  * Citations (page title, then section):
  *   [AH17]  "Sparse Communication for Distributed Gradient Descent"
@@ -25,14 +27,13 @@
  *
  * Where the pages leave a step open, the reading taken is stated at the step.
  *
- * Parity unpinned (nothing printed on the pages, no closed form): the
- * statistics of the sampled-threshold mode (orc_compress_sampled) -- its
- * sample design is a reading, and the tests pin only what holds for any
- * sample (the kept set is the superlevel set at its own threshold, a
- * superset of exact top-k when every element is sampled, the count inside a
- * binomial band); and, in the global+local combination, the reading that the
- * local node's own sparse message is summed as well as its dense gradient
- * (pinned by linearity only).
+ * The sampled-threshold mode (orc_sample_count, orc_compress_sampled)
+ * follows a reading: the page that would define its sample is cut short.
+ * Its sample size, sample positions and threshold are pinned by literal
+ * examples worked out by hand from that reading.  Parity unpinned: in the
+ * global+local combination, the reading that the local node's own sparse
+ * message is summed as well as its dense gradient (pinned by linearity
+ * only).
  */
 #include <math.h>
 #include <stdint.h>
@@ -159,7 +160,7 @@ void orc_momentum_mask(float* u, const int32_t* sent_idx, int64_t count)
 
 /* Order of the exact selection: larger |acc| first; among equal magnitudes
  * the lower index first (so the lower index wins a tie at the threshold).   */
-static const float* sort_acc;
+static _Thread_local const float* sort_acc;
 static int by_magnitude_then_index(const void* a, const void* b)
 {
     int32_t i = *(const int32_t*)a, j = *(const int32_t*)b;

@@ -359,6 +359,99 @@ def test_sampled_count_within_binomial_band(orc):
     assert abs(sp.idx.size / (n * p) - 1) < 5 * rel_sigma + 2.0 / (s * p)
 
 
+# The sampled-threshold mode of "Sparse Communication for Distributed Gradient
+# Descent" (Abstract: a threshold found from a sample of the update) is defined
+# in a method section the page no longer holds.  The reading fixed for it:
+#   s  = min(m, max(sample_min, ceil(m / sample_div)))   samples per group,
+#   i_j = floor((2j+1) m / (2s)), j = 0..s-1            systematic positions,
+#   ks = ceil(s * ppm / 1e6); T = ks-th largest sampled |acc|; keep |acc| >= T.
+# The literal values below are worked out by hand from that reading.
+@pytest.mark.parametrize("m,div,smin,want", [
+    (0, 1000, 65536, 0),                 # empty group
+    (10, 1000, 65536, 10),               # m below sample_min: every element
+    (65535, 1000, 65536, 65535),
+    (65536, 1000, 65536, 65536),
+    (65537, 1000, 65536, 65536),         # ceil(65537/1000) = 66 < sample_min
+    (65536000, 1000, 65536, 65536),      # m/div = sample_min exactly
+    (65536001, 1000, 65536, 65537),      # ceil(65536.001) = 65537
+    (1 << 30, 1000, 65536, 1073742),     # ceil(1073741.824)
+    (7, 3, 2, 3),                        # ceil(7/3) = 3 > 2
+    (6, 3, 2, 2),                        # 6/3 = 2 exactly
+    (999, 1000, 0, 1),                   # m < div: one sample
+    (5, 10, 1, 1),
+    (3000, 1000, 0, 3),
+    (3001, 1000, 0, 4),
+])
+def test_sample_count_literal(orc, m, div, smin, want):
+    assert orc.sample_count(m, div, smin) == want
+
+
+def test_sampled_positions_literal_m10(orc):
+    # m = 10, sample_div = 1000, sample_min = 4 -> s = min(10, max(4, 1)) = 4.
+    # Positions floor((2j+1)*10/8): 10/8, 30/8, 50/8, 70/8 -> 1, 3, 6, 8.
+    # Sampled |acc| = |-2|, |6|, |-4|, |5| = 2, 6, 4, 5; ppm 500000 -> ks =
+    # ceil(4/2) = 2, so T = 5 (the 2nd largest) and every |acc| >= 5 is kept:
+    # indices 0 (9), 2 (8), 3 (6), 4 (-7), 8 (5), 9 (-10).
+    acc = np.array([9, -2, 8, 6, -7, 1, -4, 3, 5, -10], np.float32)
+    r = np.zeros(10, np.float32)
+    sp = orc.compress_sampled(acc, r, [0, 10], orc.GLOBAL, 500000, cap=10, sample_div=1000, sample_min=4)
+    assert sp.idx.tolist() == [0, 2, 3, 4, 8, 9]
+    assert sp.val.tolist() == [9, 8, 6, -7, 5, -10]
+    assert sp.counts.tolist() == [6, 6]
+    assert r.tolist() == [0, -2, 0, 0, 0, 1, -4, 3, 0, 0]
+    assert sp.status == 0
+
+
+def test_sampled_positions_literal_two_segments(orc):
+    # Two tensors of 10 and 20 elements, sample_div = 1000, sample_min = 4.
+    # Per tensor: tensor 0 as in the m = 10 case (positions 1, 3, 6, 8);
+    # tensor 1 has s = 4 and positions floor((2j+1)*20/8) = 2, 7, 12, 17,
+    # i.e. global 12, 17, 22, 27.  Over the whole vector (m = 30, s = 4):
+    # floor((2j+1)*30/8) = 3, 11, 18, 26.
+    a0 = [9, -2, 8, 6, -7, 1, -4, 3, 5, -10]
+    a1 = [0.5, 7, -3, 0.25, 11, 2, 1, -6, 0.75, 4, 13, -1, 8, 9, -0.5, 1.5, 3.5, 2.5, 5, -12]
+    acc = np.array(a0 + a1, np.float32)
+    # Per tensor, ppm 500000 -> ks = 2.  Tensor 0: T = 5 -> local 0, 2, 3, 4, 8, 9.
+    # Tensor 1 samples local 2, 7, 12, 17: |-3|, |-6|, |8|, |2.5| -> T = 6 ->
+    # local |acc| >= 6: 1 (7), 4 (11), 7 (-6), 10 (13), 12 (8), 13 (9), 19 (-12)
+    # -> global 11, 14, 17, 20, 22, 23, 29.
+    r = np.zeros(30, np.float32)
+    sp = orc.compress_sampled(acc, r, [0, 10, 30], orc.PER_SEGMENT, 500000, cap=30, sample_div=1000,
+                              sample_min=4)
+    assert sp.idx.tolist() == [0, 2, 3, 4, 8, 9, 11, 14, 17, 20, 22, 23, 29]
+    assert sp.counts.tolist() == [6, 7, 13]
+    # Globally: samples at 3, 11, 18, 26 -> |6|, |7|, |0.75|, |3.5|; ks = 2 -> T = 6 ->
+    # every |acc| >= 6: 0, 2, 3, 4, 9 (tensor 0) and 11, 14, 17, 20, 22, 23, 29.
+    r = np.zeros(30, np.float32)
+    sp = orc.compress_sampled(acc, r, [0, 10, 30], orc.GLOBAL, 500000, cap=30, sample_div=1000, sample_min=4)
+    assert sp.idx.tolist() == [0, 2, 3, 4, 9, 11, 14, 17, 20, 22, 23, 29]
+    assert sp.counts.tolist() == [5, 7, 12]
+
+
+def test_sampled_positions_literal_default_sizes(orc):
+    # m = 100000 with the default sample_div = 1000, sample_min = 65536:
+    # s = 65536, positions floor((2j+1)*100000/131072): j = 0 -> 0, j = 1 ->
+    # floor(300000/131072) = 2, j = 65535 -> floor(99999.23...) = 99999.
+    # Element 1 is not sampled (positions 0 and 2 bracket it).  With ppm = 1,
+    # ks = ceil(65536/1e6) = 1, so T = the largest sampled |acc|.
+    m = 100000
+    acc = np.zeros(m, np.float32)
+    acc[1] = 2.0        # not sampled: cannot raise T
+    acc[2] = 1.0        # sampled (j = 1): T = 1.0
+    acc[50000] = 0.5    # below T
+    r = np.zeros(m, np.float32)
+    sp = orc.compress_sampled(acc, r, [0, m], orc.GLOBAL, 1, cap=m)
+    assert sp.idx.tolist() == [1, 2]
+    # Only the last element sampled (j = 65535 -> 99999): T = |acc[99999]|.
+    acc = np.zeros(m, np.float32)
+    acc[99998] = 4.0    # floor((2*65534+1)*100000/131072) = 99997: not sampled
+    acc[99999] = 3.0
+    acc[7] = 3.5
+    r = np.zeros(m, np.float32)
+    sp = orc.compress_sampled(acc, r, [0, m], orc.GLOBAL, 1, cap=m)
+    assert sp.idx.tolist() == [7, 99998, 99999]
+
+
 def test_sampled_truncation_keeps_residual(orc):
     rng = np.random.default_rng(9)
     n = 10000
