@@ -76,7 +76,8 @@ def timed(fn, reps, stream):
 
 def graph_timed(fn, reps, stream):
     """fn captured once in a HIP graph (after an eager warm-up call) and
-    replayed: the launch cost of its kernels leaves the timed region."""
+    replayed: the launch cost of its kernels leaves the timed region.  Every
+    library call in fn passes its own workspace (ws=)."""
     import torch
     fn()
     torch.cuda.synchronize()
@@ -166,10 +167,13 @@ def workload_rows(sgc, W, torch, dev, stream, reps=10):
     c = sgc.compress(L, g_in, r, keep_ppm=w.keep_ppm)
     bf = sgc.rice_param(w.keep_ppm / 1e6)
     e = sgc.encode(L, c.idx, c.counts, c.cap, b=bf)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    wsc = torch.empty(sgc.compress_workspace_bytes(L, keep_ppm=w.keep_ppm), **u8)
+    wse = torch.empty(sgc.encode_workspace_bytes(L, sgc.GLOBAL, c.cap), **u8)
 
     def step_enc():
-        sgc.compress(L, g_in, r, keep_ppm=w.keep_ppm, out=c)
-        sgc.encode(L, c.idx, c.counts, c.cap, b=bf, out=e)
+        sgc.compress(L, g_in, r, keep_ppm=w.keep_ppm, out=c, ws=wsc)
+        sgc.encode(L, c.idx, c.counts, c.cap, b=bf, out=e, ws=wse)
     t = timed(step_enc, reps, stream)
     tg = graph_timed(step_enc, reps, stream)
     row["compress_encode_exact"] = {"ms": t, "ms_graph": tg, "elements_per_s_graph": el(n, tg)}
@@ -240,11 +244,15 @@ def workload_rows(sgc, W, torch, dev, stream, reps=10):
     row = {}
     for mode, tag in ((sgc.EXACT, "exact"), (sgc.SAMPLED, "sampled")):
         ct = sgc.compress(L, gs[0], r, mode=mode, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        wsc = torch.empty(sgc.compress_workspace_bytes(L, mode=mode, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm), **u8)
+        wsb = torch.empty(sgc.binarize_workspace_bytes(L, ct.cap), **u8)
+        wse = torch.empty(sgc.encode_workspace_bytes(L, sgc.PER_SEGMENT, ct.cap), **u8)
 
         def exchange():
-            sgc.compress(L, gs[1], r, mode=mode, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm, out=ct)
-            bt = sgc.binarize(L, ct, r, sgc.BIN_SBC)
-            sgc.encode(L, bt.idx, bt.counts, bt.cap, scope=sgc.PER_SEGMENT, b=b)
+            sgc.compress(L, gs[1], r, mode=mode, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm, out=ct, ws=wsc)
+            bt = sgc.binarize(L, ct, r, sgc.BIN_SBC, ws=wsb)
+            sgc.encode(L, bt.idx, bt.counts, bt.cap, scope=sgc.PER_SEGMENT, b=b, ws=wse)
 
         def rnd():
             for s_ in range(w.delay - 1):

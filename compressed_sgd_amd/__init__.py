@@ -12,6 +12,7 @@ The entry points keep the C names without the ``sgc_`` prefix:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 from dataclasses import dataclass
@@ -22,7 +23,7 @@ import torch  # loads the HIP runtime first; libsgc binds to that same runtime
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsgc.so")
 
-OK, EINVAL, ENOSPC, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4
+OK, EINVAL, ENOSPC, EHIP, EUNSUPPORTED, ENOTREADY = 0, -1, -2, -3, -4, -5
 STATUS_TRUNCATED, STATUS_CORRUPT, STATUS_DENSE_PATH, STATUS_BAD_INPUT = 1, 2, 4, 8
 EXACT, SAMPLED, ACCUMULATE_ONLY = 0, 1, 2
 HOLD_KEPT = 0x10
@@ -34,7 +35,7 @@ INIT_ZERO, INIT_BASE, INIT_INPLACE = 0, 1, 2
 CHUNK_CODES = 256
 
 EXPORTED = (
-    "sgc_layout_create", "sgc_layout_destroy", "sgc_layout_numel", "sgc_layout_nseg",
+    "sgc_layout_create", "sgc_layout_upload", "sgc_layout_destroy", "sgc_layout_numel", "sgc_layout_nseg",
     "sgc_keep_count", "sgc_rice_param", "sgc_strerror", "sgc_abi_version",
     "sgc_compress_workspace", "sgc_compress", "sgc_compress_momentum_workspace", "sgc_compress_momentum",
     "sgc_binarize_workspace", "sgc_binarize",
@@ -75,6 +76,8 @@ def lib():
         P, i32, i64, u32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32, C.c_size_t
         L.sgc_layout_create.argtypes = [P, i32, C.POINTER(P)]
         L.sgc_layout_create.restype = C.c_int
+        L.sgc_layout_upload.argtypes = [P]
+        L.sgc_layout_upload.restype = C.c_int
         L.sgc_layout_destroy.argtypes = [P]
         L.sgc_layout_destroy.restype = None
         L.sgc_layout_numel.argtypes = [P]
@@ -133,13 +136,21 @@ def _stream(device: torch.device, stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocate (and zero-fill) under the stream the call's kernels run on:
+    torch's caching allocator then ties the memory to that stream, and fills
+    run in order with the kernels that use the result."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _zeros(stream, *shape, **kw) -> torch.Tensor:
-    """A zero-filled tensor whose fill runs on the stream the call's kernels
-    use (torch fills on its current stream, which an explicit stream may not be)."""
-    if stream is None:
+    with _on(stream):
         return torch.zeros(*shape, **kw)
-    with torch.cuda.stream(stream):
-        return torch.zeros(*shape, **kw)
+
+
+def _empty(stream, *shape, **kw) -> torch.Tensor:
+    with _on(stream):
+        return torch.empty(*shape, **kw)
 
 
 def _require_gpu(t: torch.Tensor, name: str):
@@ -163,24 +174,47 @@ def abi_version() -> int:
 
 
 class Layout:
-    """Segment sizes of the flat parameter vector (one per tensor, in order)."""
+    """Segment sizes of the flat parameter vector (one per tensor, in order).
 
-    def __init__(self, seg_numel: Sequence[int]):
+    The tables go to the current device at creation (when a GPU is present)
+    and to any other device on its first use there; the compute calls never
+    upload (the C library returns ENOTREADY for a device without them).
+    """
+
+    def __init__(self, seg_numel: Sequence[int], device: Optional[torch.device] = None):
         self.seg_numel = [int(x) for x in seg_numel]
         arr = (C.c_int64 * max(len(self.seg_numel), 1))(*self.seg_numel)
         h = C.c_void_p()
         _check(lib().sgc_layout_create(arr, len(self.seg_numel), C.byref(h)), "sgc_layout_create")
         self._h = h
+        self._devices = set()
         self.n = sum(self.seg_numel)
         self.nseg = len(self.seg_numel)
         off = [0]
         for m in self.seg_numel:
             off.append(off[-1] + m)
         self.seg_off = off
+        if device is not None or torch.cuda.is_available():
+            self.upload(device)
 
     @property
     def handle(self):
         return self._h
+
+    def upload(self, device: Optional[torch.device] = None) -> None:
+        """Put the tables on `device` (default: the current one); set-up, not capturable."""
+        d = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        index = d.index if d.index is not None else torch.cuda.current_device()
+        if index in self._devices:
+            return
+        with torch.cuda.device(index):
+            _check(lib().sgc_layout_upload(self._h), "sgc_layout_upload")
+        self._devices.add(index)
+
+    def _ready(self, device: torch.device) -> None:
+        index = device.index if device.index is not None else torch.cuda.current_device()
+        if index not in self._devices:
+            self.upload(torch.device("cuda", index))
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -195,22 +229,82 @@ class Layout:
         return sum(keep_count(m, keep_ppm) for m in self.group_sizes(scope))
 
 
-_ws_cache: Dict[Tuple[int, str], torch.Tensor] = {}
+_ws_cache: Dict[Tuple[int, int, str], torch.Tensor] = {}
 
 
-def workspace(nbytes: int, device: torch.device, slot: str = "default") -> torch.Tensor:
-    """A cached uint8 device buffer of at least nbytes (one per device and slot).
+def workspace(nbytes: int, device: torch.device, slot: str = "default", stream=None) -> torch.Tensor:
+    """A cached uint8 device buffer of at least nbytes, one per (device, stream, slot).
 
-    Calls that share a slot must not overlap in time (same stream is fine).
-    A later call that needs more replaces (and frees) the cached buffer, so a
-    call captured into a HIP graph should be given a workspace of its own.
+    It is allocated under the stream the calls run on, so the caching
+    allocator hands a replaced buffer to nothing else until that stream has
+    passed every call that used it; calls on one stream run in order, and
+    calls on two streams get two buffers.  A call captured into a HIP graph
+    must be given a workspace of its own (``ws=``): a cached buffer could be
+    replaced, and freed, while the graph still points at it.
     """
-    key = (device.index if device.index is not None else torch.cuda.current_device(), slot)
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("a call captured into a graph needs its own workspace: pass ws= "
+                           "(sized with the *_workspace_bytes helpers)")
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    s = stream if stream is not None else torch.cuda.current_stream(index)
+    key = (index, int(s.cuda_stream), slot)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache.pop(key, None)
+        buf = _empty(stream, max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
+
+
+def compress_workspace_bytes(layout: "Layout", *, mode: int = EXACT, scope: int = GLOBAL, keep_ppm: int = 10000,
+                             sample_div: int = 1000, sample_min: int = 65536, cap: Optional[int] = None,
+                             hold: bool = False, momentum: bool = False) -> int:
+    """Workspace bytes of one compress (or compress_momentum) call with these options."""
+    opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min)
+    cap = _default_cap(layout, mode, scope, keep_ppm) if cap is None else cap
+    f = lib().sgc_compress_momentum_workspace if momentum else lib().sgc_compress_workspace
+    return int(f(layout.handle, C.byref(opts), cap))
+
+
+def binarize_workspace_bytes(layout: "Layout", cap: int) -> int:
+    return int(lib().sgc_binarize_workspace(layout.handle, cap))
+
+
+def encode_workspace_bytes(layout: "Layout", scope: int, cap: int) -> int:
+    return int(lib().sgc_encode_workspace(layout.handle, scope, cap))
+
+
+def decode_accumulate_workspace_bytes(layout: "Layout", msgs: Sequence["Message"]) -> int:
+    arr = (MessageDesc * max(len(msgs), 1))(*[m.desc() for m in msgs])
+    return int(lib().sgc_decode_accumulate_workspace(layout.handle, arr, len(msgs)))
+
+
+def _default_cap(layout: "Layout", mode: int, scope: int, keep_ppm: int) -> int:
+    k = layout.keep_total(scope, keep_ppm)
+    return k if mode == EXACT else min(layout.n, 2 * k + 4096)
+
+
+def _compress_out(layout: "Layout", out: Optional["Compressed"], cap: Optional[int], mode: int, scope: int,
+                  keep_ppm: int, dev: torch.device, stream) -> Tuple["Compressed", int]:
+    """The output buffers and the capacity of a compress call: new ones, or
+    `out` reused after checking that it fits this call (cap defaults to its own)."""
+    if out is None:
+        cap = _default_cap(layout, mode, scope, keep_ppm) if cap is None else cap
+        out = Compressed(_empty(stream, max(cap, 1), dtype=torch.int32, device=dev),
+                         _empty(stream, max(cap, 1), dtype=torch.float32, device=dev),
+                         _empty(stream, layout.nseg + 1, dtype=torch.int64, device=dev),
+                         _zeros(stream, 1, dtype=torch.int32, device=dev), cap)
+        return out, cap
+    cap = out.cap if cap is None else cap
+    if cap > out.idx.numel() or cap > out.val.numel():
+        raise ValueError(f"out holds {min(out.idx.numel(), out.val.numel())} entries, this call needs cap {cap}")
+    if out.counts.numel() != layout.nseg + 1:
+        raise ValueError(f"out.counts has {out.counts.numel()} entries, the layout needs {layout.nseg + 1}")
+    for t, name in ((out.idx, "out.idx"), (out.val, "out.val"), (out.counts, "out.counts")):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the call runs on {dev}")
+    out.cap = cap
+    return out, cap
 
 
 # ----------------------------------------------------------------- compress
@@ -240,23 +334,17 @@ def compress(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode
         if t.dtype != torch.float32 or t.numel() != layout.n:
             raise ValueError(f"{name} must be float32 with {layout.n} elements")
     dev = grad.device
+    layout._ready(dev)
     opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min)
     st = _stream(dev, stream)
     if mode == ACCUMULATE_ONLY:
         _check(lib().sgc_compress(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), None, None, 0, None,
                                   None, None, 0, st), "sgc_compress")
         return None
-    if cap is None:
-        k = layout.keep_total(scope, keep_ppm)
-        cap = k if mode == EXACT else min(layout.n, 2 * k + 4096)
-    if out is None:
-        out = Compressed(torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
-                         torch.empty(max(cap, 1), dtype=torch.float32, device=dev),
-                         torch.empty(layout.nseg + 1, dtype=torch.int64, device=dev),
-                         _zeros(stream, 1, dtype=torch.int32, device=dev), cap)
+    out, cap = _compress_out(layout, out, cap, mode, scope, keep_ppm, dev, stream)
     nbytes = lib().sgc_compress_workspace(layout.handle, C.byref(opts), cap)
     if ws is None:
-        ws = workspace(nbytes, dev, "compress")
+        ws = workspace(nbytes, dev, "compress", stream)
     _check(lib().sgc_compress(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), _ptr(out.idx),
                               _ptr(out.val), cap, _ptr(out.counts), _ptr(out.status), _ptr(ws), ws.numel(), st),
            "sgc_compress")
@@ -278,6 +366,7 @@ def compress_momentum(layout: Layout, grad: torch.Tensor, momentum: torch.Tensor
         if t.dtype != torch.float32 or t.numel() != layout.n:
             raise ValueError(f"{name} must be float32 with {layout.n} elements")
     dev = grad.device
+    layout._ready(dev)
     opts = CompressOpts(mode, scope, keep_ppm, sample_div, sample_min)
     st = _stream(dev, stream)
     if mode == ACCUMULATE_ONLY:
@@ -285,17 +374,10 @@ def compress_momentum(layout: Layout, grad: torch.Tensor, momentum: torch.Tensor
                                            _ptr(residual), None, None, 0, None, None, None, 0, st),
                "sgc_compress_momentum")
         return None
-    if cap is None:
-        k = layout.keep_total(scope, keep_ppm)
-        cap = k if mode == EXACT else min(layout.n, 2 * k + 4096)
-    if out is None:
-        out = Compressed(torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
-                         torch.empty(max(cap, 1), dtype=torch.float32, device=dev),
-                         torch.empty(layout.nseg + 1, dtype=torch.int64, device=dev),
-                         _zeros(stream, 1, dtype=torch.int32, device=dev), cap)
+    out, cap = _compress_out(layout, out, cap, mode, scope, keep_ppm, dev, stream)
     nbytes = lib().sgc_compress_momentum_workspace(layout.handle, C.byref(opts), cap)
     if ws is None:
-        ws = workspace(nbytes, dev, "compress_momentum")
+        ws = workspace(nbytes, dev, "compress_momentum", stream)
     _check(lib().sgc_compress_momentum(layout.handle, C.byref(opts), float(beta), _ptr(grad), _ptr(momentum),
                                        _ptr(residual), _ptr(out.idx), _ptr(out.val), cap, _ptr(out.counts),
                                        _ptr(out.status), _ptr(ws), ws.numel(), st), "sgc_compress_momentum")
@@ -323,15 +405,15 @@ def binarize(layout: Layout, comp: Compressed, residual: torch.Tensor, mode: int
     _require_gpu(residual, "residual")
     dev = residual.device
     cap = comp.cap
-    out = Binarized(torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
-                    torch.empty(layout.nseg + 1, dtype=torch.int64, device=dev),
-                    torch.empty(layout.nseg if mode == BIN_SBC else 2 * layout.nseg, dtype=torch.float32,
-                                device=dev),
+    out = Binarized(_empty(stream, max(cap, 1), dtype=torch.int32, device=dev),
+                    _empty(stream, layout.nseg + 1, dtype=torch.int64, device=dev),
+                    _empty(stream, layout.nseg if mode == BIN_SBC else 2 * layout.nseg, dtype=torch.float32,
+                           device=dev),
                     _zeros(stream, max((cap + 15) // 16, 1), dtype=torch.int32, device=dev) if mode == BIN_2BIT
                     else None, mode, cap)
     nbytes = lib().sgc_binarize_workspace(layout.handle, cap)
     if ws is None:
-        ws = workspace(nbytes, dev, "binarize")
+        ws = workspace(nbytes, dev, "binarize", stream)
     _check(lib().sgc_binarize(layout.handle, mode | (BIN_HELD if held else 0), _ptr(comp.idx), _ptr(comp.val),
                               _ptr(comp.counts), cap,
                               _ptr(residual), _ptr(out.idx), _ptr(out.counts), _ptr(out.means), _ptr(out.codes),
@@ -352,6 +434,21 @@ class Encoded:
     cap: int
 
 
+def _encode_out(out: Optional[Encoded], scope: int, b: int, cap: int, wcap: int, ccap: int, nstreams: int,
+                dev: torch.device, stream) -> Encoded:
+    """`out` when every buffer of it fits this call (words, offsets and bit
+    counts of nstreams streams, the chunk table), else new buffers."""
+    if (out is None or out.words.numel() < wcap or out.chunk_off.numel() < ccap
+            or out.word_off.numel() < nstreams + 1 or out.nbits.numel() < nstreams or out.words.device != dev):
+        out = Encoded(_empty(stream, max(wcap, 1), dtype=torch.int32, device=dev),
+                      _empty(stream, nstreams + 1, dtype=torch.int64, device=dev),
+                      _empty(stream, nstreams, dtype=torch.int64, device=dev),
+                      _empty(stream, max(ccap, 1), dtype=torch.int64, device=dev),
+                      _zeros(stream, 1, dtype=torch.int32, device=dev), scope, b, cap)
+    out.scope, out.b, out.cap = scope, b, cap
+    return out
+
+
 def encode(layout: Layout, idx: torch.Tensor, counts: torch.Tensor, cap: int, *, scope: int = GLOBAL,
            b: Optional[int] = None, keep_ppm: Optional[int] = None, out: Optional[Encoded] = None,
            ws: Optional[torch.Tensor] = None, stream=None) -> Encoded:
@@ -362,6 +459,7 @@ def encode(layout: Layout, idx: torch.Tensor, counts: torch.Tensor, cap: int, *,
     """
     _require_gpu(idx, "idx")
     dev = idx.device
+    layout._ready(dev)
     if b is None:
         if keep_ppm is None:
             raise ValueError("give b or keep_ppm")
@@ -371,16 +469,10 @@ def encode(layout: Layout, idx: torch.Tensor, counts: torch.Tensor, cap: int, *,
     ccap = int(lib().sgc_encode_chunk_bound(layout.handle, scope, cap))
     if wcap < 0 or ccap < 0:
         raise ValueError("bad encode arguments")
-    if out is None or out.words.numel() < wcap or out.chunk_off.numel() < ccap:
-        out = Encoded(torch.empty(max(wcap, 1), dtype=torch.int32, device=dev),
-                      torch.empty(nstreams + 1, dtype=torch.int64, device=dev),
-                      torch.empty(nstreams, dtype=torch.int64, device=dev),
-                      torch.empty(max(ccap, 1), dtype=torch.int64, device=dev),
-                      _zeros(stream, 1, dtype=torch.int32, device=dev), scope, b, cap)
-    out.scope, out.b, out.cap = scope, b, cap
+    out = _encode_out(out, scope, b, cap, wcap, ccap, nstreams, dev, stream)
     nbytes = lib().sgc_encode_workspace(layout.handle, scope, cap)
     if ws is None:
-        ws = workspace(nbytes, dev, "encode")
+        ws = workspace(nbytes, dev, "encode", stream)
     _check(lib().sgc_encode(layout.handle, scope, b, _ptr(idx), _ptr(counts), cap, _ptr(out.words),
                             out.words.numel(), _ptr(out.word_off), _ptr(out.nbits), _ptr(out.chunk_off),
                             out.chunk_off.numel(), _ptr(out.status), _ptr(ws), ws.numel(), _stream(dev, stream)),
@@ -433,13 +525,14 @@ def decode_accumulate(layout: Layout, msgs: Sequence[Message], out: torch.Tensor
     """out = init; then add every message in order (present entries only)."""
     _require_gpu(out, "out")
     dev = out.device
+    layout._ready(dev)
     W = len(msgs)
     arr = (MessageDesc * max(W, 1))(*[m.desc() for m in msgs])
     nbytes = lib().sgc_decode_accumulate_workspace(layout.handle, arr, W)
     if W > 0 and nbytes == 0:
         raise SGCError(EINVAL, "sgc_decode_accumulate_workspace")
     if ws is None:
-        ws = workspace(nbytes, dev, "decode")
+        ws = workspace(nbytes, dev, "decode", stream)
     if status is None:
         status = _zeros(stream, 1, dtype=torch.int32, device=dev)
     _check(lib().sgc_decode_accumulate(layout.handle, arr, W, init, _ptr(base), _ptr(out), _ptr(status), _ptr(ws),

@@ -33,7 +33,19 @@ int device_tables(sgc_layout* L, DevTables** out)
     if (hipGetDevice(&dev) != hipSuccess) return SGC_EHIP;
     std::lock_guard<std::mutex> lock(L->mu);
     auto it = L->dev.find(dev);
-    if (it != L->dev.end()) { *out = &it->second; return SGC_OK; }
+    if (it == L->dev.end()) return SGC_ENOTREADY;
+    *out = &it->second;
+    return SGC_OK;
+}
+
+// The tables of one device: segment offsets and tile prefixes, then the
+// global group's {0, n} and {0, tiles}.  Allocated and copied once, at set-up.
+static int upload_tables(sgc_layout* L)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SGC_EHIP;
+    std::lock_guard<std::mutex> lock(L->mu);
+    if (L->dev.find(dev) != L->dev.end()) return SGC_OK;
     const int64_t ns = L->nseg + 1;
     std::vector<int64_t> host((size_t)(2 * ns + 4));
     std::memcpy(host.data(), L->seg_off.data(), ns * sizeof(int64_t));
@@ -53,8 +65,7 @@ int device_tables(sgc_layout* L, DevTables** out)
     t.seg_tile = b + ns;
     t.glob_off = b + 2 * ns;
     t.glob_tile = b + 2 * ns + 2;
-    auto res = L->dev.emplace(dev, t);
-    *out = &res.first->second;
+    L->dev.emplace(dev, t);
     return SGC_OK;
 }
 
@@ -117,6 +128,12 @@ extern "C" int sgc_layout_create(const int64_t* seg_numel, int32_t nseg, sgc_lay
     return SGC_OK;
 }
 
+extern "C" int sgc_layout_upload(sgc_layout* L)
+{
+    if (!L) return SGC_EINVAL;
+    return upload_tables(L);
+}
+
 extern "C" void sgc_layout_destroy(sgc_layout* L)
 {
     if (!L) return;
@@ -163,6 +180,7 @@ extern "C" const char* sgc_strerror(int code)
     case SGC_ENOSPC: return "workspace or output capacity too small";
     case SGC_EHIP: return "HIP runtime or launch failure";
     case SGC_EUNSUPPORTED: return "unsupported combination";
+    case SGC_ENOTREADY: return "layout not uploaded to the current device (sgc_layout_upload)";
     default: return "unknown error";
     }
 }

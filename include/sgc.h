@@ -38,12 +38,12 @@
  *   device can see are OR-ed into *dstatus (device uint32, may be NULL).
  * - Results are deterministic: no floating-point atomics; every sum has a
  *   fixed order.
- * - Graph capture: once a layout has been used on a device (its first use
- *   there uploads its tables synchronously), a call queues only kernel
- *   launches on `stream` -- no allocation, memset or synchronous copy -- so
- *   a sequence of calls can be captured into a HIP graph and replayed.  The
- *   sgc_layout_* calls and a layout's first use on a device cannot be
- *   captured.
+ * - A layout's tables are put on a device once, at set-up, by
+ *   sgc_layout_upload; the compute calls then queue only kernel launches on
+ *   `stream` -- no allocation, memset or synchronous copy -- so a sequence
+ *   of calls can be captured into a HIP graph and replayed.  A compute call
+ *   on a device the layout was not uploaded to returns SGC_ENOTREADY.  The
+ *   sgc_layout_* calls cannot be captured.
  */
 #ifndef SGC_H
 #define SGC_H
@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SGC_ABI_VERSION 1
+#define SGC_ABI_VERSION 2
 
 /* Return codes. */
 #define SGC_OK 0
@@ -63,6 +63,7 @@ extern "C" {
 #define SGC_ENOSPC (-2)       /* workspace or an output capacity below the host-computable bound */
 #define SGC_EHIP (-3)         /* a HIP runtime call or kernel launch failed */
 #define SGC_EUNSUPPORTED (-4) /* valid but unsupported combination */
+#define SGC_ENOTREADY (-5)    /* the layout was not uploaded to the current device */
 
 /* Device status bits, OR-ed into *dstatus. */
 #define SGC_STATUS_TRUNCATED 1u   /* sampled mode kept more than cap: the first cap (index order) were sent */
@@ -104,13 +105,19 @@ typedef void* sgc_stream_t; /* hipStream_t */
 
 /* ------------------------------------------------------------------------
  * Layout.  seg_numel [host, nseg entries >= 0]; n = sum < 2^31; nseg >= 1.
- * Creation checks the table and keeps a host copy; the device copy is made
- * on first use on each device (a one-time synchronous upload).  Returns
- * SGC_EINVAL on a bad table, SGC_ENOSPC if host memory runs out.
- * sgc_layout_destroy frees both copies; no call using the layout may still
- * be in flight.  A layout is immutable and may be shared across threads.  */
+ * Creation checks the table and keeps a host copy.  Returns SGC_EINVAL on a
+ * bad table, SGC_ENOSPC if host memory runs out.
+ * sgc_layout_upload puts the tables on the current device (set-up, not the
+ * hot path: one small hipMalloc and a synchronous copy; a repeated call on
+ * the same device returns SGC_OK at once).  Every compute call needs it
+ * done on its device first.  SGC_EINVAL for a NULL layout, SGC_EHIP if the
+ * allocation or the copy fails.
+ * sgc_layout_destroy frees the host copy and every device copy; no call
+ * using the layout may still be in flight.  A layout is immutable once
+ * uploaded and may be shared across threads.                               */
 typedef struct sgc_layout sgc_layout;
 int sgc_layout_create(const int64_t* seg_numel, int32_t nseg, sgc_layout** out);
+int sgc_layout_upload(sgc_layout* layout);
 void sgc_layout_destroy(sgc_layout* layout);
 int64_t sgc_layout_numel(const sgc_layout* layout);
 int32_t sgc_layout_nseg(const sgc_layout* layout);

@@ -36,9 +36,55 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert sgc.abi_version() == 1
-    for code in (0, -1, -2, -3, -4, 99):
+    assert sgc.abi_version() == 2
+    for code in (0, -1, -2, -3, -4, -5, 99):
         assert sgc.lib().sgc_strerror(code)
+    assert b"upload" in sgc.lib().sgc_strerror(sgc.ENOTREADY)
+
+
+def test_layout_upload_arguments():
+    lib = sgc.lib()
+    assert lib.sgc_layout_upload(None) == sgc.EINVAL
+    lay = sgc.Layout([10, 20])    # no GPU here: nothing uploaded
+    assert not lay._devices
+    assert lib.sgc_layout_upload(lay.handle) in (sgc.OK, sgc.EHIP)   # EHIP: no device to upload to
+
+
+def test_reused_compress_output_is_checked():
+    import torch
+    lay = sgc.Layout([1000, 24])
+    cpu = torch.device("cpu")
+    k = lay.keep_total(sgc.GLOBAL, 10000)
+    out, cap = sgc._compress_out(lay, None, None, sgc.EXACT, sgc.GLOBAL, 10000, cpu, None)
+    assert cap == k and out.cap == k and out.idx.numel() == k and out.counts.numel() == lay.nseg + 1
+    # reused: cap defaults to the buffer's own
+    again, cap2 = sgc._compress_out(lay, out, None, sgc.EXACT, sgc.GLOBAL, 50000, cpu, None)
+    assert again is out and cap2 == k
+    # a larger kept fraction, or sampled mode's larger default cap, does not fit
+    with pytest.raises(ValueError):
+        sgc._compress_out(lay, out, lay.keep_total(sgc.GLOBAL, 50000), sgc.EXACT, sgc.GLOBAL, 50000, cpu, None)
+    with pytest.raises(ValueError):
+        sgc._compress_out(lay, out, sgc._default_cap(lay, sgc.SAMPLED, sgc.GLOBAL, 10000), sgc.SAMPLED,
+                          sgc.GLOBAL, 10000, cpu, None)
+    # a buffer made for another layout
+    other = sgc.Layout([1000, 20, 4])
+    with pytest.raises(ValueError):
+        sgc._compress_out(other, out, None, sgc.EXACT, sgc.GLOBAL, 10000, cpu, None)
+    # a smaller cap is accepted and becomes the buffer's cap
+    _, cap3 = sgc._compress_out(lay, out, k - 1, sgc.SAMPLED, sgc.GLOBAL, 10000, cpu, None)
+    assert cap3 == k - 1 and out.cap == k - 1
+
+
+def test_reused_encode_output_is_checked():
+    import torch
+    cpu = torch.device("cpu")
+    g = sgc._encode_out(None, sgc.GLOBAL, 6, 100, 40, 4, 1, cpu, None)
+    assert g.word_off.numel() == 2 and g.nbits.numel() == 1
+    assert sgc._encode_out(g, sgc.GLOBAL, 6, 100, 40, 4, 1, cpu, None) is g
+    # per-tensor streams need nstreams + 1 offsets: a global buffer is replaced
+    p = sgc._encode_out(g, sgc.PER_SEGMENT, 6, 100, 40, 4, 5, cpu, None)
+    assert p is not g and p.word_off.numel() == 6 and p.nbits.numel() == 5 and p.scope == sgc.PER_SEGMENT
+    assert sgc._encode_out(p, sgc.GLOBAL, 6, 100, 41, 4, 1, cpu, None) is not p   # words too small
 
 
 def test_keep_count_matches_oracle(orc):

@@ -3,7 +3,8 @@ API) and replayed.
 
 The library allocates nothing and queues no memset or synchronous call once
 a layout's tables are on the device, so a whole step can be captured after
-one eager warm-up call.  Each test replays its graph several times, with
+one eager warm-up call.  Captured calls get workspaces of their own (the
+binding's cached ones could be replaced while a graph points at them).  Each test replays its graph several times, with
 eager work (a new gradient copied into the captured input) and a
 synchronization between replays, and checks every replay against the CPU
 oracle run on the same inputs.
@@ -28,14 +29,16 @@ def test_graph_compress_encode_flat(orc):
     ppm, b = w.keep_ppm, sgc.rice_param(w.keep_ppm / 1e6)
     g_in = torch.zeros(n, dtype=torch.float32, device="cuda")
     r = torch.zeros(n, dtype=torch.float32, device="cuda")
-    comp = sgc.compress(layout, g_in, r, keep_ppm=ppm)  # warm-up: tables, workspace, outputs
+    comp = sgc.compress(layout, g_in, r, keep_ppm=ppm)  # warm-up: outputs
     enc = sgc.encode(layout, comp.idx, comp.counts, comp.cap, b=b)
+    ws_c = torch.empty(sgc.compress_workspace_bytes(layout, keep_ppm=ppm), dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty(sgc.encode_workspace_bytes(layout, sgc.GLOBAL, comp.cap), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     r.zero_()
 
     def step():
-        sgc.compress(layout, g_in, r, keep_ppm=ppm, out=comp)
-        sgc.encode(layout, comp.idx, comp.counts, comp.cap, b=b, out=enc)
+        sgc.compress(layout, g_in, r, keep_ppm=ppm, out=comp, ws=ws_c)
+        sgc.encode(layout, comp.idx, comp.counts, comp.cap, b=b, out=enc, ws=ws_e)
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -76,14 +79,19 @@ def test_graph_per_tensor_sbc_round():
     comp = sgc.compress(layout, g_in, r, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm)
     bn = sgc.binarize(layout, comp, r, sgc.BIN_SBC)
     enc = sgc.encode(layout, bn.idx, bn.counts, bn.cap, scope=sgc.PER_SEGMENT, b=b)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    ws_c = torch.empty(sgc.compress_workspace_bytes(layout, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm), **u8)
+    ws_b = torch.empty(sgc.binarize_workspace_bytes(layout, comp.cap), **u8)
+    ws_e = torch.empty(sgc.encode_workspace_bytes(layout, sgc.PER_SEGMENT, bn.cap), **u8)
     torch.cuda.synchronize()
     r.zero_()
     box = {}
 
     def step():
-        sgc.compress(layout, g_in, r, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm, out=comp)
-        box["bn"] = sgc.binarize(layout, comp, r, sgc.BIN_SBC)
-        sgc.encode(layout, box["bn"].idx, box["bn"].counts, box["bn"].cap, scope=sgc.PER_SEGMENT, b=b, out=enc)
+        sgc.compress(layout, g_in, r, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm, out=comp, ws=ws_c)
+        box["bn"] = sgc.binarize(layout, comp, r, sgc.BIN_SBC, ws=ws_b)
+        sgc.encode(layout, box["bn"].idx, box["bn"].counts, box["bn"].cap, scope=sgc.PER_SEGMENT, b=b, out=enc,
+                   ws=ws_e)
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
