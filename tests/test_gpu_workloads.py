@@ -65,14 +65,15 @@ def check_topk(acc, comp, r_after, k_expected, what, seg_off=None):
 
 
 def test_mlp_mnist_two_bit_four_workers(orc):
-    # global top-1% + 2-bit quantization, 4 workers, 2 steps: raw 2-bit messages
-    # in step 0, Rice-coded positions (b = 6) in step 1
+    # global top-1% + 2-bit quantization, 4 workers, all 10 steps of the
+    # workload with carried residuals: raw 2-bit messages in even steps,
+    # Rice-coded positions (b = 6) in odd ones
     w = W.MLP_MNIST
     layout = sgc.Layout(w.seg_numel)
     seg_off = np.array(layout.seg_off, np.int64)
     b = sgc.rice_param(w.keep_ppm / 1e6)
     res = [torch.zeros(w.numel, dtype=torch.float32, device="cuda") for _ in range(w.workers)]
-    for step in range(2):
+    for step in range(w.steps):
         gm, om = [], []
         for wk in range(w.workers):
             g = W.gradient(w, wk, step, device="cuda")
@@ -85,7 +86,7 @@ def test_mlp_mnist_two_bit_four_workers(orc):
             r_host = host(rd).copy()
             bn, ob = check_binarize(orc, layout, comp, ref, rd, r_host, sgc.BIN_2BIT, f"mlp s{step} w{wk}")
             codes, means = host(bn.codes).view(np.uint32), host(bn.means)
-            if step == 0:
+            if step % 2 == 0:
                 gm.append(sgc.Message(sgc.MSG_RAW_2BIT, bn.counts, bn.cap, idx=comp.idx, codes=bn.codes,
                                       means=bn.means))
                 om.append(orc.Message(host(bn.counts), vkind=orc.VAL_2BIT, idx=ref.idx, codes=codes, means=means))
@@ -254,25 +255,35 @@ def test_flat_1g_sampled_full_size(orc):
 
 
 def test_flat_1g_decode_accumulate_sixteen_workers(orc):
-    # 16 workers' top-0.1% Rice messages (b = 9) summed into 2^30 elements
+    # 16 workers' top-0.1% Rice messages (b = 9) summed into 2^30 elements;
+    # each worker's exact selection is checked through its defining
+    # properties and each stream against the oracle's encoding of its indices
     w = W.FLAT_1G
     layout = sgc.Layout(w.seg_numel)
+    seg_off = np.array(layout.seg_off, np.int64)
     ppm = 1000
     b = sgc.rice_param(ppm / 1e6)
+    k = layout.keep_total(sgc.GLOBAL, ppm)
     msgs, sent = [], []
     rd = torch.zeros(w.numel, dtype=torch.float32, device="cuda")
     for wk in range(w.workers):
         g = W.gradient(w, wk, 0, device="cuda")
         rd.zero_()
+        acc = rd + g
         comp = sgc.compress(layout, g, rd, keep_ppm=ppm)
         enc = sgc.encode(layout, comp.idx, comp.counts, comp.cap, b=b)
+        torch.cuda.synchronize()
         del g
+        check_topk(acc, comp, rd, k, f"flat-1G worker {wk} top-0.1%")
+        del acc
         msgs.append(sgc.golomb_message(comp, enc))
         total = int(host(comp.counts)[-1])
         sent.append((comp.idx[:total].long(), comp.val[:total]))
-        if wk < 2:  # the oracle re-encodes two of the streams
-            ref = orc.encode(host(comp.idx)[:total], host(comp.counts), np.array(layout.seg_off, np.int64), 0, b)
-            assert_bitwise(host(enc.words[:int(ref.word_off[-1])]).view(np.uint32), ref.words, f"worker {wk} words")
+        ref = orc.encode(host(comp.idx)[:total], host(comp.counts), seg_off, 0, b)
+        nw = int(ref.word_off[-1])
+        assert_bitwise(host(enc.words[:nw]).view(np.uint32), ref.words, f"worker {wk} words")
+        assert_bitwise(host(enc.chunk_off[:ref.chunk_off.size]).view(np.uint64), ref.chunk_off,
+                       f"worker {wk} chunk table")
     del rd
     out = torch.empty(w.numel, dtype=torch.float32, device="cuda")
     announce("flat-1G decode_accumulate 16 x 0.1%")
