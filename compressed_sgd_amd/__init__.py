@@ -37,7 +37,8 @@ CHUNK_CODES = 256
 EXPORTED = (
     "sgc_layout_create", "sgc_layout_upload", "sgc_layout_destroy", "sgc_layout_numel", "sgc_layout_nseg",
     "sgc_keep_count", "sgc_rice_param", "sgc_strerror", "sgc_abi_version",
-    "sgc_compress_workspace", "sgc_compress", "sgc_compress_momentum_workspace", "sgc_compress_momentum",
+    "sgc_compress_workspace", "sgc_compress", "sgc_compress_noalloc",
+    "sgc_compress_momentum_workspace", "sgc_compress_momentum",
     "sgc_binarize_workspace", "sgc_binarize",
     "sgc_encode_word_bound", "sgc_encode_chunk_bound", "sgc_encode_workspace", "sgc_encode",
     "sgc_decode_accumulate_workspace", "sgc_decode_accumulate", "sgc_set_pass_events",
@@ -96,6 +97,8 @@ def lib():
         L.sgc_compress_workspace.restype = sz
         L.sgc_compress.argtypes = [P, P, P, P, P, P, i64, P, P, P, sz, P]
         L.sgc_compress.restype = C.c_int
+        L.sgc_compress_noalloc.argtypes = [P, P, P, P, P, P, i64, P, P, P]
+        L.sgc_compress_noalloc.restype = C.c_int
         L.sgc_compress_momentum_workspace.argtypes = [P, P, i64]
         L.sgc_compress_momentum_workspace.restype = sz
         L.sgc_compress_momentum.argtypes = [P, P, C.c_float, P, P, P, P, P, i64, P, P, P, sz, P]
@@ -348,6 +351,40 @@ def compress(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode
     _check(lib().sgc_compress(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), _ptr(out.idx),
                               _ptr(out.val), cap, _ptr(out.counts), _ptr(out.status), _ptr(ws), ws.numel(), st),
            "sgc_compress")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SGC_NOALLOC_SCRATCH_BYTES
+
+
+def compress_noalloc(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode: int = EXACT,
+                     scope: int = GLOBAL, keep_ppm: int = 10000, sample_div: int = 1000, sample_min: int = 65536,
+                     cap: Optional[int] = None, out: Optional[Compressed] = None, hold: bool = False,
+                     stream=None) -> Optional[Compressed]:
+    """compress() through sgc_compress_noalloc: the library's own scratch buffer
+    instead of a workspace.  The library allocates nothing; pass `out` to keep
+    this function from allocating the output buffers either.  Calls that may
+    overlap on one GPU share that buffer and must be serialised."""
+    for t, name in ((grad, "grad"), (residual, "residual")):
+        _require_gpu(t, name)
+        if t.dtype != torch.float32 or t.numel() != layout.n:
+            raise ValueError(f"{name} must be float32 with {layout.n} elements")
+    dev = grad.device
+    layout._ready(dev)
+    opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min)
+    st = _stream(dev, stream)
+    if mode == ACCUMULATE_ONLY:
+        _check(lib().sgc_compress_noalloc(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), None, None, 0,
+                                          None, None, st), "sgc_compress_noalloc")
+        return None
+    out, cap = _compress_out(layout, out, cap, mode, scope, keep_ppm, dev, stream)
+    rc = lib().sgc_compress_noalloc(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), _ptr(out.idx),
+                                    _ptr(out.val), cap, _ptr(out.counts), _ptr(out.status), st)
+    if rc == ENOSPC:
+        need = lib().sgc_compress_workspace(layout.handle, C.byref(opts), cap)
+        raise SGCError(rc, f"sgc_compress_noalloc (this call needs {need} bytes of workspace, the scratch "
+                           f"buffer holds {NOALLOC_SCRATCH_BYTES})")
+    _check(rc, "sgc_compress_noalloc")
     return out
 
 

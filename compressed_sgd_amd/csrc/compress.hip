@@ -1531,16 +1531,26 @@ static int compress_impl(sgc_layout* L, const sgc_compress_opts* o, bool hold, M
     return SGC_OK;
 }
 
-extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, const float* grad, float* residual,
-                            int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts, uint32_t* dstatus,
-                            void* ws, size_t ws_bytes, sgc_stream_t stream)
+namespace sgc {
+int compress_call(const sgc_layout* Lc, const sgc_compress_opts* o, const float* grad, float* residual,
+                  int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts, uint32_t* dstatus, void* ws,
+                  size_t ws_bytes, hipStream_t stream)
 {
     sgc_layout* L = const_cast<sgc_layout*>(Lc);
     if (!opts_ok(L, o)) return SGC_EINVAL;
     if ((L->n > 0 && (!grad || !residual)) || !aligned16(grad) || !aligned16(residual)) return SGC_EINVAL;
     const sgc_compress_opts p = plain_opts(o);
     return compress_impl(L, &p, (o->mode & SGC_HOLD_KEPT) != 0, NoMom{0.0f, nullptr}, grad, residual, out_idx,
-                         out_val, cap, out_counts, dstatus, ws, ws_bytes, (hipStream_t)stream);
+                         out_val, cap, out_counts, dstatus, ws, ws_bytes, stream);
+}
+}  // namespace sgc
+
+extern "C" int sgc_compress(const sgc_layout* Lc, const sgc_compress_opts* o, const float* grad, float* residual,
+                            int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts, uint32_t* dstatus,
+                            void* ws, size_t ws_bytes, sgc_stream_t stream)
+{
+    return compress_call(Lc, o, grad, residual, out_idx, out_val, cap, out_counts, dstatus, ws, ws_bytes,
+                         (hipStream_t)stream);
 }
 
 extern "C" int sgc_compress_momentum(const sgc_layout* Lc, const sgc_compress_opts* o, float beta, const float* grad,

@@ -131,7 +131,12 @@ extern "C" int sgc_layout_create(const int64_t* seg_numel, int32_t nseg, sgc_lay
 extern "C" int sgc_layout_upload(sgc_layout* L)
 {
     if (!L) return SGC_EINVAL;
-    return upload_tables(L);
+    const int rc = upload_tables(L);
+    if (rc) return rc;
+    // The no-allocation entry point's scratch address on this device.  A
+    // failure here is not the layout's: sgc_compress_noalloc reports it.
+    (void)scratch_init();
+    return SGC_OK;
 }
 
 extern "C" void sgc_layout_destroy(sgc_layout* L)

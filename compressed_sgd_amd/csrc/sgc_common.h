@@ -246,4 +246,17 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // may be captured into a graph).
 int fill_u32(void* p, int64_t count, uint32_t value, hipStream_t s);
 
+// sgc_compress with the stream already cast (shared with the no-allocation
+// entry point, which passes the library's own scratch buffer as ws).
+int compress_call(const sgc_layout* L, const sgc_compress_opts* o, const float* grad, float* residual,
+                  int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts, uint32_t* dstatus, void* ws,
+                  size_t ws_bytes, hipStream_t stream);
+
+// The device address of the no-allocation scratch buffer on the current
+// device: looked up once per device by scratch_init (called from the
+// layout upload, the library's per-device set-up); scratch_device returns
+// nullptr where that has not happened or failed.
+int scratch_init();
+void* scratch_device();
+
 }  // namespace sgc

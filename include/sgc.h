@@ -182,6 +182,31 @@ int sgc_compress(const sgc_layout* layout, const sgc_compress_opts* opt,
                  uint32_t* dstatus, void* ws, size_t ws_bytes, sgc_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Compress without allocating -- for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *
+ * Exactly sgc_compress (same arguments, results, status and errors), with
+ * the library's own scratch buffer in place of ws: a file-scope device array
+ * of SGC_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds from
+ * its first layout upload until the process ends.  The call itself performs
+ * no allocation of any kind.  Returns SGC_ENOSPC when the call would need
+ * more workspace than that (sgc_compress_workspace(layout, opt, cap) >
+ * SGC_NOALLOC_SCRATCH_BYTES: past about 75M elements at top-1% in one group,
+ * 12M at top-10%),
+ * SGC_ENOTREADY if no layout was uploaded to the current device (the upload
+ * looks up the buffer's device address).  Every call on a GPU shares that
+ * GPU's buffer, so calls that may overlap in time on one GPU (two streams,
+ * two threads) race and give wrong results: serialise them.  The buffer
+ * keeps the last call's contents; the compress kernels clear what they need
+ * cleared themselves.                                                     */
+#define SGC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sgc_compress_noalloc(const sgc_layout* layout, const sgc_compress_opts* opt,
+                         const float* grad, float* residual,
+                         int32_t* out_idx, float* out_val, int64_t cap, int64_t* out_counts,
+                         uint32_t* dstatus, sgc_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Compress one step with momentum correction and momentum masking ([SBC]
  * appendix A Momentum Correction, Warm-up Training and Momentum Masking:
  * the momentum-corrected gradient is added to the residual, and the
