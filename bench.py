@@ -19,9 +19,11 @@ SBC binarize, decode-accumulate of 16 workers' Rice messages), every other
 workload on its own shapes (flat 2^20; the MLP with 2-bit messages; the
 NMT-style model with its global+local sum; ResNet-50 per tensor with delay,
 SBC and Rice: worker step exact and sampled, and the receive step), a grid
-of communication delay (1, 10, 100) against kept fraction (25% to 0.1%)
-with time and bits per element per iteration, and the CPU oracle timed on a
-bounded sample as a baseline.
+of communication delay (1, 10, 100) against kept fraction (25% to 0.1%),
+each cell timed as its real sequence of calls, with time and bits per
+element per iteration, the warm-up schedule (kept fraction 25% -> 0.1% over
+20 carried steps) with per-step time and bits, and the CPU oracle timed on
+a bounded sample as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -97,40 +99,95 @@ def graph_timed(fn, reps, stream):
     return e0.elapsed_time(e1) / reps
 
 
-def sparsity_grid(sgc, W, torch, dev, stream, log2n=26, reps=5):
-    """Temporal versus gradient sparsity: communication delay n (n - 1
-    accumulate-only steps, then one exchange: exact top-p compress + Rice)
-    crossed with the kept fraction p, on the first 2^log2n elements of the
-    flat gradient.  Per cell: time per training iteration, ((n - 1) x the
-    measured accumulate step + the measured exchange) / n, and the bits sent
-    per element per iteration, (Rice position bits + 32 value bits per kept
-    entry) / (n x elements)."""
-    w = W.FLAT_1G
-    N = 1 << log2n
+def sparsity_grid(sgc, W, torch, dev, stream, grads, reps=2):
+    """Temporal versus gradient sparsity ([SBC] §III; §II Communication
+    Delay): communication delay n crossed with the kept fraction p, at the
+    full 2^30 elements.  Each cell is timed as the real sequence it stands
+    for -- n - 1 accumulate-only calls, then one exchange (exact top-p
+    compress + Rice encode) -- with the residual carried, `reps` times, HIP
+    events around every sequence.  Per cell: time per training iteration
+    (sequence time / n) and the bits sent per element per iteration,
+    (Rice position bits + 32 value bits per kept entry) / (n x elements)."""
+    N = grads[0].numel()
     L = sgc.Layout([N])
-    g = W.gradient(w, 0, 0, device=dev, numel=N)
     r = torch.zeros(N, dtype=torch.float32, device=dev)
-    t_acc = timed(lambda: sgc.compress(L, g, r, mode=sgc.ACCUMULATE_ONLY), reps, stream)
-    exch = {}
+    u8 = dict(dtype=torch.uint8, device=dev)
+    cells = []
     for p in (250000, 100000, 10000, 1000):
         b = sgc.rice_param(p / 1e6)
-        c = sgc.compress(L, g, r, keep_ppm=p)
+        c = sgc.compress(L, grads[0], r, keep_ppm=p)
         e = sgc.encode(L, c.idx, c.counts, c.cap, b=b)
+        wsc = torch.empty(sgc.compress_workspace_bytes(L, keep_ppm=p), **u8)
+        wse = torch.empty(sgc.encode_workspace_bytes(L, sgc.GLOBAL, c.cap), **u8)
+        for n_delay in (1, 10, 100):
+            it = [0]
 
-        def step():
-            sgc.compress(L, g, r, keep_ppm=p, out=c)
-            sgc.encode(L, c.idx, c.counts, c.cap, b=b, out=e)
-        t = timed(step, reps, stream)
-        exch[p] = (t, int(e.nbits[0].item()), c.total(), b)
-        del c, e
-    cells = []
-    for n_delay in (1, 10, 100):
-        for p, (t, nbits, kept, b) in exch.items():
-            cells.append({"delay": n_delay, "keep_pct": p / 1e4, "rice_b": b,
-                          "ms_per_iteration": ((n_delay - 1) * t_acc + t) / n_delay,
-                          "bits_per_element_per_iteration": (nbits + 32.0 * kept) / (n_delay * N)})
-    return {"elements": N, "accumulate_ms": t_acc,
-            "exchange_ms": {f"{p / 1e4:g}pct": v[0] for p, v in exch.items()}, "cells": cells}
+            def sequence():
+                for _ in range(n_delay - 1):
+                    sgc.compress(L, grads[it[0] % 2], r, mode=sgc.ACCUMULATE_ONLY)
+                    it[0] += 1
+                sgc.compress(L, grads[it[0] % 2], r, keep_ppm=p, out=c, ws=wsc)
+                sgc.encode(L, c.idx, c.counts, c.cap, b=b, out=e, ws=wse)
+                it[0] += 1
+            r.zero_()
+            t = timed(sequence, reps, stream)
+            cells.append({"delay": n_delay, "keep_pct": p / 1e4, "rice_b": b, "ms_per_sequence": t,
+                          "ms_per_iteration": t / n_delay, "kept": c.total(),
+                          "bits_per_element_per_iteration": (int(e.nbits[0].item()) + 32.0 * c.total())
+                          / (n_delay * N)})
+        del c, e, wsc, wse
+    return {"elements": N, "timed": "each cell as n - 1 accumulate-only calls + one exchange, residual carried",
+            "cells": cells}
+
+
+def warmup_run(sgc, torch, dev, stream, grads, steps=20, start_ppm=250000, end_ppm=1000):
+    """Warm-up training ([SBC] appendix A: the kept fraction falls
+    exponentially from 25% to 0.1% over the first epochs) as a carried
+    sequence at 2^30 elements: step t keeps sgc_warmup_ppm(t, steps) parts
+    per million (exact global selection, residual carried from the step
+    before) and Rice-codes them with the parameter that suits that density.
+    The schedule runs once on a scratch residual (it sizes every buffer),
+    then for real, each step between its own HIP events."""
+    N = grads[0].numel()
+    L = sgc.Layout([N])
+    ppms = [sgc.warmup_ppm(t, steps, start_ppm, end_ppm) for t in range(steps)]
+    u8 = dict(dtype=torch.uint8, device=dev)
+    cap = max(L.keep_total(sgc.GLOBAL, p) for p in ppms)
+    ws_c = torch.empty(max(sgc.compress_workspace_bytes(L, keep_ppm=p) for p in ppms), **u8)
+    ws_e = torch.empty(sgc.encode_workspace_bytes(L, sgc.GLOBAL, cap), **u8)
+    r = torch.zeros(N, dtype=torch.float32, device=dev)
+    comp = sgc.compress(L, grads[0], r, keep_ppm=ppms[0], cap=cap, ws=ws_c)
+    enc = None
+    for t, p in enumerate(ppms):  # sizing pass
+        k = L.keep_total(sgc.GLOBAL, p)
+        sgc.compress(L, grads[t % 2], r, keep_ppm=p, cap=k, out=comp, ws=ws_c)
+        enc = sgc.encode(L, comp.idx, comp.counts, k, b=sgc.rice_param(p / 1e6), out=enc, ws=ws_e)
+    r.zero_()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ppms]
+    for t, p in enumerate(ppms):
+        k = L.keep_total(sgc.GLOBAL, p)
+        a, z = ev[t]
+        a.record(stream)
+        sgc.compress(L, grads[t % 2], r, keep_ppm=p, cap=k, out=comp, ws=ws_c)
+        sgc.encode(L, comp.idx, comp.counts, k, b=sgc.rice_param(p / 1e6), out=enc, ws=ws_e)
+        z.record(stream)
+        ev[t] = (a, z, comp.counts[-1].clone(), enc.nbits[0].clone())
+    torch.cuda.synchronize()
+    rows = []
+    for t, p in enumerate(ppms):
+        a, z, kept, nbits = ev[t]
+        kept, nbits = int(kept.item()), int(nbits.item())
+        ms = a.elapsed_time(z)
+        rows.append({"step": t, "keep_ppm": p, "rice_b": sgc.rice_param(p / 1e6), "kept": kept, "ms": ms,
+                     "elements_per_s": N / (ms / 1e3),
+                     "alg_GBps": (12.0 * N + 12.0 * kept + nbits / 8.0) / (ms / 1e3) / 1e9,
+                     "bits_per_position": nbits / max(kept, 1),
+                     "bits_per_element": (nbits + 32.0 * kept) / N})
+    total = sum(x["ms"] for x in rows)
+    return {"elements": N, "steps": steps, "start_ppm": start_ppm, "end_ppm": end_ppm,
+            "schedule": "kept ppm = start * (end/start)^(t/(steps-1)), rounded", "total_ms": total,
+            "bits_per_element_total": sum(x["bits_per_element"] for x in rows), "per_step": rows}
 
 
 def workload_rows(sgc, W, torch, dev, stream, reps=10):
@@ -500,8 +557,10 @@ def main():
         del r16, outd
         print("[bench] the other workloads", file=sys.stderr, flush=True)
         out["workloads"] = workload_rows(sgc, W, torch, dev, stream)
+        print("[bench] warm-up schedule 25% -> 0.1% over 20 steps", file=sys.stderr, flush=True)
+        out["warmup_schedule"] = warmup_run(sgc, torch, dev, stream, grads)
         print("[bench] temporal x gradient sparsity grid", file=sys.stderr, flush=True)
-        out["sparsity_grid"] = sparsity_grid(sgc, W, torch, dev, stream)
+        out["sparsity_grid"] = sparsity_grid(sgc, W, torch, dev, stream, grads)
 
     if not args.no_cpu_baseline:
         import oracle as orc

@@ -36,7 +36,7 @@ CHUNK_CODES = 256
 
 EXPORTED = (
     "sgc_layout_create", "sgc_layout_upload", "sgc_layout_destroy", "sgc_layout_numel", "sgc_layout_nseg",
-    "sgc_keep_count", "sgc_rice_param", "sgc_strerror", "sgc_abi_version",
+    "sgc_keep_count", "sgc_rice_param", "sgc_warmup_ppm", "sgc_strerror", "sgc_abi_version",
     "sgc_compress_workspace", "sgc_compress", "sgc_compress_noalloc",
     "sgc_compress_momentum_workspace", "sgc_compress_momentum",
     "sgc_binarize_workspace", "sgc_binarize",
@@ -89,6 +89,8 @@ def lib():
         L.sgc_keep_count.restype = i64
         L.sgc_rice_param.argtypes = [C.c_double]
         L.sgc_rice_param.restype = i32
+        L.sgc_warmup_ppm.argtypes = [i64, i64, u32, u32]
+        L.sgc_warmup_ppm.restype = i64
         L.sgc_strerror.argtypes = [C.c_int]
         L.sgc_strerror.restype = C.c_char_p
         L.sgc_abi_version.argtypes = []
@@ -170,6 +172,14 @@ def keep_count(n: int, keep_ppm: int) -> int:
 
 def rice_param(p: float) -> int:
     return int(lib().sgc_rice_param(p))
+
+
+def warmup_ppm(step: int, steps: int, start_ppm: int = 250000, end_ppm: int = 1000) -> int:
+    """Kept parts per million at step `step` of an exponential warm-up (sgc_warmup_ppm)."""
+    v = int(lib().sgc_warmup_ppm(step, steps, start_ppm, end_ppm))
+    if v < 0:
+        raise ValueError("bad warm-up arguments")
+    return v
 
 
 def abi_version() -> int:

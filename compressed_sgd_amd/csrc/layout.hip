@@ -177,6 +177,22 @@ extern "C" int32_t sgc_rice_param(double p)
     return best;
 }
 
+// Warm-up schedule ([SBC] appendix A, Warm-up Training: the kept fraction
+// falls exponentially, from 25% to 0.1%, over the first epochs): the kept
+// parts per million of step `step` of a `steps`-step warm-up,
+// start * (end / start)^(step / (steps - 1)) rounded to the nearest integer;
+// `start` at step 0, `end` from step steps - 1 on.
+extern "C" int64_t sgc_warmup_ppm(int64_t step, int64_t steps, uint32_t start_ppm, uint32_t end_ppm)
+{
+    if (step < 0 || steps < 1 || start_ppm == 0 || end_ppm == 0 || start_ppm > 1000000 || end_ppm > 1000000)
+        return -1;
+    if (steps == 1 || step >= steps - 1) return end_ppm;
+    if (step == 0) return start_ppm;
+    const double u = (double)step / (double)(steps - 1);
+    const double p = (double)start_ppm * std::pow((double)end_ppm / (double)start_ppm, u);
+    return (int64_t)std::floor(p + 0.5);
+}
+
 extern "C" const char* sgc_strerror(int code)
 {
     switch (code) {

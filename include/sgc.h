@@ -130,9 +130,18 @@ int32_t sgc_layout_nseg(const sgc_layout* layout);
  *   Binarization: the largest fraction p is kept).  -1 on bad arguments.
  * sgc_rice_param: the Rice parameter b minimising the mean code length
  *   b + 1/(1 - (1-p)^(2^b)) of geometric gaps at density p, ties to the
- *   smaller b ([SBC] §II Optimal Position Encoding).  -1 unless 0 < p <= 1. */
+ *   smaller b ([SBC] §II Optimal Position Encoding).  -1 unless 0 < p <= 1.
+ * sgc_warmup_ppm: the kept parts per million of step `step` (0-based) of a
+ *   warm-up of `steps` steps whose kept fraction falls exponentially from
+ *   start_ppm to end_ppm ([SBC] appendix A, Warm-up Training: from 25% to
+ *   0.1% over the first epochs): start * (end/start)^(step/(steps-1))
+ *   rounded to the nearest integer, start_ppm at step 0 and end_ppm from
+ *   step steps-1 on.  -1 unless step >= 0, steps >= 1 and both fractions
+ *   are in [1, 1e6].  The compress calls take any keep_ppm, so a caller
+ *   runs the warm-up by passing this value at each step.                  */
 int64_t sgc_keep_count(int64_t n, uint32_t keep_ppm);
 int32_t sgc_rice_param(double p);
+int64_t sgc_warmup_ppm(int64_t step, int64_t steps, uint32_t start_ppm, uint32_t end_ppm);
 const char* sgc_strerror(int code);
 int32_t sgc_abi_version(void);
 

@@ -46,6 +46,8 @@ def lib():
         L.orc_keep_count.argtypes = [i64, u32]
         L.orc_sample_count.restype = i64
         L.orc_sample_count.argtypes = [i64, u32, u32]
+        L.orc_warmup_ppm.restype = i64
+        L.orc_warmup_ppm.argtypes = [i64, i64, u32, u32]
         L.orc_rice_expected_bits.restype = f64
         L.orc_rice_expected_bits.argtypes = [i32, f64]
         L.orc_rice_param.restype = i32
@@ -93,6 +95,10 @@ def keep_count(n: int, ppm: int) -> int:
 
 def sample_count(n: int, sample_div: int = 1000, sample_min: int = 65536) -> int:
     return int(lib().orc_sample_count(n, sample_div, sample_min))
+
+
+def warmup_ppm(t: int, steps: int, start: int = 250000, end: int = 1000) -> int:
+    return int(lib().orc_warmup_ppm(t, steps, start, end))
 
 
 def rice_expected_bits(b: int, p: float) -> float:

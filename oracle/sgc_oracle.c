@@ -84,6 +84,22 @@ int64_t orc_sample_count(int64_t n, uint32_t sample_div, uint32_t sample_min)
     return s > n ? n : s;
 }
 
+/* Warm-up schedule.  [SBC] appendix A (Warm-up Training): the kept fraction
+ * falls exponentially, from 25% to 0.1%, over the first epochs.  Reading:
+ * over `steps` steps the kept fraction moves geometrically from start to
+ * end, p(t) = exp((1 - u) ln start + u ln end) with u = t / (steps - 1),
+ * rounded to the nearest part per million; from the last warm-up step on
+ * it stays at end.  Returns -1 on bad arguments.                           */
+int64_t orc_warmup_ppm(int64_t t, int64_t steps, uint32_t start, uint32_t end)
+{
+    if (t < 0 || steps < 1 || start == 0 || end == 0 || start > 1000000 || end > 1000000) return -1;
+    if (t == 0 && steps > 1) return start;
+    if (t >= steps - 1) return end;
+    double u = (double)t / (double)(steps - 1);
+    double p = exp((1.0 - u) * log((double)start) + u * log((double)end));
+    return (int64_t)floor(p + 0.5);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Rice code length statistics.  [SBC] §II Optimal Position Encoding: the
  * distances between nonzero elements are Golomb coded.  For a position set

@@ -101,6 +101,17 @@ def test_rice_param_matches_oracle(orc):
     assert sgc.rice_param(0.0) == -1 and sgc.rice_param(1.5) == -1
 
 
+def test_warmup_ppm_matches_oracle(orc):
+    for T in (1, 2, 6, 20, 37, 100):
+        for t in range(0, T + 3):
+            for a, b in ((250000, 1000), (1000000, 1), (10000, 10000), (1000, 250000)):
+                assert sgc.lib().sgc_warmup_ppm(t, T, a, b) == orc.warmup_ppm(t, T, a, b)
+    assert sgc.warmup_ppm(0, 20) == 250000 and sgc.warmup_ppm(19, 20) == 1000
+    for bad in ((-1, 6, 1, 1), (0, 0, 1, 1), (0, 6, 0, 1), (0, 6, 1, 0), (0, 6, 1000001, 1)):
+        assert sgc.lib().sgc_warmup_ppm(*bad) == -1
+        assert orc.warmup_ppm(*bad) == -1
+
+
 def test_layout_validation():
     lib = sgc.lib()
     h = C.c_void_p()

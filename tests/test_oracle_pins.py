@@ -720,3 +720,34 @@ def test_sbc_equal_means_send_positive_side(orc):
     out = orc.binarize(sp, 1, orc.BIN_SBC, r)
     assert out.means.tolist() == [0.5] and out.idx.tolist() == [0, 3]
     assert r.tolist() == [0.0, -0.25, -0.75, 0.0]
+
+
+# ------------------------------------------------------------- warm-up
+# [SBC] appendix A (Warm-up Training): the kept fraction falls exponentially
+# from 25% to 0.1% over the first epochs.  Reading: geometric interpolation
+# in kept parts per million over the warm-up steps, rounded to the nearest
+# integer.  Literal values from 250000 * 0.004^(t/(T-1)) evaluated in 60-digit
+# decimal arithmetic (none lies near a rounding boundary):
+WARMUP_6 = [250000, 82861, 27464, 9103, 3017, 1000]            # 82861.35, 27464.01, 9102.82, 3017.09
+WARMUP_20 = [250000, 186953, 139806, 104549, 78183, 58466, 43722, 32696, 24450, 18284,
+             13673, 10225, 7646, 5718, 4276, 3198, 2391, 1788, 1337, 1000]
+
+
+def test_warmup_schedule_literal(orc):
+    assert [orc.warmup_ppm(t, 6) for t in range(6)] == WARMUP_6
+    assert [orc.warmup_ppm(t, 20) for t in range(20)] == WARMUP_20
+    # after the warm-up the kept fraction stays at its end value
+    assert orc.warmup_ppm(6, 6) == orc.warmup_ppm(1000, 6) == 1000
+    assert orc.warmup_ppm(0, 1) == 1000
+    assert orc.warmup_ppm(3, 7, 1000, 1000) == 1000
+    assert orc.warmup_ppm(-1, 6) == -1 and orc.warmup_ppm(0, 0) == -1 and orc.warmup_ppm(0, 6, 0, 1000) == -1
+
+
+def test_warmup_schedule_is_geometric(orc):
+    # consecutive ratios are constant up to the rounding of each term
+    for T in (6, 20, 50):
+        ps = [orc.warmup_ppm(t, T) for t in range(T)]
+        r = (1000 / 250000) ** (1 / (T - 1))
+        for a, b in zip(ps, ps[1:]):
+            assert abs(b - a * r) <= 0.5 + 0.5 * r + 1e-9
+        assert all(b < a for a, b in zip(ps, ps[1:]))
