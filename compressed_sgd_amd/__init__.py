@@ -27,6 +27,8 @@ OK, EINVAL, ENOSPC, EHIP, EUNSUPPORTED, ENOTREADY = 0, -1, -2, -3, -4, -5
 STATUS_TRUNCATED, STATUS_CORRUPT, STATUS_DENSE_PATH, STATUS_BAD_INPUT = 1, 2, 4, 8
 EXACT, SAMPLED, ACCUMULATE_ONLY = 0, 1, 2
 HOLD_KEPT = 0x10
+# compress pipelines (same result; AUTO picks by kept fraction and vector size)
+PATH_AUTO, PATH_GATHER, PATH_WINDOW = 0, 1, 2
 GLOBAL, PER_SEGMENT = 0, 1
 BIN_SBC, BIN_2BIT = 0, 1
 BIN_HELD = 0x10
@@ -53,7 +55,7 @@ class SGCError(RuntimeError):
 
 class CompressOpts(C.Structure):
     _fields_ = [("mode", C.c_int32), ("scope", C.c_int32), ("keep_ppm", C.c_uint32),
-                ("sample_div", C.c_uint32), ("sample_min", C.c_uint32)]
+                ("sample_div", C.c_uint32), ("sample_min", C.c_uint32), ("path", C.c_uint32)]
 
 
 class MessageDesc(C.Structure):
@@ -271,9 +273,9 @@ def workspace(nbytes: int, device: torch.device, slot: str = "default", stream=N
 
 def compress_workspace_bytes(layout: "Layout", *, mode: int = EXACT, scope: int = GLOBAL, keep_ppm: int = 10000,
                              sample_div: int = 1000, sample_min: int = 65536, cap: Optional[int] = None,
-                             hold: bool = False, momentum: bool = False) -> int:
+                             hold: bool = False, momentum: bool = False, path: int = 0) -> int:
     """Workspace bytes of one compress (or compress_momentum) call with these options."""
-    opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min)
+    opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min, path)
     cap = _default_cap(layout, mode, scope, keep_ppm) if cap is None else cap
     f = lib().sgc_compress_momentum_workspace if momentum else lib().sgc_compress_workspace
     return int(f(layout.handle, C.byref(opts), cap))
@@ -336,7 +338,7 @@ class Compressed:
 def compress(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode: int = EXACT,
              scope: int = GLOBAL, keep_ppm: int = 10000, sample_div: int = 1000, sample_min: int = 65536,
              cap: Optional[int] = None, out: Optional[Compressed] = None, ws: Optional[torch.Tensor] = None,
-             hold: bool = False, stream=None) -> Optional[Compressed]:
+             hold: bool = False, stream=None, path: int = 0) -> Optional[Compressed]:
     """One step: residual += grad, select, emit, zero the residual at kept entries.
 
     mode ACCUMULATE_ONLY only adds (communication delay) and returns None.
@@ -348,7 +350,7 @@ def compress(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode
             raise ValueError(f"{name} must be float32 with {layout.n} elements")
     dev = grad.device
     layout._ready(dev)
-    opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min)
+    opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min, path)
     st = _stream(dev, stream)
     if mode == ACCUMULATE_ONLY:
         _check(lib().sgc_compress(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), None, None, 0, None,
@@ -370,7 +372,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # SGC_NOALLOC_SCRATCH_BYTES
 def compress_noalloc(layout: Layout, grad: torch.Tensor, residual: torch.Tensor, *, mode: int = EXACT,
                      scope: int = GLOBAL, keep_ppm: int = 10000, sample_div: int = 1000, sample_min: int = 65536,
                      cap: Optional[int] = None, out: Optional[Compressed] = None, hold: bool = False,
-                     stream=None) -> Optional[Compressed]:
+                     stream=None, path: int = 0) -> Optional[Compressed]:
     """compress() through sgc_compress_noalloc: the library's own scratch buffer
     instead of a workspace.  The library allocates nothing; pass `out` to keep
     this function from allocating the output buffers either.  Calls that may
@@ -381,7 +383,7 @@ def compress_noalloc(layout: Layout, grad: torch.Tensor, residual: torch.Tensor,
             raise ValueError(f"{name} must be float32 with {layout.n} elements")
     dev = grad.device
     layout._ready(dev)
-    opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min)
+    opts = CompressOpts(mode | (HOLD_KEPT if hold else 0), scope, keep_ppm, sample_div, sample_min, path)
     st = _stream(dev, stream)
     if mode == ACCUMULATE_ONLY:
         _check(lib().sgc_compress_noalloc(layout.handle, C.byref(opts), _ptr(grad), _ptr(residual), None, None, 0,
@@ -402,7 +404,7 @@ def compress_momentum(layout: Layout, grad: torch.Tensor, momentum: torch.Tensor
                       beta: float, *, mode: int = EXACT, scope: int = GLOBAL, keep_ppm: int = 10000,
                       sample_div: int = 1000, sample_min: int = 65536, cap: Optional[int] = None,
                       out: Optional[Compressed] = None, ws: Optional[torch.Tensor] = None,
-                      stream=None) -> Optional[Compressed]:
+                      stream=None, path: int = 0) -> Optional[Compressed]:
     """One step with momentum correction: momentum = beta*momentum + grad, residual += momentum,
     select, emit, zero residual and momentum at the sent entries.
 
@@ -414,7 +416,7 @@ def compress_momentum(layout: Layout, grad: torch.Tensor, momentum: torch.Tensor
             raise ValueError(f"{name} must be float32 with {layout.n} elements")
     dev = grad.device
     layout._ready(dev)
-    opts = CompressOpts(mode, scope, keep_ppm, sample_div, sample_min)
+    opts = CompressOpts(mode, scope, keep_ppm, sample_div, sample_min, path)
     st = _stream(dev, stream)
     if mode == ACCUMULATE_ONLY:
         _check(lib().sgc_compress_momentum(layout.handle, C.byref(opts), float(beta), _ptr(grad), _ptr(momentum),

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SGC_ABI_VERSION 2
+#define SGC_ABI_VERSION 3
 
 /* Return codes. */
 #define SGC_OK 0
@@ -68,7 +68,7 @@ extern "C" {
 /* Device status bits, OR-ed into *dstatus. */
 #define SGC_STATUS_TRUNCATED 1u   /* sampled mode kept more than cap: the first cap (index order) were sent */
 #define SGC_STATUS_CORRUPT 2u     /* a message failed to decode (that message is skipped entirely) */
-#define SGC_STATUS_DENSE_PATH 4u  /* exact selection took its full-pass path (informational, result unchanged) */
+#define SGC_STATUS_DENSE_PATH 4u  /* exact selection could not use its sampled bounds for a group: it was selected from all its candidates or the whole residual (informational, result unchanged) */
 #define SGC_STATUS_BAD_INPUT 8u   /* encode: indices not strictly ascending inside a stream (output undefined) */
 
 /* Compress modes. */
@@ -76,6 +76,12 @@ extern "C" {
 #define SGC_SAMPLED 1         /* threshold estimated from a systematic sample, every |acc| >= T kept */
 #define SGC_ACCUMULATE_ONLY 2 /* communication delay: r <- r + g only */
 #define SGC_HOLD_KEPT 0x10    /* flag for SGC_EXACT / SGC_SAMPLED: kept entries keep acc in the residual */
+
+/* Compress pipelines (sgc_compress_opts.path); every choice gives the same
+ * result bit for bit. */
+#define SGC_PATH_AUTO 0u      /* window above about 2.5% kept or from 2^29 elements on, else gather */
+#define SGC_PATH_GATHER 1u    /* candidates copied into one array, selected and compacted (fastest at low kept fractions) */
+#define SGC_PATH_WINDOW 2u    /* only entries between the probe's bounds selected; output written from the tile regions */
 
 /* Selection / stream scope. */
 #define SGC_GLOBAL 0      /* one selection (one Rice stream) over the whole vector */
@@ -175,13 +181,15 @@ int32_t sgc_abi_version(void);
  * grad [device, n fp32] is read; residual [device, n fp32] is updated in
  * place.  cap = capacity of out_idx/out_val; SGC_EXACT requires cap >= the
  * sum of the groups' k (else SGC_EINVAL).  keep_ppm <= 1e6, sample_div >= 1.
- * sgc_compress_workspace returns the ws bytes needed (0 on bad arguments). */
+ * sgc_compress_workspace returns the ws bytes needed (0 on bad arguments),
+ * which depends on the pipeline (opts.path) the call takes. */
 typedef struct {
     int32_t mode;        /* SGC_EXACT | SGC_SAMPLED | SGC_ACCUMULATE_ONLY */
     int32_t scope;       /* SGC_GLOBAL | SGC_PER_SEGMENT */
     uint32_t keep_ppm;   /* kept parts per million: 10000 = top-1%, 1000 = top-0.1% */
     uint32_t sample_div; /* SGC_SAMPLED: sample one per sample_div elements (default 1000) */
     uint32_t sample_min; /* SGC_SAMPLED: at least this many samples per group (default 65536) */
+    uint32_t path;       /* SGC_PATH_AUTO (0), SGC_PATH_GATHER or SGC_PATH_WINDOW: how the work is done, not what */
 } sgc_compress_opts;
 
 size_t sgc_compress_workspace(const sgc_layout* layout, const sgc_compress_opts* opt, int64_t cap);

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert sgc.abi_version() == 2
+    assert sgc.abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, 99):
         assert sgc.lib().sgc_strerror(code)
     assert b"upload" in sgc.lib().sgc_strerror(sgc.ENOTREADY)
@@ -153,6 +153,30 @@ def test_compress_validation():
     assert call(o, ws=None) == sgc.ENOSPC
     assert call(o, wsb=ws_need - 1) == sgc.ENOSPC
     assert lib.sgc_compress_workspace(lay.handle, C.byref(sgc.CompressOpts(9, 0, 1, 1, 1)), 5) == 0
+    assert call(sgc.CompressOpts(0, 0, 10000, 1000, 1, 3)) == sgc.EINVAL   # no such pipeline
+    assert lib.sgc_compress_workspace(lay.handle, C.byref(sgc.CompressOpts(0, 0, 10000, 1000, 1, 3)), k) == 0
+
+
+@pytest.mark.parametrize("sizes,ppm,auto", [([1 << 20, 4097], 10000, sgc.PATH_GATHER),
+                                            ([1 << 20, 4097], 25000, sgc.PATH_GATHER),
+                                            ([1 << 20, 4097], 30000, sgc.PATH_WINDOW),
+                                            ([1 << 20, 4097], 250000, sgc.PATH_WINDOW),
+                                            ([(1 << 29) - 1], 10000, sgc.PATH_GATHER),
+                                            ([1 << 28, 1 << 28], 10000, sgc.PATH_WINDOW)])
+def test_compress_path_choice(sizes, ppm, auto):
+    # each pipeline sizes its own workspace; by default the gather pipeline takes the
+    # kept fractions whose candidate regions are the smallest (256 slots) on vectors
+    # below 2^29 elements, window the rest
+    lib = sgc.lib()
+    lay = sgc.Layout(sizes)
+    ws = {p: lib.sgc_compress_workspace(lay.handle, C.byref(sgc.CompressOpts(sgc.EXACT, 0, ppm, 1000, 65536, p)),
+                                        lay.keep_total(0, ppm))
+          for p in (sgc.PATH_AUTO, sgc.PATH_GATHER, sgc.PATH_WINDOW)}
+    assert ws[sgc.PATH_GATHER] > 0 and ws[sgc.PATH_WINDOW] > 0
+    assert ws[sgc.PATH_GATHER] != ws[sgc.PATH_WINDOW]
+    assert ws[sgc.PATH_AUTO] == ws[auto]
+    assert sgc.compress_workspace_bytes(lay, keep_ppm=ppm) == ws[auto]
+    assert sgc.compress_workspace_bytes(lay, keep_ppm=ppm, path=sgc.PATH_WINDOW) == ws[sgc.PATH_WINDOW]
 
 
 def test_compress_momentum_validation():

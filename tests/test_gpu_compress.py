@@ -4,7 +4,8 @@ Indices, kept values, residuals and per-segment counts must match the
 oracle bit for bit, for exact and sampled selection, global and per-segment
 scope, across ragged segment tables, ties, zeros, clustered inputs that
 overflow the per-tile candidate regions, and inputs that defeat the probe
-sample (the full-pass path).
+sample (the full-pass path).  Each case runs through both compress pipelines
+(the `path` fixture: gather and window), whatever the kept fraction.
 """
 import ctypes as C
 
@@ -19,12 +20,18 @@ from gpu_util import announce, assert_bitwise, dev, host
 pytestmark = pytest.mark.gpu
 
 
-def check_step(orc, layout, g, r, *, mode, scope, ppm, cap=None, sample_div=1000, sample_min=65536, what=""):
+@pytest.fixture(params=[sgc.PATH_GATHER, sgc.PATH_WINDOW], ids=["gather", "window"])
+def path(request):
+    return request.param
+
+
+def check_step(orc, layout, g, r, *, mode, scope, ppm, cap=None, sample_div=1000, sample_min=65536, what="",
+               path=sgc.PATH_AUTO):
     """Run one compress step on both sides; r (host) is advanced like the GPU residual."""
-    announce(f"compress {what} n={layout.n} nseg={layout.nseg} mode={mode} scope={scope} ppm={ppm}")
+    announce(f"compress {what} n={layout.n} nseg={layout.nseg} mode={mode} scope={scope} ppm={ppm} path={path}")
     gd, rd = dev(g), dev(r)
     out = sgc.compress(layout, gd, rd, mode=mode, scope=scope, keep_ppm=ppm, cap=cap,
-                       sample_div=sample_div, sample_min=sample_min)
+                       sample_div=sample_div, sample_min=sample_min, path=path)
     torch.cuda.synchronize()
     seg_off = np.array(layout.seg_off, np.int64)
     if mode == sgc.EXACT:
@@ -44,19 +51,20 @@ def check_step(orc, layout, g, r, *, mode, scope, ppm, cap=None, sample_div=1000
 
 
 @pytest.mark.parametrize("steps", [3])
-def test_flat_1m_exact_three_steps(orc, steps):
+def test_flat_1m_exact_three_steps(orc, path, steps):
     w = W.FLAT_1M
     layout = sgc.Layout(w.seg_numel)
     r = np.zeros(w.numel, np.float32)
     for s in range(steps):
         g = W.gradient(w, 0, s).numpy()
-        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=w.scope, ppm=w.keep_ppm, what=f"flat-1M step {s}")
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=w.scope, ppm=w.keep_ppm, path=path,
+                   what=f"flat-1M step {s}")
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("scope", [0, 1])
 @pytest.mark.parametrize("ppm", [0, 1000, 10000, 250000, 1000000])
-def test_ragged_segments(orc, seed, scope, ppm):
+def test_ragged_segments(orc, path, seed, scope, ppm):
     rng = np.random.default_rng(100 + seed)
     sizes = [0, 1, 3, 5, 10, 17, 4095, 4097, 8191, 8193, 12345, 0, 64, 70001]
     rng.shuffle(sizes)
@@ -65,12 +73,12 @@ def test_ragged_segments(orc, seed, scope, ppm):
     g = rng.laplace(0, 1e-3, n).astype(np.float32)
     r = np.zeros(n, np.float32)
     for s in range(2):
-        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=ppm, what=f"ragged seed{seed} s{s}")
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=ppm, path=path, what=f"ragged seed{seed} s{s}")
         g = rng.laplace(0, 1e-3, n).astype(np.float32)
 
 
 @pytest.mark.parametrize("scope", [0, 1])
-def test_ties_and_zeros(orc, scope):
+def test_ties_and_zeros(orc, path, scope):
     rng = np.random.default_rng(7)
     layout = sgc.Layout([30000, 50000, 7, 20000])
     n = layout.n
@@ -78,15 +86,15 @@ def test_ties_and_zeros(orc, scope):
     g = (rng.integers(-6, 7, n) * 0.125).astype(np.float32)
     g[rng.random(n) < 0.3] = -0.0
     r = np.zeros(n, np.float32)
-    check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=10000, what="quantized ties")
+    check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=10000, path=path, what="quantized ties")
     # all zeros: the threshold is 0 and the lowest indices win
     z = np.zeros(n, np.float32)
     z[::3] = -0.0
     r2 = np.zeros(n, np.float32)
-    check_step(orc, layout, z, r2, mode=sgc.EXACT, scope=scope, ppm=10000, what="all zeros")
+    check_step(orc, layout, z, r2, mode=sgc.EXACT, scope=scope, ppm=10000, path=path, what="all zeros")
 
 
-def test_probe_defeated_takes_full_pass_path(orc):
+def test_probe_defeated_takes_full_pass_path(orc, path):
     # Large values sit exactly where the exact mode's probe reads (at n = 2^20: runs of 16
     # elements starting at 2048 + 4096 j), so the probe overestimates the threshold, fewer than
     # k candidates pass, and the selection falls back to full passes over the residual.
@@ -96,16 +104,18 @@ def test_probe_defeated_takes_full_pass_path(orc):
     g[runs.ravel()] = 1.0 + np.arange(runs.size, dtype=np.float32) * 1e-3
     layout = sgc.Layout([n])
     r = np.zeros(n, np.float32)
-    out, st = check_step(orc, layout, g, r, mode=sgc.EXACT, scope=0, ppm=10000, what="probe defeated")
+    out, st = check_step(orc, layout, g, r, mode=sgc.EXACT, scope=0, ppm=10000, path=path, what="probe defeated")
     assert st & sgc.STATUS_DENSE_PATH
 
 
-def test_candidate_array_full(orc):
+def test_all_tied_candidates(orc, path):
     # Segments of equal magnitudes make every element a candidate (the candidate bound is that
-    # magnitude).  At 1% the array holds 4K + 2^18 = 280,144 entries.  Per tensor: the first
-    # segment's 100,000 fit, the second's 300,000 do not (full passes over the residual), and
-    # the small normal segment after them is also taken by full passes.  Globally: 400,000
-    # candidates, full passes.  Ties go to the lowest indices either way.
+    # magnitude).  Gather: at 1% its candidate array holds 4K + 2^18 = 280,144 entries; per
+    # tensor the first segment's 100,000 fit, the second's 300,000 do not (full passes over the
+    # residual), and the small normal segment after them is also taken by full passes; globally
+    # 400,000 candidates, full passes.  Window: every sampled key is the same, so there is no
+    # sure bound; the whole tie run is the window, the tiles' window lists overflow and the
+    # selection reads the regions.  Ties go to the lowest indices either way.
     rng = np.random.default_rng(12)
     sizes = [100000, 300000, 50000]
     n = sum(sizes)
@@ -116,12 +126,50 @@ def test_candidate_array_full(orc):
     layout = sgc.Layout(sizes)
     for scope in (1, 0):
         r = np.zeros(n, np.float32)
-        out, st = check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=10000,
-                             what=f"candidate array full scope{scope}")
+        out, st = check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=10000, path=path,
+                             what=f"all tied scope{scope}")
+        if path == sgc.PATH_GATHER:
+            assert st & sgc.STATUS_DENSE_PATH
+
+
+def _probe_positions(n):
+    # where the exact mode's probe reads at these sizes: runs of 16 elements from 2048 + 4096 j
+    return ((2048 + 4096 * np.arange(n // 4096))[:, None] + np.arange(16)[None, :]).ravel()
+
+
+def test_sure_bound_exceeded_takes_all_candidates(orc):
+    # Window pipeline.  |values| are 10% smaller where the probe reads, so the sampled threshold
+    # is low: more than k entries lie above the sure bound, and the selection takes every
+    # candidate as its window (no region overflows at 10%: about 16% of each tile are
+    # candidates, regions hold 25%).
+    n = 1 << 21
+    rng = np.random.default_rng(31)
+    g = rng.normal(0, 1.0, n).astype(np.float32)
+    g[_probe_positions(n)] *= np.float32(0.9)
+    layout = sgc.Layout([n])
+    r = np.zeros(n, np.float32)
+    out, st = check_step(orc, layout, g, r, mode=sgc.EXACT, scope=0, ppm=100000, path=sgc.PATH_WINDOW,
+                         what="sure bound exceeded")
+    assert st & sgc.STATUS_DENSE_PATH
+
+
+def test_sure_bound_exceeded_in_overflowed_tiles(orc):
+    # Window pipeline.  Tiny values where the probe reads, ordinary ones everywhere else: every element is a
+    # candidate and sure, every region overflows, and the tiles are worked from the residual.
+    # (At 10% of 2^20 or more elements the probe takes enough samples to set a sure bound.)
+    n = 1 << 21
+    rng = np.random.default_rng(32)
+    g = rng.normal(0, 1.0, n).astype(np.float32)
+    g[_probe_positions(n)] = rng.normal(0, 1e-6, _probe_positions(n).size).astype(np.float32)
+    layout = sgc.Layout([n // 2, n // 2])
+    for scope in (0, 1):
+        r = np.zeros(n, np.float32)
+        out, st = check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=100000,
+                             path=sgc.PATH_WINDOW, what=f"sure bound exceeded, overflowed, scope{scope}")
         assert st & sgc.STATUS_DENSE_PATH
 
 
-def test_clustered_overflowing_tiles(orc):
+def test_clustered_overflowing_tiles(orc, path):
     # All large values in a few contiguous runs: some tiles hold far more candidates than
     # their region, and those tiles are redone from the residual.
     n = 1 << 21
@@ -132,13 +180,14 @@ def test_clustered_overflowing_tiles(orc):
     layout = sgc.Layout([n // 2, n // 2])
     for scope in (0, 1):
         r = np.zeros(n, np.float32)
-        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=10000, what=f"clustered scope{scope}")
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=10000, path=path, what=f"clustered scope{scope}")
         r = np.zeros(n, np.float32)
-        check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=scope, ppm=10000, cap=n, what=f"clustered sampled{scope}")
+        check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=scope, ppm=10000, cap=n, path=path,
+                   what=f"clustered sampled{scope}")
 
 
 @pytest.mark.parametrize("ppm", [60000, 150000, 400000])
-def test_clustered_overflow_at_larger_regions(orc, ppm):
+def test_clustered_overflow_at_larger_regions(orc, path, ppm):
     # At these kept fractions the regions hold 512, 1024 and 4096 slots (a power of two near 1.5x
     # the expected candidates of a tile); runs of huge values still overflow the smaller ones.
     n = 1 << 21
@@ -149,30 +198,31 @@ def test_clustered_overflow_at_larger_regions(orc, ppm):
     layout = sgc.Layout([n // 3, n - n // 3])
     for scope in (0, 1):
         r = np.zeros(n, np.float32)
-        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=ppm, what=f"clustered {ppm} scope{scope}")
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=scope, ppm=ppm, path=path,
+                   what=f"clustered {ppm} scope{scope}")
         check_step(orc, layout, g * np.float32(0.25), r, mode=sgc.EXACT, scope=scope, ppm=ppm,
-                   what=f"clustered {ppm} scope{scope} step 2")
+                   path=path, what=f"clustered {ppm} scope{scope} step 2")
 
 
 @pytest.mark.parametrize("scope", [0, 1])
 @pytest.mark.parametrize("ppm", [1000, 10000])
-def test_sampled_matches_oracle(orc, scope, ppm):
+def test_sampled_matches_oracle(orc, path, scope, ppm):
     rng = np.random.default_rng(11)
     layout = sgc.Layout([1 << 20, 300000, 4096, 1, 99999])
     n = layout.n
     r = np.zeros(n, np.float32)
     for s in range(2):
         g = rng.laplace(0, 1e-3, n).astype(np.float32)
-        check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=scope, ppm=ppm, what=f"sampled s{s}")
+        check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=scope, ppm=ppm, path=path, what=f"sampled s{s}")
 
 
-def test_sampled_truncation(orc):
+def test_sampled_truncation(orc, path):
     rng = np.random.default_rng(12)
     n = 500000
     layout = sgc.Layout([n])
     g = rng.laplace(0, 1e-3, n).astype(np.float32)
     r = np.zeros(n, np.float32)
-    out, st = check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=0, ppm=10000, cap=3000, what="truncated")
+    out, st = check_step(orc, layout, g, r, mode=sgc.SAMPLED, scope=0, ppm=10000, cap=3000, path=path, what="truncated")
     assert st & sgc.STATUS_TRUNCATED
 
 
@@ -188,16 +238,16 @@ def test_accumulate_only(orc):
         assert_bitwise(host(rd), r, f"accumulate n={n}")
 
 
-def test_mlp_mnist_global_two_steps(orc):
+def test_mlp_mnist_global_two_steps(orc, path):
     w = W.MLP_MNIST
     layout = sgc.Layout(w.seg_numel)
     r = np.zeros(w.numel, np.float32)
     for s in range(2):
         g = W.gradient(w, 0, s).numpy()
-        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=w.scope, ppm=w.keep_ppm, what=f"mlp step {s}")
+        check_step(orc, layout, g, r, mode=sgc.EXACT, scope=w.scope, ppm=w.keep_ppm, path=path, what=f"mlp step {s}")
 
 
-def test_resnet50_delay_per_tensor(orc):
+def test_resnet50_delay_per_tensor(orc, path):
     w = W.RESNET50
     layout = sgc.Layout(w.seg_numel)
     r = np.zeros(w.numel, np.float32)
@@ -208,20 +258,20 @@ def test_resnet50_delay_per_tensor(orc):
         orc.accumulate(g, r)
     assert_bitwise(host(rd), r, "resnet delay accumulate")
     g = W.gradient(w, 0, w.delay - 1).numpy()
-    check_step(orc, layout, g, r, mode=sgc.EXACT, scope=w.scope, ppm=w.keep_ppm, what="resnet exchange")
+    check_step(orc, layout, g, r, mode=sgc.EXACT, scope=w.scope, ppm=w.keep_ppm, path=path, what="resnet exchange")
 
 
-def test_empty_layout(orc):
+def test_empty_layout(orc, path):
     layout = sgc.Layout([0, 0])
     g = torch.zeros(0, dtype=torch.float32, device="cuda")
     r = torch.zeros(0, dtype=torch.float32, device="cuda")
-    out = sgc.compress(layout, g, r, keep_ppm=10000)
+    out = sgc.compress(layout, g, r, keep_ppm=10000, path=path)
     torch.cuda.synchronize()
     assert host(out.counts).tolist() == [0, 0, 0]
 
 
 @pytest.mark.parametrize("fill", [0x00, 0x7F, 0xFF])
-def test_stale_workspace(orc, fill):
+def test_stale_workspace(orc, path, fill):
     # every workspace byte a call reads is written by that call first
     rng = np.random.default_rng(17)
     layout = sgc.Layout([300000, 4097, 1 << 20])
@@ -230,13 +280,13 @@ def test_stale_workspace(orc, fill):
     for scope in (0, 1):
         g = rng.laplace(0, 1e-3, n).astype(np.float32)
         r = np.zeros(n, np.float32)
-        opts = sgc.CompressOpts(sgc.EXACT, scope, 10000, 1000, 65536)
+        opts = sgc.CompressOpts(sgc.EXACT, scope, 10000, 1000, 65536, path)
         cap = layout.keep_total(scope, 10000)
         nbytes = sgc.lib().sgc_compress_workspace(layout.handle, C.byref(opts), cap)
         ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
         announce(f"compress stale workspace {fill:#x} scope={scope}")
         rd = dev(r)
-        out = sgc.compress(layout, dev(g), rd, scope=scope, keep_ppm=10000, ws=ws)
+        out = sgc.compress(layout, dev(g), rd, scope=scope, keep_ppm=10000, ws=ws, path=path)
         ref = orc.compress_exact(g, r, seg_off, scope, 10000, cap=out.cap)
         torch.cuda.synchronize()
         total = int(ref.counts[-1])
@@ -257,7 +307,7 @@ def test_stale_workspace(orc, fill):
 @pytest.mark.parametrize("mode", [sgc.EXACT, sgc.SAMPLED])
 @pytest.mark.parametrize("bmode", [sgc.BIN_SBC, sgc.BIN_2BIT])
 @pytest.mark.parametrize("scope", [0, 1])
-def test_hold_then_held_binarize(orc, mode, bmode, scope):
+def test_hold_then_held_binarize(orc, path, mode, bmode, scope):
     # compress with the hold flag leaves acc at the kept entries; binarize with the held flag then
     # gives exactly what compress + binarize without the flags give, writing half as much
     rng = np.random.default_rng(41)
@@ -271,7 +321,8 @@ def test_hold_then_held_binarize(orc, mode, bmode, scope):
     outs = []
     for hold in (False, True):
         rd = dev(r0)
-        comp = sgc.compress(layout, dev(g), rd, mode=mode, scope=scope, keep_ppm=10000, cap=cap, hold=hold)
+        comp = sgc.compress(layout, dev(g), rd, mode=mode, scope=scope, keep_ppm=10000, cap=cap, hold=hold,
+                            path=path)
         torch.cuda.synchronize()
         if hold:  # the residual after compress: acc at the sent entries
             r_ref = r0.copy()

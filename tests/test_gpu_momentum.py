@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 
 def run_steps(orc, layout, grads, beta, *, mode=sgc.EXACT, scope=0, ppm=10000, cap=None, u0=None, r0=None,
-              what="", ws_fill=None):
+              what="", ws_fill=None, path=sgc.PATH_AUTO):
     """Step both sides through `grads`; returns the last status word."""
     n = layout.n
     u = np.zeros(n, np.float32) if u0 is None else u0.copy()
@@ -30,15 +30,16 @@ def run_steps(orc, layout, grads, beta, *, mode=sgc.EXACT, scope=0, ppm=10000, c
     seg_off = np.array(layout.seg_off, np.int64)
     st = 0
     for s, g in enumerate(grads):
-        announce(f"momentum {what} step {s} n={n} nseg={layout.nseg} mode={mode} scope={scope} ppm={ppm} beta={beta}")
+        announce(f"momentum {what} step {s} n={n} nseg={layout.nseg} mode={mode} scope={scope} ppm={ppm} beta={beta} "
+                 f"path={path}")
         ws = None
         if ws_fill is not None:
-            opts = sgc.CompressOpts(mode, scope, ppm, 1000, 65536)
+            opts = sgc.CompressOpts(mode, scope, ppm, 1000, 65536, path)
             c = cap if cap is not None else layout.keep_total(scope, ppm)
             nbytes = sgc.lib().sgc_compress_momentum_workspace(layout.handle, C.byref(opts), c)
             ws = torch.full((nbytes,), ws_fill, dtype=torch.uint8, device="cuda")
         out = sgc.compress_momentum(layout, dev(g), ud, rd, beta, mode=mode, scope=scope, keep_ppm=ppm, cap=cap,
-                                    ws=ws)
+                                    ws=ws, path=path)
         torch.cuda.synchronize()
         ref = orc.compress_momentum(g, u, r, beta, seg_off, scope, ppm, sampled=(mode == sgc.SAMPLED), cap=out.cap)
         counts = host(out.counts)
@@ -52,21 +53,23 @@ def run_steps(orc, layout, grads, beta, *, mode=sgc.EXACT, scope=0, ppm=10000, c
     return st
 
 
+@pytest.mark.parametrize("path", [sgc.PATH_GATHER, sgc.PATH_WINDOW], ids=["gather", "window"])
 @pytest.mark.parametrize("scope", [0, 1])
 @pytest.mark.parametrize("ppm", [1000, 10000, 250000])
-def test_exact_ragged_steps(orc, scope, ppm):
+def test_exact_ragged_steps(orc, scope, ppm, path):
     rng = np.random.default_rng(21)
     layout = sgc.Layout([1 << 20, 300001, 4096, 1, 0, 99999])
     grads = [rng.laplace(0, 1e-3, layout.n).astype(np.float32) for _ in range(3)]
-    run_steps(orc, layout, grads, 0.9, scope=scope, ppm=ppm, what=f"exact ppm{ppm}")
+    run_steps(orc, layout, grads, 0.9, scope=scope, ppm=ppm, path=path, what=f"exact ppm{ppm}")
 
 
+@pytest.mark.parametrize("path", [sgc.PATH_GATHER, sgc.PATH_WINDOW], ids=["gather", "window"])
 @pytest.mark.parametrize("scope", [0, 1])
-def test_sampled_steps(orc, scope):
+def test_sampled_steps(orc, scope, path):
     rng = np.random.default_rng(22)
     layout = sgc.Layout([1 << 20, 300000, 4096, 1, 99999])
     grads = [rng.laplace(0, 1e-3, layout.n).astype(np.float32) for _ in range(3)]
-    run_steps(orc, layout, grads, 0.9, mode=sgc.SAMPLED, scope=scope, ppm=10000, what="sampled")
+    run_steps(orc, layout, grads, 0.9, mode=sgc.SAMPLED, scope=scope, ppm=10000, path=path, what="sampled")
 
 
 @pytest.mark.parametrize("mode", [sgc.EXACT, sgc.SAMPLED])

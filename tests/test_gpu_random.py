@@ -50,7 +50,8 @@ def random_values(rng, n):
 
 def one_message(orc, layout, rng, what, **fixed):
     """One worker step on both sides; returns the GPU and oracle messages.
-    fixed: any of ppm, scope, mode, kind, b, enc_scope, instead of a random draw."""
+    fixed: any of ppm, scope, mode, kind, b, enc_scope, instead of a random draw, and the
+    compress pipeline (path, default: chosen by the library)."""
     n = layout.n
     seg_off = np.array(layout.seg_off, np.int64)
     ppm = int(rng.choice(PPMS))
@@ -67,10 +68,11 @@ def one_message(orc, layout, rng, what, **fixed):
     enc_scope = fixed.get("enc_scope", enc_scope)
     g = random_values(rng, n)
     r = (rng.normal(0, 3e-4, n) * (rng.random(n) < 0.5)).astype(np.float32)
+    path = fixed.get("path", sgc.PATH_AUTO)
     announce(f"{what}: n={n} nseg={layout.nseg} ppm={ppm} scope={scope} mode={mode} kind={kind} b={b} "
-             f"enc_scope={enc_scope}")
+             f"enc_scope={enc_scope} path={path}")
     rd = dev(r)
-    comp = sgc.compress(layout, dev(g), rd, mode=mode, scope=scope, keep_ppm=ppm)
+    comp = sgc.compress(layout, dev(g), rd, mode=mode, scope=scope, keep_ppm=ppm, path=path)
     torch.cuda.synchronize()
     if mode == sgc.EXACT:
         ref = orc.compress_exact(g, r, seg_off, scope, ppm, cap=comp.cap)
@@ -125,7 +127,8 @@ def test_random_pipeline(orc, seed):
     W = int(rng.integers(1, 13))
     gm, om = [], []
     for wk in range(W):
-        a, o = one_message(orc, layout, rng, f"seed {seed} worker {wk}")
+        path = (sgc.PATH_AUTO, sgc.PATH_GATHER, sgc.PATH_WINDOW)[(seed + wk) % 3]
+        a, o = one_message(orc, layout, rng, f"seed {seed} worker {wk}", path=path)
         gm.append(a)
         om.append(o)
     init = int(rng.integers(0, 3))
@@ -164,7 +167,8 @@ def test_many_segments(orc, nseg):
     ]
     gm, om = [], []
     for wk, fixed in enumerate(combos):
-        a, o = one_message(orc, layout, rng, f"nseg {nseg} worker {wk}", **fixed)
+        path = (sgc.PATH_GATHER, sgc.PATH_WINDOW)[(nseg + wk) % 2]
+        a, o = one_message(orc, layout, rng, f"nseg {nseg} worker {wk}", path=path, **fixed)
         gm.append(a)
         om.append(o)
     out = torch.zeros(n, dtype=torch.float32, device="cuda")

@@ -4,8 +4,9 @@ over a sequence of worker steps, bitwise against the CPU oracle.
 Each case fixes a layout, whether momentum correction is on (and its
 coefficient), then runs 4 to 7 steps.  A step is either a communication-
 delay accumulation or an exchange: exact or sampled selection at a random
-kept fraction and scope, with or without the hold flag, followed (plain
-path only) by no binarization, SBC or 2-bit, held or not.  After every step
+kept fraction and scope (through either compress pipeline, in turn), with
+or without the hold flag, followed (plain path only) by no binarization,
+SBC or 2-bit, held or not.  After every step
 the GPU residual and momentum must equal the oracle's bit for bit, and the
 sent indices and values likewise.  Binarize means must agree to 1e-6
 relative; where they are bit-equal (the usual case) the sent set, codes and
@@ -84,9 +85,11 @@ def run_sequence(orc, rng, layout, seed):
         ppm = int(rng.choice(PPMS))
         scope = int(rng.integers(0, 2))
         mode = sgc.SAMPLED if rng.random() < 0.3 else sgc.EXACT
+        path = (sgc.PATH_AUTO, sgc.PATH_GATHER, sgc.PATH_WINDOW)[(seed + step) % 3]
         if mom:
-            announce(f"{what}: momentum beta={beta} ppm={ppm} scope={scope} mode={mode}")
-            comp = sgc.compress_momentum(layout, dev(g), ud, rd, beta, mode=mode, scope=scope, keep_ppm=ppm)
+            announce(f"{what}: momentum beta={beta} ppm={ppm} scope={scope} mode={mode} path={path}")
+            comp = sgc.compress_momentum(layout, dev(g), ud, rd, beta, mode=mode, scope=scope, keep_ppm=ppm,
+                                         path=path)
             torch.cuda.synchronize()
             ref = orc.compress_momentum(g, u, r, beta, seg_off, scope, ppm, sampled=mode == sgc.SAMPLED,
                                         cap=comp.cap)
@@ -98,8 +101,8 @@ def run_sequence(orc, rng, layout, seed):
         bmode = [None, sgc.BIN_SBC, sgc.BIN_2BIT][int(rng.integers(0, 3))]
         if bmode is None:
             hold = False  # a held residual is completed by the binarize step
-        announce(f"{what}: ppm={ppm} scope={scope} mode={mode} hold={hold} binarize={bmode}")
-        comp = sgc.compress(layout, dev(g), rd, mode=mode, scope=scope, keep_ppm=ppm, hold=hold)
+        announce(f"{what}: ppm={ppm} scope={scope} mode={mode} hold={hold} binarize={bmode} path={path}")
+        comp = sgc.compress(layout, dev(g), rd, mode=mode, scope=scope, keep_ppm=ppm, hold=hold, path=path)
         torch.cuda.synchronize()
         if mode == sgc.EXACT:
             ref = orc.compress_exact(g, r, seg_off, scope, ppm, cap=comp.cap)
