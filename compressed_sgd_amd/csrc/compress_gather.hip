@@ -1,10 +1,11 @@
-// compress.hip -- residual add + top-k selection + emission (sgc_compress).
+// compress_gather.hip -- the gather pipeline of sgc_compress (selection
+// over one ordered candidate array; the default at low kept fractions on
+// vectors below 2^29 elements).
 //
 // Method ([SBC] §II Residual Accumulation and Sparse Binarization; [AH17]
 // Abstract): acc = fp32(residual + grad); keep the largest-|acc| fraction
 // of each selection group; send (index, value) ascending; the residual
-// keeps everything else.  [SBC] §II Communication Delay: between exchanges
-// only residual += grad is done (SGC_ACCUMULATE_ONLY).
+// keeps everything else.
 //
 // GPU design (one HBM pass over the gradient in the common case):
 //  1. probe   -- read a small sample of acc per group (runs of 16 elements)

@@ -1,10 +1,11 @@
-// compress.hip -- residual add + top-k selection + emission (sgc_compress).
+// compress_window.hip -- the window pipeline of sgc_compress (selection
+// only between the probe's bounds; the default above about 2.5% kept and on
+// vectors of 2^29 elements or more).
 //
 // Method ([SBC] §II Residual Accumulation and Sparse Binarization; [AH17]
 // Abstract): acc = fp32(residual + grad); keep the largest-|acc| fraction
 // of each selection group; send (index, value) ascending; the residual
-// keeps everything else.  [SBC] §II Communication Delay: between exchanges
-// only residual += grad is done (SGC_ACCUMULATE_ONLY).
+// keeps everything else.
 //
 // GPU design (one HBM pass over the gradient in the common case):
 //  1. probe   -- read a small sample of acc per group (runs of 16 elements)
@@ -16,30 +17,34 @@
 //                Sampled mode instead takes the method's own systematic
 //                sample and its exact threshold T, with key_lo = key_z = T.
 //  2. pass 1  -- stream g and r once: acc = r + g; every element with
-//                key >= key_lo goes into its tile's candidate region (wave
-//                ballots + LDS offsets, index order kept); r is stored as
-//                acc, or as +0 for key >= key_z, so that nearly all kept
-//                entries leave the residual without a second, scattered
-//                write; the tile's sure entries (key >= key_hi) are counted.
-//                A tile whose region overflows stores plain acc everywhere.
+//                key >= key_lo goes into its tile's candidate region (value
+//                and 16-bit offset in the tile, index order kept; staged in
+//                LDS where regions are large); r is stored as acc, or as +0
+//                for key >= key_z, so that nearly all kept entries leave the
+//                residual without a second, scattered write.  Exact mode:
+//                the values of the tile's window entries (key_lo <= key <
+//                key_hi) also go on a short per-tile list, and the tile's
+//                sure entries (key >= key_hi) are counted.  A tile whose
+//                region overflows stores plain acc everywhere.
 //  3. scan    -- tile counts -> offsets; per group: candidate and sure
-//                totals, and how the group is selected: from the window
-//                [key_lo, key_hi) of its candidates (the usual case), from
-//                all its candidates (more than k sure entries), or from the
-//                whole residual (fewer than k candidates: the probe misled).
-//                Exact mode: pass 1 also puts the values of the tile's
-//                window entries (key_lo <= key < key_hi) on a short list.
-//  4. select  -- the (k - sure)-th largest window key: three radix digits
-//     (+5)       over the window lists -> T and the quota of ties at T.
-//  6. count   -- per tile, the entries kept without a tie (sure, key > T)
+//                totals, and how the group is selected: from its window
+//                (the usual case), from all its candidates (more than k sure
+//                entries), or from the whole residual (fewer than k
+//                candidates: the probe misled).
+//  4. select  -- the (k - sure)-th largest window key T and the quota of
+//                ties at T: 2048-bin histograms over the search range
+//                [key_lo, key_hi), narrowed to one bin per pass (two passes
+//                for ranges up to 2^22 keys, a third only beyond).
+//  5. count   -- per tile, the entries kept without a tie (sure, key > T)
 //                and the ties at T; a scan gives every tile's output offset
 //                (ties are taken lowest index first).
-//  7. write   -- every tile's region is read once more and the kept entries
-//                written ascending; the residual is zeroed only where pass 1
-//                did not, and given acc back where pass 1 zeroed an entry
-//                the exact selection did not keep.
+//  6. write   -- every tile's region is read once more and the kept entries
+//                written ascending (one wave per tile where regions are
+//                large); the residual is zeroed only where pass 1 did not,
+//                and given acc back where pass 1 zeroed an entry the exact
+//                selection did not keep.
 // Overflowed tiles, and every tile of a group selected from the residual,
-// are worked from r (acc there) in steps 4-7, shared out over the grid.
+// are worked from r (acc there) in steps 4-6, shared out over the grid.
 #include "compress_path.h"
 
 #include <cmath>
@@ -983,7 +988,7 @@ __device__ inline void flush_hist(const CompressWs& w, const uint32_t* h, int nb
     }
 }
 
-// Steps 4-5, selection pass P (0, 1 or 2): every open group's window keys
+// Step 4, selection pass P (0, 1 or 2): every open group's window keys
 // in its search range [wbase, wend), counted in 2048 bins -- from the window lists pass 1
 // wrote (or the region, past a list's capacity, and for groups whose window
 // is every candidate), and from r for the r-worked tiles.  Pass 0, phase B:
@@ -1175,7 +1180,7 @@ __global__ __launch_bounds__(kBlock) void k_win_resolve(CompressWs w)
     }
 }
 
-// Step 6: per tile, tile_sg = its sure entries (groups selected from the
+// Step 5: per tile, tile_sg = its sure entries (groups selected from the
 // window) + the window keys above T, tile_eq = the window keys equal to T
 // (T = kNoKey when a group needs nothing from its window).
 __global__ __launch_bounds__(kBlock) void k_tile_count(const float* __restrict__ res, const int64_t* __restrict__ goff,
@@ -1364,7 +1369,7 @@ __device__ inline void write_rtiles(float* __restrict__ res, const int64_t* __re
     }
 }
 
-// Step 7: the kept entries of every tile, written ascending, and the
+// Step 6: the kept entries of every tile, written ascending, and the
 // residual fixes.  An entry is kept if it is sure (key >= key_hi), above T,
 // or a tie at T among the first quota of its group in index order.  Phase
 // A: the output position of a kept region entry is the tile's offset plus
@@ -1498,7 +1503,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_write(float* __restrict__ res, 
     write_rtiles(res, goff, gtile, G, NT, w, out_idx, out_val, cap, m, tmp32);
 }
 
-// Step 7 where regions are large (many candidates per tile): one wave per
+// Step 6 where regions are large (many candidates per tile): one wave per
 // tile and no workgroup barrier in phase A.  The wave walks its tile's
 // region 512 entries at a time (8 per lane, all loads in flight); the
 // output position of a kept entry is the tile's offset plus the kept
@@ -1802,7 +1807,7 @@ static int run_impl(const CompressCall& a, M m)
 
     const unsigned tb = (unsigned)std::max<int64_t>(1, cdiv(gr.ntiles, kTT));
     if (o->mode == SGC_EXACT) {
-        // 4-5. selection passes over the window lists (and the r-worked tiles);
+        // 4. selection passes over the window lists (and the r-worked tiles);
         // the third only where a search range is wider than 2^22 keys
         const unsigned hb = (unsigned)std::min<int64_t>(tb, kHistBlocks);
         k_tsel_hist<0, M><<<hb, kBlock, 0, s>>>(residual, gr.off, gr.tile, G, gr.ntiles, w, m);
@@ -1817,7 +1822,7 @@ static int run_impl(const CompressCall& a, M m)
         SGC_LAUNCH_CHECK();
         k_win_resolve<2><<<(unsigned)G, kBlock, 0, s>>>(w);
         SGC_LAUNCH_CHECK();
-        // 6. per-tile kept counts -> offsets
+        // 5. per-tile kept counts -> offsets
         k_tile_count<<<tb, kBlock, 0, s>>>(residual, gr.off, gr.tile, G, gr.ntiles, w);
         SGC_LAUNCH_CHECK();
         k_tile_scan1<<<(unsigned)z.NS, kBlock, 0, s>>>(gr.ntiles, w.tile_sg, w.tile_eq, w.tile_loc, w.tile_loc2,
@@ -1825,7 +1830,7 @@ static int run_impl(const CompressCall& a, M m)
         SGC_LAUNCH_CHECK();
         k_scan_supers<<<1, kScanThreads, 0, s>>>(gr.ntiles, w);
         SGC_LAUNCH_CHECK();
-        // 7. write
+        // 6. write
         // items per thread per round: 4 (more workgroups resident) where
         // regions are small, 8 (fewer rounds) where they are large
         if (z.tcap >= kWaveWriteCap)
