@@ -40,8 +40,9 @@ sys.path.insert(0, ROOT)
 METRIC = "gradient elems/sec (GB/s, % of HBM peak) for top-1% compress+encode at 1 GPU"
 PEAK_HBM_GBS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "pass1_flat1G_top1pct_pmc.txt")
-# sources the fused pass is compiled from (its tile geometry lives in the header)
-PASS_SRCS = [os.path.join(ROOT, "compressed_sgd_amd", "csrc", f) for f in ("compress.hip", "sgc_common.h")]
+# sources the fused pass is compiled from (the 2^30 step takes the window pipeline;
+# its tile geometry lives in the header)
+PASS_SRCS = [os.path.join(ROOT, "compressed_sgd_amd", "csrc", f) for f in ("compress_window.hip", "sgc_common.h")]
 
 
 def pass_traffic():
@@ -329,6 +330,84 @@ def workload_rows(sgc, W, torch, dev, stream, reps=10):
     return rows
 
 
+def cpu_configs(W, log):
+    """The CPU oracle (single-threaded, as it stands) on every workload's own
+    shapes: the worker step and the receive step, timed with perf_counter on
+    host copies of the same synthetic inputs.  Receive steps sum one worker's
+    message W times (the same work as W distinct messages)."""
+    import numpy as np
+    import oracle as orc
+
+    res = {}
+
+    def clock(f):
+        t0 = time.perf_counter()
+        out = f()
+        return time.perf_counter() - t0, out
+
+    # flat-1M: exact global top-1%, residual carried over 3 steps
+    w = W.FLAT_1M
+    off = np.array(w.seg_off, np.int64)
+    r = np.zeros(w.numel, np.float32)
+    ts = []
+    for s in range(w.steps):
+        g = W.gradient(w, 0, s).numpy()
+        ts.append(clock(lambda: orc.compress_exact(g, r, off, orc.GLOBAL, w.keep_ppm))[0])
+    res[w.name] = {"worker_step_s": sum(ts) / len(ts), "worker_elements_per_s": w.numel / (sum(ts) / len(ts)),
+                   "steps": "compress (exact global 1%)"}
+    log(f"[cpu] {w.name} done")
+    # mlp-mnist: exact global 1% + 2-bit; receive 4 raw 2-bit messages into zeros
+    w = W.MLP_MNIST
+    off = np.array(w.seg_off, np.int64)
+    g = W.gradient(w, 0, 0).numpy()
+    r = np.zeros(w.numel, np.float32)
+    t1, sp = clock(lambda: orc.compress_exact(g, r, off, orc.GLOBAL, w.keep_ppm))
+    t2, bn = clock(lambda: orc.binarize(sp, len(off) - 1, orc.BIN_2BIT, r))
+    msg = orc.Message(bn.counts, vkind=orc.VAL_2BIT, idx=sp.idx, codes=bn.codes, means=bn.means)
+    out = np.zeros(w.numel, np.float32)
+    t3, _ = clock(lambda: orc.decode_accumulate([msg] * w.workers, off, out))
+    res[w.name] = {"worker_step_s": t1 + t2, "worker_elements_per_s": w.numel / (t1 + t2),
+                   "receive_s": t3, "receive_elements_per_s": w.numel / t3,
+                   "steps": "compress (exact global 1%) + 2-bit; receive 4 raw 2-bit messages"}
+    log(f"[cpu] {w.name} done")
+    # nmt-rnn: exact global 1%; receive 4 raw messages onto the local gradient
+    w = W.NMT_RNN
+    off = np.array(w.seg_off, np.int64)
+    g = W.gradient(w, 0, 0).numpy()
+    r = np.zeros(w.numel, np.float32)
+    t1, sp = clock(lambda: orc.compress_exact(g, r, off, orc.GLOBAL, w.keep_ppm))
+    out = g.copy()
+    msg = orc.Message(sp.counts, idx=sp.idx, val=sp.val)
+    t3, _ = clock(lambda: orc.decode_accumulate([msg] * w.workers, off, out))
+    res[w.name] = {"worker_step_s": t1, "worker_elements_per_s": w.numel / t1,
+                   "receive_s": t3, "receive_elements_per_s": w.numel / t3,
+                   "steps": "compress (exact global 1%); receive 4 raw messages onto the local gradient"}
+    log(f"[cpu] {w.name} done")
+    # resnet50: 7 accumulations + per-tensor 0.1% + SBC + Rice (b = 9); receive 8 messages
+    w = W.RESNET50
+    off = np.array(w.seg_off, np.int64)
+    b = orc.rice_param(w.keep_ppm / 1e6)
+    gs = [W.gradient(w, 0, s).numpy() for s in range(w.delay)]
+    r = np.zeros(w.numel, np.float32)
+
+    def rnd():
+        for s in range(w.delay - 1):
+            orc.accumulate(gs[s], r)
+        sp = orc.compress_exact(gs[-1], r, off, orc.PER_SEGMENT, w.keep_ppm)
+        bn = orc.binarize(sp, len(off) - 1, orc.BIN_SBC, r)
+        return bn, orc.encode(bn.idx, bn.counts, off, orc.PER_SEGMENT, b)
+    t1, (bn, enc) = clock(rnd)
+    msg = orc.Message(bn.counts, vkind=orc.VAL_SBC, golomb=True, scope=orc.PER_SEGMENT, b=b, means=bn.means,
+                      enc=enc)
+    out = np.zeros(w.numel, np.float32)
+    t3, _ = clock(lambda: orc.decode_accumulate([msg] * w.workers, off, out))
+    res[w.name] = {"worker_round_s": t1, "worker_elements_per_s": w.numel / t1,
+                   "receive_s": t3, "receive_elements_per_s": w.numel / t3,
+                   "steps": "7 accumulations + compress (exact per-tensor 0.1%) + SBC + Rice; receive 8 messages"}
+    log(f"[cpu] {w.name} done")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +415,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-sample-log2", type=int, default=26)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="only time the CPU oracle on every workload's own shapes (no GPU needed)")
     ap.add_argument("--no-rows", action="store_true", help="skip the extra rows and workloads (e.g. under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of 2^28 fp32 (1 GiB each way) three times: "
@@ -349,8 +430,15 @@ def main():
     import numpy as np
     import torch
 
-    import compressed_sgd_amd as sgc
     import workloads as W
+
+    if args.cpu_configs:
+        log = lambda m: print(m, file=sys.stderr, flush=True)
+        print(json.dumps({"cpu_configs": cpu_configs(W, log), "cores": 1, "kind": "oracle",
+                          "host_cpus": os.cpu_count()}), flush=True)
+        return
+
+    import compressed_sgd_amd as sgc
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
@@ -572,11 +660,17 @@ def main():
         sp = orc.compress_exact(g0, r0, np.array([0, m], np.int64), orc.GLOBAL, ppm)
         orc.encode(sp.idx, sp.counts, np.array([0, m], np.int64), orc.GLOBAL, b)
         dt = time.perf_counter() - t0
+        # the full sort dominates: n log n from the sample size to the headline's 2^30
+        L2 = args.cpu_sample_log2
+        scale = (n / m) * (30.0 / L2)
         out["cpu_baseline"] = {
             "value": m / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"first 2^{args.cpu_sample_log2} elements of the step-0 gradient: exact top-1% "
+            "sample": f"first 2^{L2} elements of the step-0 gradient: exact top-1% "
                       f"(full sort) + Rice b={b} encode, single-threaded C oracle ({dt:.1f} s)",
             "host_cpus": os.cpu_count(),
+            "extrapolated_2e30": {"value": n / (dt * scale), "seconds": dt * scale,
+                                  "how": f"n log n extrapolation from the 2^{L2} measurement (x{scale:.2f}), "
+                                         "not measured"},
         }
     print(json.dumps(out), flush=True)
 
