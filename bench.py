@@ -48,20 +48,7 @@ PASS_SRCS = [os.path.join(ROOT, "compressed_sgd_amd", "csrc", f) for f in ("comp
 def pass_traffic():
     """HBM bytes per launch of the fused pass from the committed PMC summary,
     or None when the kernel source changed since the counters were taken."""
-    if not os.path.exists(PMC_FILE):
-        return None
-    vals = {}
-    for line in open(PMC_FILE):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            vals[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    for f in PASS_SRCS:
-        h.update(open(f, "rb").read())
-    want = h.hexdigest()
-    if vals.get("source_sha256") != want or "traffic_bytes_per_launch" not in vals:
-        return None
-    return float(vals["traffic_bytes_per_launch"])
+    return summary_traffic(PMC_FILE, PASS_SRCS)
 
 
 def timed(fn, reps, stream):
@@ -408,6 +395,71 @@ def cpu_configs(W, log):
     return res
 
 
+RECV_PMC_FILE = os.path.join(ROOT, "profiles", "receive_flat1G_16x1pct_pmc.txt")
+RECV_SRCS = [os.path.join(ROOT, "compressed_sgd_amd", "csrc", f) for f in ("accumulate.hip", "sgc_common.h")]
+
+
+def summary_traffic(path, srcs):
+    """HBM bytes per call from a committed PMC summary, or None when a source
+    it was taken from has changed since."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    if vals.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def receive_rows(sgc, W, torch, dev, stream, layout, reps=3):
+    """a7: decode-accumulate of 16 workers' Rice + fp32 messages (flat 2^30
+    recipe, workers 0..15, exact top-1% / top-0.1%) into 4 GiB, onto zeros and
+    onto the local dense gradient.  Algorithmic bytes: the dense write (+ the
+    dense read of the local gradient) + the messages (code words + 4 B per
+    value).  The 1% row onto zeros carries a roofline entry."""
+    w = W.FLAT_1G
+    n = w.numel
+    rows = {}
+    r16 = torch.zeros(n, dtype=torch.float32, device=dev)
+    outd = torch.empty(n, dtype=torch.float32, device=dev)
+    local = W.gradient(w, 0, 0, device=dev)
+    for p, tag in ((1000, "0.1pct"), (10000, "1pct")):
+        msgs = []
+        for wk in range(16):
+            g = W.gradient(w, wk, 0, device=dev)
+            r16.zero_()
+            c = sgc.compress(layout, g, r16, keep_ppm=p)
+            e = sgc.encode(layout, c.idx, c.counts, c.cap, b=sgc.rice_param(p / 1e6))
+            msgs.append(sgc.golomb_message(c, e))
+            del g
+        kp = layout.keep_total(sgc.GLOBAL, p)
+        msg_bytes = sum(4.0 * kp + 4.0 * int(m.enc.word_off[-1].item()) for m in msgs)
+        t = timed(lambda: sgc.decode_accumulate(layout, msgs, outd), reps, stream)
+        alg = 4.0 * n + msg_bytes
+        rows[f"decode_accumulate_16x{tag}"] = {
+            "ms": t, "entries": 16 * kp, "GBps_alg": alg / (t / 1e3) / 1e9}
+        if tag == "1pct":
+            traffic = summary_traffic(RECV_PMC_FILE, RECV_SRCS)
+            achieved = alg / (t / 1e3) / 1e9
+            rows[f"decode_accumulate_16x{tag}"]["roofline"] = {
+                "kernels": "k_msg_setup, k_msg_decode, k_msg_holes (per batch of 8), k_merge, k_fold_status",
+                "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "alg_bytes_per_call": alg, "traffic": traffic,
+                "traffic_over_alg": None if traffic is None else traffic / alg}
+        t = timed(lambda: sgc.decode_accumulate(layout, msgs, outd, init=sgc.INIT_BASE, base=local), reps, stream)
+        rows[f"decode_accumulate_16x{tag}_on_local"] = {
+            "ms": t, "entries": 16 * kp, "GBps_alg": (8.0 * n + msg_bytes) / (t / 1e3) / 1e9}
+        del msgs
+    del r16, outd, local
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -418,6 +470,8 @@ def main():
     ap.add_argument("--cpu-configs", action="store_true",
                     help="only time the CPU oracle on every workload's own shapes (no GPU needed)")
     ap.add_argument("--no-rows", action="store_true", help="skip the extra rows and workloads (e.g. under a profiler)")
+    ap.add_argument("--receive-only", action="store_true",
+                    help="only the 16-worker decode-accumulate rows at 2^30 (e.g. under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of 2^28 fp32 (1 GiB each way) three times: "
                          "the reference the HBM byte counters are scaled by")
@@ -452,6 +506,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.receive_only:
+        print(json.dumps({"rows": receive_rows(sgc, W, torch, dev, stream, sgc.Layout(W.FLAT_1G.seg_numel))}),
+              flush=True)
+        return
     w = W.FLAT_1G
     n = w.numel
     ppm = 10000
@@ -618,29 +676,7 @@ def main():
         rows["binarize_sbc_1pct_held"] = {"ms": t, "entries": kept}
         res.copy_(rsave)
         del rsave
-        # a7: decode-accumulate of 16 workers' Rice messages into 4 GiB, onto zeros
-        # and onto the local dense gradient; bytes = dense write (+ dense read) + messages
-        r16 = torch.zeros(n, dtype=torch.float32, device=dev)
-        outd = torch.empty(n, dtype=torch.float32, device=dev)
-        for p, tag in ((1000, "0.1pct"), (10000, "1pct")):
-            msgs = []
-            for wk in range(16):
-                g = W.gradient(w, wk, 0, device=dev)
-                r16.zero_()
-                c = sgc.compress(layout, g, r16, keep_ppm=p)
-                e = sgc.encode(layout, c.idx, c.counts, c.cap, b=sgc.rice_param(p / 1e6))
-                msgs.append(sgc.golomb_message(c, e))
-                del g
-            kp = layout.keep_total(sgc.GLOBAL, p)
-            msg_bytes = sum(4.0 * kp + 4.0 * int(m.enc.word_off[-1].item()) for m in msgs)
-            t = timed(lambda: sgc.decode_accumulate(layout, msgs, outd), 3, stream)
-            rows[f"decode_accumulate_16x{tag}"] = {
-                "ms": t, "entries": 16 * kp, "GBps_alg": (4.0 * n + msg_bytes) / (t / 1e3) / 1e9}
-            t = timed(lambda: sgc.decode_accumulate(layout, msgs, outd, init=sgc.INIT_BASE, base=grads[0]), 3,
-                      stream)
-            rows[f"decode_accumulate_16x{tag}_on_local"] = {
-                "ms": t, "entries": 16 * kp, "GBps_alg": (8.0 * n + msg_bytes) / (t / 1e3) / 1e9}
-            del msgs
+        rows.update(receive_rows(sgc, W, torch, dev, stream, layout))
         out["rows"] = rows
         del r16, outd
         print("[bench] the other workloads", file=sys.stderr, flush=True)

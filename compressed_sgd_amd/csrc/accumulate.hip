@@ -391,9 +391,9 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
     // output tile of the previous entry (before a stream's first entry: of the
     // stream's origin minus one; arithmetic shift, so -1 stays -1)
     int32_t tp = (J.base + (int32_t)prev) >> kOutTileLog;
-    auto group = [&](int32_t i0, auto full) __attribute__((always_inline)) {
+    // codes i0 .. i0+3: positions to pb (stored by the caller), values stored here
+    auto group = [&](int32_t i0, auto full, int32_t (&pb)[4]) __attribute__((always_inline)) {
         constexpr bool kFull = decltype(full)::value;
-        int32_t pb[4];
         float vb[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -456,22 +456,54 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
                 }
             }
         }
-        const int32_t jb = J.j0 + i0;
-        if (kFull && vec) {
-            *(i4v*)(w.pos + jb) = i4v{pb[0], pb[1], pb[2], pb[3]};
-            if (FMT != SGC_MSG_GOLOMB_F32) *(f4a*)(w.val + jb) = f4a{vb[0], vb[1], vb[2], vb[3]};
-        } else {
+        if (FMT != SGC_MSG_GOLOMB_F32) {
+            const int32_t jb = J.j0 + i0;
+            if (kFull && vec) {
+                *(f4a*)(w.val + jb) = f4a{vb[0], vb[1], vb[2], vb[3]};
+            } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (!kFull && i0 + q >= J.nc) continue;
-                w.pos[jb + q] = pb[q];
-                if (FMT != SGC_MSG_GOLOMB_F32) w.val[jb + q] = vb[q];
+                for (int q = 0; q < 4; ++q)
+                    if (kFull || i0 + q < J.nc) w.val[jb + q] = vb[q];
             }
         }
     };
+    auto store4 = [&](int32_t i0, const int32_t (&pb)[4], auto full) __attribute__((always_inline)) {
+        constexpr bool kFull = decltype(full)::value;
+        const int32_t jb = J.j0 + i0;
+        if (kFull && vec) {
+            *(i4v*)(w.pos + jb) = i4v{pb[0], pb[1], pb[2], pb[3]};
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (kFull || i0 + q < J.nc) w.pos[jb + q] = pb[q];
+        }
+    };
     int32_t i0 = 0;
-    for (; i0 + 4 <= J.nc; i0 += 4) group(i0, std::true_type{});
-    if (i0 < J.nc) group(i0, std::false_type{});
+    int32_t pb[4];
+    // whole blocks of 32 codes: the positions stay in registers and leave as
+    // eight back-to-back 16-byte stores, one whole 128-byte cache line (every
+    // lane writes its own chunk, so stores in 16-byte pieces left partly
+    // written lines: 2.4 times the position bytes reached memory)
+    if (vec) {
+        for (; i0 + 32 <= J.nc; i0 += 32) {
+            i4v buf[8];
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                group(i0 + 4 * g, std::true_type{}, pb);
+                buf[g] = i4v{pb[0], pb[1], pb[2], pb[3]};
+            }
+#pragma unroll
+            for (int g = 0; g < 8; ++g) *(i4v*)(w.pos + J.j0 + i0 + 4 * g) = buf[g];
+        }
+    }
+    for (; i0 + 4 <= J.nc; i0 += 4) {
+        group(i0, std::true_type{}, pb);
+        store4(i0, pb, std::true_type{});
+    }
+    if (i0 < J.nc) {
+        group(i0, std::false_type{}, pb);
+        store4(i0, pb, std::false_type{});
+    }
     *rel_out = rel;
     *prev_out = (int32_t)prev;
     return !err;
@@ -587,11 +619,14 @@ static void launch_decode(int colw, dim3 grid, const Batch& B, int32_t nseg, hip
 }
 
 // ------------------------------------------------------------------ merge
-// Persistent workgroups over the output tiles (kOutTile elements each),
-// workgroup i taking tiles i, i + G, i + 2G, ... for a grid of G: clustered
-// entries (runs of dense tiles, as the rows of a Zipf-sampled embedding
-// give) spread over every workgroup instead of loading the few that a
-// contiguous range would give them to.  A group of threads per message (a power of two)
+// Persistent workgroups over the output tiles (kOutTile elements each), in
+// runs of kTileRun consecutive tiles: workgroup i takes runs i, i + G, i + 2G,
+// ... for a grid of G.  Spread out like this, clustered entries (runs of
+// dense tiles, as the rows of a Zipf-sampled embedding give) load every
+// workgroup instead of the few that a contiguous range would give them to;
+// in runs, the cache line that holds the end of one tile's entries and the
+// start of the next is fetched once rather than by two workgroups (single
+// tiles: 1.44 times the entry bytes were fetched).  A group of threads per message (a power of two)
 // follows that message's entries, which stay in the registers of the thread
 // that loaded them.  Per tile:
 //  1  the tile's initial contents go to LDS; every entry marks its message
@@ -627,6 +662,7 @@ static void launch_decode(int colw, dim3 grid, const Batch& B, int32_t nseg, hip
 // kRound in all) is applied from memory instead, in rounds of kRound entries
 // taken in message order.
 constexpr int kMergeThreads = 256;                          // threads per merge workgroup
+constexpr int kTileRun = 4;                                 // consecutive tiles a workgroup takes in a row
 constexpr int kPre = 8;                                     // entries per thread per tile (or round)
 constexpr int kRound = kPre * kMergeThreads;                // entries per round
 constexpr int kQ = (int)(kOutTile / (4 * kMergeThreads));  // 16-byte words per thread in a tile
@@ -719,11 +755,18 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
     const float* valk = live ? M.val[mk] : nullptr;
     const int32_t* tsk = live ? M.tstart[mk] : nullptr;
     const float* src = init == SGC_INIT_BASE ? base : out;
-    // this workgroup's tiles: blockIdx.x, + gridDim.x, + 2 gridDim.x, ... (j-th: tile(j))
-    if ((int64_t)blockIdx.x >= ntiles) return;
+    // this workgroup's tiles: the groups of kTileRun consecutive tiles numbered
+    // blockIdx.x, + gridDim.x, + 2 gridDim.x, ... (j-th tile: tile(j); past
+    // the sequence's end tile(j) >= ntiles)
+    const int64_t ngr = (ntiles + kTileRun - 1) / kTileRun;
+    if ((int64_t)blockIdx.x >= ngr) return;
     const int64_t G = gridDim.x;
-    const int64_t J = (ntiles - (int64_t)blockIdx.x + G - 1) / G;
-    auto tile = [&](int64_t j) -> int64_t { return (int64_t)blockIdx.x + j * G; };
+    const int64_t my_groups = (ngr - (int64_t)blockIdx.x + G - 1) / G;
+    const int64_t last_group = (int64_t)blockIdx.x + (my_groups - 1) * G;
+    const int64_t J = (my_groups - 1) * kTileRun + min((int64_t)kTileRun, ntiles - last_group * kTileRun);
+    auto tile = [&](int64_t j) -> int64_t {
+        return ((int64_t)blockIdx.x + (j / kTileRun) * G) * kTileRun + (j % kTileRun);
+    };
 
     // pipeline registers: the next tile's entries (global positions) and initial contents
     int32_t n_pos[kPre];
@@ -1023,7 +1066,8 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         while (lg_tpm > 0 && (kMergeThreads >> lg_tpm) < M.n) --lg_tpm;
         const int32_t im = mb == 0 ? init : SGC_INIT_INPLACE;
         const bool load = im != SGC_INIT_ZERO;
-        const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(ntiles, load ? merge_blocks<true>() : merge_blocks<false>()));
+        const int64_t grid = std::max<int64_t>(
+            1, std::min<int64_t>(cdiv(ntiles, kTileRun), load ? merge_blocks<true>() : merge_blocks<false>()));
         if (load)
             k_merge<true><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles);
         else
