@@ -21,7 +21,9 @@ from gpu_util import announce, assert_bitwise, dev, host
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_compress_encode_flat(orc):
+@pytest.mark.parametrize("path", [sgc.PATH_GATHER, sgc.PATH_WINDOW], ids=["gather", "window"])
+def test_graph_compress_encode_flat(orc, path):
+    # flat-1M top-1% compress + Rice, through either compress pipeline
     w = W.FLAT_1M
     layout = sgc.Layout(w.seg_numel)
     n = w.numel
@@ -29,15 +31,16 @@ def test_graph_compress_encode_flat(orc):
     ppm, b = w.keep_ppm, sgc.rice_param(w.keep_ppm / 1e6)
     g_in = torch.zeros(n, dtype=torch.float32, device="cuda")
     r = torch.zeros(n, dtype=torch.float32, device="cuda")
-    comp = sgc.compress(layout, g_in, r, keep_ppm=ppm)  # warm-up: outputs
+    comp = sgc.compress(layout, g_in, r, keep_ppm=ppm, path=path)  # warm-up: outputs
     enc = sgc.encode(layout, comp.idx, comp.counts, comp.cap, b=b)
-    ws_c = torch.empty(sgc.compress_workspace_bytes(layout, keep_ppm=ppm), dtype=torch.uint8, device="cuda")
+    ws_c = torch.empty(sgc.compress_workspace_bytes(layout, keep_ppm=ppm, path=path), dtype=torch.uint8,
+                       device="cuda")
     ws_e = torch.empty(sgc.encode_workspace_bytes(layout, sgc.GLOBAL, comp.cap), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     r.zero_()
 
     def step():
-        sgc.compress(layout, g_in, r, keep_ppm=ppm, out=comp, ws=ws_c)
+        sgc.compress(layout, g_in, r, keep_ppm=ppm, out=comp, ws=ws_c, path=path)
         sgc.encode(layout, comp.idx, comp.counts, comp.cap, b=b, out=enc, ws=ws_e)
 
     graph = torch.cuda.CUDAGraph()
@@ -49,7 +52,7 @@ def test_graph_compress_encode_flat(orc):
         g = W.gradient(w, 0, it).numpy()
         g_in.copy_(torch.from_numpy(g))
         torch.cuda.synchronize()
-        announce(f"graph replay {it}: flat-1M compress + encode")
+        announce(f"graph replay {it}: flat-1M compress + encode, path {path}")
         graph.replay()
         torch.cuda.synchronize()
         ref = orc.compress_exact(g, r_host, seg_off, sgc.GLOBAL, ppm, cap=comp.cap)

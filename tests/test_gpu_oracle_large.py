@@ -9,11 +9,13 @@ steps one after the other.
 
 Cases (the kernel paths the benchmark's full-size step takes):
 * a 2^28-element gradient of the flat-1G recipe, exact global top-1%, two
-  carried steps, with the Rice streams (b = 6) of both steps;
+  carried steps, with the Rice streams (b = 6) of both steps, through the
+  window pipeline (the one the 2^30 step takes) and the gather pipeline;
 * the NMT-shaped gradient (97.8M elements, clustered embedding rows), exact
   global top-1%, two carried steps;
-* 2^27 elements at 55% kept, which takes the compaction's chunk-count scan
-  split over workgroups (more than 16,384 chunks of kept entries).
+* 2^27 elements at 55% kept, which takes the gather pipeline's chunk-count
+  scan split over workgroups (more than 16,384 chunks of kept entries), and
+  the window pipeline on the same input.
 Every output is compared: indices, values, per-segment counts, status and
 the whole residual.
 """
@@ -52,17 +54,17 @@ class OracleThread(threading.Thread):
         return self.result
 
 
-def gpu_steps(layout, grads, ppm, scope=sgc.GLOBAL, b=None):
+def gpu_steps(layout, grads, ppm, scope=sgc.GLOBAL, b=None, path=sgc.PATH_AUTO):
     """Run the carried steps on the GPU; host copies of every output, the
     residual before each step, and (with b) the Rice streams."""
     n = layout.n
     rd = torch.zeros(n, dtype=torch.float32, device="cuda")
     steps = []
     for s, g in enumerate(grads):
-        announce(f"GPU step {s}: n={n} ppm={ppm}")
+        announce(f"GPU step {s}: n={n} ppm={ppm} path={path}")
         r_in = host(rd).copy()
         gd = torch.from_numpy(g).cuda()
-        comp = sgc.compress(layout, gd, rd, keep_ppm=ppm, scope=scope)
+        comp = sgc.compress(layout, gd, rd, keep_ppm=ppm, scope=scope, path=path)
         enc = sgc.encode(layout, comp.idx, comp.counts, comp.cap, b=b, scope=scope) if b is not None else None
         torch.cuda.synchronize()
         del gd
@@ -113,14 +115,24 @@ def check_against_oracle(orc, layout, grads, steps, ppm, scope=sgc.GLOBAL, b=Non
 
 def test_flat_2e28_exact_two_steps_with_rice(orc):
     # the headline step's kernels (exact global top-1% + Rice b = 6) on a
-    # 2^28-element draw of the flat-1G recipe, two carried steps
+    # 2^28-element draw of the flat-1G recipe, two carried steps, through both
+    # compress pipelines (the 2^30 step takes the window pipeline): the two
+    # runs must agree bit for bit, and the window run with the oracle
     w = W.FLAT_1G
     n = 1 << 28
     layout = sgc.Layout([n])
     ppm = 10000
     b = sgc.rice_param(ppm / 1e6)
     grads = [host(W.gradient(w, 0, s, device="cuda", numel=n)) for s in range(2)]
-    steps = gpu_steps(layout, grads, ppm, b=b)
+    steps = gpu_steps(layout, grads, ppm, b=b, path=sgc.PATH_WINDOW)
+    other = gpu_steps(layout, grads, ppm, b=b, path=sgc.PATH_GATHER)
+    for s, (a, o) in enumerate(zip(steps, other)):
+        for key in ("counts", "idx", "val", "r_out"):
+            assert_bitwise(o[key], a[key], f"step {s} {key}: gather against window")
+        nch = 2 * ((int(a["counts"][-1]) + 255) // 256)  # the chunk table's valid part (the rest is unused)
+        for key, m in (("words", a["enc"]["words"].size), ("word_off", None), ("nbits", None), ("chunk_off", nch)):
+            assert_bitwise(o["enc"][key][:m], a["enc"][key][:m], f"step {s} {key}: gather against window")
+    del other
     assert all(int(st["counts"][-1]) == layout.keep_total(sgc.GLOBAL, ppm) for st in steps)
     check_against_oracle(orc, layout, grads, steps, ppm, b=b, what="flat 2^28 top-1%")
 
@@ -137,7 +149,9 @@ def test_nmt_exact_two_steps_carried(orc):
 
 def test_split_chunk_scan_2e27_55pct(orc):
     # 55% of 2^27 kept: 73.8M entries in more than 16,384 chunks, so the
-    # compaction's chunk-count scan is split over workgroups
+    # gather pipeline's chunk-count scan is split over workgroups; the window
+    # pipeline (the default at this density: whole-tile regions, one wave per
+    # tile in the write) must agree with it bit for bit
     w = W.FLAT_1G
     n = 1 << 27
     layout = sgc.Layout([n])
@@ -145,6 +159,10 @@ def test_split_chunk_scan_2e27_55pct(orc):
     k = layout.keep_total(sgc.GLOBAL, ppm)
     assert (k + 4095) // 4096 > 16384
     grads = [host(W.gradient(w, 0, 0, device="cuda", numel=n))]
-    steps = gpu_steps(layout, grads, ppm)
+    steps = gpu_steps(layout, grads, ppm, path=sgc.PATH_GATHER)
+    other = gpu_steps(layout, grads, ppm, path=sgc.PATH_WINDOW)
+    for key in ("counts", "idx", "val", "r_out"):
+        assert_bitwise(other[0][key], steps[0][key], f"{key}: window against gather")
+    del other
     assert int(steps[0]["counts"][-1]) == k
     check_against_oracle(orc, layout, grads, steps, ppm, what="2^27 at 55%")
