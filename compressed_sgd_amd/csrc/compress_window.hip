@@ -62,6 +62,11 @@ constexpr int kTPer = 8;                         // items per thread per round o
 constexpr int kRoundItems = kBlock * kTPer;      // items per round
 constexpr int64_t kWaveWriteCap = 1024;          // regions this large take the wave-per-tile write
 constexpr int64_t kStageCap = 1024;              // and pass 1 stages their candidates in LDS
+// Regions and window lists fill only the front of their power-of-two slots;
+// a slot stride of that size would put the filled parts of every tile on the
+// same HBM channels.  A pad after each slot shifts them from tile to tile.
+constexpr int64_t kRegPad = 64;                  // entries after each region slot
+constexpr int64_t kListPad = 32;                 // entries after each window list slot
 
 // How a group is selected after pass 1.
 constexpr int32_t kGNone = 0;    // k = 0: nothing kept
@@ -101,10 +106,10 @@ struct CompressWs {
     int64_t* tile_loc2; // [NT] prefix inside the super block: sure entries, later ties
     int64_t* sup_pre;   // [NS+1] super block prefix of the same
     int64_t* sup_pre2;  // [NS+1]
-    uint16_t* reg_idx;  // [NT * tcap] offset of each candidate from its tile's first element
-    float* reg_val;     // [NT * tcap]
-    float* reg_mom;     // [NT * tcap] u' of each candidate (momentum correction only)
-    float* wlist;       // [NT * wcap] window values per tile (exact mode)
+    uint16_t* reg_idx;  // [NT * tstride] offset of each candidate from its tile's first element
+    float* reg_val;     // [NT * tstride]
+    float* reg_mom;     // [NT * tstride] u' of each candidate (momentum correction only)
+    float* wlist;       // [NT * wstride] window values per tile (exact mode)
     int32_t* over;      // [NT] overflowed tiles (any order)
     uint32_t* nover;    // [1] entries in over
     int32_t* dgrp;      // [G] groups selected from the residual
@@ -114,12 +119,14 @@ struct CompressWs {
     uint32_t* status;   // [1] used when the caller passes no dstatus
     uint32_t tcap;      // candidate slots per tile region (a power of two)
     uint32_t wcap;      // window list slots per tile (a power of two; exact mode)
+    uint32_t tstride;   // region of tile t at t * tstride (tcap + kRegPad)
+    uint32_t wstride;   // window list of tile t at t * wstride (wcap + kListPad)
     uint32_t hold;      // SGC_HOLD_KEPT: kept entries keep acc in the residual (nothing is zeroed)
 };
 
 struct CompressSizes {
     int32_t G;
-    int64_t NT, NS, S, tcap, wcap;
+    int64_t NT, NS, S, tcap, wcap, tstride, wstride;
 };
 
 // Window list slots per tile: about twice the window entries a tile
@@ -152,6 +159,8 @@ static CompressSizes compress_sizes(const sgc_layout* L, const sgc_compress_opts
     z.NS = cdiv(z.NT, kSuper);
     z.tcap = region_capacity(o->keep_ppm);
     z.wcap = (o->mode == SGC_EXACT) ? window_capacity(off, o->keep_ppm) : 0;
+    z.tstride = z.tcap + kRegPad;
+    z.wstride = z.wcap ? z.wcap + kListPad : 0;
     z.S = 0;
     for (int32_t g = 0; g < z.G; ++g) {
         int64_t m = off[g + 1] - off[g];
@@ -187,15 +196,17 @@ static void carve_compress(Carver& c, const CompressSizes& z, int mode, bool mom
     w->sup_pre = c.take<int64_t>(z.NS + 1);
     w->sup_pre2 = c.take<int64_t>(z.NS + 1);
     w->tcap = (uint32_t)z.tcap;
-    w->reg_idx = c.take<uint16_t>(z.NT * z.tcap);
-    w->reg_val = c.take<float>(z.NT * z.tcap);
-    w->reg_mom = mom ? c.take<float>(z.NT * z.tcap) : nullptr;
+    w->tstride = (uint32_t)z.tstride;
+    w->reg_idx = c.take<uint16_t>(z.NT * z.tstride);
+    w->reg_val = c.take<float>(z.NT * z.tstride);
+    w->reg_mom = mom ? c.take<float>(z.NT * z.tstride) : nullptr;
     w->wcap = (uint32_t)z.wcap;
+    w->wstride = (uint32_t)z.wstride;
     if (mode == SGC_EXACT) {
         w->tile_win = c.take<uint32_t>(z.NT);
         w->tile_sg = c.take<uint32_t>(z.NT);
         w->tile_eq = c.take<uint32_t>(z.NT);
-        w->wlist = c.take<float>(z.NT * z.wcap);
+        w->wlist = c.take<float>(z.NT * z.wstride);
     } else {
         w->tile_win = w->tile_sg = w->tile_eq = nullptr;
         w->wlist = nullptr;
@@ -698,11 +709,11 @@ __global__ __launch_bounds__(kPassThreads) void k_pass1(const float* __restrict_
     const int64_t g = tile_group(gtile, G, t);
     const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
     const int32_t A = tile_base(goff, gtile, g, t);
-    uint16_t* ridx = w.reg_idx + t * w.tcap;
-    float* rval = w.reg_val + t * w.tcap;
-    float* rmom = M::on ? w.reg_mom + t * w.tcap : nullptr;
+    uint16_t* ridx = w.reg_idx + t * w.tstride;
+    float* rval = w.reg_val + t * w.tstride;
+    float* rmom = M::on ? w.reg_mom + t * w.tstride : nullptr;
     uint32_t win = 0;
-    float* wl = w.wlist ? w.wlist + t * w.wcap : nullptr;  // window lists: exact mode only
+    float* wl = w.wlist ? w.wlist + t * w.wstride : nullptr;  // window lists: exact mode only
     const uint32_t cnt = tile_candidates<kPassThreads, (int)(kTile / (4 * kPassThreads))>(
         grad, res, lo, hi, A, w.key_lo[g], w.key_z[g], w.key_hi[g], w.tcap, m, wl, w.wcap, &win,
         [&](uint32_t pos, int32_t i, float v, float up) {
@@ -719,12 +730,15 @@ __global__ __launch_bounds__(kPassThreads) void k_pass1(const float* __restrict_
             }
         });
     if constexpr (ST) {
+        // whole lines, stored nontemporally: the regions are read back only
+        // after the pass, and at this volume cached stores cost the pass
+        // about a tenth of its time
         __syncthreads();
         const uint32_t c = min(cnt, w.tcap);
         for (uint32_t k = threadIdx.x; k < c; k += kPassThreads) {
-            ridx[k] = s_off[k];
-            rval[k] = s_val[k];
-            if constexpr (M::on) rmom[k] = s_mom[k];
+            __builtin_nontemporal_store(s_off[k], ridx + k);
+            __builtin_nontemporal_store(s_val[k], rval + k);
+            if constexpr (M::on) __builtin_nontemporal_store(s_mom[k], rmom + k);
         }
     }
     if (threadIdx.x == 0) {
@@ -1051,7 +1065,7 @@ __global__ __launch_bounds__(kBlock) void k_tsel_hist(float* __restrict__ res, c
                 const uint32_t e = min(e0 + u * kBlock + threadIdx.x, E - 1);
                 const int q = tile_of(s_pre, e);
                 const uint32_t jj = e - s_pre[q];
-                const float* src = s_list[q] ? w.wlist + (t0 + q) * w.wcap : w.reg_val + (t0 + q) * w.tcap;
+                const float* src = s_list[q] ? w.wlist + (t0 + q) * w.wstride : w.reg_val + (t0 + q) * w.tstride;
                 v[u] = src[jj];
                 qs[u] = e0 + u * kBlock + threadIdx.x < E ? q : -1;
             }
@@ -1078,7 +1092,7 @@ __global__ __launch_bounds__(kBlock) void k_tsel_hist(float* __restrict__ res, c
         if (P == 0 && w.gmode[g] == kGDense && w.tile_cnt[rt.t] <= w.tcap) {
             // pass 1 zeroed this tile's keys >= key_z: acc (and u') back from the region
             const uint32_t kz = w.key_z[g], c = w.tile_cnt[rt.t];
-            const int64_t rb = rt.t * w.tcap;
+            const int64_t rb = rt.t * w.tstride;
             const int32_t A = tile_base(goff, gtile, g, rt.t);
             for (uint32_t j0 = 0; j0 < c; j0 += kBlock) {  // uniform
                 const uint32_t q = j0 + threadIdx.x;
@@ -1233,7 +1247,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_count(const float* __restrict__
             const uint32_t e = min(e0 + u * kBlock + threadIdx.x, E - 1);
             const int q = tile_of(s_pre, e);
             const uint32_t jj = e - s_pre[q];
-            const float* src = s_list[q] ? w.wlist + (t0 + q) * w.wcap : w.reg_val + (t0 + q) * w.tcap;
+            const float* src = s_list[q] ? w.wlist + (t0 + q) * w.wstride : w.reg_val + (t0 + q) * w.tstride;
             v[u] = src[jj];
             qs[u] = e0 + u * kBlock + threadIdx.x < E ? q : -1;
         }
@@ -1449,7 +1463,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_write(float* __restrict__ res, 
         for (int u = 0; u < WP; ++u) {
             const uint32_t e = min(e0 + u * kBlock + threadIdx.x, E - 1);
             const int q = tile_of(s_pre, e);
-            const int64_t at = (t0 + q) * w.tcap + (e - s_pre[q]);
+            const int64_t at = (t0 + q) * w.tstride + (e - s_pre[q]);
             id[u] = s_A[q] + (int32_t)w.reg_idx[at];
             v[u] = w.reg_val[at];
             um[u] = M::on ? w.reg_mom[at] : 0.0f;
@@ -1533,7 +1547,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_write_wave(float* __restrict__ 
             const int64_t eqb = tile_prefix2(w, NT, t) - tile_prefix2(w, NT, gtile[g]);
             int64_t pos0 = w.kpre[g] + sgb + min(quota, eqb);  // next output position of the tile
             int64_t trank = eqb;                                // tie rank of the tile's next tie
-            const int64_t rb = t * w.tcap;
+            const int64_t rb = t * w.tstride;
             for (uint32_t j0 = 0; j0 < cnt; j0 += U * 64) {  // uniform
                 int32_t id[U];
                 float v[U], um[U];
@@ -1622,7 +1636,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_write_sampled(float* __restrict
         for (int u = 0; u < kTPer; ++u) {
             const uint32_t e = min(e0 + u * kBlock + threadIdx.x, E - 1);
             const int q = tile_of(s_pre, e);
-            const int64_t at = (t0 + q) * w.tcap + (e - s_pre[q]);
+            const int64_t at = (t0 + q) * w.tstride + (e - s_pre[q]);
             id[u] = s_A[q] + (int32_t)w.reg_idx[at];
             v[u] = w.reg_val[at];
             um[u] = M::on ? w.reg_mom[at] : 0.0f;
