@@ -31,7 +31,7 @@ namespace sgc {
 typedef float f4a __attribute__((ext_vector_type(4)));
 typedef int32_t i4v __attribute__((ext_vector_type(4)));
 
-constexpr int kBatch = 8;     // messages per decode launch
+constexpr int kBatch = 16;    // messages per decode launch
 constexpr int kMerge = 16;    // messages per merge launch
 
 struct MsgWs {
@@ -744,13 +744,19 @@ __device__ int32_t g_zero_word = 0;
 template <bool LOAD>
 __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t lg_tpm, int32_t init,
                                                  const float* __restrict__ base, float* __restrict__ out, int64_t n,
-                                                 int64_t ntiles)
+                                                 int64_t ntiles, uint32_t* status)
 {
     __shared__ __align__(16) MergeLds S;
     const int tid = threadIdx.x;
     const int tpm = 1 << lg_tpm;  // threads per message slot
     const int mk = tid >> lg_tpm, ml = tid & (tpm - 1);
     const bool live = mk < M.n && !*M.bad[mk];
+    // the batch's corrupt messages (their flags are final before the merge)
+    // reach the caller's status word, from workgroup 0
+    if (status && blockIdx.x == 0 && tid < 64) {
+        const bool bad = tid < M.n && *M.bad[tid] != 0u;
+        if (__ballot(bad) != 0ull && tid == 0) *status |= SGC_STATUS_CORRUPT;
+    }
     const int32_t* posk = live ? M.pos[mk] : nullptr;
     const float* valk = live ? M.val[mk] : nullptr;
     const int32_t* tsk = live ? M.tstart[mk] : nullptr;
@@ -916,15 +922,6 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
     }
 }
 
-__global__ void k_fold_status(MergeBatch M, uint32_t* status)
-{
-    if (threadIdx.x) return;
-    uint32_t st = 0;
-    for (int k = 0; k < M.n; ++k)
-        if (*M.bad[k]) st |= SGC_STATUS_CORRUPT;
-    if (st) *status |= st;
-}
-
 }  // namespace sgc
 
 using namespace sgc;
@@ -1069,14 +1066,12 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         const int64_t grid = std::max<int64_t>(
             1, std::min<int64_t>(cdiv(ntiles, kTileRun), load ? merge_blocks<true>() : merge_blocks<false>()));
         if (load)
-            k_merge<true><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles);
+            k_merge<true><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles,
+                                                                   M.n > 0 ? dstatus : nullptr);
         else
-            k_merge<false><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles);
+            k_merge<false><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles,
+                                                                    M.n > 0 ? dstatus : nullptr);
         SGC_LAUNCH_CHECK();
-        if (dstatus && M.n > 0) {
-            k_fold_status<<<1, 64, 0, s>>>(M, dstatus);
-            SGC_LAUNCH_CHECK();
-        }
     }
     return SGC_OK;
 }
