@@ -232,18 +232,18 @@ def workload_rows(sgc, W, torch, dev, stream, reps=10):
     rs = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(w.workers)]
     msgs = []
     for k in range(w.workers):
-        c = sgc.compress(L, gs[k], rs[k], keep_ppm=w.keep_ppm)
-        bn = sgc.binarize(L, c, rs[k], sgc.BIN_2BIT)
+        c = sgc.compress(L, gs[k], rs[k], keep_ppm=w.keep_ppm, hold=True)
+        bn = sgc.binarize(L, c, rs[k], sgc.BIN_2BIT, held=True)
         msgs.append(sgc.Message(sgc.MSG_RAW_2BIT, bn.counts, bn.cap, idx=c.idx, codes=bn.codes, means=bn.means))
     row = {}
     for mode, tag in ((sgc.EXACT, "exact"), (sgc.SAMPLED, "sampled")):
         ct = sgc.compress(L, gs[0], rs[0], mode=mode, keep_ppm=w.keep_ppm)
 
         def step():
-            sgc.compress(L, gs[1], rs[0], mode=mode, keep_ppm=w.keep_ppm, out=ct)
-            sgc.binarize(L, ct, rs[0], sgc.BIN_2BIT)
+            sgc.compress(L, gs[1], rs[0], mode=mode, keep_ppm=w.keep_ppm, out=ct, hold=True)
+            sgc.binarize(L, ct, rs[0], sgc.BIN_2BIT, held=True)
         t = timed(step, reps, stream)
-        row[f"worker_step_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "steps": "compress + 2-bit"}
+        row[f"worker_step_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "steps": "compress (hold flag) + 2-bit (held)"}
     out = torch.empty(n, dtype=torch.float32, device=dev)
     t = timed(lambda: sgc.decode_accumulate(L, msgs, out), reps, stream)
     row["receive"] = {"ms": t, "elements_per_s": el(n, t), "messages": len(msgs), "format": "raw 2-bit"}
@@ -282,8 +282,8 @@ def workload_rows(sgc, W, torch, dev, stream, reps=10):
     r = torch.zeros(n, dtype=torch.float32, device=dev)
     for k in range(w.workers):
         r.zero_()
-        c = sgc.compress(L, gs[k % 2], r, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm)
-        bn = sgc.binarize(L, c, r, sgc.BIN_SBC)
+        c = sgc.compress(L, gs[k % 2], r, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm, hold=True)
+        bn = sgc.binarize(L, c, r, sgc.BIN_SBC, held=True)
         e = sgc.encode(L, bn.idx, bn.counts, bn.cap, scope=sgc.PER_SEGMENT, b=b)
         msgs.append(sgc.golomb_message(bn, e))
     row = {}
@@ -295,8 +295,9 @@ def workload_rows(sgc, W, torch, dev, stream, reps=10):
         wse = torch.empty(sgc.encode_workspace_bytes(L, sgc.PER_SEGMENT, ct.cap), **u8)
 
         def exchange():
-            sgc.compress(L, gs[1], r, mode=mode, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm, out=ct, ws=wsc)
-            bt = sgc.binarize(L, ct, r, sgc.BIN_SBC, ws=wsb)
+            sgc.compress(L, gs[1], r, mode=mode, scope=sgc.PER_SEGMENT, keep_ppm=w.keep_ppm, out=ct, ws=wsc,
+                         hold=True)
+            bt = sgc.binarize(L, ct, r, sgc.BIN_SBC, ws=wsb, held=True)
             sgc.encode(L, bt.idx, bt.counts, bt.cap, scope=sgc.PER_SEGMENT, b=b, ws=wse)
 
         def rnd():
@@ -305,7 +306,7 @@ def workload_rows(sgc, W, torch, dev, stream, reps=10):
             exchange()
         t = timed(exchange, reps, stream)
         tr = timed(rnd, reps, stream)
-        row[f"exchange_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "steps": "compress + SBC + Rice"}
+        row[f"exchange_{tag}"] = {"ms": t, "elements_per_s": el(n, t), "steps": "compress (hold flag) + SBC (held) + Rice"}
         row[f"round_{tag}"] = {"ms": tr, "steps": f"{w.delay - 1} accumulations + exchange"}
         if mode == sgc.EXACT:  # the same, replayed from a HIP graph
             row[f"exchange_{tag}"]["ms_graph"] = graph_timed(exchange, reps, stream)

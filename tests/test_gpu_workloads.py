@@ -257,14 +257,16 @@ def test_flat_1g_sampled_full_size(orc):
 def test_flat_1g_decode_accumulate_sixteen_workers(orc):
     # 16 workers' top-0.1% Rice messages (b = 9) summed into 2^30 elements;
     # each worker's exact selection is checked through its defining
-    # properties and each stream against the oracle's encoding of its indices
+    # properties, each stream against the oracle's encoding of its indices,
+    # and the 16-worker sum against the oracle's decode-accumulate of the
+    # oracle's own streams
     w = W.FLAT_1G
     layout = sgc.Layout(w.seg_numel)
     seg_off = np.array(layout.seg_off, np.int64)
     ppm = 1000
     b = sgc.rice_param(ppm / 1e6)
     k = layout.keep_total(sgc.GLOBAL, ppm)
-    msgs, sent = [], []
+    msgs, omsgs = [], []
     rd = torch.zeros(w.numel, dtype=torch.float32, device="cuda")
     for wk in range(w.workers):
         g = W.gradient(w, wk, 0, device="cuda")
@@ -278,22 +280,22 @@ def test_flat_1g_decode_accumulate_sixteen_workers(orc):
         del acc
         msgs.append(sgc.golomb_message(comp, enc))
         total = int(host(comp.counts)[-1])
-        sent.append((comp.idx[:total].long(), comp.val[:total]))
-        ref = orc.encode(host(comp.idx)[:total], host(comp.counts), seg_off, 0, b)
+        counts = host(comp.counts)
+        ref = orc.encode(host(comp.idx)[:total], counts, seg_off, 0, b)
         nw = int(ref.word_off[-1])
         assert_bitwise(host(enc.words[:nw]).view(np.uint32), ref.words, f"worker {wk} words")
         assert_bitwise(host(enc.chunk_off[:ref.chunk_off.size]).view(np.uint64), ref.chunk_off,
                        f"worker {wk} chunk table")
+        omsgs.append(orc.Message(counts, golomb=True, scope=orc.GLOBAL, b=b, val=host(comp.val)[:total], enc=ref))
     del rd
     out = torch.empty(w.numel, dtype=torch.float32, device="cuda")
     announce("flat-1G decode_accumulate 16 x 0.1%")
     st = sgc.decode_accumulate(layout, msgs, out)
-    ref = torch.zeros(w.numel, dtype=torch.float32, device="cuda")
-    for idx, val in sent:  # one addition per element and message, in message order
-        ref[idx] = ref[idx] + val
     torch.cuda.synchronize()
     assert int(host(st)[0]) == 0
-    assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), "flat-1G 16-worker sum"
+    want = np.zeros(w.numel, np.float32)
+    assert orc.decode_accumulate(omsgs, seg_off, want) == 0
+    assert_bitwise(host(out).view(np.uint32), want.view(np.uint32), "flat-1G 16-worker sum")
 
 
 @pytest.mark.parametrize("scope", [sgc.GLOBAL, sgc.PER_SEGMENT])
