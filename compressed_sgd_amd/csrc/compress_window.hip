@@ -34,7 +34,9 @@
 //  4. select  -- the (k - sure)-th largest window key T and the quota of
 //                ties at T: 2048-bin histograms over the search range
 //                [key_lo, key_hi), narrowed to one bin per pass (two passes
-//                for ranges up to 2^22 keys, a third only beyond).
+//                for ranges up to 2^22 keys, a third only beyond); with one
+//                group, the later passes read the keys the first pass
+//                counted from a flat copy it made.
 //  5. count   -- per tile, the entries kept without a tie (sure, key > T)
 //                and the ties at T; a scan gives every tile's output offset
 //                (ties are taken lowest index first).
@@ -110,12 +112,19 @@ struct CompressWs {
     float* reg_val;     // [NT * tstride]
     float* reg_mom;     // [NT * tstride] u' of each candidate (momentum correction only)
     float* wlist;       // [NT * wstride] window values per tile (exact mode)
+    float* wflat;       // [fcap] exact mode, one group: the keys selection pass 0
+                        // counted, in no order, in one segment of fcap / grid
+                        // per workgroup; passes 1 and 2 (same grid) read
+                        // these instead of the tiles
+    uint32_t* fcnt;     // [kHistBlocks] keys in each workgroup's segment
+    int64_t fcap;
     int32_t* over;      // [NT] overflowed tiles (any order)
     uint32_t* nover;    // [1] entries in over
     int32_t* dgrp;      // [G] groups selected from the residual
     int64_t* dpre;      // [G+1] their tile prefix
     int64_t* scal;      // [8]: 0 output total, 1 candidate total, 2 groups in dgrp,
-                        // 4 + p: some group still searching after selection pass p
+                        // 4 + p: some group still searching after selection pass p,
+                        // 6: a workgroup's wflat segment overflowed
     uint32_t* status;   // [1] used when the caller passes no dstatus
     uint32_t tcap;      // candidate slots per tile region (a power of two)
     uint32_t wcap;      // window list slots per tile (a power of two; exact mode)
@@ -207,9 +216,15 @@ static void carve_compress(Carver& c, const CompressSizes& z, int mode, bool mom
         w->tile_sg = c.take<uint32_t>(z.NT);
         w->tile_eq = c.take<uint32_t>(z.NT);
         w->wlist = c.take<float>(z.NT * z.wstride);
+        w->fcap = G == 1 ? z.NT * z.wcap : 0;
+        w->wflat = G == 1 ? c.take<float>(w->fcap) : nullptr;
+        w->fcnt = G == 1 ? c.take<uint32_t>(kHistBlocks) : nullptr;
     } else {
         w->tile_win = w->tile_sg = w->tile_eq = nullptr;
         w->wlist = nullptr;
+        w->wflat = nullptr;
+        w->fcnt = nullptr;
+        w->fcap = 0;
     }
     w->over = c.take<int32_t>(z.NT);
     w->nover = c.take<uint32_t>(1);
@@ -908,7 +923,7 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_scan2(const int64_t* __re
     if (threadIdx.x != 0) return;
     w.dpre[nd] = dt;
     w.scal[2] = nd;
-    w.scal[4] = w.scal[5] = 0;
+    w.scal[4] = w.scal[5] = w.scal[6] = 0;
     w.scal[0] = w.kpre[G];
     if (fallback) *status |= SGC_STATUS_DENSE_PATH;
 }
@@ -1002,6 +1017,37 @@ __device__ inline void flush_hist(const CompressWs& w, const uint32_t* h, int nb
     }
 }
 
+// Selection pass 0 of a single group selected from its window: the lane's
+// hits go to the workgroup's segment of the flat array (seg entries at
+// dst), slots handed out by an LDS counter, one atomic per wave; entries
+// past the segment are counted but not stored.
+template <int N>
+__device__ inline void flat_append(float* dst, uint32_t seg, uint32_t* s_cnt, const float (&v)[N],
+                                   const bool (&hit)[N])
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t n = 0;
+#pragma unroll
+    for (int u = 0; u < N; ++u) n += hit[u] ? 1u : 0u;
+    uint32_t x = n;  // inclusive wave scan of the lanes' hits
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    const uint32_t tot = __shfl(x, 63, 64);
+    if (tot == 0) return;  // uniform
+    uint32_t base = 0;
+    if (lane == 63) base = atomicAdd(s_cnt, tot);
+    uint32_t pos = __shfl(base, 63, 64) + x - n;
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        if (hit[u]) {
+            if (pos < seg) dst[pos] = v[u];
+            ++pos;
+        }
+}
+
 // Step 4, selection pass P (0, 1 or 2): every open group's window keys
 // in its search range [wbase, wend), counted in 2048 bins -- from the window lists pass 1
 // wrote (or the region, past a list's capacity, and for groups whose window
@@ -1011,7 +1057,11 @@ __device__ inline void flush_hist(const CompressWs& w, const uint32_t* h, int nb
 // once when no group is still searching.  A workgroup takes kTT tiles at a
 // time, a grid-stride over the blocks of kTT tiles: its LDS histogram
 // counts the group of its first tile (the others go straight to memory),
-// flushed once at the end.
+// flushed once at the end.  A single group selected from its window: pass 0
+// also copies every key it counts into its workgroup's segment of a flat
+// array, and passes 1 and 2 (launched on the same grid) each read their own
+// segment (a few keys per tile) instead of walking the tiles -- unless a
+// segment overflowed.
 template <int P, typename M>
 __global__ __launch_bounds__(kBlock) void k_tsel_hist(float* __restrict__ res, const int64_t* __restrict__ goff,
                                                      const int64_t* __restrict__ gtile, int32_t G, int64_t NT,
@@ -1022,7 +1072,36 @@ __global__ __launch_bounds__(kBlock) void k_tsel_hist(float* __restrict__ res, c
     __shared__ uint32_t s_end[kTT], s_base[kTT];
     __shared__ int32_t s_sh[kTT], s_hg[kTT], s_list[kTT];
     __shared__ uint32_t h[kBins];
+    __shared__ uint32_t s_fcnt;
     for (int b = threadIdx.x; b < kBins; b += kBlock) h[b] = 0;
+    if (threadIdx.x == 0) s_fcnt = 0;
+    const bool flat = w.wflat != nullptr && w.gmode[0] == kGWindow;  // uniform
+    const uint32_t seg = flat ? (uint32_t)(w.fcap / gridDim.x) : 0u;
+    float* const fdst = flat ? w.wflat + (int64_t)blockIdx.x * seg : nullptr;
+    if (P > 0 && flat && w.scal[6] == 0) {  // uniform
+        const uint32_t nf = w.fcnt[blockIdx.x];
+        const uint32_t base = w.wbase[0], end = w.wend[0];
+        const int32_t sh = w.wshift[0];
+        __syncthreads();  // h is clear
+        if (sh >= 0) {
+            for (uint32_t e0 = 0; e0 < nf; e0 += kRoundItems) {  // uniform
+                float v[kTPer];
+#pragma unroll
+                for (int u = 0; u < kTPer; ++u) v[u] = fdst[min(e0 + u * kBlock + threadIdx.x, nf - 1)];
+#pragma unroll
+                for (int u = 0; u < kTPer; ++u) {
+                    const uint32_t key = mag_key(v[u]);
+                    const uint32_t bin = (key - base) >> sh;
+                    const bool hit = e0 + u * kBlock + threadIdx.x < nf && key >= base && key < end &&
+                                     bin < (uint32_t)kBins;
+                    lds_count(h, hit, bin);
+                }
+            }
+        }
+        __syncthreads();
+        flush_hist(w, h, kBins, 0);
+        return;
+    }
     const int32_t g_lds = (int32_t)tile_group(gtile, G, min((int64_t)blockIdx.x * kTT, NT - 1));
     uint32_t* const ghist = w.hist + (blockIdx.x & (kRep - 1)) * kBins;  // + group * kRep * kBins
     const int64_t nblk = cdiv(NT, kTT);
@@ -1069,6 +1148,7 @@ __global__ __launch_bounds__(kBlock) void k_tsel_hist(float* __restrict__ res, c
                 v[u] = src[jj];
                 qs[u] = e0 + u * kBlock + threadIdx.x < E ? q : -1;
             }
+            bool hits[kTPer];
 #pragma unroll
             for (int u = 0; u < kTPer; ++u) {
                 const int q = qs[u] < 0 ? 0 : qs[u];
@@ -1079,7 +1159,9 @@ __global__ __launch_bounds__(kBlock) void k_tsel_hist(float* __restrict__ res, c
                 const int32_t hg = s_hg[q];
                 if (hit && hg != g_lds) atomicAdd(&ghist[(int64_t)hg * kRep * kBins + bin], 1u);
                 lds_count(h, hit && hg == g_lds, bin);
+                hits[u] = hit;
             }
+            if (P == 0 && flat) flat_append<kTPer>(fdst, seg, &s_fcnt, v, hits);
         }
     }
     const uint32_t nover = *w.nover;
@@ -1115,6 +1197,7 @@ __global__ __launch_bounds__(kBlock) void k_tsel_hist(float* __restrict__ res, c
             float x[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) x[u] = res[min(e0 + u * kBlock + (int64_t)threadIdx.x, rt.e1 - 1)];
+            bool hits[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t key = mag_key(x[u]);
@@ -1123,11 +1206,17 @@ __global__ __launch_bounds__(kBlock) void k_tsel_hist(float* __restrict__ res, c
                                  bin < (uint32_t)kBins;
                 if (hit && !lds) atomicAdd(&ghist[g * kRep * kBins + bin], 1u);
                 lds_count(h, hit && lds, bin);
+                hits[u] = hit;
             }
+            if (P == 0 && flat) flat_append<4>(fdst, seg, &s_fcnt, x, hits);
         }
     }
     __syncthreads();
     flush_hist(w, h, kBins, g_lds);
+    if (P == 0 && flat && threadIdx.x == 0) {
+        w.fcnt[blockIdx.x] = s_fcnt;
+        if (s_fcnt > seg) w.scal[6] = 1;  // passes 1 and 2 walk the tiles
+    }
 }
 
 // The bin of selection pass P that holds the mrem-th largest key of each

@@ -209,8 +209,8 @@ int sgc_compress(const sgc_layout* layout, const sgc_compress_opts* opt,
  * its first layout upload until the process ends.  The call itself performs
  * no allocation of any kind.  Returns SGC_ENOSPC when the call would need
  * more workspace than that (sgc_compress_workspace(layout, opt, cap) >
- * SGC_NOALLOC_SCRATCH_BYTES: past about 75M elements at top-1% in one group,
- * 12M at top-10%),
+ * SGC_NOALLOC_SCRATCH_BYTES: past about 77M elements at top-1% in one group,
+ * 35M at top-10%),
  * SGC_ENOTREADY if no layout was uploaded to the current device (the upload
  * looks up the buffer's device address).  Every call on a GPU shares that
  * GPU's buffer, so calls that may overlap in time on one GPU (two streams,
