@@ -391,10 +391,11 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
     // output tile of the previous entry (before a stream's first entry: of the
     // stream's origin minus one; arithmetic shift, so -1 stays -1)
     int32_t tp = (J.base + (int32_t)prev) >> kOutTileLog;
-    // codes i0 .. i0+3: positions to pb (stored by the caller), values stored here
-    auto group = [&](int32_t i0, auto full, int32_t (&pb)[4]) __attribute__((always_inline)) {
+    // positions of codes i0 .. i0+3 to pb (stored by the caller), one code at
+    // a time with every check in place: partial groups, and whole groups
+    // that hold a long code
+    auto careful = [&](int32_t i0, auto full, int32_t (&pb)[4]) __attribute__((always_inline)) {
         constexpr bool kFull = decltype(full)::value;
-        float vb[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const bool act = kFull || i0 + q < J.nc;
@@ -438,25 +439,85 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
                 tp = t1;
             }
             pb[q] = (int32_t)((uint32_t)J.base + prev);
-            vb[q] = 0.0f;
-            if (FMT != SGC_MSG_GOLOMB_F32 && act) {
-                const int32_t j = J.j0 + i0 + q;
-                while (j >= tend) {  // entered the next segment (global scope): rare
-                    ++t;
-                    tend = (int32_t)w.estart[t + 1];
-                    seg_means<FMT>(in, t, &m0, &m1);
-                }
-                if (FMT == SGC_MSG_GOLOMB_SBC) {
-                    vb[q] = m0;
-                } else {
-                    const int32_t r = i0 + q + (J.j0 & 15);  // entry within the lane's code words
-                    const uint32_t code = (code_col[(r >> 4) * kDecLanes] >> (2 * (r & 15))) & 3u;
-                    err |= code == 3u;
-                    vb[q] = code == 0u ? 0.0f : code == 1u ? m0 : m1;
-                }
+        }
+    };
+    // a whole group without a branch per code (long codes and tile-table
+    // marks are rare): the four codes first, then one wave vote for a long
+    // code among them (such a lane redoes its group carefully, from the
+    // state before it) and one for marks to write
+    auto fast = [&](int32_t i0, int32_t (&pb)[4]) __attribute__((always_inline)) {
+        const uint32_t rel0 = rel, prev0 = prev;
+        const int32_t tp0 = tp;
+        const bool err0 = err;
+        bool slow = false;
+        uint32_t marks = 0;
+        int32_t t1s[4], tps[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t win = src.win(min(rel, last_rd));
+            const uint32_t ones = __builtin_ctzg(~win, 32);
+            const uint32_t len = ones + 1 + b;
+            const uint32_t z = (ones << b) | ((win >> min(ones, 31u) >> 1) & mask);
+            slow |= len > 32;
+            const uint32_t pu = prev + 1 + z;
+            err |= pu >= (uint32_t)J.size;
+            const int32_t t1 = (int32_t)(J.base + pu) >> kOutTileLog;
+            marks |= (!err && t1 != tp) ? 1u << q : 0u;
+            tps[q] = tp;
+            t1s[q] = t1;
+            rel += len;
+            prev = pu;
+            tp = t1;
+            pb[q] = (int32_t)((uint32_t)J.base + prev);
+        }
+        if (__builtin_expect(__any(slow), 0)) {
+            if (slow) {
+                rel = rel0;
+                prev = prev0;
+                tp = tp0;
+                err = err0;
+                marks = 0;  // the careful pass writes its own
+                careful(i0, std::true_type{}, pb);
             }
         }
-        if (FMT != SGC_MSG_GOLOMB_F32) {
+        if (__builtin_expect(__any(marks != 0u), 0)) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if ((marks >> q) & 1u) {
+                    const int32_t j = J.j0 + i0 + q;
+                    J.tstart[t1s[q]] = j;
+                    if (t1s[q] - tps[q] >= 2) J.tstart[t1s[q] - 1] = j;
+                }
+        }
+    };
+    // codes i0 .. i0+3: positions to pb (stored by the caller), then the
+    // values (SBC and 2-bit formats), stored here
+    auto group = [&](int32_t i0, auto full, int32_t (&pb)[4]) __attribute__((always_inline)) {
+        constexpr bool kFull = decltype(full)::value;
+        if constexpr (kFull) fast(i0, pb);
+        else careful(i0, full, pb);
+        if constexpr (FMT != SGC_MSG_GOLOMB_F32) {
+            float vb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                vb[q] = 0.0f;
+                if (kFull || i0 + q < J.nc) {
+                    const int32_t j = J.j0 + i0 + q;
+                    while (j >= tend) {  // entered the next segment (global scope): rare
+                        ++t;
+                        tend = (int32_t)w.estart[t + 1];
+                        seg_means<FMT>(in, t, &m0, &m1);
+                    }
+                    if (FMT == SGC_MSG_GOLOMB_SBC) {
+                        vb[q] = m0;
+                    } else {
+                        const int32_t r = i0 + q + (J.j0 & 15);  // entry within the lane's code words
+                        const uint32_t code = (code_col[(r >> 4) * kDecLanes] >> (2 * (r & 15))) & 3u;
+                        err |= code == 3u;
+                        vb[q] = code == 0u ? 0.0f : code == 1u ? m0 : m1;
+                    }
+                }
+            }
             const int32_t jb = J.j0 + i0;
             if (kFull && vec) {
                 *(f4a*)(w.val + jb) = f4a{vb[0], vb[1], vb[2], vb[3]};
