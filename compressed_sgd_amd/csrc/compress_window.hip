@@ -19,7 +19,9 @@
 //  2. pass 1  -- stream g and r once: acc = r + g; every element with
 //                key >= key_lo goes into its tile's candidate region (value
 //                and 16-bit offset in the tile, index order kept; staged in
-//                LDS where regions are large); r is stored as acc, or as +0
+//                LDS where regions are large; with the largest regions, in
+//                exact mode, a 4096-bit candidate mask per tile in place of
+//                the offsets); r is stored as acc, or as +0
 //                for key >= key_z, so that nearly all kept entries leave the
 //                residual without a second, scattered write.  Exact mode:
 //                the values of the tile's window entries (key_lo <= key <
@@ -64,6 +66,8 @@ constexpr int kTPer = 8;                         // items per thread per round o
 constexpr int kRoundItems = kBlock * kTPer;      // items per round
 constexpr int64_t kWaveWriteCap = 1024;          // regions this large take the wave-per-tile write
 constexpr int64_t kStageCap = 1024;              // and pass 1 stages their candidates in LDS
+constexpr int64_t kMaskCap = 2048;               // exact mode: candidate masks in place of offsets
+static_assert(kMaskCap >= kStageCap && kMaskCap >= kWaveWriteCap, "masks are built staged and read by the wave write");
 // Regions and window lists fill only the front of their power-of-two slots;
 // a slot stride of that size would put the filled parts of every tile on the
 // same HBM channels.  A pad after each slot shifts them from tile to tile.
@@ -109,6 +113,8 @@ struct CompressWs {
     int64_t* sup_pre;   // [NS+1] super block prefix of the same
     int64_t* sup_pre2;  // [NS+1]
     uint16_t* reg_idx;  // [NT * tstride] offset of each candidate from its tile's first element
+    uint64_t* reg_mask; // [NT * 64] large regions, exact mode, in place of reg_idx: bit i of
+                        // tile t's mask marks element i of the tile a candidate
     float* reg_val;     // [NT * tstride]
     float* reg_mom;     // [NT * tstride] u' of each candidate (momentum correction only)
     float* wlist;       // [NT * wstride] window values per tile (exact mode)
@@ -206,7 +212,12 @@ static void carve_compress(Carver& c, const CompressSizes& z, int mode, bool mom
     w->sup_pre2 = c.take<int64_t>(z.NS + 1);
     w->tcap = (uint32_t)z.tcap;
     w->tstride = (uint32_t)z.tstride;
-    w->reg_idx = c.take<uint16_t>(z.NT * z.tstride);
+    // exact mode with the largest regions: a 512-byte candidate mask per
+    // tile instead of 2 bytes per candidate (at 2^30 and 25% kept: 108 us
+    // less per call; at 10% the expansion costs what the bytes save)
+    const bool mask_mode = mode == SGC_EXACT && z.tcap >= kMaskCap;
+    w->reg_idx = mask_mode ? nullptr : c.take<uint16_t>(z.NT * z.tstride);
+    w->reg_mask = mask_mode ? c.take<uint64_t>(z.NT * (kTile / 64)) : nullptr;
     w->reg_val = c.take<float>(z.NT * z.tstride);
     w->reg_mom = mom ? c.take<float>(z.NT * z.tstride) : nullptr;
     w->wcap = (uint32_t)z.wcap;
@@ -699,6 +710,23 @@ __device__ inline uint32_t tile_candidates(const float* __restrict__ grad, float
     return run;
 }
 
+// Candidate masks (exact mode, large regions): a region holds the values in
+// index order and bit i of the tile's 64-word mask marks element i.  Lane L of
+// a wave takes word L (m): its candidates are entries pre .. pre + popc(m) - 1
+// of the region, pre the candidates of the words before it (a wave scan).
+__device__ inline uint32_t mask_word_prefix(uint64_t m)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t c = (uint32_t)__popcll(m);
+    uint32_t x = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x - c;
+}
+
 __device__ inline int64_t tile_group(const int64_t* gtile, int32_t G, int64_t t)
 {
     return G == 1 ? 0 : find_bucket(gtile, (int64_t)G + 1, t);
@@ -720,11 +748,14 @@ __global__ __launch_bounds__(kPassThreads) void k_pass1(const float* __restrict_
     __shared__ float s_val[ST ? kTile : 1];
     __shared__ uint16_t s_off[ST ? kTile : 1];
     __shared__ float s_mom[ST && M::on ? kTile : 1];
+    __shared__ uint32_t s_mask[ST ? kTile / 32 : 1];  // candidate bits (mask mode)
+    const bool mm = ST && w.reg_mask != nullptr;    // uniform
+    if (mm && threadIdx.x < kTile / 32) s_mask[threadIdx.x] = 0;  // read after tile_candidates' barriers
     const int64_t t = blockIdx.x;
     const int64_t g = tile_group(gtile, G, t);
     const int32_t lo = (int32_t)goff[g], hi = (int32_t)goff[g + 1];
     const int32_t A = tile_base(goff, gtile, g, t);
-    uint16_t* ridx = w.reg_idx + t * w.tstride;
+    uint16_t* ridx = w.reg_idx ? w.reg_idx + t * w.tstride : nullptr;
     float* rval = w.reg_val + t * w.tstride;
     float* rmom = M::on ? w.reg_mom + t * w.tstride : nullptr;
     uint32_t win = 0;
@@ -732,9 +763,10 @@ __global__ __launch_bounds__(kPassThreads) void k_pass1(const float* __restrict_
     const uint32_t cnt = tile_candidates<kPassThreads, (int)(kTile / (4 * kPassThreads))>(
         grad, res, lo, hi, A, w.key_lo[g], w.key_z[g], w.key_hi[g], w.tcap, m, wl, w.wcap, &win,
         [&](uint32_t pos, int32_t i, float v, float up) {
+            if (mm) atomicOr(&s_mask[(i - A) >> 5], 1u << ((i - A) & 31));
             if (pos < w.tcap) {
                 if constexpr (ST) {
-                    s_off[pos] = (uint16_t)(i - A);  // < kTile
+                    if (!mm) s_off[pos] = (uint16_t)(i - A);  // < kTile
                     s_val[pos] = v;
                     if constexpr (M::on) s_mom[pos] = up;
                 } else {
@@ -751,9 +783,13 @@ __global__ __launch_bounds__(kPassThreads) void k_pass1(const float* __restrict_
         __syncthreads();
         const uint32_t c = min(cnt, w.tcap);
         for (uint32_t k = threadIdx.x; k < c; k += kPassThreads) {
-            __builtin_nontemporal_store(s_off[k], ridx + k);
+            if (!mm) __builtin_nontemporal_store(s_off[k], ridx + k);
             __builtin_nontemporal_store(s_val[k], rval + k);
             if constexpr (M::on) __builtin_nontemporal_store(s_mom[k], rmom + k);
+        }
+        if (mm && threadIdx.x < kTile / 64) {
+            const uint64_t mw = (uint64_t)s_mask[2 * threadIdx.x] | ((uint64_t)s_mask[2 * threadIdx.x + 1] << 32);
+            __builtin_nontemporal_store(mw, w.reg_mask + t * (kTile / 64) + threadIdx.x);
         }
     }
     if (threadIdx.x == 0) {
@@ -1176,14 +1212,29 @@ __global__ __launch_bounds__(kBlock) void k_tsel_hist(float* __restrict__ res, c
             const uint32_t kz = w.key_z[g], c = w.tile_cnt[rt.t];
             const int64_t rb = rt.t * w.tstride;
             const int32_t A = tile_base(goff, gtile, g, rt.t);
-            for (uint32_t j0 = 0; j0 < c; j0 += kBlock) {  // uniform
-                const uint32_t q = j0 + threadIdx.x;
-                if (q < c) {
-                    const float v = w.reg_val[rb + q];
-                    if (mag_key(v) >= kz) {
-                        const int32_t i = A + (int32_t)w.reg_idx[rb + q];
-                        res[i] = v;
-                        if constexpr (M::on) m.u[i] = w.reg_mom[rb + q];
+            if (w.reg_mask) {  // uniform; wave 0 walks the mask, a word per lane
+                if (threadIdx.x < 64) {
+                    uint64_t mw = w.reg_mask[rt.t * (kTile / 64) + threadIdx.x];
+                    uint32_t q = mask_word_prefix(mw);
+                    for (; mw; mw &= mw - 1, ++q) {
+                        const float v = w.reg_val[rb + q];  // q < c <= tcap: the mask holds c bits
+                        if (mag_key(v) >= kz) {
+                            const int32_t i = A + (int32_t)threadIdx.x * 64 + __builtin_ctzll(mw);
+                            res[i] = v;
+                            if constexpr (M::on) m.u[i] = w.reg_mom[rb + q];
+                        }
+                    }
+                }
+            } else {
+                for (uint32_t j0 = 0; j0 < c; j0 += kBlock) {  // uniform
+                    const uint32_t q = j0 + threadIdx.x;
+                    if (q < c) {
+                        const float v = w.reg_val[rb + q];
+                        if (mag_key(v) >= kz) {
+                            const int32_t i = A + (int32_t)w.reg_idx[rb + q];
+                            res[i] = v;
+                            if constexpr (M::on) m.u[i] = w.reg_mom[rb + q];
+                        }
                     }
                 }
             }
@@ -1620,14 +1671,34 @@ __global__ __launch_bounds__(kBlock) void k_tile_write_wave(float* __restrict__ 
 {
     constexpr int U = 8;  // entries per lane per step
     __shared__ uint32_t tmp32[kBlock / 64 + 1];
+    extern __shared__ uint16_t s_offs[];  // mask mode: tcap offsets per wave
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * (kBlock / 64) + wave;
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    int64_t g = 0;
+    int32_t gm = kGNone;
+    uint32_t cnt = 0;
     if (t < NT) {  // uniform per wave
-        const int64_t g = tile_group(gtile, G, t);
-        const int32_t gm = w.gmode[g];
-        const uint32_t cnt = w.tile_cnt[t];
-        if ((gm == kGWindow || gm == kGWide) && cnt <= w.tcap) {
+        g = tile_group(gtile, G, t);
+        gm = w.gmode[g];
+        cnt = w.tile_cnt[t];
+    }
+    const bool work = t < NT && (gm == kGWindow || gm == kGWide) && cnt <= w.tcap;  // uniform per wave
+    const bool mm = w.reg_mask != nullptr;                                           // uniform
+    uint16_t* const so = s_offs + (int64_t)wave * w.tcap;
+    if (mm) {
+        // every wave turns its tile's mask into the region's offsets in LDS
+        // (a word per lane; an empty mask where the wave has no tile), then
+        // the one barrier of the kernel before phase B
+        uint64_t mw = work ? w.reg_mask[t * (kTile / 64) + lane] : 0ull;
+        uint32_t q = mask_word_prefix(mw);
+        for (; mw; mw &= mw - 1, ++q)
+            if (q < w.tcap) so[q] = (uint16_t)(lane * 64 + __builtin_ctzll(mw));
+        __syncthreads();
+    }
+    if (work) {
+        {
             const uint32_t T = w.rank[g] > 0 ? w.prefix[g] : kNoKey;
             const int64_t quota = w.rank[g] > 0 ? w.mrem[g] : 0;
             const uint32_t khi = w.key_hi[g], kz = w.key_z[g];
@@ -1642,8 +1713,9 @@ __global__ __launch_bounds__(kBlock) void k_tile_write_wave(float* __restrict__ 
                 float v[U], um[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int64_t at = rb + min(j0 + u * 64 + lane, cnt - 1);
-                    id[u] = A + (int32_t)w.reg_idx[at];
+                    const uint32_t jj = min(j0 + u * 64 + lane, cnt - 1);
+                    const int64_t at = rb + jj;
+                    id[u] = A + (int32_t)(mm ? so[jj] : w.reg_idx[at]);
                     v[u] = w.reg_val[at];
                     um[u] = M::on ? w.reg_mom[at] : 0.0f;
                 }
@@ -1937,7 +2009,8 @@ static int run_impl(const CompressCall& a, M m)
         // items per thread per round: 4 (more workgroups resident) where
         // regions are small, 8 (fewer rounds) where they are large
         if (z.tcap >= kWaveWriteCap)
-            k_tile_write_wave<M><<<(unsigned)cdiv(gr.ntiles, kBlock / 64), kBlock, 0, s>>>(
+            k_tile_write_wave<M><<<(unsigned)cdiv(gr.ntiles, kBlock / 64), kBlock,
+                                   w.reg_mask ? (size_t)(kBlock / 64) * z.tcap * sizeof(uint16_t) : 0, s>>>(
                 residual, gr.off, gr.tile, G, gr.ntiles, w, out_idx, out_val, cap, m);
         else if (z.tcap <= 256)
             k_tile_write<4, M><<<tb, kBlock, 0, s>>>(residual, gr.off, gr.tile, G, gr.ntiles, w, out_idx, out_val,
