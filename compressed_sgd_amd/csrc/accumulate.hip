@@ -722,13 +722,22 @@ static void launch_decode(int colw, dim3 grid, const Batch& B, int32_t nseg, hip
 // message with more than kPre * group-size entries in it, or more than
 // kRound in all) is applied from memory instead, in rounds of kRound entries
 // taken in message order.
-constexpr int kMergeThreads = 256;                          // threads per merge workgroup
-constexpr int kTileRun = 4;                                 // consecutive tiles a workgroup takes in a row
-constexpr int kPre = 8;                                     // entries per thread per tile (or round)
-constexpr int kRound = kPre * kMergeThreads;                // entries per round
-constexpr int kQ = (int)(kOutTile / (4 * kMergeThreads));  // 16-byte words per thread in a tile
-constexpr int kMaskWords = (int)(kOutTile / 2) / kMergeThreads;  // mask words each thread clears
+constexpr int kTileRun = 4;  // consecutive tiles a workgroup takes in a row
+constexpr int kPre = 8;      // entries per thread per tile (or round)
 static_assert(kMerge <= 16, "message masks are 16 bits");
+// The merge runs with NT threads per workgroup: 256, or 512 for sparse
+// batches (few entries per tile: more waves per CU keep the output stream
+// busy, 16 x 0.1% onto zeros 0.96 -> 0.86 ms; at 16 x 1% 512 threads were
+// slower, 1.55 -> 1.69 ms).
+constexpr int kMergeSparseEntries = 256;  // entries per tile (by capacity) up to which the batch is sparse
+template <int NT>
+struct MergeShape {
+    static constexpr int kRound = kPre * NT;                    // entries per round
+    static constexpr int kQ = (int)(kOutTile / (4 * NT));       // 16-byte words per thread in a tile
+    static constexpr int kMaskWords = (int)(kOutTile / 2) / NT;  // mask words each thread clears
+    static_assert(kMaskWords % 4 == 0, "mask clear in 16-byte words");
+    static_assert((int64_t)kQ * 4 * NT == kOutTile, "a tile is whole 16-byte words per thread");
+};
 
 struct MergeLds {
     float tile[kOutTile];
@@ -739,6 +748,7 @@ struct MergeLds {
 
 // Wave 0: bookkeeping of the tile with range parity par and slot z: entry
 // total, whether the prefetch holds all its entries, collision depth 1.
+template <int NT>
 __device__ inline void tile_meta(MergeLds& S, int par, int z, int32_t nmsg, int32_t cap_per_msg)
 {
     const int lane = threadIdx.x;
@@ -748,16 +758,17 @@ __device__ inline void tile_meta(MergeLds& S, int par, int z, int32_t nmsg, int3
     const bool over = __any(c > cap_per_msg);
     if (lane == 0) {
         S.total[z] = total;
-        S.fits[z] = !over && total <= kRound;
+        S.fits[z] = !over && total <= MergeShape<NT>::kRound;
         S.maxc[z] = 1;
     }
 }
 
+template <int NT>
 __device__ inline void clear_mask(uint32_t* mask)
 {
-    static_assert(kMaskWords % 4 == 0, "mask clear in 16-byte words");
+    constexpr int MW = MergeShape<NT>::kMaskWords;
 #pragma unroll
-    for (int q = 0; q < kMaskWords / 4; ++q) *(i4v*)&mask[kMaskWords * threadIdx.x + 4 * q] = i4v{0, 0, 0, 0};
+    for (int q = 0; q < MW / 4; ++q) *(i4v*)&mask[MW * threadIdx.x + 4 * q] = i4v{0, 0, 0, 0};
 }
 
 // Step 1: every entry (message k[i], tile position p[i] >= 0) marks its message.
@@ -771,6 +782,7 @@ __device__ inline void mark_entries(uint32_t* mask, const int32_t (&k)[kPre], co
 // Steps 2 and 3, after a barrier that follows the marks.  The mask is
 // cleared after the barrier that ends its reads; the function ends with a
 // barrier after both the last addition and the clear.
+template <int NT>
 __device__ inline void add_entries(MergeLds& S, uint32_t* mask, int z, const int32_t (&k)[kPre],
                                    const int32_t (&p)[kPre], const float (&v)[kPre])
 {
@@ -787,7 +799,7 @@ __device__ inline void add_entries(MergeLds& S, uint32_t* mask, int z, const int
     }
     if (deep > 1) atomicMax(&S.maxc[z], deep);
     __syncthreads();
-    clear_mask(mask);  // every read of the mask is done
+    clear_mask<NT>(mask);  // every read of the mask is done
     const int32_t depth = S.maxc[z];  // uniform
     if (depth == 1) __syncthreads();  // the clear ends before the next marks
     for (int32_t r = 1; r < depth; ++r) {
@@ -802,8 +814,8 @@ __device__ inline void add_entries(MergeLds& S, uint32_t* mask, int z, const int
 // is unconditional.
 __device__ int32_t g_zero_word = 0;
 
-template <bool LOAD>
-__global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t lg_tpm, int32_t init,
+template <bool LOAD, int NT>
+__global__ __launch_bounds__(NT) void k_merge(MergeBatch M, int32_t lg_tpm, int32_t init,
                                                  const float* __restrict__ base, float* __restrict__ out, int64_t n,
                                                  int64_t ntiles, uint32_t* status)
 {
@@ -838,6 +850,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
     // pipeline registers: the next tile's entries (global positions) and initial contents
     int32_t n_pos[kPre];
     float n_val[kPre];
+    constexpr int kQ = MergeShape<NT>::kQ;
+    constexpr int kRound = MergeShape<NT>::kRound;
     f4a ini[kQ];
     // entry-range bounds, clamped to the message's entries (memory safety
     // does not depend on the tile table being right).  The table load is
@@ -865,7 +879,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         }
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            const int i = 4 * (q * kMergeThreads + tid);
+            const int i = 4 * (q * NT + tid);
             f4a v = {0.0f, 0.0f, 0.0f, 0.0f};
             if (LOAD) {
                 if (cnt == kOutTile) {
@@ -888,10 +902,10 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         S.a[0][mk] = a0;
         S.cnt[0][mk] = span(a0, e0);
     }
-    clear_mask(S.mask);
+    clear_mask<NT>(S.mask);
     load_tile(tile(0), a0, span(a0, e0));
     __syncthreads();
-    if (tid < 64) tile_meta(S, 0, 0, M.n, kPre * tpm);
+    if (tid < 64) tile_meta<NT>(S, 0, 0, M.n, kPre * tpm);
 
     for (int64_t j = 0; j < J; ++j) {
         const int64_t u = tile(j);
@@ -901,7 +915,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         // the previous tile (always whole) leaves LDS for memory; tile u's initial contents enter
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            const int i = 4 * (q * kMergeThreads + tid);
+            const int i = 4 * (q * NT + tid);
             const f4a pt = *(const f4a*)(S.tile + i);
             *(f4a*)(S.tile + i) = ini[q];
             if (j > 0) __builtin_nontemporal_store(pt, (f4a*)(out + tile(j - 1) * kOutTile + i));
@@ -930,19 +944,19 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
         }
         __syncthreads();
         const int32_t total = S.total[z], fits = S.fits[z];  // uniform
-        if (tid < 64 && j + 1 < J) tile_meta(S, b ^ 1, (int)((j + 1) % 3), M.n, kPre * tpm);
+        if (tid < 64 && j + 1 < J) tile_meta<NT>(S, b ^ 1, (int)((j + 1) % 3), M.n, kPre * tpm);
         if (total == 0) {
             // nothing to add (and nothing was marked)
         } else if (fits) {
-            add_entries(S, S.mask, z, ck, cp, cv);
+            add_entries<NT>(S, S.mask, z, ck, cp, cv);
         } else {
             // from memory, kRound entries at a time in message order
-            clear_mask(S.mask);  // drop the marks of the prefetched share
+            clear_mask<NT>(S.mask);  // drop the marks of the prefetched share
             __syncthreads();
             for (int32_t R0 = 0; R0 < total; R0 += kRound) {
 #pragma unroll
                 for (int i = 0; i < kPre; ++i) {
-                    const int32_t e = R0 + tid + i * kMergeThreads;
+                    const int32_t e = R0 + tid + i * NT;
                     cp[i] = -1;
                     ck[i] = 0;
                     cv[i] = 0.0f;
@@ -957,7 +971,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
                 }
                 mark_entries(S.mask, ck, cp);
                 __syncthreads();
-                add_entries(S, S.mask, z, ck, cp, cv);
+                add_entries<NT>(S, S.mask, z, ck, cp, cv);
                 __syncthreads();  // mask cleared, depth read: the next round may start
                 if (tid == 0) S.maxc[z] = 1;
             }
@@ -971,7 +985,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
     const int32_t cnt = (int32_t)min((int64_t)kOutTile, n - lo);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-        const int i = 4 * (q * kMergeThreads + tid);
+        const int i = 4 * (q * NT + tid);
         const f4a r = *(const f4a*)(S.tile + i);
         if (cnt == kOutTile) {
             __builtin_nontemporal_store(r, (f4a*)(out + lo + i));
@@ -988,12 +1002,12 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch M, int32_t l
 using namespace sgc;
 
 // Persistent merge workgroups: as many as are resident at once on the device.
-template <bool LOAD>
+template <bool LOAD, int NT>
 static int64_t merge_blocks()
 {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_merge<LOAD>, kMergeThreads, 0) != hipSuccess || cus <= 0 || per_cu <= 0)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_merge<LOAD, NT>, NT, 0) != hipSuccess || cus <= 0 || per_cu <= 0)
         return 1024;
     return (int64_t)cus * per_cu;
 }
@@ -1118,20 +1132,29 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
             M.tstart[k] = w.tstart;
             M.bad[k] = w.bad;
         }
+        // sparse batch (by the messages' capacities): 512 threads per workgroup
+        int64_t capsum = 0;
+        for (int32_t k = 0; k < M.n; ++k) capsum += msgs[b0 + k].cap;
+        const bool sparse = capsum <= kMergeSparseEntries * ntiles;
+        const int32_t nt = sparse ? 512 : 256;
         // threads per message slot: the workgroup / (message count rounded up to a power of two)
         int32_t lg_tpm = 0;
-        while ((1 << (lg_tpm + 1)) <= kMergeThreads) ++lg_tpm;
-        while (lg_tpm > 0 && (kMergeThreads >> lg_tpm) < M.n) --lg_tpm;
+        while ((1 << (lg_tpm + 1)) <= nt) ++lg_tpm;
+        while (lg_tpm > 0 && (nt >> lg_tpm) < M.n) --lg_tpm;
         const int32_t im = mb == 0 ? init : SGC_INIT_INPLACE;
         const bool load = im != SGC_INIT_ZERO;
-        const int64_t grid = std::max<int64_t>(
-            1, std::min<int64_t>(cdiv(ntiles, kTileRun), load ? merge_blocks<true>() : merge_blocks<false>()));
-        if (load)
-            k_merge<true><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles,
-                                                                   M.n > 0 ? dstatus : nullptr);
+        const int64_t resident = load ? (sparse ? merge_blocks<true, 512>() : merge_blocks<true, 256>())
+                                      : (sparse ? merge_blocks<false, 512>() : merge_blocks<false, 256>());
+        const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(ntiles, kTileRun), resident));
+        uint32_t* st = M.n > 0 ? dstatus : nullptr;
+        if (load && sparse)
+            k_merge<true, 512><<<(unsigned)grid, 512, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles, st);
+        else if (load)
+            k_merge<true, 256><<<(unsigned)grid, 256, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles, st);
+        else if (sparse)
+            k_merge<false, 512><<<(unsigned)grid, 512, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles, st);
         else
-            k_merge<false><<<(unsigned)grid, kMergeThreads, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles,
-                                                                    M.n > 0 ? dstatus : nullptr);
+            k_merge<false, 256><<<(unsigned)grid, 256, 0, s>>>(M, lg_tpm, im, base, out, L->n, ntiles, st);
         SGC_LAUNCH_CHECK();
     }
     return SGC_OK;
