@@ -709,9 +709,10 @@ static void launch_decode(int colw, dim3 grid, const Batch& B, int32_t nseg, hip
 // a message's share of a tile at 1% (82 entries on average) in 16 threads.
 // The output and the initial contents are streamed with non-temporal
 // stores and loads (each is touched once; 3-5% faster than plain ones).
-// The kernel is built twice: without initial contents to load (sums onto
-// zeros) it needs no registers for them and runs three workgroups per CU
-// (the LDS limit); with them, two.
+// The kernel is built with and without initial contents to load: without
+// them (sums onto zeros) it needs no registers for them and runs three
+// workgroups per CU (the LDS limit); with them, two.  Each comes in two
+// workgroup sizes (below).
 //
 // Software pipeline: while tile j of the sequence is worked on, the entries
 // and initial contents of tile j+1 (LOAD only; and the entry-range bounds of
