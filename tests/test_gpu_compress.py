@@ -153,6 +153,29 @@ def test_sure_bound_exceeded_takes_all_candidates(orc):
     assert st & sgc.STATUS_DENSE_PATH
 
 
+def test_dense_and_wide_with_candidate_masks(orc):
+    # Window pipeline at 25% kept, where regions keep candidate masks in place of offsets.
+    # Large values where the probe reads: fewer than k candidates, the group is selected
+    # from the residual, and selection pass 0 first restores acc from the masked regions.
+    # Values 10% smaller there: more than k sure entries, every candidate is searched.
+    n = 1 << 20
+    rng = np.random.default_rng(33)
+    layout = sgc.Layout([n])
+    g = rng.normal(0, 1e-4, n).astype(np.float32)
+    pp = _probe_positions(n)
+    g[pp] = 1.0 + np.arange(pp.size, dtype=np.float32) * 1e-3
+    out, st = check_step(orc, layout, g, np.zeros(n, np.float32), mode=sgc.EXACT, scope=0, ppm=250000,
+                         path=sgc.PATH_WINDOW, what="probe defeated, masks")
+    assert st & sgc.STATUS_DENSE_PATH
+    g = rng.normal(0, 1.0, 1 << 21).astype(np.float32)
+    g[_probe_positions(1 << 21)] *= np.float32(0.9)
+    for scope, sizes in ((0, [1 << 21]), (1, [1 << 20, 1 << 20])):
+        out, st = check_step(orc, sgc.Layout(sizes), g, np.zeros(1 << 21, np.float32), mode=sgc.EXACT, scope=scope,
+                             ppm=250000, path=sgc.PATH_WINDOW, what=f"sure bound exceeded, masks, scope{scope}")
+        if scope == 0:  # per tensor, each group's own probe keeps a window here: parity only
+            assert st & sgc.STATUS_DENSE_PATH
+
+
 def test_sure_bound_exceeded_in_overflowed_tiles(orc):
     # Window pipeline.  Tiny values where the probe reads, ordinary ones everywhere else: every element is a
     # candidate and sure, every region overflows, and the tiles are worked from the residual.
