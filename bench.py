@@ -466,7 +466,7 @@ def receive_rows(sgc, W, torch, dev, stream, layout, reps=3):
             traffic = summary_traffic(RECV_PMC_FILE, RECV_SRCS)
             achieved = alg / (t / 1e3) / 1e9
             rows[f"decode_accumulate_16x{tag}"]["roofline"] = {
-                "kernels": "k_msg_setup, k_msg_decode, k_msg_holes (one batch of 16), k_merge",
+                "kernels": "k_msg_setup, k_msg_decode, k_fill_max, k_fill (one batch of 16), k_merge",
                 "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "alg_bytes_per_call": alg, "traffic": traffic,
                 "traffic_over_alg": None if traffic is None else traffic / alg}

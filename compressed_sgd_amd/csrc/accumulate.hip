@@ -8,16 +8,17 @@
 //
 // GPU design, per batch of messages (blockIdx.y = message):
 //  setup   validate counts / stream tables, entry and chunk prefixes;
-//  gaps    output-tile table entries for stretches no entry reaches;
 //  raw     check that raw positions ascend; resolve 2-bit values;
 //  decode  Rice streams: one thread per 256-code chunk starts from its
 //          chunk-table entry (bit offset, position reached), decodes from
-//          a copy of its words in LDS, writes global positions (and
-//          resolved SBC / 2-bit values), and checks that it ends exactly
-//          where the next chunk's entry says (or at the stream's bit count).
-// Every message then has a sorted position list (its own idx if raw), a
-// value list (its own val if fp32) and, per output tile, the index of its
-// first entry at or beyond the tile.  The merge then gives
+//          a copy of its words in LDS, writes positions (and resolved SBC
+//          / 2-bit values), and checks that it ends exactly where the next
+//          chunk's entry says (or at the stream's bit count);
+//  fill    the output-tile table from the marks the two passes above left.
+// Every message then has a sorted list of 16-bit positions (each less its
+// output tile's first element), a value list (its own val if fp32) and,
+// per output tile, the index of its first entry at or beyond the tile.
+// The merge then gives
 // each output tile to one workgroup: the initial tile and every message's
 // entries for it are loaded in parallel, each thread applies the messages
 // in order to the elements it owns (no atomics), and the tile is stored
@@ -33,6 +34,8 @@ typedef int32_t i4v __attribute__((ext_vector_type(4)));
 
 constexpr int kBatch = 16;    // messages per decode launch
 constexpr int kMerge = 16;    // messages per merge launch
+constexpr int kFillPer = 16;  // output tiles per thread in the tile-table fill
+constexpr int64_t kFillTiles = (int64_t)kBlock * kFillPer;
 
 struct MsgWs {
     int64_t* estart;  // [nseg+1] entry prefix per segment
@@ -41,7 +44,8 @@ struct MsgWs {
     int64_t* sbase;   // [S] first element of each stream
     int64_t* ssize;   // [S]
     int64_t* chpre;   // [S+1] chunk prefix
-    int32_t* pos;     // [cap] decoded global positions
+    uint16_t* pos;    // [cap] decoded positions less their output tile's first element
+    int32_t* bmax;    // [cdiv(ntiles, kFillTiles)] largest tile mark of each block (fill)
     float* val;       // [cap] resolved values
     int32_t* tstart;  // [ntiles+1] first entry at or beyond each output tile
     uint32_t* bad;    // [1]
@@ -70,7 +74,7 @@ struct Batch {
 
 struct MergeBatch {
     int32_t n;
-    const int32_t* pos[kMerge];
+    const uint16_t* pos[kMerge];  // entry positions less their output tile's first element
     const float* val[kMerge];
     const int32_t* tstart[kMerge];
     const uint32_t* bad[kMerge];
@@ -100,16 +104,16 @@ static void carve_msg(Carver& c, const sgc_layout* L, const sgc_message& m, MsgW
     w->sbase = c.take<int64_t>(S);
     w->ssize = c.take<int64_t>(S);
     w->chpre = c.take<int64_t>(S + 1);
-    w->pos = c.take<int32_t>(m.cap);
+    w->pos = c.take<uint16_t>(m.cap);
     w->val = c.take<float>(m.cap);
     w->tstart = c.take<int32_t>(out_tiles(L) + 1);
+    w->bmax = c.take<int32_t>(cdiv(out_tiles(L), kFillTiles));
     w->bad = c.take<uint32_t>(1);
     w->total = c.take<int64_t>(1);
 }
 
 // ------------------------------------------------------------------ setup
-// Every thread marks output tiles as not yet known (-1: k_msg_holes fills
-// what the entry pass leaves); workgroup 0 of each message checks its
+// Every thread clears the output-tile marks (-1: no mark); workgroup 0 of each message checks its
 // tables, one thread per segment / stream in rounds (workgroup scans for the
 // prefixes, an OR over the workgroup for the verdict).  A message that fails
 // any check is skipped whole: its stream tables are cleared.
@@ -199,33 +203,20 @@ __global__ __launch_bounds__(kBlock) void k_msg_setup(Batch B, const int64_t* __
 }
 
 // ---------------------------------------------------- entries, tile table
-// After decoding, every message is a list of ascending global positions
-// (its own idx if raw, the decoded positions otherwise).  The output-tile
+// After decoding, every message is a list of ascending positions, each
+// stored less its output tile's first element in 16 bits.  The output-tile
 // table holds, per tile, the first entry at or beyond the tile's first
-// element.  Raw messages: one thread per entry checks the order (raw input
-// is not trusted), resolves raw 2-bit values, and writes the table for the
-// tiles whose first element lies after the previous entry and at or before
-// this one -- all of them when there are at most kGapTiles, else only the
-// last.  Coded messages: the decoder writes the table as it goes (at most
-// two tiles per entry).  The remaining tiles (long gaps, and those after the
-// last entry) are found by a binary search per tile.
-constexpr int64_t kGapTiles = 16;
-
-__device__ inline int64_t lower_bound_pos(const int32_t* pos, int64_t total, int64_t x)
-{
-    int64_t lo = 0, hi = total;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if ((int64_t)pos[mid] < x) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
-__device__ inline const int32_t* msg_positions(const MsgIn& in, const MsgWs& w)
-{
-    return in.format >= SGC_MSG_GOLOMB_F32 ? w.pos : in.idx;
-}
-
+// element.  It is built as marks and a prefix maximum: an entry j whose
+// tile lies past the previous entry's marks the tile after the previous
+// entry's (every tile from there up to j's own has j as its first entry),
+// and a stream's last entry marks the tile after its own with the entry
+// count so far (a lower bound when the next stream starts in the same tile;
+// marks on one tile are kept by their maximum).  Marks grow with the tile
+// (entries ascend), so each tile's value is the largest mark at or before
+// it; tiles before any mark take 0.  Raw messages: one thread per entry
+// checks the order (raw input is not trusted), stores the 16-bit position,
+// resolves raw 2-bit values and writes its mark.  Coded messages: the
+// decoder writes the marks as it goes.
 constexpr int kEntPer = 8;  // entries per thread per round, loads all in flight
 
 __global__ __launch_bounds__(kBlock) void k_msg_entries(Batch B, int32_t nseg, int64_t n, int64_t ntiles)
@@ -233,7 +224,7 @@ __global__ __launch_bounds__(kBlock) void k_msg_entries(Batch B, int32_t nseg, i
     const int m = blockIdx.y;
     const MsgIn& in = B.in[m];
     const MsgWs& w = B.ws[m];
-    if (in.format >= SGC_MSG_GOLOMB_F32 || w.bad[0]) return;  // the decoder writes the table of a coded message
+    if (in.format >= SGC_MSG_GOLOMB_F32 || w.bad[0]) return;  // the decoder writes the marks of a coded message
     const int64_t total = w.total[0];
     const int32_t* pos = in.idx;
     bool bad = false;
@@ -263,26 +254,100 @@ __global__ __launch_bounds__(kBlock) void k_msg_entries(Batch B, int32_t nseg, i
                 if (code == 3u) bad = true;
                 w.val[j] = code == 0u ? 0.0f : code == 1u ? in.means[2 * t] : in.means[2 * t + 1];
             }
+            w.pos[j] = (uint16_t)(p & (kOutTile - 1));
             const int64_t t1 = p >> kOutTileLog, t0 = prev < 0 ? 0 : (prev >> kOutTileLog) + 1;
-            for (int64_t t = max(t0, t1 - kGapTiles + 1); t <= t1; ++t) w.tstart[t] = (int32_t)j;
-            if (j == total - 1)
-                for (int64_t t = t1 + 1; t < min(ntiles, t1 + 1 + kGapTiles); ++t) w.tstart[t] = (int32_t)total;
+            if (t0 <= t1) w.tstart[t0] = (int32_t)j;
+            if (j == total - 1 && t1 + 1 < ntiles) w.tstart[t1 + 1] = (int32_t)total;
         }
     }
     if (bad) atomicOr(w.bad, 1u);
 }
 
-// Tiles the entry pass left unset (still negative): binary search.
-__global__ __launch_bounds__(kBlock) void k_msg_holes(Batch B, int64_t ntiles)
+// The prefix maximum over the marks, in blocks of kFillTiles tiles: the
+// largest mark of each block first, then every block's running maximum
+// from the blocks before it.
+
+__global__ __launch_bounds__(kBlock) void k_fill_max(Batch B, int64_t ntiles)
 {
-    const int m = blockIdx.y;
-    const MsgIn& in = B.in[m];
-    const MsgWs& w = B.ws[m];
+    __shared__ int32_t red[kBlock / 64];
+    const MsgWs& w = B.ws[blockIdx.y];
     if (w.bad[0]) return;
-    const int64_t total = w.total[0];
-    const int32_t* pos = msg_positions(in, w);
-    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < ntiles; t += (int64_t)gridDim.x * kBlock)
-        if (w.tstart[t] < 0) w.tstart[t] = (int32_t)lower_bound_pos(pos, total, t << kOutTileLog);
+    const int64_t t0 = (int64_t)blockIdx.x * kFillTiles;
+    int32_t mx = -1;
+#pragma unroll
+    for (int i = 0; i < kFillPer; ++i) {
+        const int64_t t = t0 + i * kBlock + threadIdx.x;
+        mx = max(mx, t < ntiles ? w.tstart[t] : -1);
+    }
+    for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int v = 1; v < kBlock / 64; ++v) mx = max(mx, red[v]);
+        w.bmax[blockIdx.x] = mx;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_fill(Batch B, int64_t ntiles)
+{
+    __shared__ int32_t wmax[kBlock / 64];
+    const MsgWs& w = B.ws[blockIdx.y];
+    if (w.bad[0]) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the blocks before this one (a few dozen at most)
+    int32_t carry = -1;
+    for (int64_t q = threadIdx.x; q < (int64_t)blockIdx.x; q += kBlock) carry = max(carry, w.bmax[q]);
+    for (int d = 32; d >= 1; d >>= 1) carry = max(carry, __shfl_xor(carry, d, 64));
+    if (lane == 0) wmax[wave] = carry;
+    __syncthreads();
+    carry = -1;
+    for (int v = 0; v < kBlock / 64; ++v) carry = max(carry, wmax[v]);
+    __syncthreads();  // wmax is rewritten below
+    // this block: kFillPer consecutive tiles per thread
+    const int64_t t0 = (int64_t)blockIdx.x * kFillTiles + (int64_t)threadIdx.x * kFillPer;
+    const bool whole = t0 + kFillPer <= ntiles;  // 16-byte loads and stores (the table is 256-byte aligned)
+    int32_t v[kFillPer];
+    if (whole) {
+#pragma unroll
+        for (int i = 0; i < kFillPer; i += 4) {
+            const i4v x = *(const i4v*)(w.tstart + t0 + i);
+            v[i] = x[0];
+            v[i + 1] = x[1];
+            v[i + 2] = x[2];
+            v[i + 3] = x[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kFillPer; ++i) v[i] = t0 + i < ntiles ? w.tstart[t0 + i] : -1;
+    }
+    int32_t run = -1;
+#pragma unroll
+    for (int i = 0; i < kFillPer; ++i) {
+        run = max(run, v[i]);
+        v[i] = run;
+    }
+    // exclusive maximum of the threads before this one
+    int32_t x = run;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x = max(x, y);
+    }
+    if (lane == 63) wmax[wave] = x;
+    __syncthreads();
+    int32_t before = carry;
+    for (int u = 0; u < wave; ++u) before = max(before, wmax[u]);
+    const int32_t up = __shfl_up(x, 1, 64);
+    if (lane > 0) before = max(before, up);
+#pragma unroll
+    for (int i = 0; i < kFillPer; ++i) v[i] = max(max(v[i], before), 0);
+    if (whole) {
+#pragma unroll
+        for (int i = 0; i < kFillPer; i += 4) *(i4v*)(w.tstart + t0 + i) = i4v{v[i], v[i + 1], v[i + 2], v[i + 3]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < kFillPer; ++i)
+            if (t0 + i < ntiles) w.tstart[t0 + i] = v[i];
+    }
 }
 
 // --------------------------------------------------------- Rice decoding
@@ -387,7 +452,7 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
     float m0 = 0.0f, m1 = 0.0f;
     int32_t t = J.t, tend = J.tend;
     if (FMT != SGC_MSG_GOLOMB_F32) seg_means<FMT>(in, t, &m0, &m1);
-    const bool vec = (J.j0 & 3) == 0;
+    const bool vec = (J.j0 & 7) == 0;  // 16-byte aligned stores of 8 positions
     // output tile of the previous entry (before a stream's first entry: of the
     // stream's origin minus one; arithmetic shift, so -1 stays -1)
     int32_t tp = (J.base + (int32_t)prev) >> kOutTileLog;
@@ -423,16 +488,11 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
             const uint32_t pu = prev + 1 + z;  // below 2^32 unless already in error
             err |= act && pu >= (uint32_t)J.size;
             // output-tile table: an entry in a later tile than the entry before
-            // it starts its tile, and the one before that when the gap spans
-            // it; every other tile is left to the binary search.  Global
-            // positions are below 2^31.  A corrupt chunk may mark wrongly: its
-            // message is dropped whole.
+            // it marks the tile after that entry's.  Global positions are below
+            // 2^31.  A corrupt chunk may mark wrongly: its message is dropped
+            // whole.
             const int32_t t1 = (int32_t)(J.base + pu) >> kOutTileLog;
-            if (__builtin_expect(act && !err && t1 != tp, 0)) {
-                const int32_t j = J.j0 + i0 + q;
-                J.tstart[t1] = j;
-                if (t1 - tp >= 2) J.tstart[t1 - 1] = j;
-            }
+            if (__builtin_expect(act && !err && t1 != tp, 0)) J.tstart[tp + 1] = J.j0 + i0 + q;
             if (act) {
                 rel += len;
                 prev = pu;
@@ -451,7 +511,7 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
         const bool err0 = err;
         bool slow = false;
         uint32_t marks = 0;
-        int32_t t1s[4], tps[4];
+        int32_t tps[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint32_t win = src.win(min(rel, last_rd));
@@ -464,7 +524,6 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
             const int32_t t1 = (int32_t)(J.base + pu) >> kOutTileLog;
             marks |= (!err && t1 != tp) ? 1u << q : 0u;
             tps[q] = tp;
-            t1s[q] = t1;
             rel += len;
             prev = pu;
             tp = t1;
@@ -483,11 +542,7 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
         if (__builtin_expect(__any(marks != 0u), 0)) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if ((marks >> q) & 1u) {
-                    const int32_t j = J.j0 + i0 + q;
-                    J.tstart[t1s[q]] = j;
-                    if (t1s[q] - tps[q] >= 2) J.tstart[t1s[q] - 1] = j;
-                }
+                if ((marks >> q) & 1u) J.tstart[tps[q] + 1] = J.j0 + i0 + q;
         }
     };
     // codes i0 .. i0+3: positions to pb (stored by the caller), then the
@@ -528,33 +583,39 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
             }
         }
     };
+    // positions are stored less their output tile's first element, in 16
+    // bits (the merge knows each entry's tile from the tile table)
+    constexpr int32_t kOff = (int32_t)kOutTile - 1;
+    auto pair = [](int32_t a, int32_t b) -> int32_t { return (a & kOff) | ((b & kOff) << 16); };
     auto store4 = [&](int32_t i0, const int32_t (&pb)[4], auto full) __attribute__((always_inline)) {
         constexpr bool kFull = decltype(full)::value;
         const int32_t jb = J.j0 + i0;
         if (kFull && vec) {
-            *(i4v*)(w.pos + jb) = i4v{pb[0], pb[1], pb[2], pb[3]};
+            *(int2*)(w.pos + jb) = int2{pair(pb[0], pb[1]), pair(pb[2], pb[3])};
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (kFull || i0 + q < J.nc) w.pos[jb + q] = pb[q];
+                if (kFull || i0 + q < J.nc) w.pos[jb + q] = (uint16_t)(pb[q] & kOff);
         }
     };
     int32_t i0 = 0;
     int32_t pb[4];
-    // whole blocks of 32 codes: the positions stay in registers and leave as
+    // whole blocks of 64 codes: the positions stay in registers and leave as
     // eight back-to-back 16-byte stores, one whole 128-byte cache line (every
     // lane writes its own chunk, so stores in 16-byte pieces left partly
     // written lines: 2.4 times the position bytes reached memory)
     if (vec) {
-        for (; i0 + 32 <= J.nc; i0 += 32) {
+        for (; i0 + 64 <= J.nc; i0 += 64) {
             i4v buf[8];
 #pragma unroll
             for (int g = 0; g < 8; ++g) {
-                group(i0 + 4 * g, std::true_type{}, pb);
-                buf[g] = i4v{pb[0], pb[1], pb[2], pb[3]};
+                group(i0 + 8 * g, std::true_type{}, pb);
+                const int32_t lo0 = pair(pb[0], pb[1]), lo1 = pair(pb[2], pb[3]);
+                group(i0 + 8 * g + 4, std::true_type{}, pb);
+                buf[g] = i4v{lo0, lo1, pair(pb[0], pb[1]), pair(pb[2], pb[3])};
             }
 #pragma unroll
-            for (int g = 0; g < 8; ++g) *(i4v*)(w.pos + J.j0 + i0 + 4 * g) = buf[g];
+            for (int g = 0; g < 8; ++g) *(i4v*)(w.pos + J.j0 + i0 + 8 * g) = buf[g];
         }
     }
     for (; i0 + 4 <= J.nc; i0 += 4) {
@@ -571,7 +632,8 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
 }
 
 template <int FMT, int COLW>
-__device__ __forceinline__ void decode_lanes(const MsgIn& in, const MsgWs& w, int32_t nseg, uint32_t* col, uint32_t* ccol)
+__device__ __forceinline__ void decode_lanes(const MsgIn& in, const MsgWs& w, int32_t nseg, int64_t ntiles, uint32_t* col,
+                                             uint32_t* ccol)
 {
     const int lane = threadIdx.x;
     const int64_t nch = w.chpre[in.S];
@@ -644,6 +706,13 @@ __device__ __forceinline__ void decode_lanes(const MsgIn& in, const MsgWs& w, in
             if (rel_end != J.relend || in.chunk_off[2 * (c + 1) + 1] != (uint64_t)(prev_end + 1)) bad = true;
         } else if (rel_end != J.relend) {
             bad = true;  // bits left over
+        } else if (J.nc > 0) {
+            // the stream's last entry marks the tile after its own with the
+            // entry count so far.  A later stream may still have entries in
+            // that entry's tile, so this count is only a lower bound, and
+            // other streams may mark the same tile: the largest mark is right.
+            const int64_t te = (((int64_t)J.base + prev_end) >> kOutTileLog) + 1;
+            if (te < ntiles) atomicMax(w.tstart + te, J.j0 + J.nc);
         }
     }
     if (bad) atomicOr(w.bad, 1u);
@@ -653,7 +722,7 @@ __device__ __forceinline__ void decode_lanes(const MsgIn& in, const MsgWs& w, in
 // code words get a column of their own).  LDS per workgroup is what limits
 // how many decoding waves a CU holds.
 template <int COLW, bool CODES>
-__global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg)
+__global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg, int64_t ntiles)
 {
     __shared__ uint32_t col[COLW * kDecLanes];
     __shared__ uint32_t ccol[(CODES ? kColCodes : 1) * kDecLanes];
@@ -662,21 +731,22 @@ __global__ __launch_bounds__(kDecLanes) void k_msg_decode(Batch B, int32_t nseg)
     const MsgWs& w = B.ws[m];
     if (w.bad[0]) return;
     switch (in.format) {
-    case SGC_MSG_GOLOMB_F32: decode_lanes<SGC_MSG_GOLOMB_F32, COLW>(in, w, nseg, col, ccol); break;
-    case SGC_MSG_GOLOMB_SBC: decode_lanes<SGC_MSG_GOLOMB_SBC, COLW>(in, w, nseg, col, ccol); break;
+    case SGC_MSG_GOLOMB_F32: decode_lanes<SGC_MSG_GOLOMB_F32, COLW>(in, w, nseg, ntiles, col, ccol); break;
+    case SGC_MSG_GOLOMB_SBC: decode_lanes<SGC_MSG_GOLOMB_SBC, COLW>(in, w, nseg, ntiles, col, ccol); break;
     case SGC_MSG_GOLOMB_2BIT:
-        if constexpr (CODES) decode_lanes<SGC_MSG_GOLOMB_2BIT, COLW>(in, w, nseg, col, ccol);
+        if constexpr (CODES) decode_lanes<SGC_MSG_GOLOMB_2BIT, COLW>(in, w, nseg, ntiles, col, ccol);
         break;
     default: break;
     }
 }
 
 template <bool CODES>
-static void launch_decode(int colw, dim3 grid, const Batch& B, int32_t nseg, hipStream_t s)
+static void launch_decode(int colw, dim3 grid, const Batch& B, int32_t nseg, int64_t ntiles, hipStream_t s)
 {
-    if (colw == col_words_for(6)) k_msg_decode<col_words_for(6), CODES><<<grid, kDecLanes, 0, s>>>(B, nseg);
-    else if (colw == col_words_for(9)) k_msg_decode<col_words_for(9), CODES><<<grid, kDecLanes, 0, s>>>(B, nseg);
-    else k_msg_decode<kColWords, CODES><<<grid, kDecLanes, 0, s>>>(B, nseg);
+    if (colw == col_words_for(6)) k_msg_decode<col_words_for(6), CODES><<<grid, kDecLanes, 0, s>>>(B, nseg, ntiles);
+    else if (colw == col_words_for(9))
+        k_msg_decode<col_words_for(9), CODES><<<grid, kDecLanes, 0, s>>>(B, nseg, ntiles);
+    else k_msg_decode<kColWords, CODES><<<grid, kDecLanes, 0, s>>>(B, nseg, ntiles);
 }
 
 // ------------------------------------------------------------------ merge
@@ -831,7 +901,7 @@ __global__ __launch_bounds__(NT) void k_merge(MergeBatch M, int32_t lg_tpm, int3
         const bool bad = tid < M.n && *M.bad[tid] != 0u;
         if (__ballot(bad) != 0ull && tid == 0) *status |= SGC_STATUS_CORRUPT;
     }
-    const int32_t* posk = live ? M.pos[mk] : nullptr;
+    const uint16_t* posk = live ? M.pos[mk] : nullptr;
     const float* valk = live ? M.val[mk] : nullptr;
     const int32_t* tsk = live ? M.tstart[mk] : nullptr;
     const float* src = init == SGC_INIT_BASE ? base : out;
@@ -848,7 +918,7 @@ __global__ __launch_bounds__(NT) void k_merge(MergeBatch M, int32_t lg_tpm, int3
         return ((int64_t)blockIdx.x + (j / kTileRun) * G) * kTileRun + (j % kTileRun);
     };
 
-    // pipeline registers: the next tile's entries (global positions) and initial contents
+    // pipeline registers: the next tile's entries (positions in the tile, -1 for none) and initial contents
     int32_t n_pos[kPre];
     float n_val[kPre];
     constexpr int kQ = MergeShape<NT>::kQ;
@@ -927,8 +997,7 @@ __global__ __launch_bounds__(NT) void k_merge(MergeBatch M, int32_t lg_tpm, int3
 #pragma unroll
         for (int i = 0; i < kPre; ++i) {
             ck[i] = mk;
-            const int32_t q = n_pos[i] - (int32_t)lo;
-            cp[i] = (n_pos[i] >= 0 && (uint32_t)q < (uint32_t)cnt) ? q : -1;  // always inside, for a clean message
+            cp[i] = (uint32_t)n_pos[i] < (uint32_t)cnt ? n_pos[i] : -1;  // always inside, for a clean message
             cv[i] = n_val[i];
         }
         mark_entries(S.mask, ck, cp);
@@ -965,7 +1034,7 @@ __global__ __launch_bounds__(NT) void k_merge(MergeBatch M, int32_t lg_tpm, int3
                     int32_t k = 0, off = 0;
                     while (e >= off + S.cnt[b][k]) off += S.cnt[b][k++];
                     const int32_t j = S.a[b][k] + (e - off);
-                    const int32_t q = M.pos[k][j] - (int32_t)lo;
+                    const int32_t q = M.pos[k][j];
                     ck[i] = k;
                     cp[i] = (uint32_t)q < (uint32_t)cnt ? q : -1;
                     cv[i] = M.val[k][j];
@@ -1107,8 +1176,8 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         k_msg_setup<<<gtile, kBlock, 0, s>>>(B, dt->seg_off, L->nseg, ntiles);
         SGC_LAUNCH_CHECK();
         const dim3 gch((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxch, kDecLanes), 16384)), (unsigned)B.n);
-        if (any_2bit) launch_decode<true>(colw, gch, B, L->nseg, s);
-        else launch_decode<false>(colw, gch, B, L->nseg, s);
+        if (any_2bit) launch_decode<true>(colw, gch, B, L->nseg, ntiles, s);
+        else launch_decode<false>(colw, gch, B, L->nseg, ntiles, s);
         SGC_LAUNCH_CHECK();
         if (any_raw) {
             const dim3 gent((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(maxcap, kBlock * kEntPer), 4096)),
@@ -1116,7 +1185,10 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
             k_msg_entries<<<gent, kBlock, 0, s>>>(B, L->nseg, L->n, ntiles);
             SGC_LAUNCH_CHECK();
         }
-        k_msg_holes<<<gtile, kBlock, 0, s>>>(B, ntiles);
+        const dim3 gfill((unsigned)cdiv(ntiles, kFillTiles), (unsigned)B.n);
+        k_fill_max<<<gfill, kBlock, 0, s>>>(B, ntiles);
+        SGC_LAUNCH_CHECK();
+        k_fill<<<gfill, kBlock, 0, s>>>(B, ntiles);
         SGC_LAUNCH_CHECK();
     }
     // merge in fixed message order; later batches continue in place
@@ -1128,7 +1200,7 @@ extern "C" int sgc_decode_accumulate(const sgc_layout* Lc, const sgc_message* ms
         for (int32_t k = 0; k < M.n; ++k) {
             const MsgWs& w = mws[(size_t)(b0 + k)];
             const sgc_message& mg = msgs[b0 + k];
-            M.pos[k] = is_golomb(mg.format) ? w.pos : mg.idx;
+            M.pos[k] = w.pos;
             M.val[k] = (mg.format == SGC_MSG_RAW_F32 || mg.format == SGC_MSG_GOLOMB_F32) ? mg.val : w.val;
             M.tstart[k] = w.tstart;
             M.bad[k] = w.bad;
