@@ -510,25 +510,37 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
         const int32_t tp0 = tp;
         const bool err0 = err;
         bool slow = false;
-        uint32_t marks = 0;
+        uint32_t marks = 0, top = 0;
         int32_t tps[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint32_t win = src.win(min(rel, last_rd));
             const uint32_t ones = __builtin_ctzg(~win, 32);
-            const uint32_t len = ones + 1 + b;
-            const uint32_t z = (ones << b) | ((win >> min(ones, 31u) >> 1) & mask);
+            const uint32_t run = ones + 1;  // the unary run and its stop bit
+            const uint32_t len = run + b;
+            // the low bits follow the stop bit; run & 31 is the shift the
+            // hardware takes anyway, and only ever differs from run for a
+            // 32-bit run: then b = 0 and there are no low bits, or the code
+            // is long and the group is redone carefully
+            const uint32_t z = (ones << b) | ((win >> (run & 31u)) & mask);
             slow |= len > 32;
             const uint32_t pu = prev + 1 + z;
-            err |= pu >= (uint32_t)J.size;
+            top = max(top, pu);
             const int32_t t1 = (int32_t)(J.base + pu) >> kOutTileLog;
-            marks |= (!err && t1 != tp) ? 1u << q : 0u;
+            marks |= t1 != tp ? 1u << q : 0u;
             tps[q] = tp;
             rel += len;
             prev = pu;
             tp = t1;
             pb[q] = (int32_t)((uint32_t)J.base + prev);
         }
+        // One check for the group: with codes of at most 32 bits each gap is
+        // below 2^31, so the first position at or past the stream's size is
+        // formed without wrapping (every one before it is below the size) and
+        // the largest of the four is at or past it too.  A corrupt chunk
+        // writes no marks (its message is dropped whole).
+        err |= top >= (uint32_t)J.size;
+        if (err) marks = 0;
         if (__builtin_expect(__any(slow), 0)) {
             if (slow) {
                 rel = rel0;
