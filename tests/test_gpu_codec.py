@@ -220,6 +220,43 @@ def test_corrupt_message_is_skipped(orc):
     assert_bitwise(host(out2), ref2, "non-ascending raw skipped")
 
 
+def test_positions_past_stream_size_in_whole_group_are_corrupt(orc):
+    # A Rice stream written for a 50,100-element tensor, decoded as a
+    # 50,000-element one: 600 codes, only the last four (codes 596..599, the
+    # last whole group of four in the last 256-code chunk) lie past the
+    # stream's size.  No later chunk-table entry and no partial group follows
+    # them, and the bit count is consistent, so only the decoder's check on a
+    # whole group's positions can reject the message.  It must be skipped,
+    # with the corrupt status, and the other message summed exactly.
+    rng = np.random.default_rng(79)
+    n = 50000
+    layout = sgc.Layout([n])
+    gm, om = make_messages(orc, layout, rng, ["golomb_f32"])
+    head = np.sort(rng.choice(n - 100, size=596, replace=False)).astype(np.int32)
+    tail = np.array([n + 3, n + 17, n + 40, n + 71], np.int32)
+    idx = np.concatenate([head, tail])
+    total = idx.size
+    counts = np.array([total, total], np.int64)
+    b = 6
+    oenc = orc.encode(idx, counts, np.array([0, n + 100], np.int64), orc.GLOBAL, b)
+    nw = int(oenc.word_off[-1])
+    bound = int(sgc.lib().sgc_encode_word_bound(layout.handle, sgc.GLOBAL, b, total))
+    assert nw <= bound  # the set-up's word check passes
+    enc = sgc.Encoded(dev(oenc.words.view(np.int32)), dev(oenc.word_off.view(np.int64)),
+                      dev(oenc.nbits.view(np.int64)), dev(oenc.chunk_off.view(np.int64)),
+                      torch.zeros(1, dtype=torch.int32, device="cuda"), sgc.GLOBAL, b, total)
+    val = dev(rng.normal(0, 1e-3, total).astype(np.float32))
+    bad = sgc.Message(sgc.MSG_GOLOMB_F32, dev(counts), total, scope=sgc.GLOBAL, b=b, val=val, enc=enc)
+    out = torch.zeros(n, dtype=torch.float32, device="cuda")
+    announce("positions past the stream size in the last whole group")
+    st = sgc.decode_accumulate(layout, [gm[0], bad], out)
+    ref = np.zeros(n, np.float32)
+    assert orc.decode_accumulate([om[0]], np.array(layout.seg_off, np.int64), ref) == 0
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) & sgc.STATUS_CORRUPT
+    assert_bitwise(host(out), ref, "message with positions past its stream skipped")
+
+
 def test_corrupt_per_segment_stream_is_skipped(orc):
     # per-tensor Rice streams over 1500 tensors, one message corrupted at a
     # tensor past the first 1024 (the set-up's later rounds); each corruption
