@@ -119,7 +119,7 @@ def one_message(orc, layout, rng, what, **fixed):
                         enc=oenc))
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(60))
 def test_random_pipeline(orc, seed):
     rng = np.random.default_rng(7000 + seed)
     layout = random_layout(rng)

@@ -34,7 +34,7 @@ def check_sparse(comp, ref, what):
     assert_bitwise(host(comp.val)[:total], ref.val, f"{what} val")
 
 
-@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("seed", range(45))
 def test_random_steps(orc, seed):
     rng = np.random.default_rng(8100 + seed)
     nseg = int(rng.integers(1, 8))
