@@ -552,9 +552,16 @@ __device__ __forceinline__ bool decode_chunk(const Src& src, uint32_t rel, const
             }
         }
         if (__builtin_expect(__any(marks != 0u), 0)) {
+            // the first crossing of the group: every code before it lies in
+            // the tile the group started in, so its mark goes to the tile
+            // after that one -- a single store
+            if (marks != 0u) J.tstart[tp0 + 1] = J.j0 + i0 + __builtin_ctz(marks);
+            marks &= marks - 1u;
+            if (__builtin_expect(__any(marks != 0u), 0)) {  // more than one tile crossed in four codes
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if ((marks >> q) & 1u) J.tstart[tps[q] + 1] = J.j0 + i0 + q;
+                for (int q = 1; q < 4; ++q)
+                    if ((marks >> q) & 1u) J.tstart[tps[q] + 1] = J.j0 + i0 + q;
+            }
         }
     };
     // codes i0 .. i0+3: positions to pb (stored by the caller), then the
